@@ -1,0 +1,185 @@
+"""Float64 CPU oracle for one EM iteration of a Gaussian mixture model.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; the product path never imports it.
+The arithmetic lives in ``gmm_oracle.c`` (plain C, float64, OpenMP over rows);
+this module builds it with gcc and marshals numpy arrays through ctypes.
+
+Sources it follows: "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
+Clustering", Section 2 (E-step score, log-sum-exp responsibilities, M-step
+eqs. 1-3) and Section 4 / Conclusion (multi-assignment by a threshold on the
+final responsibilities); "ML0094 GMM vs K-Means", Mathematical Formulation
+(responsibility-weighted covariance); GMMXX README, Covariance Coverage (the
+four covariance types and their shapes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+COV = {"spherical": 0, "diag": 1, "tied": 2, "full": 3}
+XTYPE = {"f64": 0, "f32": 1, "bf16": 2, "f16": 3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gmm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gmm_oracle.c into liboracle.so with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_estep.argtypes = [i32, i32, i64, i32, i32, P, i32, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_mstep.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P, f64, P, P, P, P]
+        lib.oracle_mstep_twopass.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, f64, P, P, P]
+        lib.oracle_responsibilities.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, P, P, P]
+        lib.oracle_topm.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, i32, f64, P, P, P, P, P, i32]
+        for f in (lib.oracle_estep, lib.oracle_mstep, lib.oracle_mstep_twopass,
+                  lib.oracle_responsibilities, lib.oracle_topm):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _x_and_type(X):
+    """X is float64/float32 ndarray, or a (uint16 ndarray, 'bf16'|'f16') pair."""
+    if isinstance(X, tuple):
+        arr, kind = X
+        arr = np.ascontiguousarray(arr, dtype=np.uint16)
+        return arr, XTYPE[kind]
+    arr = np.ascontiguousarray(X)
+    if arr.dtype == np.float64:
+        return arr, XTYPE["f64"]
+    if arr.dtype == np.float32:
+        return arr, XTYPE["f32"]
+    raise TypeError("oracle input must be float32/float64 or (uint16, 'bf16'|'f16')")
+
+
+def cov_len(cov: str, D: int, K: int) -> int:
+    return {"spherical": K, "diag": K * D, "tied": D * D, "full": K * D * D}[cov]
+
+
+def _params(w, mu, cv, B, K, D, cov):
+    w = np.ascontiguousarray(w, dtype=np.float64).reshape(B, K)
+    mu = np.ascontiguousarray(mu, dtype=np.float64).reshape(B, K, D)
+    cv = np.ascontiguousarray(cv, dtype=np.float64).reshape(B, cov_len(cov, D, K))
+    return w, mu, cv
+
+
+def estep(cov, X, w, mu, cv, nthreads=0):
+    """Sufficient statistics of one E-step.  X shape (B,N,D) or (N,D).
+
+    Returns dict(nk (B,K), sx (B,K,D), sxx (B,len), ll (B) = sum_i log p(x_i),
+    flags (B,K)).  sxx is centred at the means `mu` that entered the step.
+    """
+    Xa, xt = _x_and_type(X)
+    single = Xa.ndim == 2
+    if single:
+        Xa = Xa[None]
+    B, N, D = Xa.shape
+    K = np.asarray(w).reshape(B, -1).shape[1]
+    w, mu, cv = _params(w, mu, cv, B, K, D, cov)
+    nk = np.zeros((B, K))
+    sx = np.zeros((B, K, D))
+    sxx = np.zeros((B, cov_len(cov, D, K)))
+    ll = np.zeros(B)
+    flags = np.zeros((B, K), dtype=np.int32)
+    rc = _load().oracle_estep(COV[cov], B, N, D, K, _ptr(Xa), xt, _ptr(w), _ptr(mu), _ptr(cv),
+                              _ptr(nk), _ptr(sx), _ptr(sxx), _ptr(ll), _ptr(flags), int(nthreads))
+    if rc:
+        raise ValueError("oracle_estep rejected its arguments")
+    return dict(nk=nk, sx=sx, sxx=sxx, ll=ll, flags=flags)
+
+
+def mstep(cov, stats, n, w, mu, cv, eps=1e-6):
+    """Parameters after the M-step.  Returns (w', mu', cv', flags)."""
+    nk = np.ascontiguousarray(stats["nk"], dtype=np.float64)
+    B, K = nk.shape
+    D = stats["sx"].shape[2]
+    w, mu, cv = _params(w, mu, cv, B, K, D, cov)
+    sx = np.ascontiguousarray(stats["sx"], dtype=np.float64)
+    sxx = np.ascontiguousarray(stats["sxx"], dtype=np.float64)
+    wo, mo, co = np.zeros_like(w), np.zeros_like(mu), np.zeros_like(cv)
+    flags = np.zeros((B, K), dtype=np.int32)
+    rc = _load().oracle_mstep(COV[cov], B, int(n), D, K, _ptr(nk), _ptr(sx), _ptr(sxx),
+                              _ptr(w), _ptr(mu), _ptr(cv), float(eps),
+                              _ptr(wo), _ptr(mo), _ptr(co), _ptr(flags))
+    if rc:
+        raise ValueError("oracle_mstep rejected its arguments")
+    return wo, mo, co, flags
+
+
+def mstep_twopass(cov, X, w, mu, cv, eps=1e-6):
+    """Literal two-pass M-step for one problem (cross-check of the identity)."""
+    Xa, xt = _x_and_type(X)
+    N, D = Xa.shape
+    K = np.asarray(w).size
+    w, mu, cv = (a[0] for a in _params(w, mu, cv, 1, K, D, cov))
+    wo, mo, co = np.zeros_like(w), np.zeros_like(mu), np.zeros_like(cv)
+    _load().oracle_mstep_twopass(COV[cov], N, D, K, _ptr(Xa), xt, _ptr(w), _ptr(mu), _ptr(cv),
+                                 float(eps), _ptr(wo), _ptr(mo), _ptr(co))
+    return wo, mo, co
+
+
+def responsibilities(cov, X, w, mu, cv):
+    """(logscore (N,K), r (N,K), lse (N)) for one problem (small N only)."""
+    Xa, xt = _x_and_type(X)
+    N, D = Xa.shape
+    K = np.asarray(w).size
+    w, mu, cv = (a[0] for a in _params(w, mu, cv, 1, K, D, cov))
+    ls, r, lse = np.zeros((N, K)), np.zeros((N, K)), np.zeros(N)
+    _load().oracle_responsibilities(COV[cov], N, D, K, _ptr(Xa), xt, _ptr(w), _ptr(mu), _ptr(cv),
+                                    _ptr(ls), _ptr(r), _ptr(lse))
+    return ls, r, lse
+
+
+def topm(cov, X, w, mu, cv, m, thr, nthreads=0):
+    """Soft multi-assignment for one problem: (idx, resp, count, logp, margin)."""
+    Xa, xt = _x_and_type(X)
+    N, D = Xa.shape
+    K = np.asarray(w).size
+    w, mu, cv = (a[0] for a in _params(w, mu, cv, 1, K, D, cov))
+    idx = np.zeros((N, m), dtype=np.int32)
+    resp = np.zeros((N, m))
+    count = np.zeros(N, dtype=np.int32)
+    logp = np.zeros(N)
+    margin = np.zeros(N)
+    rc = _load().oracle_topm(COV[cov], N, D, K, _ptr(Xa), xt, _ptr(w), _ptr(mu), _ptr(cv),
+                             int(m), float(thr), _ptr(idx), _ptr(resp), _ptr(count), _ptr(logp),
+                             _ptr(margin), int(nthreads))
+    if rc:
+        raise ValueError("oracle_topm rejected its arguments")
+    return idx, resp, count, logp, margin
+
+
+def fit_step(cov, X, w, mu, cv, eps=1e-6, nthreads=0):
+    """One EM iteration theta_t -> theta_{t+1} (float64), with the mean LL of theta_t."""
+    Xa, _ = _x_and_type(X)
+    n = Xa.shape[-2]
+    st = estep(cov, X, w, mu, cv, nthreads)
+    B = st["nk"].shape[0]
+    wo, mo, co, fl = mstep(cov, st, n, np.asarray(w).reshape(B, -1),
+                           np.asarray(mu).reshape(st["sx"].shape), np.asarray(cv).reshape(st["sxx"].shape), eps)
+    return dict(w=wo, mu=mo, cv=co, mean_ll=st["ll"] / n, stats=st, flags=fl)
