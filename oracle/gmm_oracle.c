@@ -342,8 +342,9 @@ int oracle_mstep(int cov, int B, int64_t n, int D, int K,
           for (int k = 0; k < K; ++k) s -= Nk[k] * delta[(size_t)k * D + d] * delta[(size_t)k * D + e];
           co[d * D + e] = s / (double)n + (d == e ? eps : 0.0);
         }
-      if (cholesky(D, co, L)) {
+      if (cholesky(D, co, L)) {   /* keep the whole previous model */
         memcpy(co, c0, sizeof(double) * (size_t)D * D);
+        memcpy(mo, m0, sizeof(double) * (size_t)K * D);
         if (fl) for (int k = 0; k < K; ++k) fl[k] |= 2;
       }
       continue;
