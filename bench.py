@@ -1,0 +1,177 @@
+"""Benchmark of the fused EM iteration on one MI355X.
+
+A step is one EM iteration (gmm_fit_step: precision prologue, fused E-step
+with statistics, deterministic reduction, M-step) over the whole synthetic
+workload, with the rows already resident in device memory.  The default
+workload is the diagonal-covariance one (N = 1,000,000 rows, D = 64, K = 256,
+float32); the others are available with --workload.
+
+Prints ONE JSON line (rank 0): value = points*components per second
+(B*N*K / time per iteration), plus the roofline of the fused E-step kernel
+(timed with HIP events that the library records around that kernel on the
+stream it runs on) and the float64 CPU oracle timed on the host cores on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("EM iterations/sec and N·K points·components/s per iteration; "
+          "% MFMA or HBM roofline")
+
+# MI355X published dense peaks (TFLOP/s)
+PEAK_FP32_MFMA = 157.3
+PEAK_FP64_MFMA = 78.6
+
+
+def flops_per_pair(cov, D):
+    """Algorithmic flops per (point, component) of the two contractions
+    (2 per multiply-add) plus the N_k sum: logits over F features, statistics
+    over the same F features."""
+    if cov == "spherical":
+        f = D              # x . (lambda mu); |x|^2 term on the VALU
+        return 4 * f + 4   # + |x|^2 coefficient, N_k, sum r|x|^2
+    if cov == "diag":
+        return 8 * D + 2
+    q = D * (D + 1) // 2
+    return 4 * (D + q) + 2
+
+
+def contraction_split(cov, D):
+    """(float32 flops, float64 flops) per pair: logits run on the float32 MFMA,
+    statistics on the float64 MFMA."""
+    total = flops_per_pair(cov, D)
+    half = total // 2
+    return half, total - half
+
+
+def cpu_baseline(wl, budget_s=20.0, max_steps=4):
+    import oracle
+    nthreads = os.cpu_count() or 1
+    X = wl.X if wl.xdtype == "f32" else (wl.X, "bf16")
+    w, mu, cv = (a.astype(np.float64) for a in (wl.w0, wl.mu0, wl.cv0))
+    times = []
+    t_start = time.perf_counter()
+    for _ in range(max_steps):
+        t0 = time.perf_counter()
+        out = oracle.fit_step(wl.cov, X, w, mu, cv, eps=wl.eps, nthreads=nthreads)
+        times.append(time.perf_counter() - t0)
+        w, mu, cv = out["w"], out["mu"], out["cv"]
+        if time.perf_counter() - t_start > budget_s:
+            break
+    t = float(np.median(times))
+    return {"value": wl.B * wl.N * wl.K / t, "unit": "points*components/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{len(times)} float64 EM iterations of the full {wl.name} workload "
+                      f"(B={wl.B}, N={wl.N}, D={wl.D}, K={wl.K}) from theta_0, median "
+                      f"{t:.2f} s/iteration"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="diag_large",
+                    choices=["diag_large", "spherical_small", "diag_batched", "full_large"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (traffic counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import soft_clustering_em_amd as g
+    from soft_clustering_em_amd import synth
+
+    dev = "cuda"
+    torch.cuda.init()
+    wl = synth.WORKLOADS[args.workload]()
+    X = torch.from_numpy(wl.X).to(dev)
+    w = torch.from_numpy(wl.w0.copy()).to(dev)
+    mu = torch.from_numpy(wl.mu0.copy()).to(dev)
+    cv = torch.from_numpy(wl.cv0.copy()).to(dev)
+    mll = torch.zeros(wl.B, dtype=torch.float64, device=dev)
+    ws = torch.empty(g.gmm_workspace_bytes(X, wl.K, wl.cov), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        g.gmm_fit_step(X, w, mu, cv, wl.cov, reg_covar=wl.eps, mean_loglik=mll, ws=ws)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in evs:  # materialise the event handles before handing them to the library
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        g.gmm_fit_step(X, w, mu, cv, wl.cov, reg_covar=wl.eps, mean_loglik=mll, ws=ws, events=evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    k_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
+
+    pairs = wl.B * wl.N * wl.K
+    f32f, f64f = contraction_split(wl.cov, wl.D)
+    flops = pairs * (f32f + f64f)
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    peak = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
+    res = {
+        "metric": METRIC,
+        "value": pairs / step_s,
+        "unit": "points*components/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "iters_per_sec": 1.0 / step_s,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "cov": wl.cov, "B": wl.B, "N": wl.N, "D": wl.D, "K": wl.K,
+                   "iters_per_fit": wl.iters},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "kernel": "fused E-step + statistics",
+            "kernel_ms": k_ms,
+            "flops_per_launch": flops,
+            "peak_note": (f"float32 MFMA logits ({f32f} flop/pair at {PEAK_FP32_MFMA} TF) + float64 MFMA "
+                          f"statistics ({f64f} flop/pair at {PEAK_FP64_MFMA} TF), time-weighted"),
+        },
+        "mean_loglik_last": float(mll.mean().item()),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * gmm.h -- C ABI of the MI355X (gfx950) fused EM library for Gaussian mixture
+ * models.
+ *
+ * The method: one EM iteration for a mixture of K Gaussians, as described in
+ * "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft Clustering",
+ * Section 2 (E-step score pi_k N(x_i | mu_k, Sigma_k), responsibilities r_ik
+ * normalised in log space with log-sum-exp, M-step eqs. 1-3: N_k, pi_k = N_k/N,
+ * mu_k = sum_i r_ik x_i / N_k, updated variance) and Section 3 (the N x K
+ * responsibility matrix is never written to device memory: each tile of rows
+ * folds its responsibilities straight into O(K D) sufficient statistics).
+ * Covariance types and parameter shapes follow the GMMXX README, "Covariance
+ * Coverage"; soft multi-assignment follows Flash-GMM Section 4 / Conclusion
+ * (a threshold on the final responsibilities).
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller, except the
+ *     descriptor structs themselves, which live in host memory and are read
+ *     during the call only.
+ *   - The library allocates no device memory.  Scratch space is the caller's
+ *     workspace `ws` of `ws_bytes` bytes (256-byte aligned), sized with
+ *     gmm_workspace_bytes(); for the fit / statistics calls its size does not
+ *     grow with N once N exceeds a few hundred thousand rows per problem.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued asynchronously on it; nothing synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     status other than GMM_OK means nothing was enqueued;
+ *     gmm_last_error() then returns a message for the calling thread.
+ *   - Numerical events are reported per component in `comp_status` (B,K)
+ *     int32 (nullable), never as call failures:
+ *        1  N_k == 0 after the E-step: mu_k and Sigma_k kept, pi_k = 0;
+ *        2  the updated full/tied covariance is not positive definite: the
+ *           previous mu_k and Sigma_k are kept;
+ *        4  the input full/tied covariance is not positive definite: the
+ *           component gets zero responsibility in this E-step.
+ *   - Results are deterministic: no atomics; every reduction runs in a fixed
+ *     order for a given shape.
+ *   - Calls on distinct streams with distinct workspaces may run concurrently.
+ */
+#ifndef GMM_H
+#define GMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GMM_COV_SPHERICAL = 0, /* Sigma_k = sigma_k^2 I; covars (B,K)            */
+  GMM_COV_DIAG = 1,      /* Sigma_k = diag(sigma_k^2); covars (B,K,D)      */
+  GMM_COV_TIED = 2,      /* Sigma_k = Sigma for all k; covars (B,D,D)      */
+  GMM_COV_FULL = 3       /* one full Sigma_k per component; (B,K,D,D)      */
+} gmm_cov_type;
+
+typedef enum {
+  GMM_DT_F32 = 0,  /* IEEE float32 rows                                     */
+  GMM_DT_BF16 = 1, /* bfloat16 rows (arithmetic accumulates in float32)     */
+  GMM_DT_F16 = 2   /* IEEE half rows  (arithmetic accumulates in float32)   */
+} gmm_dtype;
+
+typedef enum {
+  GMM_OK = 0,
+  GMM_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride, ...  */
+  GMM_ERR_UNSUPPORTED = 2, /* valid but outside the supported shape/type window */
+  GMM_ERR_WORKSPACE = 3,   /* ws is NULL, misaligned or smaller than required   */
+  GMM_ERR_HIP = 4          /* a HIP launch or runtime call failed               */
+} gmm_status;
+
+/* Operation selector for gmm_workspace_bytes. */
+enum { GMM_OP_FIT = 0, GMM_OP_ESTEP = 1, GMM_OP_TOPM = 2 };
+
+/* Input rows: problem b, row i, dimension d is element
+ *   x[b * stride_b + i * ld_x + d]   (elements of `dtype`),
+ * with ld_x >= D and stride_b >= N * ld_x (stride_b ignored when B == 1).
+ * x must be 16-byte aligned and ld_x * sizeof(element) a multiple of 16 bytes
+ * for the vectorised loads; other layouts return GMM_ERR_UNSUPPORTED. */
+typedef struct {
+  const void* x;
+  int32_t dtype;  /* gmm_dtype */
+  int64_t B, N, D;
+  int64_t ld_x, stride_b;
+} gmm_data;
+
+/* Mixture parameters theta, float32, row-major:
+ *   weights (B,K); means (B,K,D);
+ *   covars  spherical (B,K) | diag (B,K,D) | tied (B,D,D) | full (B,K,D,D). */
+typedef struct {
+  int32_t K;
+  int32_t cov;  /* gmm_cov_type */
+  float* weights;
+  float* means;
+  float* covars;
+} gmm_params;
+
+/* Sufficient statistics of one E-step, float64, device:
+ *   nk (B,K)      N_k = sum_i r_ik                        (Flash-GMM eq. 1)
+ *   sx (B,K,D)    sum_i r_ik x_i                           (numerator of eq. 2)
+ *   sxx           sum_i r_ik (x_i - mu_k)(x_i - mu_k)^T about the means that
+ *                 entered the E-step: spherical (B,K) trace form
+ *                 sum_i r_ik |x_i - mu_k|^2; diag (B,K,D) diagonal;
+ *                 full (B,K,D,D); tied (B,D,D) summed over k
+ *   loglik (B)    sum_i log p(x_i) under the parameters that entered the step */
+typedef struct {
+  double* nk;
+  double* sx;
+  double* sxx;
+  double* loglik;
+} gmm_stats;
+
+/* Options.  reg_covar is added to every variance / covariance diagonal after
+ * the update (the covariance floor; 1e-6 is the usual value).  flags must be 0.
+ * event_begin / event_end: optional hipEvent_t handles; when non-NULL they are
+ * recorded on `stream` immediately before and after the fused E-step kernel,
+ * so a caller can time that kernel alone. */
+typedef struct {
+  double reg_covar;
+  uint32_t flags;
+  void* event_begin;
+  void* event_end;
+} gmm_options;
+
+/* Bytes of workspace needed by an operation on `data` with K components of
+ * type `cov` (op: GMM_OP_FIT / GMM_OP_ESTEP / GMM_OP_TOPM; m: the top-m width,
+ * ignored otherwise).  Returns 0 when the arguments are invalid or the shape is
+ * unsupported (the compute call then reports why).  Host-only; no HIP call. */
+size_t gmm_workspace_bytes(const gmm_data* data, int32_t K, int32_t cov, int32_t op, int32_t m);
+
+/* E-step with statistics (Flash-GMM Section 2; the fused, R-free form of
+ * Section 3).  Computes the statistics of `data` under `params` and writes
+ * them to `out`, or adds them to `out` when accumulate != 0 (chunked
+ * streaming: call once per chunk of rows with the same params, then
+ * gmm_mstep with n_total = all rows).  The sxx centre is params->means. */
+gmm_status gmm_estep_stats(const gmm_data* data, const gmm_params* params, gmm_stats* out,
+                           int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* M-step (Flash-GMM Section 2, eqs. 1-3, extended to diag/tied/full as in
+ * "ML0094 GMM vs K-Means", Mathematical Formulation) from statistics `st` of
+ * B problems of dimension D over n_total rows each.  `inout` holds on entry
+ * the parameters the statistics were computed with and receives theta':
+ *   pi_k = N_k / n_total;  mu'_k = sx_k / N_k;  delta_k = mu'_k - mu_k;
+ *   spherical  var' = (sxx_k / N_k - |delta_k|^2) / D + reg_covar
+ *   diag       var'_d = sxx_kd / N_k - delta_kd^2 + reg_covar
+ *   full       Sigma'_k = sxx_k / N_k - delta_k delta_k^T + reg_covar I
+ *   tied       Sigma' = (sxx - sum_k N_k delta_k delta_k^T) / n_total + reg_covar I
+ * comp_status (B,K) int32, nullable.  opts may be NULL (reg_covar = 1e-6). */
+gmm_status gmm_mstep(int64_t B, int64_t D, const gmm_stats* st, int64_t n_total, gmm_params* inout,
+                     const gmm_options* opts, int32_t* comp_status, void* stream);
+
+/* One EM iteration (E-step statistics + M-step) in place on `inout`.
+ * mean_loglik (B) float64 device, nullable: (1/N) sum_i log p(x_i) under the
+ * parameters that ENTERED the step.  comp_status nullable. */
+gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_options* opts,
+                        double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Soft multi-assignment (Flash-GMM Section 4 / Conclusion): for every row,
+ * components ordered by decreasing responsibility (ties: lower index first);
+ * the first is always kept, ranks 2..m are kept while r >= threshold.
+ *   idx   (B,N,m) int32, -1 padded      resp (B,N,m) float32, 0 padded
+ *   count (B,N) int32, nullable          logp (B,N) float32 = log p(x_i), nullable
+ * The ranking and the kept responsibilities are decided in float64 for every
+ * component whose single-precision score lies within a safety band of the
+ * best one.  1 <= m <= 16. */
+gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m,
+                                  float threshold, int32_t* idx, float* resp, int32_t* count,
+                                  float* logp, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gmm_status_str(int32_t status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* gmm_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMM_H */

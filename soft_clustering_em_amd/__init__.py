@@ -1,1 +1,145 @@
-"""MI355X-native fused EM for Gaussian mixture models (placeholder until the binding lands)."""
+"""MI355X-native fused EM for Gaussian mixture models.
+
+Python names mirror the C ABI of include/gmm.h.  They take torch tensors that
+live on the GPU, fill the descriptor structs and call libgmm.so on the current
+torch stream; every step of the computation runs in the HIP kernels.
+
+  gmm_workspace_bytes(X, K, cov, op)          -> int
+  gmm_estep_stats(X, w, mu, cv, stats, accumulate=False, ws=None)
+  gmm_mstep(stats, n_total, w, mu, cv, reg_covar=1e-6, comp_status=None)
+  gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
+  gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
+
+X is (N, D) or (B, N, D) with unit stride along D; w (B,K), mu (B,K,D) and the
+covariance parameters are float32 and are updated in place by the M-step.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+from ._abi import (COV_CODES, GmmError, GmmData, GmmOptions, GmmParams, GmmStats, OP_ESTEP, OP_FIT,
+                   OP_TOPM)
+
+__all__ = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
+           "gmm_predict_proba_topm", "new_stats", "GmmError", "cov_shape"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    return {torch.float32: _abi.DT_F32, torch.bfloat16: _abi.DT_BF16, torch.float16: _abi.DT_F16}[t.dtype]
+
+
+def _data(X) -> GmmData:
+    if X.dim() == 2:
+        B, (N, D) = 1, X.shape
+        ld, sb = X.stride(0), N * X.stride(0)
+    elif X.dim() == 3:
+        B, N, D = X.shape
+        ld, sb = X.stride(1), X.stride(0)
+    else:
+        raise ValueError("X must be (N, D) or (B, N, D)")
+    if D > 0 and N > 0 and X.stride(-1) != 1:
+        raise ValueError("X needs unit stride along D")
+    return GmmData(ctypes.c_void_p(X.data_ptr()), _dtype_code(X), B, N, D, ld, sb)
+
+
+def _cov_code(cov):
+    return COV_CODES[cov] if isinstance(cov, str) else int(cov)
+
+
+def cov_shape(cov, B, K, D):
+    return {"spherical": (B, K), "diag": (B, K, D), "tied": (B, D, D), "full": (B, K, D, D)}[cov]
+
+
+def _params(w, mu, cv, cov) -> GmmParams:
+    for t in (w, mu, cv):
+        if not t.is_contiguous():
+            raise ValueError("parameter tensors must be contiguous")
+    K = w.shape[-1]
+    return GmmParams(K, _cov_code(cov), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(mu.data_ptr()),
+                     ctypes.c_void_p(cv.data_ptr()))
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def gmm_workspace_bytes(X, K, cov, op=OP_FIT, m=0) -> int:
+    d = _data(X)
+    return int(_abi.lib().gmm_workspace_bytes(ctypes.byref(d), int(K), _cov_code(cov), int(op), int(m)))
+
+
+def _workspace(X, K, cov, op, m, ws):
+    if ws is not None:
+        return ws
+    torch = _torch()
+    n = gmm_workspace_bytes(X, K, cov, op, m)
+    if n == 0:
+        # let the compute call report the precise reason
+        return torch.empty(256, dtype=torch.uint8, device=X.device)
+    return torch.empty(n, dtype=torch.uint8, device=X.device)
+
+
+def new_stats(B, K, D, cov, device):
+    """Zeroed float64 statistics buffers (nk, sx, sxx, loglik) for gmm_estep_stats."""
+    torch = _torch()
+    return dict(nk=torch.zeros(B, K, dtype=torch.float64, device=device),
+                sx=torch.zeros(B, K, D, dtype=torch.float64, device=device),
+                sxx=torch.zeros(cov_shape(cov, B, K, D), dtype=torch.float64, device=device),
+                loglik=torch.zeros(B, dtype=torch.float64, device=device))
+
+
+def gmm_estep_stats(X, w, mu, cv, cov, stats, accumulate=False, ws=None, stream=None):
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    st = GmmStats(_ptr(stats["nk"]), _ptr(stats["sx"]), _ptr(stats["sxx"]), _ptr(stats["loglik"]))
+    ws = _workspace(X, p.K, cov, OP_ESTEP, 0, ws)
+    _abi.check(_abi.lib().gmm_estep_stats(ctypes.byref(d), ctypes.byref(p), ctypes.byref(st),
+                                          int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream)))
+    return stats
+
+
+def gmm_mstep(stats, n_total, w, mu, cv, cov, reg_covar=1e-6, comp_status=None, stream=None):
+    B, K, D = stats["sx"].shape
+    p = _params(w, mu, cv, cov)
+    st = GmmStats(_ptr(stats["nk"]), _ptr(stats["sx"]), _ptr(stats["sxx"]), _ptr(stats["loglik"]))
+    o = GmmOptions(float(reg_covar), 0, None, None)
+    _abi.check(_abi.lib().gmm_mstep(B, D, ctypes.byref(st), int(n_total), ctypes.byref(p), ctypes.byref(o),
+                                    _ptr(comp_status), _stream(stream)))
+
+
+def gmm_fit_step(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None,
+                 stream=None, events=None):
+    """One EM iteration in place.  events: optional (begin, end) torch.cuda.Event
+    pair recorded around the fused E-step kernel."""
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    eb = ee = None
+    if events is not None:
+        eb, ee = (ctypes.c_void_p(e.cuda_event) for e in events)
+    o = GmmOptions(float(reg_covar), 0, eb, ee)
+    ws = _workspace(X, p.K, cov, OP_FIT, 0, ws)
+    _abi.check(_abi.lib().gmm_fit_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o), _ptr(mean_loglik),
+                                       _ptr(comp_status), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gmm_predict_proba_topm(X, w, mu, cv, cov, m, threshold, idx, resp, count=None, logp=None, ws=None,
+                           stream=None):
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    ws = _workspace(X, p.K, cov, OP_TOPM, m, ws)
+    _abi.check(_abi.lib().gmm_predict_proba_topm(ctypes.byref(d), ctypes.byref(p), int(m), float(threshold),
+                                                 _ptr(idx), _ptr(resp), _ptr(count), _ptr(logp), _ptr(ws),
+                                                 ws.numel(), _stream(stream)))

@@ -1,0 +1,309 @@
+// gmm_api.hip -- the C ABI declared in include/gmm.h: argument validation,
+// the launch plan (tiling, workgroup count, workspace layout) and the kernel
+// sequence of each entry point.
+#include "gmm.h"
+#include "gmm_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+namespace gmm {
+
+static thread_local std::string g_err;
+
+static gmm_status fail(gmm_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static gmm_status fail(gmm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+static size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+static int64_t cov_len(int cov, int64_t D, int64_t K) {
+  switch (cov) {
+    case SPH: return K;
+    case DIAG: return K * D;
+    case TIED: return D * D;
+    default: return K * D * D;
+  }
+}
+
+static gmm_status check_data(const gmm_data* d) {
+  if (!d) return fail(GMM_ERR_INVALID_ARG, "data descriptor is NULL");
+  if (d->B < 1 || d->N < 0 || d->D < 1)
+    return fail(GMM_ERR_INVALID_ARG, "need B >= 1, N >= 0, D >= 1 (got B=%lld N=%lld D=%lld)", (long long)d->B,
+                (long long)d->N, (long long)d->D);
+  if (d->ld_x < d->D) return fail(GMM_ERR_INVALID_ARG, "ld_x (%lld) < D (%lld)", (long long)d->ld_x, (long long)d->D);
+  if (d->B > 1 && d->stride_b < d->N * d->ld_x)
+    return fail(GMM_ERR_INVALID_ARG, "stride_b (%lld) < N*ld_x", (long long)d->stride_b);
+  if (d->N > 0 && !d->x) return fail(GMM_ERR_INVALID_ARG, "x is NULL");
+  if (d->dtype != GMM_DT_F32 && d->dtype != GMM_DT_BF16 && d->dtype != GMM_DT_F16)
+    return fail(GMM_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->dtype != GMM_DT_F32)
+    return fail(GMM_ERR_UNSUPPORTED, "this entry point supports float32 rows only");
+  if (d->N > ((int64_t)1 << 40)) return fail(GMM_ERR_UNSUPPORTED, "N too large");
+  return GMM_OK;
+}
+
+static gmm_status check_params(const gmm_params* p, int64_t B, int64_t D, bool need_ptrs) {
+  if (!p) return fail(GMM_ERR_INVALID_ARG, "params descriptor is NULL");
+  if (p->K < 1) return fail(GMM_ERR_INVALID_ARG, "K must be >= 1 (got %d)", p->K);
+  if (p->cov < SPH || p->cov > FULL) return fail(GMM_ERR_INVALID_ARG, "unknown covariance type %d", p->cov);
+  if (need_ptrs && (!p->weights || !p->means || !p->covars))
+    return fail(GMM_ERR_INVALID_ARG, "weights/means/covars must be non-NULL");
+  (void)B;
+  (void)D;
+  return GMM_OK;
+}
+
+// Choose the tiling of the fused kernel and lay out the workspace.
+static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) {
+  gmm_status st = check_data(d);
+  if (st != GMM_OK) return st;
+  if (K < 1) return fail(GMM_ERR_INVALID_ARG, "K must be >= 1");
+  if (cov < SPH || cov > FULL) return fail(GMM_ERR_INVALID_ARG, "unknown covariance type %d", cov);
+  if (op == GMM_OP_TOPM) return fail(GMM_ERR_UNSUPPORTED, "top-m is not available for this shape");
+  Plan q;
+  q.cov = cov;
+  q.dtype = d->dtype;
+  q.B = d->B;
+  q.N = d->N;
+  q.D = d->D;
+  q.K = K;
+  q.ld_x = d->ld_x;
+  q.stride_b = d->B > 1 ? d->stride_b : 0;
+  if (cov == SPH || cov == DIAG) {
+    q.DP = d->D <= 16 ? 16 : d->D <= 32 ? 32 : d->D <= 64 ? 64 : d->D <= 128 ? 128 : 0;
+  } else {
+    q.DP = d->D <= 8 ? 8 : d->D <= 16 ? 16 : 0;
+  }
+  if (!q.DP)
+    return fail(GMM_ERR_UNSUPPORTED, "D=%lld is outside the supported window for this covariance type",
+                (long long)d->D);
+  q.F = feat_F(cov, q.DP);
+  q.G = feat_G(cov, q.DP);
+  q.FS = feat_stride(std::max(q.F, q.G));
+  q.PR = 2 + q.G;
+  if ((K + 15) / 16 <= kMaxWaves) {
+    q.KW = 16;
+  } else if ((K + 31) / 32 <= kMaxWaves) {
+    q.KW = 32;
+  } else {
+    return fail(GMM_ERR_UNSUPPORTED, "K=%d is above the single-pass window (<= %d)", K, 32 * kMaxWaves);
+  }
+  q.NW = (K + q.KW - 1) / q.KW;
+  q.KP = q.KW * q.NW;
+  auto lds_for = [&](int T) {
+    // weights, feature tile, |x|^2 (float64), two per-wave row reductions
+    return sizeof(float) * ((size_t)q.KP * q.F + (size_t)T * q.FS + 2 * (size_t)T + 2 * (size_t)q.NW * T);
+  };
+  q.T = 0;
+  for (int T : {64, 32, 16}) {
+    if (lds_for(T) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
+      q.T = T;
+      break;
+    }
+  }
+  if (!q.T) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld does not fit in LDS", K, (long long)d->D);
+  q.lds = lds_for(q.T);
+  q.ntiles = (q.N + q.T - 1) / q.T;
+  const int wg_lds = (int)std::max<size_t>(1, kLdsBytes / q.lds);
+  const int wg_per_cu = std::max(1, std::min(wg_lds, 8 / q.NW));
+  const int64_t total = (int64_t)kNumCU * wg_per_cu;
+  int64_t gb = std::max<int64_t>(1, total / q.B);
+  gb = std::min<int64_t>(gb, std::max<int64_t>(1, q.ntiles));
+  q.Gb = (int)gb;
+  q.vec4 = (((uintptr_t)d->x) % 16 == 0) && (q.ld_x % 4 == 0) && (q.stride_b % 4 == 0);
+  // workspace
+  size_t o = 0;
+  q.off_W = o;    o = align_up(o + sizeof(float) * (size_t)q.B * q.KP * q.F);
+  q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
+  q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
+  q.off_flag = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
+  q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
+  q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
+  q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.PR);
+  if (op == GMM_OP_FIT) {
+    q.off_nk = o;  o = align_up(o + sizeof(double) * (size_t)q.B * K);
+    q.off_sx = o;  o = align_up(o + sizeof(double) * (size_t)q.B * K * q.D);
+    q.off_sxx = o; o = align_up(o + sizeof(double) * (size_t)q.B * cov_len(cov, q.D, K));
+    q.off_ll = o;  o = align_up(o + sizeof(double) * (size_t)q.B);
+  }
+  q.ws_bytes = o;
+  *p = q;
+  return GMM_OK;
+}
+
+static gmm_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(GMM_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws) % kAlign) return fail(GMM_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < p.ws_bytes)
+    return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, p.ws_bytes);
+  return GMM_OK;
+}
+
+static gmm_status hip_fail(hipError_t e, const char* where) {
+  return fail(GMM_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// prologue + fused E-step + reduction; statistics to the given buffers
+static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk, double* sx,
+                            double* sxx, double* ll, double* mean_ll, int accumulate, const gmm_options* opts,
+                            hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  float* W = reinterpret_cast<float*>(w + p.off_W);
+  double* c = reinterpret_cast<double*>(w + p.off_c);
+  double* a = reinterpret_cast<double*>(w + p.off_a);
+  int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
+  double* part = reinterpret_cast<double*>(w + p.off_part);
+  double* llp = reinterpret_cast<double*>(w + p.off_llp);
+  double* raw = reinterpret_cast<double*>(w + p.off_aux);
+  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, W, c, a, flag, s);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  EStepArgs A;
+  A.x = d->x;
+  A.N = p.N;
+  A.D = p.D;
+  A.ld_x = p.ld_x;
+  A.stride_b = p.stride_b;
+  A.K = (int)p.K;
+  A.KP = p.KP;
+  A.NW = p.NW;
+  A.Gb = p.Gb;
+  A.ntiles = p.ntiles;
+  A.vec4 = p.vec4 ? 1 : 0;
+  A.W = W;
+  A.c = c;
+  A.a = a;
+  A.part = part;
+  A.llpart = llp;
+  if (opts && opts->event_begin) {
+    e = hipEventRecord((hipEvent_t)opts->event_begin, s);
+    if (e != hipSuccess) return hip_fail(e, "event record");
+  }
+  e = launch_estep(p, A, s);
+  if (e != hipSuccess) return hip_fail(e, "fused E-step launch");
+  if (opts && opts->event_end) {
+    e = hipEventRecord((hipEvent_t)opts->event_end, s);
+    if (e != hipSuccess) return hip_fail(e, "event record");
+  }
+  e = launch_reduce_raw(p, part, llp, prm->means, raw, nk, sx, sxx, ll, mean_ll, accumulate, s);
+  if (e != hipSuccess) return hip_fail(e, "reduction launch");
+  return GMM_OK;
+}
+
+}  // namespace gmm
+
+using namespace gmm;
+
+extern "C" {
+
+size_t gmm_workspace_bytes(const gmm_data* data, int32_t K, int32_t cov, int32_t op, int32_t m) {
+  (void)m;
+  Plan p;
+  if (make_plan(data, K, cov, op, &p) != GMM_OK) return 0;
+  return p.ws_bytes;
+}
+
+gmm_status gmm_estep_stats(const gmm_data* data, const gmm_params* params, gmm_stats* out, int32_t accumulate,
+                           void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  gmm_status st = check_params(params, 0, 0, true);
+  if (st != GMM_OK) return st;
+  Plan p;
+  st = make_plan(data, params->K, params->cov, GMM_OP_ESTEP, &p);
+  if (st != GMM_OK) return st;
+  if (!out || !out->nk || !out->sx || !out->sxx || !out->loglik)
+    return fail(GMM_ERR_INVALID_ARG, "statistics buffers must be non-NULL");
+  st = check_ws(p, ws, ws_bytes);
+  if (st != GMM_OK) return st;
+  return run_estep(p, data, params, ws, out->nk, out->sx, out->sxx, out->loglik, nullptr, accumulate ? 1 : 0,
+                   nullptr, (hipStream_t)stream);
+}
+
+gmm_status gmm_mstep(int64_t B, int64_t D, const gmm_stats* st_in, int64_t n_total, gmm_params* inout,
+                     const gmm_options* opts, int32_t* comp_status, void* stream) {
+  g_err.clear();
+  gmm_status st = check_params(inout, B, D, true);
+  if (st != GMM_OK) return st;
+  if (B < 1 || D < 1) return fail(GMM_ERR_INVALID_ARG, "need B >= 1 and D >= 1");
+  if (n_total < 1) return fail(GMM_ERR_INVALID_ARG, "n_total must be >= 1");
+  if (!st_in || !st_in->nk || !st_in->sx || !st_in->sxx)
+    return fail(GMM_ERR_INVALID_ARG, "statistics buffers must be non-NULL");
+  if (D > 128) return fail(GMM_ERR_UNSUPPORTED, "D > 128");
+  if ((inout->cov == FULL || inout->cov == TIED) && D > 16)
+    return fail(GMM_ERR_UNSUPPORTED, "full/tied covariance supports D <= 16");
+  if (opts && opts->flags) return fail(GMM_ERR_INVALID_ARG, "options.flags must be 0");
+  const double reg = opts ? opts->reg_covar : 1e-6;
+  if (!(reg >= 0.0)) return fail(GMM_ERR_INVALID_ARG, "reg_covar must be >= 0");
+  hipError_t e = launch_mstep_strided(inout->cov, B, D, inout->K, st_in->nk, st_in->sx, st_in->sxx, n_total,
+                                      inout->weights, inout->means, inout->covars, reg, nullptr, 0, comp_status,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "M-step launch");
+  return GMM_OK;
+}
+
+gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_options* opts, double* mean_loglik,
+                        int32_t* comp_status, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  gmm_status st = check_params(inout, 0, 0, true);
+  if (st != GMM_OK) return st;
+  Plan p;
+  st = make_plan(data, inout->K, inout->cov, GMM_OP_FIT, &p);
+  if (st != GMM_OK) return st;
+  if (p.N < 1) return fail(GMM_ERR_INVALID_ARG, "a fit step needs N >= 1");
+  if (opts && opts->flags) return fail(GMM_ERR_INVALID_ARG, "options.flags must be 0");
+  const double reg = opts ? opts->reg_covar : 1e-6;
+  if (!(reg >= 0.0)) return fail(GMM_ERR_INVALID_ARG, "reg_covar must be >= 0");
+  st = check_ws(p, ws, ws_bytes);
+  if (st != GMM_OK) return st;
+  char* w = static_cast<char*>(ws);
+  double* nk = reinterpret_cast<double*>(w + p.off_nk);
+  double* sx = reinterpret_cast<double*>(w + p.off_sx);
+  double* sxx = reinterpret_cast<double*>(w + p.off_sxx);
+  double* ll = reinterpret_cast<double*>(w + p.off_ll);
+  hipStream_t s = (hipStream_t)stream;
+  st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s);
+  if (st != GMM_OK) return st;
+  const int32_t* flag = reinterpret_cast<const int32_t*>(w + p.off_flag);
+  hipError_t e = launch_mstep_strided(p.cov, p.B, p.D, p.K, nk, sx, sxx, p.N, inout->weights, inout->means,
+                                      inout->covars, reg, flag, p.KP, comp_status, s);
+  if (e != hipSuccess) return hip_fail(e, "M-step launch");
+  return GMM_OK;
+}
+
+gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
+                                  int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  (void)data; (void)params; (void)m; (void)threshold; (void)idx; (void)resp; (void)count; (void)logp;
+  (void)ws; (void)ws_bytes; (void)stream;
+  g_err.clear();
+  return fail(GMM_ERR_UNSUPPORTED, "top-m is not available yet");
+}
+
+const char* gmm_status_str(int32_t status) {
+  switch (status) {
+    case GMM_OK: return "ok";
+    case GMM_ERR_INVALID_ARG: return "invalid argument";
+    case GMM_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case GMM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GMM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* gmm_last_error(void) { return g_err.c_str(); }
+
+int32_t gmm_version(void) { return 100; }
+
+}  // extern "C"

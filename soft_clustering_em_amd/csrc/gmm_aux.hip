@@ -1,0 +1,416 @@
+// gmm_aux.hip -- the small kernels around the fused E-step:
+//   prologue : theta -> logit weights W (fragment order) and constants c
+//   reduce   : fixed-order float64 sum of the workgroup partials, converted to
+//              statistics centred at the input means
+//   mstep    : the M-step on O(K D) data
+//
+// The log-score of component k (Flash-GMM, Section 2: the unnormalised score
+// pi_k N(x | mu_k, Sigma_k), taken in log space) is written as a linear
+// function of a feature vector phi(x) plus a constant:
+//   log pi_k N(x|mu_k,Sigma_k) = log pi_k - 1/2 (D log 2pi + log det Sigma_k
+//                                 + mu^T P mu) + x^T P mu - 1/2 x^T P x,
+// with P = Sigma_k^{-1}.  The prologue evaluates the weights of that linear
+// form in float64 and stores them (times log2 e) as float32.
+#include "gmm_internal.h"
+
+#include <math.h>
+
+namespace gmm {
+
+static constexpr double kLog2e = 1.4426950408889634074;
+static constexpr double kLog2Pi = 1.8378770664093454836;
+
+__device__ __forceinline__ size_t wfrag_index(int k, int f, int KW, int F) {
+  const int w = k / KW, kk = k % KW, nt = kk / 16, col = kk % 16;
+  const int ks = f / 4, kq = ks / 4, j = ks % 4, lane = (f % 4) * 16 + col;
+  const int NT = KW / 16, KQ = F / 16;
+  return ((((size_t)(w * NT + nt) * KQ + kq) * 64 + lane) * 4 + j);
+}
+
+// row-major upper-triangle index of (d, e), d <= e, in a DP x DP matrix
+__device__ __forceinline__ int quad_index(int d, int e, int DP) { return d * DP - d * (d - 1) / 2 + (e - d); }
+
+// Cholesky of the D x D matrix in S (row-major, float64) into L (lower);
+// returns false if S is not positive definite.  Serial, D <= 16.
+__device__ bool chol_serial(int D, const double* S, double* L) {
+  for (int i = 0; i < D * D; ++i) L[i] = 0.0;
+  for (int j = 0; j < D; ++j) {
+    double s = S[j * D + j];
+    for (int p = 0; p < j; ++p) s -= L[j * D + p] * L[j * D + p];
+    if (!(s > 0.0)) return false;
+    const double l = sqrt(s);
+    L[j * D + j] = l;
+    for (int i = j + 1; i < D; ++i) {
+      double t = S[i * D + j];
+      for (int p = 0; p < j; ++p) t -= L[i * D + p] * L[j * D + p];
+      L[i * D + j] = t / l;
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ prologue
+// grid: B*KP blocks of 64 threads; block (b, k).
+__global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int KP, int DP, int F, int KW,
+                                                      const float* __restrict__ w, const float* __restrict__ mu,
+                                                      const float* __restrict__ cv, float* __restrict__ W,
+                                                      double* __restrict__ c, double* __restrict__ a,
+                                                      int32_t* __restrict__ flag) {
+  const int b = blockIdx.x / KP, k = blockIdx.x % KP, tid = threadIdx.x;
+  float* Wb = W + (size_t)b * KP * F;
+  __shared__ double sm_mu[128];
+  __shared__ double sm_v[128];                // diag precisions / P mu
+  __shared__ double sm_S[16 * 16], sm_L[16 * 16], sm_Li[16 * 16], sm_P[16 * 16];
+  __shared__ double sm_c;
+  __shared__ int sm_ok;
+
+  if (k >= K) {  // padding component: never responsible
+    for (int f = tid; f < F; f += blockDim.x) Wb[wfrag_index(k, f, KW, F)] = 0.f;
+    if (tid == 0) {
+      c[(size_t)b * KP + k] = -INFINITY;
+      a[(size_t)b * KP + k] = 0.0;
+      flag[(size_t)b * KP + k] = 0;
+    }
+    return;
+  }
+  for (int d = tid; d < D; d += blockDim.x) sm_mu[d] = (double)mu[((size_t)b * K + k) * D + d];
+  const double logpi = log((double)w[(size_t)b * K + k]);
+  __syncthreads();
+
+  if (cov == SPH || cov == DIAG) {
+    // precisions lambda_d (spherical: one value)
+    for (int d = tid; d < D; d += blockDim.x)
+      sm_v[d] = (cov == SPH) ? 1.0 / (double)cv[(size_t)b * K + k] : 1.0 / (double)cv[((size_t)b * K + k) * D + d];
+    __syncthreads();
+    if (tid == 0) {
+      bool ok = true;
+      double logdet = 0.0, quad = 0.0;
+      for (int d = 0; d < D; ++d) {
+        const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
+        if (!(v > 0.0) || isinf(v)) ok = false;
+        logdet += log(v);
+        quad += sm_v[d] * sm_mu[d] * sm_mu[d];
+      }
+      sm_ok = ok;
+      sm_c = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e : -INFINITY;
+    }
+    __syncthreads();
+    const bool ok = sm_ok;
+    for (int f = tid; f < F; f += blockDim.x) {
+      double val = 0.0;
+      if (ok) {
+        if (f < DP) {
+          if (f < D) val = sm_v[f] * sm_mu[f] * kLog2e;
+        } else if (cov == DIAG && f - DP < D) {
+          val = -0.5 * sm_v[f - DP] * kLog2e;
+        }
+      }
+      Wb[wfrag_index(k, f, KW, F)] = (float)val;
+    }
+    if (tid == 0) {
+      c[(size_t)b * KP + k] = sm_c;
+      a[(size_t)b * KP + k] = (cov == SPH && ok) ? -0.5 * sm_v[0] * kLog2e : 0.0;
+      flag[(size_t)b * KP + k] = ok ? 0 : 4;
+    }
+    return;
+  }
+
+  // full / tied: P = Sigma^{-1} through the Cholesky factor Sigma = L L^T
+  const float* S = (cov == FULL) ? cv + ((size_t)b * K + k) * D * D : cv + (size_t)b * D * D;
+  for (int i = tid; i < D * D; i += blockDim.x) sm_S[i] = (double)S[i];
+  __syncthreads();
+  if (tid == 0) sm_ok = chol_serial(D, sm_S, sm_L);
+  __syncthreads();
+  const bool ok = sm_ok;
+  if (ok) {
+    // column j of L^{-1}: forward substitution on e_j
+    if (tid < D) {
+      const int j = tid;
+      for (int i = 0; i < D; ++i) {
+        double t = (i == j) ? 1.0 : 0.0;
+        for (int p = j; p < i; ++p) t -= sm_L[i * D + p] * sm_Li[p * D + j];
+        sm_Li[i * D + j] = (i < j) ? 0.0 : t / sm_L[i * D + i];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < D * D; i += blockDim.x) {
+      const int d = i / D, e = i % D;
+      double s = 0.0;
+      for (int p = 0; p < D; ++p) s += sm_Li[p * D + d] * sm_Li[p * D + e];
+      sm_P[i] = s;
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += blockDim.x) {
+      double s = 0.0;
+      for (int e = 0; e < D; ++e) s += sm_P[d * D + e] * sm_mu[e];
+      sm_v[d] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double logdet = 0.0, quad = 0.0;
+      for (int d = 0; d < D; ++d) {
+        logdet += 2.0 * log(sm_L[d * D + d]);
+        quad += sm_mu[d] * sm_v[d];
+      }
+      sm_c = (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e;
+    }
+  }
+  __syncthreads();
+  for (int f = tid; f < F; f += blockDim.x) {
+    double val = 0.0;
+    if (ok) {
+      if (f < DP) {
+        if (f < D) val = sm_v[f] * kLog2e;
+      } else if (f - DP < quad_count(DP)) {
+        // invert the upper-triangle index
+        int q = f - DP, d = 0, base = 0;
+        while (q >= base + (DP - d)) { base += DP - d; ++d; }
+        const int e = d + (q - base);
+        if (d < D && e < D) val = (d == e ? -0.5 : -1.0) * sm_P[d * D + e] * kLog2e;
+      }
+    }
+    Wb[wfrag_index(k, f, KW, F)] = (float)val;
+  }
+  if (tid == 0) {
+    c[(size_t)b * KP + k] = ok ? sm_c : -INFINITY;
+    a[(size_t)b * KP + k] = 0.0;
+    flag[(size_t)b * KP + k] = ok ? 0 : 4;
+  }
+}
+
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W, double* c,
+                           double* a, int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(p.B * p.KP)), dim3(64), 0, s, p.cov, (int)p.D, (int)p.K,
+                     p.KP, p.DP, p.F, p.KW, w, mu, cv, W, c, a, flag);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ reduce
+// grid: B*K + B blocks.  Block (b, k) sums the Gb partials of component k in
+// workgroup order (float64) into raw[b][k][:], and (non-tied) writes the
+// statistics centred at the input means.  Blocks B*K + b sum the
+// log-likelihood partials.  Tied covariance is centred by centre_tied_kernel.
+__global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int KP, int DP, int PR, int Gb,
+                                                     int64_t N, const double* __restrict__ part,
+                                                     const double* __restrict__ llpart,
+                                                     const float* __restrict__ mu, double* __restrict__ raw,
+                                                     double* nk, double* sx, double* sxx, double* ll,
+                                                     double* mean_ll, int accumulate, int B) {
+  const int tid = threadIdx.x;
+  if ((int64_t)blockIdx.x >= (int64_t)B * K) {
+    const int b = blockIdx.x - B * K;
+    if (tid == 0) {
+      double s = 0.0;
+      for (int g = 0; g < Gb; ++g) s += llpart[(size_t)b * Gb + g];
+      ll[b] = accumulate ? ll[b] + s : s;
+      if (mean_ll) mean_ll[b] = s / (double)N;
+    }
+    return;
+  }
+  const int b = blockIdx.x / K, k = blockIdx.x % K;
+  extern __shared__ double sm[];
+  double* r = sm;            // PR
+  double* m = sm + PR;       // D
+  for (int j = tid; j < PR; j += blockDim.x) {
+    double s = 0.0;
+    const double* src = part + ((size_t)b * Gb * KP + k) * PR + j;
+    for (int g = 0; g < Gb; ++g) s += src[(size_t)g * KP * PR];
+    r[j] = s;
+    raw[((size_t)b * KP + k) * PR + j] = s;
+  }
+  for (int d = tid; d < D; d += blockDim.x) m[d] = (double)mu[((size_t)b * K + k) * D + d];
+  __syncthreads();
+  if (cov == TIED) return;
+  const double n = r[0];
+  const size_t bk = (size_t)b * K + k;
+  if (tid == 0) nk[bk] = accumulate ? nk[bk] + n : n;
+  for (int d = tid; d < D; d += blockDim.x) {
+    const double v = r[2 + d];
+    sx[bk * D + d] = accumulate ? sx[bk * D + d] + v : v;
+  }
+  if (cov == SPH) {
+    if (tid == 0) {
+      double dot = 0.0, mm = 0.0;
+      for (int d = 0; d < D; ++d) {
+        dot += m[d] * r[2 + d];
+        mm += m[d] * m[d];
+      }
+      const double v = r[1] - 2.0 * dot + mm * n;
+      sxx[bk] = accumulate ? sxx[bk] + v : v;
+    }
+  } else if (cov == DIAG) {
+    for (int d = tid; d < D; d += blockDim.x) {
+      const double v = r[2 + DP + d] - 2.0 * m[d] * r[2 + d] + m[d] * m[d] * n;
+      sxx[bk * D + d] = accumulate ? sxx[bk * D + d] + v : v;
+    }
+  } else {  // FULL
+    for (int i = tid; i < D * D; i += blockDim.x) {
+      const int d = i / D, e = i % D;
+      const int q = d <= e ? quad_index(d, e, DP) : quad_index(e, d, DP);
+      const double v = r[2 + DP + q] - m[d] * r[2 + e] - r[2 + d] * m[e] + m[d] * m[e] * n;
+      sxx[bk * D * D + i] = accumulate ? sxx[bk * D * D + i] + v : v;
+    }
+  }
+}
+
+// Tied: sxx = sum_k sum_i r_ik (x_i - mu_k)(x_i - mu_k)^T from the raw sums.
+// grid: B blocks.
+__global__ void __launch_bounds__(256) centre_tied_kernel(int D, int K, int KP, int DP, int PR,
+                                                          const double* __restrict__ raw,
+                                                          const float* __restrict__ mu, double* nk, double* sx,
+                                                          double* sxx, int accumulate) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int k = tid; k < K; k += blockDim.x) {
+    const size_t bk = (size_t)b * K + k;
+    const double v = raw[((size_t)b * KP + k) * PR];
+    nk[bk] = accumulate ? nk[bk] + v : v;
+  }
+  for (int i = tid; i < K * D; i += blockDim.x) {
+    const int k = i / D, d = i % D;
+    const double v = raw[((size_t)b * KP + k) * PR + 2 + d];
+    sx[(size_t)b * K * D + i] = accumulate ? sx[(size_t)b * K * D + i] + v : v;
+  }
+  for (int i = tid; i < D * D; i += blockDim.x) {
+    const int d = i / D, e = i % D;
+    const int q = d <= e ? quad_index(d, e, DP) : quad_index(e, d, DP);
+    double s = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double* r = raw + ((size_t)b * KP + k) * PR;
+      const double md = (double)mu[((size_t)b * K + k) * D + d];
+      const double me = (double)mu[((size_t)b * K + k) * D + e];
+      s += r[2 + DP + q] - md * r[2 + e] - r[2 + d] * me + md * me * r[0];
+    }
+    sxx[(size_t)b * D * D + i] = accumulate ? sxx[(size_t)b * D * D + i] + s : s;
+  }
+}
+
+hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
+                             double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
+                             int accumulate, hipStream_t s) {
+  const size_t lds = sizeof(double) * (size_t)(p.PR + p.D);
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(128), lds, s, p.cov, (int)p.D,
+                     (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
+                     accumulate, (int)p.B);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.cov != TIED) return e;
+  hipLaunchKernelGGL(centre_tied_kernel, dim3((unsigned)p.B), dim3(256), 0, s, (int)p.D, (int)p.K, p.KP, p.DP,
+                     p.PR, raw, mu, nk, sx, sxx, accumulate);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ M-step
+// Flash-GMM Section 2, eqs. 1-3 (pi_k = N_k / n; mu'_k = sx_k / N_k; variance
+// about the new mean, written through the centred statistics), diag / full
+// forms as in "ML0094 GMM vs K-Means", Mathematical Formulation.
+// grid: B*K blocks of 64 threads (spherical, diag, full).
+__global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const double* __restrict__ nk,
+                                                   const double* __restrict__ sx, const double* __restrict__ sxx,
+                                                   int64_t n_total, float* w, float* mu, float* cv, double reg,
+                                                   const int32_t* in_flag, int in_flag_stride,
+                                                   int32_t* comp_status) {
+  const int b = blockIdx.x / K, k = blockIdx.x % K, tid = threadIdx.x;
+  const size_t bk = (size_t)b * K + k;
+  __shared__ double sm_delta[128];
+  __shared__ double sm_S[16 * 16], sm_L[16 * 16];
+  __shared__ int sm_pd;
+  const double n = nk[bk];
+  const bool empty = !(n > 0.0);
+  int32_t st = empty ? 1 : 0;
+  if (in_flag) st |= in_flag[(size_t)b * in_flag_stride + k];
+  if (tid == 0) w[bk] = (float)(n / (double)n_total);
+  if (empty) {
+    if (tid == 0 && comp_status) comp_status[bk] = st;
+    return;  // mu_k and Sigma_k kept
+  }
+  for (int d = tid; d < D; d += blockDim.x) {
+    const double m1 = sx[bk * D + d] / n;
+    sm_delta[d] = m1 - (double)mu[bk * D + d];
+  }
+  __syncthreads();
+  if (cov == SPH) {
+    if (tid == 0) {
+      double dd = 0.0;
+      for (int d = 0; d < D; ++d) dd += sm_delta[d] * sm_delta[d];
+      cv[bk] = (float)((sxx[bk] / n - dd) / (double)D + reg);
+    }
+  } else if (cov == DIAG) {
+    for (int d = tid; d < D; d += blockDim.x)
+      cv[bk * D + d] = (float)(sxx[bk * D + d] / n - sm_delta[d] * sm_delta[d] + reg);
+  } else {  // FULL: check positive definiteness before committing
+    for (int i = tid; i < D * D; i += blockDim.x) {
+      const int d = i / D, e = i % D;
+      sm_S[i] = sxx[bk * D * D + i] / n - sm_delta[d] * sm_delta[e] + (d == e ? reg : 0.0);
+    }
+    __syncthreads();
+    if (tid == 0) sm_pd = chol_serial(D, sm_S, sm_L);
+    __syncthreads();
+    if (!sm_pd) {
+      if (tid == 0 && comp_status) comp_status[bk] = st | 2;
+      return;  // previous mu_k and Sigma_k kept
+    }
+    for (int i = tid; i < D * D; i += blockDim.x) cv[bk * D * D + i] = (float)sm_S[i];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += blockDim.x) mu[bk * D + d] = (float)(sx[bk * D + d] / n);
+  if (tid == 0 && comp_status) comp_status[bk] = st;
+}
+
+// Tied: one block per problem.
+__global__ void __launch_bounds__(256) mstep_tied_kernel(int D, int K, const double* __restrict__ nk,
+                                                         const double* __restrict__ sx,
+                                                         const double* __restrict__ sxx, int64_t n_total, float* w,
+                                                         float* mu, float* cv, double reg, const int32_t* in_flag,
+                                                         int in_flag_stride, int32_t* comp_status) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ double sm_S[16 * 16], sm_L[16 * 16];
+  __shared__ int sm_pd;
+  extern __shared__ double sm_delta[];  // K*D
+  for (int i = tid; i < K * D; i += blockDim.x) {
+    const int k = i / D;
+    const double n = nk[(size_t)b * K + k];
+    sm_delta[i] = n > 0.0 ? sx[(size_t)b * K * D + i] / n - (double)mu[(size_t)b * K * D + i] : 0.0;
+  }
+  __syncthreads();
+  for (int i = tid; i < D * D; i += blockDim.x) {
+    const int d = i / D, e = i % D;
+    double s = sxx[(size_t)b * D * D + i];
+    for (int k = 0; k < K; ++k) s -= nk[(size_t)b * K + k] * sm_delta[k * D + d] * sm_delta[k * D + e];
+    sm_S[i] = s / (double)n_total + (d == e ? reg : 0.0);
+  }
+  __syncthreads();
+  if (tid == 0) sm_pd = chol_serial(D, sm_S, sm_L);
+  __syncthreads();
+  const bool pd = sm_pd;
+  if (pd)
+    for (int i = tid; i < D * D; i += blockDim.x) cv[(size_t)b * D * D + i] = (float)sm_S[i];
+  for (int k = tid; k < K; k += blockDim.x) {
+    const size_t bk = (size_t)b * K + k;
+    const double n = nk[bk];
+    w[bk] = (float)(n / (double)n_total);
+    int32_t st = (n > 0.0 ? 0 : 1) | (pd ? 0 : 2);
+    if (in_flag) st |= in_flag[(size_t)b * in_flag_stride + k];
+    if (comp_status) comp_status[bk] = st;
+  }
+  __syncthreads();
+  if (pd)
+    for (int i = tid; i < K * D; i += blockDim.x) {
+      const int k = i / D;
+      const double n = nk[(size_t)b * K + k];
+      if (n > 0.0) mu[(size_t)b * K * D + i] = (float)(sx[(size_t)b * K * D + i] / n);
+    }
+}
+
+hipError_t launch_mstep_strided(int cov, int64_t B, int64_t D, int64_t K, const double* nk, const double* sx,
+                                const double* sxx, int64_t n_total, float* w, float* mu, float* cv, double reg,
+                                const int32_t* in_flag, int in_flag_stride, int32_t* comp_status, hipStream_t s) {
+  if (cov == TIED) {
+    hipLaunchKernelGGL(mstep_tied_kernel, dim3((unsigned)B), dim3(256), sizeof(double) * (size_t)(K * D), s,
+                       (int)D, (int)K, nk, sx, sxx, n_total, w, mu, cv, reg, in_flag, in_flag_stride, comp_status);
+  } else {
+    hipLaunchKernelGGL(mstep_kernel, dim3((unsigned)(B * K)), dim3(64), 0, s, cov, (int)D, (int)K, nk, sx, sxx,
+                       n_total, w, mu, cv, reg, in_flag, in_flag_stride, comp_status);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gmm

@@ -1,0 +1,77 @@
+// gmm_internal.h -- launch plan and kernel entry points shared by the host
+// side of the library (gmm_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gmm {
+
+enum Cov { SPH = 0, DIAG = 1, TIED = 2, FULL = 3 };
+
+constexpr int kNumCU = 256;          // MI355X compute units (8 XCDs x 32)
+constexpr size_t kLdsBytes = 163840; // LDS per workgroup on gfx950
+constexpr int kMaxWaves = 8;         // waves per workgroup (512 threads)
+constexpr size_t kAlign = 256;
+
+// Number of logit features F and statistic rows G for a covariance type and a
+// padded dimension DP (both multiples of 16).
+//   spherical: phi = x                          (the |x|^2 term is added on the VALU)
+//   diag:      phi = [x, x*x]
+//   full:      phi = [x, x_d x_e (d <= e)]       (upper triangle, row-major)
+//   tied:      same features as full; the quadratic weights are shared by all k
+__host__ __device__ constexpr int quad_count(int dp) { return dp * (dp + 1) / 2; }
+__host__ __device__ constexpr int round16(int v) { return (v + 15) / 16 * 16; }
+__host__ __device__ constexpr int feat_F(int cov, int dp) {
+  return cov == DIAG ? 2 * dp : (cov == FULL || cov == TIED) ? round16(dp + quad_count(dp)) : dp;
+}
+__host__ __device__ constexpr int feat_G(int cov, int dp) { return feat_F(cov, dp); }
+// LDS row stride (floats) of the feature tile: >= F and == 2 (mod 32), which
+// keeps the MFMA A-operand reads of the logit step free of bank conflicts.
+__host__ __device__ constexpr int feat_stride(int f) { return (f + 29) / 32 * 32 + 2; }
+
+struct Plan {
+  int cov = 0, dtype = 0;
+  int64_t B = 0, N = 0, D = 0, K = 0, ld_x = 0, stride_b = 0;
+  int DP = 0, F = 0, G = 0, FS = 0;
+  int KW = 0, NW = 0, KP = 0, T = 0;
+  int PR = 0;               // doubles per component in a workgroup partial: [N_k, Q_k, G rows]
+  int Gb = 0;               // workgroups per problem
+  int64_t ntiles = 0;       // row tiles per problem
+  size_t lds = 0;           // dynamic LDS of the fused kernel
+  bool vec4 = false;        // rows can be read with 16-byte loads
+  // workspace layout (byte offsets)
+  size_t off_W = 0, off_c = 0, off_a = 0, off_flag = 0, off_part = 0, off_llp = 0;
+  size_t off_nk = 0, off_sx = 0, off_sxx = 0, off_ll = 0, off_aux = 0;
+  size_t ws_bytes = 0;
+};
+
+struct EStepArgs {
+  const void* x;
+  int64_t N, D, ld_x, stride_b;
+  int K, KP, NW, Gb;
+  int64_t ntiles;
+  int vec4;
+  const float* W;     // (B, KP*F) fragment-ordered logit weights (log2 units)
+  const double* c;    // (B, KP) logit constants (log2 units), -inf for absent
+  const double* a;    // (B, KP) spherical |x|^2 coefficient (log2 units)
+  double* part;       // (B*Gb, KP, PR)
+  double* llpart;     // (B*Gb)
+};
+
+// fused E-step + statistics (gmm_estep.hip)
+hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
+bool estep_variant_exists(int cov, int dp, int kw, int t);
+
+// prologue / reduction / M-step (gmm_aux.hip)
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv,
+                           float* W, double* c, double* a, int32_t* flag, hipStream_t s);
+hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
+                             double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
+                             int accumulate, hipStream_t s);
+hipError_t launch_mstep_strided(int cov, int64_t B, int64_t D, int64_t K, const double* nk, const double* sx,
+                                const double* sxx, int64_t n_total, float* w, float* mu, float* cv, double reg,
+                                const int32_t* in_flag, int in_flag_stride, int32_t* comp_status, hipStream_t s);
+
+}  // namespace gmm
