@@ -103,19 +103,28 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   }
   q.NW = (K + q.KW - 1) / q.KW;
   q.KP = q.KW * q.NW;
-  auto lds_for = [&](int T) {
-    // weights, feature tile, |x|^2 (float64), two per-wave row reductions
-    return sizeof(float) * ((size_t)q.KP * q.F + (size_t)T * q.FS + 2 * (size_t)T + 2 * (size_t)q.NW * T);
+  const bool direct_ok =
+      (((uintptr_t)d->x) % 16 == 0) && (q.ld_x == q.D) && (q.D % 4 == 0) && (q.stride_b % 4 == 0);
+  auto lds_for = [&](int T, int nraw) {
+    // weights, feature tile, raw row tile(s), |x|^2 (float64), per-wave (max, sum), product table
+    return sizeof(float) * ((size_t)q.KP * q.F + (size_t)T * q.FS + (size_t)nraw * T * q.DP + 2 * (size_t)T +
+                            2 * (size_t)q.NW * T + q.F);
   };
   q.T = 0;
-  for (int T : {64, 32, 16}) {
-    if (lds_for(T) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
-      q.T = T;
-      break;
+  // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
+  for (int nraw : {2, 1}) {
+    if (nraw == 2 && !direct_ok) continue;
+    for (int T : {64, 32, 16}) {
+      if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
+        q.T = T;
+        q.direct = nraw == 2;
+        break;
+      }
     }
+    if (q.T) break;
   }
   if (!q.T) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld does not fit in LDS", K, (long long)d->D);
-  q.lds = lds_for(q.T);
+  q.lds = lds_for(q.T, q.direct ? 2 : 1);
   q.ntiles = (q.N + q.T - 1) / q.T;
   const int wg_lds = (int)std::max<size_t>(1, kLdsBytes / q.lds);
   const int wg_per_cu = std::max(1, std::min(wg_lds, 8 / q.NW));
@@ -123,13 +132,16 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   int64_t gb = std::max<int64_t>(1, total / q.B);
   gb = std::min<int64_t>(gb, std::max<int64_t>(1, q.ntiles));
   q.Gb = (int)gb;
-  q.vec4 = (((uintptr_t)d->x) % 16 == 0) && (q.ld_x % 4 == 0) && (q.stride_b % 4 == 0);
   // workspace
   size_t o = 0;
   q.off_W = o;    o = align_up(o + sizeof(float) * (size_t)q.B * q.KP * q.F);
+  q.prec_stride = (cov == SPH) ? 1 : (cov == DIAG) ? (int)q.D : (int)(q.D * q.D);
+  q.off_prec = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.prec_stride);
+  q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_flag = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
+  q.off_sharp = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
   q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
   q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.PR);
@@ -162,13 +174,16 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
                             hipStream_t s) {
   char* w = static_cast<char*>(ws);
   float* W = reinterpret_cast<float*>(w + p.off_W);
+  double* prec = reinterpret_cast<double*>(w + p.off_prec);
+  double* c0 = reinterpret_cast<double*>(w + p.off_c0);
+  int32_t* sharp = reinterpret_cast<int32_t*>(w + p.off_sharp);
   double* c = reinterpret_cast<double*>(w + p.off_c);
   double* a = reinterpret_cast<double*>(w + p.off_a);
   int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
   double* part = reinterpret_cast<double*>(w + p.off_part);
   double* llp = reinterpret_cast<double*>(w + p.off_llp);
   double* raw = reinterpret_cast<double*>(w + p.off_aux);
-  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, W, c, a, flag, s);
+  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, W, prec, c0, c, a, flag, sharp, s);
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   EStepArgs A;
   A.x = d->x;
@@ -181,8 +196,13 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   A.NW = p.NW;
   A.Gb = p.Gb;
   A.ntiles = p.ntiles;
-  A.vec4 = p.vec4 ? 1 : 0;
+  A.direct = p.direct ? 1 : 0;
   A.W = W;
+  A.mu = prm->means;
+  A.prec = prec;
+  A.c0 = c0;
+  A.prec_stride = p.prec_stride;
+  A.sharp = sharp;
   A.c = c;
   A.a = a;
   A.part = part;

@@ -15,9 +15,16 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace gmm {
 
 static constexpr double kLog2e = 1.4426950408889634074;
+// A component is "sharp" when the terms of its expanded log-score reach
+// lambda_max * (|mu|^2 + tr Sigma) > kSharp: float32 products and partial sums
+// of that size no longer give the log-score to the accuracy the
+// responsibilities need, and the fused kernel evaluates it in float64.
+static constexpr double kSharp = 1.0e4;
 static constexpr double kLog2Pi = 1.8378770664093454836;
 
 __device__ __forceinline__ size_t wfrag_index(int k, int f, int KW, int F) {
@@ -54,10 +61,13 @@ __device__ bool chol_serial(int D, const double* S, double* L) {
 __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int KP, int DP, int F, int KW,
                                                       const float* __restrict__ w, const float* __restrict__ mu,
                                                       const float* __restrict__ cv, float* __restrict__ W,
-                                                      double* __restrict__ c, double* __restrict__ a,
-                                                      int32_t* __restrict__ flag) {
+                                                      double* __restrict__ prec, int prec_stride,
+                                                      double* __restrict__ c0, double* __restrict__ c,
+                                                      double* __restrict__ a, int32_t* __restrict__ flag,
+                                                      int32_t* __restrict__ sharp) {
   const int b = blockIdx.x / KP, k = blockIdx.x % KP, tid = threadIdx.x;
   float* Wb = W + (size_t)b * KP * F;
+  double* precb = prec + ((size_t)b * KP + k) * prec_stride;
   __shared__ double sm_mu[128];
   __shared__ double sm_v[128];                // diag precisions / P mu
   __shared__ double sm_S[16 * 16], sm_L[16 * 16], sm_Li[16 * 16], sm_P[16 * 16];
@@ -68,8 +78,10 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     for (int f = tid; f < F; f += blockDim.x) Wb[wfrag_index(k, f, KW, F)] = 0.f;
     if (tid == 0) {
       c[(size_t)b * KP + k] = -INFINITY;
+      c0[(size_t)b * KP + k] = -INFINITY;
       a[(size_t)b * KP + k] = 0.0;
       flag[(size_t)b * KP + k] = 0;
+      sharp[(size_t)b * KP + k] = 0;
     }
     return;
   }
@@ -84,15 +96,24 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     __syncthreads();
     if (tid == 0) {
       bool ok = true;
-      double logdet = 0.0, quad = 0.0;
+      double logdet = 0.0, quad = 0.0, lmax = 0.0, scale = 0.0;
       for (int d = 0; d < D; ++d) {
         const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
         if (!(v > 0.0) || isinf(v)) ok = false;
         logdet += log(v);
         quad += sm_v[d] * sm_mu[d] * sm_mu[d];
+        lmax = fmax(lmax, sm_v[d]);
+        scale += sm_mu[d] * sm_mu[d] + v;
       }
       sm_ok = ok;
       sm_c = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e : -INFINITY;
+      c0[(size_t)b * KP + k] = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e : -INFINITY;
+      sharp[(size_t)b * KP + k] = (ok && lmax * scale > kSharp) ? 1 : 0;
+    }
+    if (cov == SPH) {
+      if (tid == 0) precb[0] = sm_v[0];
+    } else {
+      for (int d = tid; d < D; d += blockDim.x) precb[d] = sm_v[d];
     }
     __syncthreads();
     const bool ok = sm_ok;
@@ -147,13 +168,18 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     }
     __syncthreads();
     if (tid == 0) {
-      double logdet = 0.0, quad = 0.0;
+      double logdet = 0.0, quad = 0.0, trp = 0.0, scale = 0.0;
       for (int d = 0; d < D; ++d) {
         logdet += 2.0 * log(sm_L[d * D + d]);
         quad += sm_mu[d] * sm_v[d];
+        trp += sm_P[d * D + d];
+        scale += sm_mu[d] * sm_mu[d] + sm_S[d * D + d];
       }
       sm_c = (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e;
+      c0[(size_t)b * KP + k] = (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e;
+      sharp[(size_t)b * KP + k] = trp * scale > kSharp ? 1 : 0;
     }
+    for (int i = tid; i < D * D; i += blockDim.x) precb[i] = sm_Li[i];
   }
   __syncthreads();
   for (int f = tid; f < F; f += blockDim.x) {
@@ -175,13 +201,15 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     c[(size_t)b * KP + k] = ok ? sm_c : -INFINITY;
     a[(size_t)b * KP + k] = 0.0;
     flag[(size_t)b * KP + k] = ok ? 0 : 4;
+    if (!ok) sharp[(size_t)b * KP + k] = 0;
   }
 }
 
-hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W, double* c,
-                           double* a, int32_t* flag, hipStream_t s) {
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W,
+                           double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
+                           hipStream_t s) {
   hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(p.B * p.KP)), dim3(64), 0, s, p.cov, (int)p.D, (int)p.K,
-                     p.KP, p.DP, p.F, p.KW, w, mu, cv, W, c, a, flag);
+                     p.KP, p.DP, p.F, p.KW, w, mu, cv, W, prec, p.prec_stride, c0, c, a, flag, sharp);
   return hipGetLastError();
 }
 
@@ -211,10 +239,20 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
   extern __shared__ double sm[];
   double* r = sm;            // PR
   double* m = sm + PR;       // D
+  const size_t stride = (size_t)KP * PR;
   for (int j = tid; j < PR; j += blockDim.x) {
+    // workgroup order 0..Gb-1; eight loads in flight, additions still in order
     double s = 0.0;
     const double* src = part + ((size_t)b * Gb * KP + k) * PR + j;
-    for (int g = 0; g < Gb; ++g) s += src[(size_t)g * KP * PR];
+    int g = 0;
+    for (; g + 8 <= Gb; g += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(g + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; g < Gb; ++g) s += src[(size_t)g * stride];
     r[j] = s;
     raw[((size_t)b * KP + k) * PR + j] = s;
   }
@@ -288,7 +326,8 @@ hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* ll
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s) {
   const size_t lds = sizeof(double) * (size_t)(p.PR + p.D);
-  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(128), lds, s, p.cov, (int)p.D,
+  const unsigned threads = (unsigned)std::min(256, std::max(64, (p.PR + 63) / 64 * 64));
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(threads), lds, s, p.cov, (int)p.D,
                      (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
                      accumulate, (int)p.B);
   hipError_t e = hipGetLastError();

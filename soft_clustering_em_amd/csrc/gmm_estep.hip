@@ -11,31 +11,33 @@
 // How it is laid out on gfx950 (CDNA4):
 //   * Every log-score is linear in a feature vector phi(x) (x, x^2, or the
 //     products x_d x_e) plus a per-component constant, so the logits of a
-//     tile are one dense contraction
-//     phi(X) (T x F) * W (F x K) and the statistics are another,
-//     phi(X)^T (F x T) * R (T x K).  The logits run on v_mfma_f32_16x16x4_f32;
-//     the statistics on v_mfma_f64_16x16x4_f64 with features rebuilt in
-//     float64 (x, x*x and x_d*x_e are exact there), so raw moments are summed
-//     without the cancellation that turning them into variances would expose:
-//     a component that has collapsed onto a few rows has a variance many
-//     orders below mu^2, and only float64 sums keep it.
-//   * The logit accumulator's register layout (lane l holds component l%16 of
-//     rows 4(l/16)+v) is exactly the B-operand layout the statistics MFMA needs
-//     for R, so responsibilities go from the exponential straight into the
-//     second contraction without an LDS transpose.
+//     tile are one dense contraction phi(X) (T x F) * W (F x K) and the
+//     statistics are another, phi(X)^T (F x T) * R (T x K).  The logits run on
+//     v_mfma_f32_16x16x4_f32; the statistics on v_mfma_f64_16x16x4_f64 with
+//     features rebuilt in float64 (x, x*x and x_d*x_e are exact there), so
+//     raw moments are summed without the cancellation that turning them into
+//     variances would expose: a component that has collapsed onto a few rows
+//     has a variance many orders below mu^2, and only float64 sums keep it.
 //   * The float32 logit contraction is flushed into float64 every 32
 //     features, and the per-component constant (and the spherical |x|^2 term)
 //     is added in float64: the terms of the expanded quadratic form are far
-//     larger than their sum, and a float32 accumulator alone would lose the
-//     absolute accuracy that the responsibilities of distant rows need.
-//   * Components are split across the waves of a workgroup (KW per wave); a
-//     row's max and sum over its own KW components is a 16-lane DPP all-reduce
-//     plus an in-register fold, and the per-wave partials meet in LDS.
-//   * The tile of features is staged once in LDS and read by both
-//     contractions; the next tile's rows are loaded into registers while the
-//     current tile computes.
-//   * N_k (and, for spherical components, sum r |x|^2) accumulate on the VALU
-//     in float64; the workgroup partial is written in float64.
+//     larger than their sum.  Components whose precision times squared scale
+//     is too large even for that ("sharp" ones, e.g. collapsed onto a row)
+//     are flagged by the prologue; for them every log-score that comes within
+//     60 (log2 units) of its row's maximum is recomputed in float64 from
+//     direct differences, -1/2 (x - mu)^T P (x - mu) -- the scores further
+//     down carry responsibilities below 2^-60 whatever their rounding.
+//   * The logit accumulator's register layout (lane l holds component l%16 of
+//     rows 4(l/16)+v) is exactly the B-operand layout the statistics MFMA
+//     needs for R, so responsibilities go from the exponential straight into
+//     the second contraction without an LDS transpose.
+//   * Components are split across the waves of a workgroup (KW per wave).  A
+//     wave reduces its own components (in-register fold + 16-lane DPP
+//     all-reduce) to a per-row (max, sum of exp) pair; the pairs of all waves
+//     meet in LDS once per tile and are combined in wave order.
+//   * Rows arrive with global_load_lds_dwordx4 straight into a double-buffered
+//     LDS tile while the previous tile computes; features are built from it
+//     into a padded LDS tile read by both contractions.
 //   * Workgroups stride over tiles (tile t -> workgroup t mod Gb), and each
 //     writes its own partial slot: no atomics, fixed reduction order.
 #include "gmm_internal.h"
@@ -68,6 +70,47 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// product feature f >= DP of the quadratic feature map: (d, e) packed as d << 16 | e
+template <int DP>
+__device__ __forceinline__ int quad_pair(int q) {
+  int d = 0, base = 0;
+  while (q >= base + (DP - d)) { base += DP - d; ++d; }
+  return (d << 16) | (d + (q - base));
+}
+
+// log2 of pi_k N(x | mu_k, Sigma_k) for one row x (float32 values in LDS), by
+// direct differences in float64: c0_k - 1/2 log2(e) (x - mu)^T P (x - mu).
+// prec holds 1/sigma^2 (spherical: one value; diag: D values) or, for
+// full/tied, the lower-triangular L^{-1} of Sigma = L L^T (D x D).
+template <int COV, int DP>
+__device__ __forceinline__ double exact_score(const EStepArgs& A, int b, int k, int D, const float* x) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  const float* mu = A.mu + ((size_t)b * A.K + k) * D;
+  const double* P = A.prec + ((size_t)b * A.KP + k) * (size_t)A.prec_stride;
+  double q = 0.0;
+  if constexpr (COV == SPH) {
+    for (int d = 0; d < D; ++d) {
+      const double t = (double)x[d] - (double)mu[d];
+      q += t * t;
+    }
+    q *= P[0];
+  } else if constexpr (COV == DIAG) {
+    for (int d = 0; d < D; ++d) {
+      const double t = (double)x[d] - (double)mu[d];
+      q += P[d] * t * t;
+    }
+  } else {
+    for (int i = 0; i < D; ++i) {
+      double z = 0.0;
+      for (int j = 0; j <= i; ++j) z += P[i * D + j] * ((double)x[j] - (double)mu[j]);
+      q += z * z;
+    }
+  }
+  return A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;
+}
 
 template <int COV, int DP, int KW, int T>
 __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
@@ -80,7 +123,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   constexpr int KQ = F / 16;    // groups of 4 MFMA k-steps
   constexpr int NQ = quad_count(DP);
   constexpr bool QUAD = (COV == FULL || COV == TIED);
-  constexpr float LN2 = 0.693147180559945309f;
+  constexpr double LN2 = 0.69314718055994530942;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -92,11 +135,12 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   const int D = (int)A.D;
 
   extern __shared__ float lds[];
-  float* Wl = lds;                          // KP*F, fragment order
-  float* phi = Wl + (size_t)KP * F;         // T*FS features
-  double* xsq = reinterpret_cast<double*>(phi + T * FS);  // T (spherical), float64
-  float* redm = reinterpret_cast<float*>(xsq + T);         // NW*T
-  float* reds = redm + NW * T;              // NW*T
+  float* Wl = lds;                                             // KP*F, fragment order
+  float* phi = Wl + (size_t)KP * F;                            // T*FS features
+  float* raw0 = phi + T * FS;                                  // 2 (direct) or 1 x T*DP raw rows
+  double* xsq = reinterpret_cast<double*>(raw0 + (A.direct ? 2 : 1) * T * DP);  // T (spherical), float64
+  float* red = reinterpret_cast<float*>(xsq + T);              // NW*T*2: per-wave (max, sum)
+  int* qtab = reinterpret_cast<int*>(red + 2 * NW * T);        // F: (d, e) of product features
 
   // ---- stage this problem's logit weights in LDS (linear copy, 16 B per lane)
   {
@@ -105,12 +149,21 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     const int n4 = KP * F / 4;
     for (int i = threadIdx.x; i < n4; i += nthr) dst[i] = src[i];
   }
+  if constexpr (QUAD) {
+    for (int f = threadIdx.x; f < F; f += nthr)
+      qtab[f] = f < DP ? ((f << 16) | 0xFFFF) : (f - DP < NQ ? quad_pair<DP>(f - DP) : -1);
+  }
   double creg[NT], areg[NT];
+  bool sharp[NT];
+  bool any_sharp = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int k = wv * KW + nt * 16 + (lane & 15);
     creg[nt] = A.c[(size_t)b * KP + k];
     areg[nt] = (COV == SPH) ? A.a[(size_t)b * KP + k] : 0.0;
+    sharp[nt] = A.sharp[(size_t)b * KP + k] != 0;
+    // one decision per wave: does any of its components need the exact path
+    any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(sharp[nt]) != 0);
   }
 
   doublex4 sacc[GM][NT];
@@ -122,8 +175,8 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) nk[nt] = qs[nt] = 0.0;
   double ll = 0.0;
-  // statistic feature held by this lane in row tile mt: f = 16 mt + lane%16;
-  // for the product features its two factors (d, e); -1 marks padding
+  // statistic feature held by this lane in row tile mt: f = 16 mt + lane%16,
+  // as (fd, fe): fe < 0 -> x_fd (or 0 when fd < 0); else x_fd * x_fe
   int fd[GM], fe[GM];
 #pragma unroll
   for (int mt = 0; mt < GM; ++mt) {
@@ -134,11 +187,10 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
       if (f >= DP) { fd[mt] = f - DP; fe[mt] = f - DP; }
     } else if constexpr (QUAD) {
       if (f >= DP) {
-        int q = f - DP, d = 0, base = 0;
-        if (q < NQ) {
-          while (q >= base + (DP - d)) { base += DP - d; ++d; }
-          fd[mt] = d;
-          fe[mt] = d + (q - base);
+        if (f - DP < NQ) {
+          const int de = quad_pair<DP>(f - DP);
+          fd[mt] = de >> 16;
+          fe[mt] = de & 0xFFFF;
         } else {
           fd[mt] = -1;
         }
@@ -146,94 +198,88 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     }
   }
 
-  // ---- register prefetch of one tile of rows (x part only)
-  // Each thread owns rows/columns of the tile in 4-element chunks:
-  // chunk j -> row j / (DP/4), columns 4*(j % (DP/4)) .. +3.
-  constexpr int CPR = DP / 4;                  // chunks per row
-  constexpr int NCH = T * CPR;                 // chunks per tile
-  // chunks per thread held in registers between tiles (at most four, i.e. 16
-  // registers); a tile with more chunks than that is loaded directly instead
-  constexpr int MAXC = (NCH + 63) / 64 < 4 ? (NCH + 63) / 64 : 4;
-  const bool prefetch = NCH <= MAXC * nthr;
-  floatx4 pre[MAXC];
+  // ---- rows: a tile of T rows x D floats.  Direct path: the rows of a tile
+  // are contiguous and 16-byte aligned, so they are copied into LDS with
+  // global_load_lds_dwordx4 (one 16-byte chunk per lane, lanes in order).
   const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)b * A.stride_b;
-
-  auto load_chunk = [&](int64_t row0, int j) {
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j < NCH) {
-      const int r = j / CPR, c4 = (j % CPR) * 4;
-      const int64_t row = row0 + r;
-      if (row < N) {
-        const float* src = xb + row * A.ld_x + c4;
-        if (A.vec4 && c4 + 4 <= D) {
-          v = *reinterpret_cast<const floatx4*>(src);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (c4 + e < D) ? src[e] : 0.f;
-        }
-      }
+  const int rawstride = A.direct ? D : DP;  // floats per row in the raw LDS tile
+  auto issue_tile = [&](int64_t tile, float* rawbuf) {
+    const int64_t row0 = tile * T;
+    const int64_t nrows = (N - row0) < T ? (N - row0) : T;
+    const int nch = (int)(nrows * D / 4);  // valid 16-byte chunks of this tile
+    for (int c0 = wv * 64; c0 < nch; c0 += nthr) {
+      const int c = c0 + lane;
+      if (c < nch)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(xb + row0 * D + (int64_t)c * 4),
+            (__attribute__((address_space(3))) void*)(rawbuf + c0 * 4), 16, 0, 0);
     }
-    return v;
   };
-  auto load_tile = [&](int64_t tile) {
-#pragma unroll
-    for (int q = 0; q < MAXC; ++q) pre[q] = load_chunk(tile * T, threadIdx.x + q * nthr);
-  };
-  auto store_chunk = [&](int j, floatx4 v) {
-    const int r = j / CPR, c4 = (j % CPR) * 4;
-    *reinterpret_cast<float2*>(&phi[r * FS + c4]) = float2{v[0], v[1]};
-    *reinterpret_cast<float2*>(&phi[r * FS + c4 + 2]) = float2{v[2], v[3]};
-    if constexpr (COV == DIAG) {
-      *reinterpret_cast<float2*>(&phi[r * FS + DP + c4]) = float2{v[0] * v[0], v[1] * v[1]};
-      *reinterpret_cast<float2*>(&phi[r * FS + DP + c4 + 2]) = float2{v[2] * v[2], v[3] * v[3]};
+  auto load_tile_sync = [&](int64_t tile, float* rawbuf) {
+    const int64_t row0 = tile * T;
+    for (int j = threadIdx.x; j < T * DP; j += nthr) {
+      const int r = j / DP, d = j % DP;
+      const int64_t row = row0 + r;
+      rawbuf[j] = (row < N && d < D) ? xb[row * A.ld_x + d] : 0.f;
     }
   };
 
   int64_t t = g;
-  if (prefetch && t < A.ntiles) load_tile(t);
-  for (; t < A.ntiles; t += A.Gb) {
+  int cur = 0;
+  if (A.direct && t < A.ntiles) issue_tile(t, raw0);
+  for (; t < A.ntiles; t += A.Gb, cur ^= 1) {
     const int64_t row0 = t * T;
-    __syncthreads();  // every wave is done reading the previous tile's features
-    // ---- features: x part (and x^2 for diag), from the prefetch registers
-    if (prefetch) {
-#pragma unroll
-      for (int q = 0; q < MAXC; ++q) {
-        const int j = threadIdx.x + q * nthr;
-        if (j < NCH) store_chunk(j, pre[q]);
-      }
-    } else {
-      for (int j = threadIdx.x; j < NCH; j += nthr) store_chunk(j, load_chunk(row0, j));
-    }
-    if constexpr (COV == SPH || QUAD) {
+    float* raw = A.direct ? raw0 + cur * T * DP : raw0;
+    if (A.direct) wait_vmem();
+    __syncthreads();  // rows of this tile have landed; every wave is done with the previous tile
+    if (!A.direct) {
+      load_tile_sync(t, raw);
       __syncthreads();
-      if constexpr (COV == SPH) {
-        for (int r = threadIdx.x; r < T; r += nthr) {
-          double s = 0.0;
-#pragma unroll 8
-          for (int d = 0; d < DP; ++d) s += (double)phi[r * FS + d] * (double)phi[r * FS + d];
-          xsq[r] = s;
-        }
-      } else {
-        // products x_d x_e, d <= e, upper triangle in row-major order, then zero padding
-        constexpr int NQP = F - DP;
-        for (int j = threadIdx.x; j < T * NQP; j += nthr) {
-          const int r = j / NQP, qi = j % NQP;
-          float v = 0.f;
-          if (qi < NQ) {
-            // invert qi -> (d, e): row d holds DP - d entries
-            int d = 0, base = 0;
-            while (qi >= base + (DP - d)) { base += DP - d; ++d; }
-            const int e = d + (qi - base);
-            v = phi[r * FS + d] * phi[r * FS + e];
-          }
-          phi[r * FS + DP + qi] = v;
-        }
+    }
+    // ---- features of this tile (rows past N are zero)
+    for (int j = threadIdx.x; j < T * (DP / 4); j += nthr) {
+      const int r = j / (DP / 4), c4 = (j % (DP / 4)) * 4;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (row0 + r < N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (c4 + e < D) ? raw[r * rawstride + c4 + e] : 0.f;
+      }
+      *reinterpret_cast<float2*>(&phi[r * FS + c4]) = float2{v[0], v[1]};
+      *reinterpret_cast<float2*>(&phi[r * FS + c4 + 2]) = float2{v[2], v[3]};
+      if constexpr (COV == DIAG) {
+        *reinterpret_cast<float2*>(&phi[r * FS + DP + c4]) = float2{v[0] * v[0], v[1] * v[1]};
+        *reinterpret_cast<float2*>(&phi[r * FS + DP + c4 + 2]) = float2{v[2] * v[2], v[3] * v[3]};
       }
     }
-    __syncthreads();  // features of this tile are visible
-    if (prefetch && t + A.Gb < A.ntiles) load_tile(t + A.Gb);  // in flight during the compute below
+    if constexpr (COV == SPH) {
+      for (int r = threadIdx.x; r < T; r += nthr) {
+        double s = 0.0;
+        if (row0 + r < N)
+          for (int d = 0; d < D; ++d) {
+            const double x = (double)raw[r * rawstride + d];
+            s += x * x;
+          }
+        xsq[r] = s;
+      }
+    }
+    if constexpr (QUAD) {
+      constexpr int NQP = F - DP;
+      for (int j = threadIdx.x; j < T * NQP; j += nthr) {
+        const int r = j / NQP, qi = j % NQP;
+        const int de = qtab[DP + qi];
+        float v = 0.f;
+        if (de >= 0 && row0 + r < N) {
+          const int d = de >> 16, e = de & 0xFFFF;
+          if (d < D && e < D) v = raw[r * rawstride + d] * raw[r * rawstride + e];
+        }
+        phi[r * FS + DP + qi] = v;
+      }
+    }
+    // the next tile's rows into the other raw buffer, in flight during the compute below
+    if (A.direct && t + A.Gb < A.ntiles) issue_tile(t + A.Gb, raw0 + (cur ^ 1) * T * DP);
+    __syncthreads();  // features visible
 
-    // ---- logits (log2 units): lg[rb][nt] = c + phi(X) W, float32 MFMA partial
+    // ---- logits (log2 units): lg[rb][nt] = c + phi(X) W; float32 MFMA partial
     // sums over 32 features flushed into float64
     floatx4 acc[RB][NT];
     double lg[RB][NT][4];
@@ -287,8 +333,8 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
         }
     }
 
-    // ---- row max over all components (a float32 shift; any value near the max will do)
-    float mrow[RB][4];
+    // ---- per-wave row max and sum of exponentials over this wave's components
+    float mrow[RB][4], srow[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -296,70 +342,94 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
         float m = (float)lg[rb][0][v];
 #pragma unroll
         for (int nt = 1; nt < NT; ++nt) m = fmaxf(m, (float)lg[rb][nt][v]);
-        mrow[rb][v] = row16_max(m);
-      }
-    if (NW > 1) {
-      if ((lane & 15) == 0)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) redm[wv * T + rb * 16 + 4 * (lane >> 4) + v] = mrow[rb][v];
-      __syncthreads();
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        m = row16_max(m);
+        if (any_sharp) {
+          // sharp components: scores near the top of the row again, exactly
           const int p = rb * 16 + 4 * (lane >> 4) + v;
-          float m = redm[p];
-          for (int w2 = 1; w2 < NW; ++w2) m = fmaxf(m, redm[w2 * T + p]);
-          mrow[rb][v] = m;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if (sharp[nt] && (float)lg[rb][nt][v] >= m - 60.f && row0 + p < N) {
+              const int k = wv * KW + nt * 16 + (lane & 15);
+              lg[rb][nt][v] = exact_score<COV, DP>(A, b, k, D, phi + p * FS);
+            }
+          }
+          m = (float)lg[rb][0][v];
+#pragma unroll
+          for (int nt = 1; nt < NT; ++nt) m = fmaxf(m, (float)lg[rb][nt][v]);
+          m = row16_max(m);
         }
-    }
-    // ---- exponentials and row sums
-    float srow[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
+        if (m == -INFINITY) m = 0.f;  // no live component in this wave: every exp below is 0
         float s = 0.f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float e = __builtin_amdgcn_exp2f((float)(lg[rb][nt][v] - (double)mrow[rb][v]));
+          const float e = __builtin_amdgcn_exp2f((float)(lg[rb][nt][v] - (double)m));
           acc[rb][nt][v] = e;
           s += e;
         }
+        mrow[rb][v] = m;
         srow[rb][v] = row16_sum(s);
       }
+    // ---- combine the waves: M = max_w m_w, S = sum_w s_w 2^(m_w - M).
+    // Each 16-lane group holds rows 4g..4g+3 of a row block; lane j of the
+    // group takes row v = j/4 and waves q, q+4 (q = j%4), then the quad
+    // (lanes 4v..4v+3) reduces with DPP and its first lane's result is
+    // broadcast to the group with ds_swizzle.  Waves enter in a fixed order.
+    float scale[RB][4];
     if (NW > 1) {
+      float* redm = red;            // [NW][T]
+      float* reds = red + NW * T;   // [NW][T]
       if ((lane & 15) == 0)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) reds[wv * T + rb * 16 + 4 * (lane >> 4) + v] = srow[rb][v];
+        for (int rb = 0; rb < RB; ++rb) {
+          const int p = rb * 16 + 4 * (lane >> 4);
+          *reinterpret_cast<floatx4*>(&redm[wv * T + p]) = floatx4{mrow[rb][0], mrow[rb][1], mrow[rb][2], mrow[rb][3]};
+          *reinterpret_cast<floatx4*>(&reds[wv * T + p]) = floatx4{srow[rb][0], srow[rb][1], srow[rb][2], srow[rb][3]};
+        }
       __syncthreads();
+      const int j = lane & 15, vq = j >> 2, q = j & 3;
+      const int w0 = q < NW ? q : NW - 1, w1 = q + 4 < NW ? q + 4 : NW - 1;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int p = rb * 16 + 4 * (lane >> 4) + vq;
+        const float m0 = redm[w0 * T + p], s0 = reds[w0 * T + p];
+        const float m1 = redm[w1 * T + p], s1 = reds[w1 * T + p];
+        const bool ok0 = q < NW && s0 > 0.f, ok1 = q + 4 < NW && s1 > 0.f;
+        float M = fmaxf(ok0 ? m0 : -INFINITY, ok1 ? m1 : -INFINITY);
+        M = fmaxf(M, dpp_mov<0xB1>(M));
+        M = fmaxf(M, dpp_mov<0x4E>(M));
+        float S = (ok0 ? s0 * __builtin_amdgcn_exp2f(m0 - M) : 0.f) + (ok1 ? s1 * __builtin_amdgcn_exp2f(m1 - M) : 0.f);
+        S = S + dpp_mov<0xB1>(S);
+        S = S + dpp_mov<0x4E>(S);
+        // this wave's share of row v: 2^(m_own - M) / S
+        const float mown = vq == 0 ? mrow[rb][0] : vq == 1 ? mrow[rb][1] : vq == 2 ? mrow[rb][2] : mrow[rb][3];
+        const bool valid = row0 + p < N && S > 0.f;
+        const float sc = valid ? __builtin_amdgcn_exp2f(mown - M) / S : 0.f;
+        if (wv == 0 && q == 0 && valid) ll += ((double)M + (double)__builtin_amdgcn_logf(S)) * LN2;
+        // broadcast lane 4v of the 16-lane group: and_mask 0x10, or_mask 4v
+        scale[rb][0] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (0 << 5)));
+        scale[rb][1] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (4 << 5)));
+        scale[rb][2] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (8 << 5)));
+        scale[rb][3] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (12 << 5)));
+      }
+    } else {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int p = rb * 16 + 4 * (lane >> 4) + v;
-          float s = 0.f;
-          for (int w2 = 0; w2 < NW; ++w2) s += reds[w2 * T + p];
-          srow[rb][v] = s;
+          const bool valid = row0 + p < N;
+          scale[rb][v] = valid ? 1.0f / srow[rb][v] : 0.f;
+          if ((lane & 15) == 0 && valid)
+            ll += ((double)mrow[rb][v] + (double)__builtin_amdgcn_logf(srow[rb][v])) * LN2;
         }
     }
-    // ---- responsibilities (rows past N get weight 0) and the log-likelihood
+    // ---- responsibilities (rows past N get weight 0)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int p = rb * 16 + 4 * (lane >> 4) + v;
-        const bool valid = row0 + p < N;
-        const float inv = valid ? 1.0f / srow[rb][v] : 0.f;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[rb][nt][v] *= inv;
-        if (wv == 0 && (lane & 15) == 0 && valid)
-          ll += ((double)mrow[rb][v] + (double)__builtin_amdgcn_logf(srow[rb][v])) * (double)LN2;
-      }
+        for (int v = 0; v < 4; ++v) acc[rb][nt][v] *= scale[rb][v];
 
     // ---- statistics: sacc[mt][nt] += phi(X)^T R in float64; N_k (and sum r |x|^2) on the VALU
 #pragma unroll
@@ -404,8 +474,8 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 
   // ---- epilogue: this workgroup's float64 partial
   const size_t bg = (size_t)b * A.Gb + g;
-  double* part = A.part + bg * (size_t)KP * (2 + G);
   constexpr int PR = 2 + G;
+  double* part = A.part + bg * (size_t)KP * PR;
 #pragma unroll
   for (int mt = 0; mt < GM; ++mt)
 #pragma unroll
@@ -420,17 +490,14 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     }
   // N_k and sum r|x|^2: the four lanes l, l+16, l+32, l+48 hold the same component
   __syncthreads();
-  double* red64 = reinterpret_cast<double*>(lds);  // reuse the weight tile: KP*F floats >= 8*KP+4 doubles
+  double* red64 = reinterpret_cast<double*>(lds);  // reuse the weight tile (8*KP + 64 doubles fit in it)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int k = wv * KW + nt * 16 + (lane & 15);
     red64[(k * 4 + (lane >> 4)) * 2 + 0] = nk[nt];
     red64[(k * 4 + (lane >> 4)) * 2 + 1] = qs[nt];
   }
-  if (wv == 0 && (lane & 15) == 0) {
-    // row log-likelihoods: lanes 0, 16, 32, 48 of wave 0 hold them
-    red64[(size_t)KP * 8 + (lane >> 4)] = ll;
-  }
+  if (wv == 0) red64[(size_t)KP * 8 + lane] = ll;  // row log-likelihoods, held by lanes of wave 0
   __syncthreads();
   for (int k = threadIdx.x; k < KP; k += nthr) {
     double s0 = 0.0, s1 = 0.0;
@@ -443,7 +510,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   }
   if (threadIdx.x == 0) {
     double s = 0.0;
-    for (int q = 0; q < 4; ++q) s += red64[(size_t)KP * 8 + q];
+    for (int q = 0; q < 64; ++q) s += red64[(size_t)KP * 8 + q];
     A.llpart[bg] = s;
   }
 }
@@ -454,8 +521,7 @@ static hipError_t launch_one(const Plan& p, const EStepArgs& a, hipStream_t s) {
   auto kern = estep_kernel<COV, DP, KW, T>;
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     attr_set = true;
   }
   dim3 grid((unsigned)(p.B * p.Gb)), block((unsigned)(64 * p.NW));
@@ -512,14 +578,14 @@ bool estep_variant_exists(int cov, int dp, int kw, int t) {
   if (kw != 16 && kw != 32) return false;
   if (t != 16 && t != 32 && t != 64) return false;
   if (cov == SPH) {
-    if (dp == 16) return true;
-    if (dp == 32 || dp == 64) return !(kw == 32 && t == 64);
+    if (dp == 16 || dp == 32) return !(kw == 32 && t == 64);
+    if (dp == 64) return kw == 16 || t <= 32;
     if (dp == 128) return kw == 16 ? t <= 32 : t == 16;
     return false;
   }
   if (cov == DIAG) {
-    if (dp == 16 || dp == 32) return !(kw == 32 && t == 64);
-    if (dp == 64) return kw == 16 || t == 16;
+    if (dp == 16 || dp == 32) return kw == 16 || t <= 32;
+    if (dp == 64) return kw == 16 ? t <= 32 : t == 16;
     if (dp == 128) return kw == 16 && t == 16;
     return false;
   }

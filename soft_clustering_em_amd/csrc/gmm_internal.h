@@ -40,9 +40,11 @@ struct Plan {
   int Gb = 0;               // workgroups per problem
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
-  bool vec4 = false;        // rows can be read with 16-byte loads
+  bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
   // workspace layout (byte offsets)
-  size_t off_W = 0, off_c = 0, off_a = 0, off_flag = 0, off_part = 0, off_llp = 0;
+  size_t off_W = 0, off_prec = 0, off_c0 = 0, off_c = 0, off_a = 0, off_flag = 0, off_sharp = 0, off_part = 0,
+         off_llp = 0;
+  int prec_stride = 0;      // doubles of precision data per component
   size_t off_nk = 0, off_sx = 0, off_sxx = 0, off_ll = 0, off_aux = 0;
   size_t ws_bytes = 0;
 };
@@ -52,12 +54,17 @@ struct EStepArgs {
   int64_t N, D, ld_x, stride_b;
   int K, KP, NW, Gb;
   int64_t ntiles;
-  int vec4;
-  const float* W;     // (B, KP*F) fragment-ordered logit weights (log2 units)
-  const double* c;    // (B, KP) logit constants (log2 units), -inf for absent
-  const double* a;    // (B, KP) spherical |x|^2 coefficient (log2 units)
-  double* part;       // (B*Gb, KP, PR)
-  double* llpart;     // (B*Gb)
+  int direct;          // rows of a tile are contiguous and 16-byte aligned (LDS-DMA loads)
+  const float* W;      // (B, KP*F) fragment-ordered logit weights (log2 units)
+  const double* c;     // (B, KP) logit constants (log2 units), -inf for absent
+  const double* a;     // (B, KP) spherical |x|^2 coefficient (log2 units)
+  const int32_t* sharp;  // (B, KP) 1: top log-scores of this component are recomputed exactly
+  const float* mu;     // (B, K, D) means (the parameters)
+  const double* prec;  // (B, KP, prec_stride) precisions / inverse Cholesky factors, float64
+  const double* c0;    // (B, KP) log2 pi_k - 1/2 log2 det(2 pi Sigma_k)
+  int prec_stride;
+  double* part;        // (B*Gb, KP, PR)
+  double* llpart;      // (B*Gb)
 };
 
 // fused E-step + statistics (gmm_estep.hip)
@@ -65,8 +72,9 @@ hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);
 
 // prologue / reduction / M-step (gmm_aux.hip)
-hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv,
-                           float* W, double* c, double* a, int32_t* flag, hipStream_t s);
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W,
+                           double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
+                           hipStream_t s);
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s);

@@ -127,11 +127,9 @@ SHAPES = [
     ("diag", 1, 4096, 32, 17),          # ragged K
     ("diag", 1, 5000, 64, 100),
     ("diag", 1, 8191, 65, 16),          # D just past a padding step
-    pytest.param("diag", 1, 4096, 128, 128, marks=pytest.mark.xfail(
-        reason="components collapse to the variance floor; needs the float64 logit path", strict=False)),
+    ("diag", 1, 4096, 128, 128),       # components collapse onto single rows
     ("diag", 3, 3000, 16, 40),          # batched
-    pytest.param("diag", 1, 65536, 32, 256, marks=pytest.mark.xfail(
-        reason="a near-collapsed component (precision ~4e3); needs the float64 logit path", strict=False)),
+    ("diag", 1, 65536, 32, 256),       # a near-collapsed component (precision ~4e3)
     ("full", 1, 5000, 16, 32),
     ("full", 1, 3001, 5, 7),
     ("full", 2, 2048, 8, 16),
