@@ -55,6 +55,24 @@ def contraction_split(cov, D):
     return half, total - half
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, if it was taken on this workload with the current kernel source."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"estep_{workload}_traffic.md")
+    src = os.path.join(ROOT, "soft_clustering_em_amd", "csrc", "gmm_estep.hip")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- machine-readable: (\{.*\}) -->", open(path).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec["kernel_sha256"] != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(wl, budget_s=20.0, max_steps=4):
     import oracle
     nthreads = os.cpu_count() or 1
@@ -159,7 +177,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
+            "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "fused E-step + statistics",
             "kernel_ms": k_ms,
             "flops_per_launch": flops,
