@@ -72,7 +72,6 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   if (st != GMM_OK) return st;
   if (K < 1) return fail(GMM_ERR_INVALID_ARG, "K must be >= 1");
   if (cov < SPH || cov > FULL) return fail(GMM_ERR_INVALID_ARG, "unknown covariance type %d", cov);
-  if (op == GMM_OP_TOPM) return fail(GMM_ERR_UNSUPPORTED, "top-m is not available for this shape");
   Plan q;
   q.cov = cov;
   q.dtype = d->dtype;
@@ -111,8 +110,19 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
                             2 * (size_t)q.NW * T + q.F);
   };
   q.T = 0;
+  if (op == GMM_OP_TOPM) {
+    if (K > kTopmMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m supports K <= %d", kTopmMaxK);
+    const size_t T = kTopmRows, C = kTopmCap;
+    q.T = (int)T;
+    q.direct = false;
+    q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F) +
+            sizeof(double) * (T + (size_t)q.NW * T + T * C);
+    if (q.lds > kLdsBytes) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K,
+                                       (long long)d->D);
+  }
   // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
   for (int nraw : {2, 1}) {
+    if (q.T) break;
     if (nraw == 2 && !direct_ok) continue;
     for (int T : {64, 32, 16}) {
       if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
@@ -124,7 +134,7 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     if (q.T) break;
   }
   if (!q.T) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld does not fit in LDS", K, (long long)d->D);
-  q.lds = lds_for(q.T, q.direct ? 2 : 1);
+  if (op != GMM_OP_TOPM) q.lds = lds_for(q.T, q.direct ? 2 : 1);
   q.ntiles = (q.N + q.T - 1) / q.T;
   const int wg_lds = (int)std::max<size_t>(1, kLdsBytes / q.lds);
   const int wg_per_cu = std::max(1, std::min(wg_lds, 8 / q.NW));
@@ -142,9 +152,11 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_flag = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
   q.off_sharp = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
-  q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
-  q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
-  q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.PR);
+  if (op != GMM_OP_TOPM) {
+    q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
+    q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
+    q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.PR);
+  }
   if (op == GMM_OP_FIT) {
     q.off_nk = o;  o = align_up(o + sizeof(double) * (size_t)q.B * K);
     q.off_sx = o;  o = align_up(o + sizeof(double) * (size_t)q.B * K * q.D);
@@ -305,10 +317,56 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
 gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
                                   int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, size_t ws_bytes,
                                   void* stream) {
-  (void)data; (void)params; (void)m; (void)threshold; (void)idx; (void)resp; (void)count; (void)logp;
-  (void)ws; (void)ws_bytes; (void)stream;
   g_err.clear();
-  return fail(GMM_ERR_UNSUPPORTED, "top-m is not available yet");
+  gmm_status st = check_params(params, 0, 0, true);
+  if (st != GMM_OK) return st;
+  if (m < 1 || m > 16) return fail(GMM_ERR_INVALID_ARG, "m must be in [1, 16] (got %d)", m);
+  if (!(threshold >= 0.0f && threshold <= 1.0f)) return fail(GMM_ERR_INVALID_ARG, "threshold must be in [0, 1]");
+  Plan p;
+  st = make_plan(data, params->K, params->cov, GMM_OP_TOPM, &p);
+  if (st != GMM_OK) return st;
+  if (p.N > 0 && (!idx || !resp)) return fail(GMM_ERR_INVALID_ARG, "idx and resp must be non-NULL");
+  st = check_ws(p, ws, ws_bytes);
+  if (st != GMM_OK) return st;
+  if (p.N == 0) return GMM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  float* W = reinterpret_cast<float*>(w + p.off_W);
+  double* prec = reinterpret_cast<double*>(w + p.off_prec);
+  double* c0 = reinterpret_cast<double*>(w + p.off_c0);
+  double* c = reinterpret_cast<double*>(w + p.off_c);
+  double* a = reinterpret_cast<double*>(w + p.off_a);
+  int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
+  int32_t* sharp = reinterpret_cast<int32_t*>(w + p.off_sharp);
+  hipError_t e = launch_prologue(p, params->weights, params->means, params->covars, W, prec, c0, c, a, flag, sharp, s);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  TopmArgs A;
+  A.x = data->x;
+  A.N = p.N;
+  A.D = p.D;
+  A.ld_x = p.ld_x;
+  A.stride_b = p.stride_b;
+  A.K = (int)p.K;
+  A.KP = p.KP;
+  A.NW = p.NW;
+  A.Gb = p.Gb;
+  A.ntiles = p.ntiles;
+  A.W = W;
+  A.c = c;
+  A.a = a;
+  A.mu = params->means;
+  A.prec = prec;
+  A.c0 = c0;
+  A.prec_stride = p.prec_stride;
+  A.m = m;
+  A.thr = threshold;
+  A.idx = idx;
+  A.resp = resp;
+  A.count = count;
+  A.logp = logp;
+  e = launch_topm(p, A, s);
+  if (e != hipSuccess) return hip_fail(e, "top-m launch");
+  return GMM_OK;
 }
 
 const char* gmm_status_str(int32_t status) {

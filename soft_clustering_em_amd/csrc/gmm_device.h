@@ -1,0 +1,78 @@
+// gmm_device.h -- device helpers shared by the fused E-step kernel and the
+// top-m kernel: 16-lane DPP reductions, the product-feature index map, and
+// the float64 log-score by direct differences.
+#pragma once
+
+#include "gmm_internal.h"
+
+#include <math.h>
+
+namespace gmm {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// 16-lane all-reduce with DPP (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror); every lane of a 16-lane row ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_mov<0xB1>(v);
+  v = v + dpp_mov<0x4E>(v);
+  v = v + dpp_mov<0x141>(v);
+  v = v + dpp_mov<0x140>(v);
+  return v;
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// product feature f >= DP of the quadratic feature map: (d, e) packed as d << 16 | e
+template <int DP>
+__device__ __forceinline__ int quad_pair(int q) {
+  int d = 0, base = 0;
+  while (q >= base + (DP - d)) { base += DP - d; ++d; }
+  return (d << 16) | (d + (q - base));
+}
+
+// log2 of pi_k N(x | mu_k, Sigma_k) for one row x (float32 values in LDS), by
+// direct differences in float64: c0_k - 1/2 log2(e) (x - mu)^T P (x - mu).
+// prec holds 1/sigma^2 (spherical: one value; diag: D values) or, for
+// full/tied, the lower-triangular L^{-1} of Sigma = L L^T (D x D).
+template <int COV, int DP, class Args>
+__device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D, const float* x) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  const float* mu = A.mu + ((size_t)b * A.K + k) * D;
+  const double* P = A.prec + ((size_t)b * A.KP + k) * (size_t)A.prec_stride;
+  double q = 0.0;
+  if constexpr (COV == SPH) {
+    for (int d = 0; d < D; ++d) {
+      const double t = (double)x[d] - (double)mu[d];
+      q += t * t;
+    }
+    q *= P[0];
+  } else if constexpr (COV == DIAG) {
+    for (int d = 0; d < D; ++d) {
+      const double t = (double)x[d] - (double)mu[d];
+      q += P[d] * t * t;
+    }
+  } else {
+    for (int i = 0; i < D; ++i) {
+      double z = 0.0;
+      for (int j = 0; j <= i; ++j) z += P[i * D + j] * ((double)x[j] - (double)mu[j]);
+      q += z * z;
+    }
+  }
+  return A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;
+}
+
+}  // namespace gmm

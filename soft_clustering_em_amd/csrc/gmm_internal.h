@@ -67,6 +67,32 @@ struct EStepArgs {
   double* llpart;      // (B*Gb)
 };
 
+// soft multi-assignment (gmm_topm.hip)
+constexpr int kTopmRows = 16;   // rows per tile
+constexpr int kTopmCap = 64;    // candidates per row kept in LDS before the all-K path
+constexpr int kTopmMaxK = 256;
+
+struct TopmArgs {
+  const void* x;
+  int64_t N, D, ld_x, stride_b;
+  int K, KP, NW, Gb;
+  int64_t ntiles;
+  const float* W;
+  const double* c;
+  const double* a;
+  const float* mu;
+  const double* prec;
+  const double* c0;
+  int prec_stride;
+  int m;
+  float thr;
+  int32_t* idx;
+  float* resp;
+  int32_t* count;
+  float* logp;
+};
+hipError_t launch_topm(const Plan& p, const TopmArgs& a, hipStream_t s);
+
 // fused E-step + statistics (gmm_estep.hip)
 hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);

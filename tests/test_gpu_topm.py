@@ -1,0 +1,142 @@
+"""Parity of gmm_predict_proba_topm against the float64 oracle.
+
+The kept component indices (and their count) must match exactly on every row
+whose oracle margin exceeds 1e-6 (the smallest gap among consecutive ranks
+1..m+1 and between ranks 2..m and the threshold); the other rows are counted
+and excluded.  Responsibilities and log p(x) are compared to 1e-6 (they are
+returned in float32).  Soft multi-assignment as in Flash-GMM, Section 4 and
+Conclusion.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity import oracle_trajectory
+from soft_clustering_em_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import soft_clustering_em_amd._abi as abi
+    abi.lib()
+    return torch
+
+
+def gpu_topm(torch, X, cov, w, mu, cv, m, thr):
+    import soft_clustering_em_amd as g
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to("cuda")
+    if Xd.dim() == 2:
+        Xd = Xd[None]
+    B, N, _ = Xd.shape
+    wd, mud, cvd = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda") for a in (w, mu, cv))
+    idx = torch.full((B, N, m), -7, dtype=torch.int32, device="cuda")
+    resp = torch.full((B, N, m), -7.0, dtype=torch.float32, device="cuda")
+    cnt = torch.full((B, N), -7, dtype=torch.int32, device="cuda")
+    logp = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+    g.gmm_predict_proba_topm(Xd, wd, mud, cvd, cov, m, thr, idx, resp, cnt, logp)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), resp.cpu().numpy(), cnt.cpu().numpy(), logp.cpu().numpy()
+
+
+def check_topm(torch, X, cov, w, mu, cv, m=4, thr=0.1, label=""):
+    """X (B,N,D) float32; parameters float32 with a leading B axis."""
+    B = X.shape[0]
+    gi, gr, gc, gl = gpu_topm(torch, X, cov, w, mu, cv, m, thr)
+    thr32 = float(np.float32(thr))
+    excluded = 0
+    for b in range(B):
+        oi, orr, oc, ol, om = oracle.topm(cov, X[b], w[b].astype(np.float64), mu[b].astype(np.float64),
+                                          cv[b].astype(np.float64), m, thr32)
+        ok = om > 1e-6
+        excluded += int((~ok).sum())
+        bad = np.nonzero(ok & ((gi[b] != oi).any(1) | (gc[b] != oc)))[0]
+        assert bad.size == 0, (label, b, bad[:5], gi[b][bad[:5]], oi[bad[:5]], om[bad[:5]])
+        kept = oi >= 0
+        np.testing.assert_allclose(gr[b][ok[:, None] & kept], orr[ok[:, None] & kept], rtol=1e-6, atol=1e-7)
+        assert (gr[b][~kept & ok[:, None]] == 0).all()
+        np.testing.assert_allclose(gl[b], ol, rtol=2e-6, atol=1e-5)
+    print(f"{label}: rows={B * X.shape[1]} excluded(margin<=1e-6)={excluded}", flush=True)
+    return excluded
+
+
+def test_topm_spherical_small_final_model(torch_cuda):
+    wl = synth.spherical_small()
+    th, _ = oracle_trajectory(wl, wl.iters)
+    w, mu, cv = th[-1]
+    check_topm(torch_cuda, wl.X, "spherical", w, mu, cv, label="spherical_small")
+
+
+def test_topm_diag_large_reduced(torch_cuda):
+    wl = synth.diag_large(N=100_000)
+    th, _ = oracle_trajectory(wl, 3)
+    w, mu, cv = th[-1]
+    check_topm(torch_cuda, wl.X, "diag", w, mu, cv, label="diag_large N=100k")
+
+
+def test_topm_diag_batched(torch_cuda):
+    wl = synth.diag_batched(B=3, N=20_000)
+    th, _ = oracle_trajectory(wl, 2)
+    w, mu, cv = th[-1]
+    check_topm(torch_cuda, wl.X, "diag", w, mu, cv, m=3, thr=0.05, label="diag_batched")
+
+
+def test_topm_full(torch_cuda):
+    wl = synth.full_large(N=50_000)
+    th, _ = oracle_trajectory(wl, 2)
+    w, mu, cv = th[-1]
+    check_topm(torch_cuda, wl.X, "full", w, mu, cv, m=4, thr=0.1, label="full N=50k")
+
+
+def test_topm_tied(torch_cuda):
+    rng = np.random.default_rng(3)
+    K, D, N = 12, 6, 8000
+    X = (3 * rng.standard_normal((1, N, D))).astype(np.float32)
+    w = np.full((1, K), 1 / K, np.float32)
+    mu = (3 * rng.standard_normal((1, K, D))).astype(np.float32)
+    A = rng.standard_normal((D, D))
+    cv = (A @ A.T + D * np.eye(D)).astype(np.float32)[None]
+    check_topm(torch_cuda, X, "tied", w, mu, cv, m=5, thr=0.02, label="tied")
+
+
+@pytest.mark.parametrize("m,K", [(1, 16), (16, 20), (4, 3), (6, 256)])
+def test_topm_widths(torch_cuda, m, K):
+    rng = np.random.default_rng(m * 100 + K)
+    D, N = 10, 3000
+    X = rng.standard_normal((1, N, D)).astype(np.float32)
+    w = rng.dirichlet(np.ones(K))[None].astype(np.float32)
+    mu = rng.standard_normal((1, K, D)).astype(np.float32)
+    cv = rng.uniform(0.5, 2.0, (1, K, D)).astype(np.float32)
+    check_topm(torch_cuda, X, "diag", w, mu, cv, m=m, thr=0.05, label=f"m={m} K={K}")
+
+
+def test_topm_many_candidates_path(torch_cuda):
+    """Every component close to every row: more than 64 candidates per row, so
+    the all-components path runs."""
+    rng = np.random.default_rng(5)
+    K, D, N = 200, 4, 2000
+    X = (0.1 * rng.standard_normal((1, N, D))).astype(np.float32)
+    mu = (0.01 * rng.standard_normal((1, K, D))).astype(np.float32)
+    w = np.full((1, K), 1 / K, np.float32)
+    cv = np.full((1, K), 4.0, np.float32)
+    check_topm(torch_cuda, X, "spherical", w, mu, cv, m=4, thr=0.001, label="flat")
+
+
+def test_argmax_is_nearest_mean_for_shared_variance(torch_cuda):
+    """Equal weights, one shared spherical variance: rank 1 is the nearest mean
+    (the k-means limit of the GMM, exact for any variance)."""
+    rng = np.random.default_rng(6)
+    K, D, N = 64, 16, 20000
+    X = rng.standard_normal((1, N, D)).astype(np.float32)
+    mu = rng.standard_normal((1, K, D)).astype(np.float32)
+    w = np.full((1, K), 1 / K, np.float32)
+    cv = np.full((1, K), 0.7, np.float32)
+    gi, _, gc, _ = gpu_topm(torch_cuda, X, "spherical", w, mu, cv, 1, 0.1)
+    d2 = ((X[0].astype(np.float64)[:, None, :] - mu[0].astype(np.float64)[None]) ** 2).sum(-1)
+    srt = np.sort(d2, 1)
+    clear = (srt[:, 1] - srt[:, 0]) > 1e-4
+    np.testing.assert_array_equal(gi[0, clear, 0], d2.argmin(1)[clear])
+    assert (gc == 1).all()
