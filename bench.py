@@ -32,6 +32,7 @@ METRIC = ("EM iterations/sec and N·K points·components/s per iteration; "
 # MI355X published dense peaks (TFLOP/s)
 PEAK_FP32_MFMA = 157.3
 PEAK_FP64_MFMA = 78.6
+PEAK_BF16_MFMA = 2500.0
 
 
 def flops_per_pair(cov, D):
@@ -47,6 +48,13 @@ def flops_per_pair(cov, D):
     return 4 * (D + q) + 2
 
 
+def largek_roofline(D):
+    """(algorithmic flops, executed flops) per pair of the bf16 large-K E-step:
+    logits 2D (the hi and lo weight terms, in pass A and again in pass C:
+    4 x 2D executed) and statistics 2D, plus N_k and sum r|x|^2."""
+    return 4 * D + 4, 10 * D + 4
+
+
 def contraction_split(cov, D):
     """(float32 flops, float64 flops) per pair: logits run on the float32 MFMA,
     statistics on the float64 MFMA."""
@@ -55,13 +63,13 @@ def contraction_split(cov, D):
     return half, total - half
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the fused kernel from the committed counter
-    summary, if it was taken on this workload with the current kernel source."""
+def measured_traffic(workload, source):
+    """HBM bytes per launch of the E-step from the committed counter summary,
+    if it was taken on this workload with the current kernel source."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"estep_{workload}_traffic.md")
-    src = os.path.join(ROOT, "soft_clustering_em_amd", "csrc", "gmm_estep.hip")
+    src = os.path.join(ROOT, "soft_clustering_em_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     m = re.search(r"<!-- machine-readable: (\{.*\}) -->", open(path).read())
@@ -73,10 +81,16 @@ def measured_traffic(workload):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, budget_s=20.0, max_steps=4):
+def cpu_baseline(wl, budget_s=20.0, max_steps=4, target_macs=2e10):
+    """The float64 oracle's EM iteration on the host cores, on the first rows of
+    the workload (all of them when one iteration stays near target_macs
+    multiply-adds), reported per point*component."""
     import oracle
     nthreads = os.cpu_count() or 1
-    X = wl.X if wl.xdtype == "f32" else (wl.X, "bf16")
+    per_pair = wl.D * (wl.D + 1) if wl.cov in ("full", "tied") else wl.D
+    rows = int(min(wl.N, max(1024, target_macs // (wl.B * wl.K * per_pair))))
+    Xs = wl.X[:, :rows]
+    X = Xs if wl.xdtype == "f32" else (Xs, "bf16")
     w, mu, cv = (a.astype(np.float64) for a in (wl.w0, wl.mu0, wl.cv0))
     times = []
     t_start = time.perf_counter()
@@ -88,9 +102,10 @@ def cpu_baseline(wl, budget_s=20.0, max_steps=4):
         if time.perf_counter() - t_start > budget_s:
             break
     t = float(np.median(times))
-    return {"value": wl.B * wl.N * wl.K / t, "unit": "points*components/s", "cores": nthreads,
+    what = "the full" if rows == wl.N else f"the first {rows} rows of the"
+    return {"value": wl.B * rows * wl.K / t, "unit": "points*components/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": f"{len(times)} float64 EM iterations of the full {wl.name} workload "
+            "sample": f"{len(times)} float64 EM iterations of {what} {wl.name} workload "
                       f"(B={wl.B}, N={wl.N}, D={wl.D}, K={wl.K}) from theta_0, median "
                       f"{t:.2f} s/iteration"}
 
@@ -101,7 +116,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="diag_large",
-                    choices=["diag_large", "spherical_small", "diag_batched", "full_large"])
+                    choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (traffic counter calibration)")
@@ -117,7 +132,10 @@ def main():
     dev = "cuda"
     torch.cuda.init()
     wl = synth.WORKLOADS[args.workload]()
-    X = torch.from_numpy(wl.X).to(dev)
+    if wl.xdtype == "bf16":
+        X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(wl.X).to(dev)
     w = torch.from_numpy(wl.w0.copy()).to(dev)
     mu = torch.from_numpy(wl.mu0.copy()).to(dev)
     cv = torch.from_numpy(wl.cv0.copy()).to(dev)
@@ -151,10 +169,23 @@ def main():
     k_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
 
     pairs = wl.B * wl.N * wl.K
-    f32f, f64f = contraction_split(wl.cov, wl.D)
-    flops = pairs * (f32f + f64f)
+    if wl.xdtype == "bf16":
+        alg, executed = largek_roofline(wl.D)
+        flops = pairs * alg
+        peak = PEAK_BF16_MFMA
+        kernel = "large-K E-step (prologue + passes A, B, C)"
+        peak_note = (f"bf16 MFMA dense peak; {alg} algorithmic flop/pair (2D logits + 2D statistics); "
+                     f"{executed} flop/pair executed (two-term weights, logits recomputed in pass C)")
+        dtype = "bf16"
+    else:
+        f32f, f64f = contraction_split(wl.cov, wl.D)
+        flops = pairs * (f32f + f64f)
+        peak = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
+        kernel = "fused E-step + statistics"
+        peak_note = (f"float32 MFMA logits ({f32f} flop/pair at {PEAK_FP32_MFMA} TF) + float64 MFMA "
+                     f"statistics ({f64f} flop/pair at {PEAK_FP64_MFMA} TF), time-weighted")
+        dtype = "f32"
     achieved = flops / (k_ms * 1e-3) / 1e12
-    peak = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
     res = {
         "metric": METRIC,
         "value": pairs / step_s,
@@ -167,7 +198,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "cov": wl.cov, "B": wl.B, "N": wl.N, "D": wl.D, "K": wl.K,
                    "iters_per_fit": wl.iters},
@@ -177,13 +208,12 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": measured_traffic(wl.name),
+            "traffic": measured_traffic(wl.name, "gmm_largek.hip" if wl.xdtype == "bf16" else "gmm_estep.hip"),
             "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "fused E-step + statistics",
+            "kernel": kernel,
             "kernel_ms": k_ms,
             "flops_per_launch": flops,
-            "peak_note": (f"float32 MFMA logits ({f32f} flop/pair at {PEAK_FP32_MFMA} TF) + float64 MFMA "
-                          f"statistics ({f64f} flop/pair at {PEAK_FP64_MFMA} TF), time-weighted"),
+            "peak_note": peak_note,
         },
         "mean_loglik_last": float(mll.mean().item()),
     }

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = ["gmm_api.hip", "gmm_aux.hip", "gmm_estep.hip", "gmm_topm.hip"]
+SOURCES = ["gmm_api.hip", "gmm_aux.hip", "gmm_estep.hip", "gmm_topm.hip", "gmm_largek.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,9 +25,15 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# per-file additions: the large-K kernels take maxima of finite values only
+# (dead components carry a finite floor), so min/max need no NaN quieting and
+# fold with their DPP operands
+EXTRA = {"gmm_largek.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

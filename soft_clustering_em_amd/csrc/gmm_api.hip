@@ -49,8 +49,7 @@ static gmm_status check_data(const gmm_data* d) {
   if (d->N > 0 && !d->x) return fail(GMM_ERR_INVALID_ARG, "x is NULL");
   if (d->dtype != GMM_DT_F32 && d->dtype != GMM_DT_BF16 && d->dtype != GMM_DT_F16)
     return fail(GMM_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
-  if (d->dtype != GMM_DT_F32)
-    return fail(GMM_ERR_UNSUPPORTED, "this entry point supports float32 rows only");
+  if (d->dtype == GMM_DT_F16) return fail(GMM_ERR_UNSUPPORTED, "float16 rows are not supported");
   if (d->N > ((int64_t)1 << 40)) return fail(GMM_ERR_UNSUPPORTED, "N too large");
   return GMM_OK;
 }
@@ -64,6 +63,33 @@ static gmm_status check_params(const gmm_params* p, int64_t B, int64_t D, bool n
   (void)B;
   (void)D;
   return GMM_OK;
+}
+
+// Workspace of the large-K E-step for chunks of `chunk` rows (a multiple of
+// the 32-row tile): weights and constants, per-(row, slice) maxima and sums,
+// row LSE, statistics partials, and (fit) the reduced statistics.
+static void largek_layout(Plan& q, int64_t chunk) {
+  q.chunk_rows = chunk;
+  size_t o = 0;
+  q.off_W = o;    o = align_up(o + (size_t)q.KP * q.DP * 2 * 2);
+  q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.KP);
+  q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.KP);
+  q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.KP);
+  q.off_prec = o; o = align_up(o + sizeof(double) * (size_t)q.KP);
+  q.off_sharp = o; o = align_up(o + sizeof(float) * 2 * (size_t)q.KP);
+  q.off_P = o;    o = align_up(o + sizeof(float) * 2 * (size_t)chunk * q.S);
+  q.off_lse = o;  o = align_up(o + sizeof(float) * (size_t)chunk);
+  q.off_xsq = o;  o = align_up(o + sizeof(double) * (size_t)chunk);
+  q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
+  q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.llG);
+  q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.KP * q.PR);
+  if (q.op == GMM_OP_FIT) {
+    q.off_nk = o;  o = align_up(o + sizeof(double) * (size_t)q.K);
+    q.off_sx = o;  o = align_up(o + sizeof(double) * (size_t)q.K * q.D);
+    q.off_sxx = o; o = align_up(o + sizeof(double) * (size_t)q.K);
+    q.off_ll = o;  o = align_up(o + sizeof(double));
+  }
+  q.ws_bytes = o;
 }
 
 // Choose the tiling of the fused kernel and lay out the workspace.
@@ -81,6 +107,37 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.K = K;
   q.ld_x = d->ld_x;
   q.stride_b = d->B > 1 ? d->stride_b : 0;
+  if (d->dtype == GMM_DT_BF16) {
+    // bf16 rows: spherical components through the slice-parallel three-pass E-step
+    if (cov != SPH) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows are supported for spherical components only");
+    if (op == GMM_OP_TOPM) return fail(GMM_ERR_UNSUPPORTED, "top-m over bf16 rows is not supported");
+    if (d->B != 1) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: one problem per call (B = 1)");
+    if (d->D > 128) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: D <= 128");
+    q.largek = true;
+    q.DP = 128;
+    q.F = q.G = q.DP;
+    q.PR = 2 + q.G;
+    q.KW = 32;
+    q.NW = kLargeKSlice / 32;
+    q.S = (K + kLargeKSlice - 1) / kLargeKSlice;
+    q.KP = q.S * kLargeKSlice;
+    q.T = 32;
+    q.SC = q.KP / (kLargeKSlice / 2);
+    // row groups: about one workgroup per CU; a multiple of 8 keeps a row
+    // group's slices on one XCD
+    q.GbA = (std::max(1, kNumCU / q.S) + 7) / 8 * 8;
+    q.Gb = (std::max(1, kNumCU / q.SC) + 7) / 8 * 8;
+    q.lse_blocks = 512;
+    q.llG = q.lse_blocks;
+    q.ntiles = (q.N + 31) / 32;
+    q.lds_a = largek_lds_bytes(q.DP, 0);
+    q.lds_c = largek_lds_bytes(q.DP, 2);
+    q.prec_stride = 1;
+    q.op = op;
+    largek_layout(q, std::min<int64_t>((q.N + 31) / 32 * 32, kLargeKChunk));
+    *p = q;
+    return GMM_OK;
+  }
   if (cov == SPH || cov == DIAG) {
     q.DP = d->D <= 16 ? 16 : d->D <= 32 ? 32 : d->D <= 64 ? 64 : d->D <= 128 ? 128 : 0;
   } else {
@@ -142,6 +199,7 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   int64_t gb = std::max<int64_t>(1, total / q.B);
   gb = std::min<int64_t>(gb, std::max<int64_t>(1, q.ntiles));
   q.Gb = (int)gb;
+  q.llG = q.Gb;
   // workspace
   size_t o = 0;
   q.off_W = o;    o = align_up(o + sizeof(float) * (size_t)q.B * q.KP * q.F);
@@ -168,9 +226,24 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   return GMM_OK;
 }
 
-static gmm_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
   if (!ws) return fail(GMM_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)ws) % kAlign) return fail(GMM_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (p.largek && ws_bytes < p.ws_bytes) {
+    // a smaller workspace streams the rows in shorter chunks (multiples of 32 rows)
+    Plan q = p;
+    largek_layout(q, 32);
+    if (ws_bytes >= q.ws_bytes) {
+      const size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
+      int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
+      chunk = std::min<int64_t>(chunk, p.chunk_rows);
+      for (largek_layout(q, chunk); q.ws_bytes > ws_bytes && chunk > 32; largek_layout(q, chunk)) chunk -= 32;
+      if (q.ws_bytes <= ws_bytes) {
+        p = q;
+        return GMM_OK;
+      }
+    }
+  }
   if (ws_bytes < p.ws_bytes)
     return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, p.ws_bytes);
   return GMM_OK;
@@ -181,9 +254,50 @@ static gmm_status hip_fail(hipError_t e, const char* where) {
 }
 
 // prologue + fused E-step + reduction; statistics to the given buffers
+static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk,
+                                   double* sx, double* sxx, double* ll, double* mean_ll, int accumulate,
+                                   const gmm_options* opts, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  LargeKArgs A;
+  A.x = d->x;
+  A.N = p.N;
+  A.D = p.D;
+  A.ld_x = p.ld_x;
+  A.vec16 = (((uintptr_t)d->x) % 16 == 0) && (p.ld_x % 8 == 0);
+  A.K = (int)p.K;
+  A.KP = p.KP;
+  A.S = p.S;
+  A.G = p.Gb;
+  A.W = w + p.off_W;
+  A.c = reinterpret_cast<double*>(w + p.off_c);
+  A.a = reinterpret_cast<double*>(w + p.off_a);
+  A.mu = prm->means;
+  A.c0 = reinterpret_cast<double*>(w + p.off_c0);
+  A.lam = reinterpret_cast<double*>(w + p.off_prec);
+  A.esh = reinterpret_cast<float*>(w + p.off_sharp);
+  A.P = reinterpret_cast<float2*>(w + p.off_P);
+  A.lse = reinterpret_cast<float*>(w + p.off_lse);
+  A.xsq = reinterpret_cast<double*>(w + p.off_xsq);
+  A.llpart = reinterpret_cast<double*>(w + p.off_llp);
+  A.part = reinterpret_cast<double*>(w + p.off_part);
+  A.accumulate = 0;
+  hipError_t e;
+  if (opts && opts->event_begin && (e = hipEventRecord((hipEvent_t)opts->event_begin, s)) != hipSuccess)
+    return hip_fail(e, "event record");
+  e = launch_largek(p, A, prm->weights, prm->means, prm->covars, s);
+  if (e != hipSuccess) return hip_fail(e, "large-K E-step launch");
+  if (opts && opts->event_end && (e = hipEventRecord((hipEvent_t)opts->event_end, s)) != hipSuccess)
+    return hip_fail(e, "event record");
+  e = launch_reduce_raw(p, A.part, A.llpart, prm->means, reinterpret_cast<double*>(w + p.off_aux), nk, sx, sxx, ll,
+                        mean_ll, accumulate, s);
+  if (e != hipSuccess) return hip_fail(e, "reduction launch");
+  return GMM_OK;
+}
+
 static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk, double* sx,
                             double* sxx, double* ll, double* mean_ll, int accumulate, const gmm_options* opts,
                             hipStream_t s) {
+  if (p.largek) return run_estep_largek(p, d, prm, ws, nk, sx, sxx, ll, mean_ll, accumulate, opts, s);
   char* w = static_cast<char*>(ws);
   float* W = reinterpret_cast<float*>(w + p.off_W);
   double* prec = reinterpret_cast<double*>(w + p.off_prec);
@@ -307,7 +421,7 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
   hipStream_t s = (hipStream_t)stream;
   st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s);
   if (st != GMM_OK) return st;
-  const int32_t* flag = reinterpret_cast<const int32_t*>(w + p.off_flag);
+  const int32_t* flag = p.largek ? nullptr : reinterpret_cast<const int32_t*>(w + p.off_flag);
   hipError_t e = launch_mstep_strided(p.cov, p.B, p.D, p.K, nk, sx, sxx, p.N, inout->weights, inout->means,
                                       inout->covars, reg, flag, p.KP, comp_status, s);
   if (e != hipSuccess) return hip_fail(e, "M-step launch");

@@ -218,7 +218,7 @@ hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const
 // workgroup order (float64) into raw[b][k][:], and (non-tied) writes the
 // statistics centred at the input means.  Blocks B*K + b sum the
 // log-likelihood partials.  Tied covariance is centred by centre_tied_kernel.
-__global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int KP, int DP, int PR, int Gb,
+__global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int KP, int DP, int PR, int Gb, int llG,
                                                      int64_t N, const double* __restrict__ part,
                                                      const double* __restrict__ llpart,
                                                      const float* __restrict__ mu, double* __restrict__ raw,
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
     const int b = blockIdx.x - B * K;
     if (tid == 0) {
       double s = 0.0;
-      for (int g = 0; g < Gb; ++g) s += llpart[(size_t)b * Gb + g];
+      for (int g = 0; g < llG; ++g) s += llpart[(size_t)b * llG + g];
       ll[b] = accumulate ? ll[b] + s : s;
       if (mean_ll) mean_ll[b] = s / (double)N;
     }
@@ -328,7 +328,7 @@ hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* ll
   const size_t lds = sizeof(double) * (size_t)(p.PR + p.D);
   const unsigned threads = (unsigned)std::min(256, std::max(64, (p.PR + 63) / 64 * 64));
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(threads), lds, s, p.cov, (int)p.D,
-                     (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
+                     (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.llG, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
                      accumulate, (int)p.B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.cov != TIED) return e;

@@ -38,6 +38,16 @@ struct Plan {
   int KW = 0, NW = 0, KP = 0, T = 0;
   int PR = 0;               // doubles per component in a workgroup partial: [N_k, Q_k, G rows]
   int Gb = 0;               // workgroups per problem
+  int llG = 0;              // log-likelihood partials per problem
+  int op = 0;               // GMM_OP_* the plan was made for
+  bool largek = false;      // spherical bf16 rows through the slice-parallel three-pass E-step
+  int S = 0;                // 256-component slices (large K, pass A)
+  int SC = 0;               // 128-component slices (large K, pass C)
+  int GbA = 0;              // row groups of pass A (pass C uses Gb)
+  int64_t chunk_rows = 0;   // rows per chunk (large K)
+  int lse_blocks = 0;       // blocks of the large-K LSE pass
+  size_t lds_a = 0, lds_c = 0;
+  size_t off_P = 0, off_lse = 0, off_xsq = 0;
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
@@ -66,6 +76,33 @@ struct EStepArgs {
   double* part;        // (B*Gb, KP, PR)
   double* llpart;      // (B*Gb)
 };
+
+// spherical E-step for large K and bfloat16 rows (gmm_largek.hip)
+constexpr int kLargeKSlice = 256;          // components per workgroup
+constexpr int64_t kLargeKChunk = 1 << 20;  // rows per chunk (scratch is O(chunk))
+
+struct LargeKArgs {
+  const void* x;        // bf16 rows of the current chunk
+  int64_t N, D, ld_x;   // N: rows in the chunk
+  int vec16;            // rows can be read with 16-byte loads
+  int K, KP, S, G;      // S slices of kLargeKSlice components; G row groups of the launch
+  const void* W;        // (KP/16, 2, DP/32, 64, 8) bf16 weights, hi and lo parts, fragment order
+  const double* c;      // (KP)
+  const double* a;      // (KP)
+  const float* mu;      // (K, D) means, for the exact scores of sharp components
+  const double* c0;     // (KP) log2(pi_k) - (D log2(2 pi var_k)) / 2
+  const double* lam;    // (KP) 1 / var_k
+  const float* esh;     // (KP, 2) error bound of the expanded score (0: component not sharp)
+  float2* P;            // (chunk, S) per-slice (max, sum)
+  float* lse;           // (chunk) row log-sum-exp, log2 units
+  double* xsq;          // (chunk) |x|^2 of each row (pass A writes, pass C reads)
+  double* llpart;       // (lse blocks)
+  double* part;         // (G, KP, 2 + DP)
+  int accumulate;       // add to part / llpart (every chunk after the first)
+};
+hipError_t launch_largek(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,
+                         hipStream_t s);
+size_t largek_lds_bytes(int DP, int pass);  // dynamic LDS of pass A (0) / C (2)
 
 // soft multi-assignment (gmm_topm.hip)
 constexpr int kTopmRows = 16;   // rows per tile

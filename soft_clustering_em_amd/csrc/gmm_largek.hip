@@ -1,0 +1,603 @@
+// gmm_largek.hip -- the E-step for spherical components when K is too large
+// for one workgroup to hold every component's statistics (the IVF-sized
+// workload: K = 4096, D = 128, bfloat16 rows).
+//
+// What it computes is the same as the fused kernel of gmm_estep.hip ("Flash-
+// GMM: A Memory-Efficient Kernel for Scalable Soft Clustering", Sections 2 and
+// 3): log-scores, row log-sum-exp, responsibilities, and the statistics N_k,
+// sum r x, sum r |x|^2 and sum LSE, with no N x K matrix in memory.  The
+// difference is the decomposition.  Components are cut into slices; a
+// workgroup owns one slice (its logit weights in LDS, its statistics in
+// registers) and streams rows.  A row's normaliser needs every slice, so each
+// chunk of rows takes three passes:
+//   A  per (row, 256-component slice): max and sum of 2^(l - max)
+//   B  per row: combine the slices -> LSE (log2 units) and sum LSE
+//   C  per (row, 128-component slice): logits again, r = 2^(l - LSE),
+//      statistics
+// Scratch is O(chunk), not O(N).
+//
+// gfx950 specifics: the x . (lambda mu) contraction runs on
+// v_mfma_f32_16x16x32_bf16 with the weights split into bf16 hi + lo parts (x
+// itself is exact in bf16); the statistics contraction X^T R runs on the same
+// instruction with r rounded to bf16.  Every statistic (N_k, sum r x,
+// sum r |x|^2) uses that same rounded r, so the M-step sees the exact moments
+// of one set of weights.  Each tile's MFMA results (32 rows: exact bf16
+// products) are added into float64 accumulators, and the responsibilities of
+// a tile are summed in two magnitude classes (r >= 2^-8 and below) by
+// separate MFMAs: a component collapsed onto a row far from the origin has a
+// variance many orders below |mu|^2, carried by rows of tiny r that a
+// float32 sum with its own row, or float32 sums over many tiles, would bury.  The logit accumulator layout
+// (lane l: component l%16, rows 4(l/16)+v of a 16-row block) provides R as
+// the B operand of the statistics MFMA directly when the 32 rows of a tile
+// are ordered k = 8g + j <-> row 4g + j (j < 4), 16 + 4g + (j - 4) (j >= 4);
+// the A operand X^T is kept in LDS in that order.  Workgroups of one row
+// group and different slices have ids that differ by multiples of 8, so they
+// share an XCD and its L2 copy of the rows.
+#include "gmm_device.h"
+#include "gmm_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace gmm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int KSA = kLargeKSlice;      // components per workgroup in pass A (256)
+constexpr int KSC = kLargeKSlice / 2;  // components per workgroup in pass C (128)
+constexpr int LNW = 8;                 // waves per workgroup
+constexpr int LT = 32;                 // rows per tile
+constexpr int LRS = 136;               // LDS row stride of the row tile, in bf16 (272 bytes)
+constexpr int XTS = 40;                // LDS row stride of the transposed tile, in bf16 (80 bytes)
+// A component is "sharp" when the terms of its expanded log-score reach
+// lambda (|mu|^2 + D sigma^2) > kSharpLowp: with bf16 weights (two-term
+// split) their rounding would reach about 1% of a responsibility.
+constexpr double kSharpLowp = 2.0e3;
+// responsibilities at or above this go to the "big" class of the statistics MFMA
+constexpr float kBigR = 0x1p-8f;
+// log-score constant of padded and dead components: finite, so that maxima
+// and differences stay finite, and far enough down that 2^(l - max) is 0
+constexpr float kDead = -1.0e30f;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
+
+// 16-lane all-reduce of a double (the two halves moved by the DPP patterns of
+// row16_sum)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffLL), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return v;
+}
+
+// The 16-byte piece of a row tile that thread j loads: pass A takes row
+// j / 16, dims 8 (j % 16) .. +7 (a row's pieces in 16 consecutive lanes);
+// pass C takes row j % 32, dims 8 (j / 32) .. +7 (a piece's 32 rows in
+// consecutive lanes, for the transposed copy).
+template <bool STATS>
+__device__ __forceinline__ void piece_of(int j, int& r, int& c8) {
+  if constexpr (STATS) {
+    r = j % LT;
+    c8 = (j / LT) * 8;
+  } else {
+    r = j / 16;
+    c8 = (j % 16) * 8;
+  }
+}
+
+struct Piece {
+  u16x8 v;
+  double xs;  // pass C: |x|^2 of row j (threads j < LT), computed by pass A
+};
+
+template <bool STATS>
+__device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, int64_t ntiles) {
+  const unsigned short* xb = reinterpret_cast<const unsigned short*>(A.x);
+  const int j = threadIdx.x;
+  int r, c8;
+  piece_of<STATS>(j, r, c8);
+  const int64_t row = tile * LT + r;
+  Piece pc;
+  pc.v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  pc.xs = 0.0;
+  if (tile < ntiles && row < A.N) {
+    if (c8 + 8 <= A.D && A.vec16) {
+      pc.v = *reinterpret_cast<const u16x8*>(xb + row * A.ld_x + c8);
+    } else {
+      for (int e = 0; e < 8; ++e) pc.v[e] = (c8 + e < A.D) ? xb[row * A.ld_x + c8 + e] : (unsigned short)0;
+    }
+  }
+  if constexpr (STATS) {
+    const int64_t xrow = tile * LT + j;
+    if (j < LT && tile < ntiles && xrow < A.N) pc.xs = A.xsq[xrow];
+  }
+  return pc;
+}
+
+// Write a thread's piece into the LDS tile.  Pass A also forms |x|^2 of each
+// row (each bf16 square is exact in float32, their sum exact in float64) and,
+// in the workgroups of slice 0, stores it for pass C; pass C writes the
+// transposed copy X^T[d][k] with the k order of the statistics MFMA.
+template <bool STATS>
+__device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc, int64_t row0, int slice,
+                                            unsigned short* rows, unsigned short* xt, double* xsq) {
+  const int j = threadIdx.x;
+  int r, c8;
+  piece_of<STATS>(j, r, c8);
+  *reinterpret_cast<u16x8*>(rows + r * LRS + c8) = pc.v;
+  if constexpr (STATS) {
+    const int g = (r & 15) >> 2, j4 = r & 3;
+    const int kpos = 8 * g + (r < 16 ? j4 : 4 + j4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xt[(c8 + e) * XTS + kpos] = pc.v[e];
+    if (j < LT) xsq[j] = pc.xs;
+  } else {
+    double sq = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf16_to_f32(pc.v[e]);
+      sq += (double)(f * f);
+    }
+    sq = row16_sum_f64(sq);
+    if ((j & 15) == 0) {
+      xsq[r] = sq;
+      if (slice == 0 && row0 + r < A.N) A.xsq[row0 + r] = sq;
+    }
+  }
+}
+
+// log2-units score of one row against component k from direct differences:
+// c0_k - (lambda_k / 2) |x - mu_k|^2 log2(e), in float64
+__device__ __forceinline__ float largek_exact_score(const float* __restrict__ mu, double c0, double lam, int D,
+                                                   const unsigned short* xrow) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  double q = 0.0;
+#pragma unroll 1
+  for (int d = 0; d < D; ++d) {
+    const double t = (double)bf16_to_f32(xrow[d]) - (double)mu[d];
+    q += t * t;
+  }
+  return (float)(c0 - 0.5 * kLog2e * lam * q);
+}
+
+}  // namespace
+
+size_t largek_lds_bytes(int DP, int pass) {
+  const int ksl = pass == 0 ? KSA : KSC;
+  size_t b = (size_t)(ksl / 16) * 2 * (DP / 32) * 64 * 16;  // weights
+  b += (size_t)LT * LRS * 2;                                // row tile
+  if (pass != 0) b += (size_t)DP * XTS * 2;                 // transposed tile
+  b += (size_t)LT * 8;                                      // |x|^2
+  if (pass == 0) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
+  return b;
+}
+
+// PASS: 0 = A (slice max/sum), 2 = C (statistics).
+// Weights in global memory: 16-component tiles, [tile][hi/lo][kstep][lane] x 16 bytes.
+template <int DP, int PASS>
+__global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
+  constexpr bool STATS = (PASS == 2);
+  constexpr int KSL = STATS ? KSC : KSA;  // components of this workgroup
+  constexpr int NT = KSL / LNW / 16;      // 16-column tiles per wave (2 in A, 1 in C)
+  constexpr int KSTEP = DP / 32;          // MFMA k-steps over the features
+  constexpr int GM = DP / 16;             // statistic row tiles (dimensions)
+  constexpr int WFRAG = (KSL / 16) * 2 * KSTEP * 64;
+  constexpr int PF = 3;                   // row tiles in flight (registers)
+  static_assert(DP == 128 && LT * DP / 8 == 64 * LNW, "one 16-byte piece per thread");
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int slice = blockIdx.x / A.G;
+  const int g = blockIdx.x % A.G;
+  const int64_t nrows = A.N;
+  const int64_t ntiles = (nrows + LT - 1) / LT;
+
+  extern __shared__ float lds[];
+  bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
+  unsigned short* rows = reinterpret_cast<unsigned short*>(Wl + WFRAG);
+  unsigned short* xt = rows + LT * LRS;
+  double* xsq = reinterpret_cast<double*>(xt + (STATS ? DP * XTS : 0));
+  float* red = reinterpret_cast<float*>(xsq + LT);   // pass A: 2 buffers of LNW * LT * 2
+
+  // the first row tiles start loading before the weights are staged
+  Piece pf[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) pf[u] = fetch_piece<STATS>(A, g + (int64_t)u * A.G, ntiles);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(A.W) + (size_t)slice * WFRAG;
+    uint4* dst = reinterpret_cast<uint4*>(Wl);
+    for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
+  }
+  float creg[NT], areg[NT];
+  float eb[NT], e0[NT];  // error bound of a sharp component's expanded score: eb |x|^2 + e0 (0: not sharp)
+  bool any_sharp = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+    creg[nt] = (float)A.c[k];
+    areg[nt] = (float)A.a[k];
+    eb[nt] = A.esh[2 * k];
+    e0[nt] = A.esh[2 * k + 1];
+    any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(eb[nt] > 0.f) != 0);
+  }
+  // pass C: statistics of the r >= 2^-8 class in float64 (one tile at a
+  // time), of the small class in the MFMA's float32 accumulator
+  double sbig[STATS ? GM : 1][NT][4];
+  floatx4 ssmall[STATS ? GM : 1][NT];
+  double nk[NT], qs[NT];
+#pragma unroll
+  for (int mt = 0; mt < (STATS ? GM : 1); ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ssmall[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sbig[mt][nt][v] = 0.0;
+    }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) nk[nt] = qs[nt] = 0.0;
+
+  // pass A: combine the waves' (max, sum) of a finished tile into P; run by
+  // one wave (rotating) while the others go on with the next tile
+  auto combine = [&](int64_t prow0, const float* rb) {
+    if (lane < LT) {
+      const int p = lane;
+      const int64_t row = prow0 + p;
+      if (row < nrows) {
+        float M = rb[p * 2];
+#pragma unroll
+        for (int w2 = 1; w2 < LNW; ++w2) M = fmaxf(M, rb[(w2 * LT + p) * 2]);
+        float S = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < LNW; ++w2)
+          S += rb[(w2 * LT + p) * 2 + 1] * __builtin_amdgcn_exp2f(rb[(w2 * LT + p) * 2] - M);
+        A.P[(size_t)row * A.S + slice] = float2{M, S};
+      }
+    }
+  };
+
+  auto process = [&](int64_t row0, int it) {
+    // ---- logits (log2 units): c + a |x|^2 + x . w_hi + x . w_lo
+    floatx4 acc[2][NT];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) {
+      bf16x8 av[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        av[rb] = *reinterpret_cast<const bf16x8*>(rows + (rb * 16 + (lane & 15)) * LRS + ks * 32 + 8 * (lane >> 4));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 bw = Wl[(((wv * NT + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bw, acc[rb][nt], 0, 0, 0);
+        }
+    }
+    // lane's rows: q = rb * 4 + v <-> tile row rb * 16 + 4 (lane / 16) + v
+    float lg[8][NT];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float xs = (float)xsq[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) lg[q][nt] = fmaf(areg[nt], xs, creg[nt]) + acc[q >> 2][nt][q & 3];
+    }
+    if (any_sharp) {
+      // sharp components: every score that may come within 60 (log2 units)
+      // of the row's top, recomputed from direct differences in float64.
+      // The reference is the row LSE in pass C and, in pass A, the best
+      // score of this wave's other components (accurate in expanded form).
+      float ref[8];
+      if constexpr (PASS == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float m = kDead;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) m = fmaxf(m, eb[nt] > 0.f ? kDead : lg[q][nt]);
+          ref[q] = row16_max(m);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+          ref[q] = row < nrows ? A.lse[row] : INFINITY;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+        const float xs = (float)xsq[p];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (eb[nt] > 0.f && row0 + p < nrows && lg[q][nt] + eb[nt] * xs + e0[nt] >= ref[q] - 60.f) {
+            const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+            lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + p * LRS);
+          }
+        }
+      }
+    }
+
+    if constexpr (PASS == 0) {
+      // ---- per-row max and sum over this wave's components (the eight rows'
+      // reductions interleaved); the waves are combined one tile later
+      float m[8], sm[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        m[q] = lg[q][0];
+#pragma unroll
+        for (int nt = 1; nt < NT; ++nt) m[q] = fmaxf(m[q], lg[q][nt]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0xB1>(m[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x4E>(m[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x141>(m[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x140>(m[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        sm[q] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sm[q] += __builtin_amdgcn_exp2f(lg[q][nt] - m[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0xB1>(sm[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x4E>(sm[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x141>(sm[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x140>(sm[q]);
+      float* rbuf = red + (it & 1) * (LNW * LT * 2);
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+          *reinterpret_cast<float2*>(rbuf + (wv * LT + p) * 2) = float2{m[q], sm[q]};
+        }
+      }
+    } else {
+      // ---- responsibilities r = 2^(l - LSE), rounded to bf16 once; statistics
+      float lse[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+        lse[q] = row < nrows ? A.lse[row] : INFINITY;  // rows past N: r = 0
+      }
+      // two magnitude classes, summed by separate MFMAs: a row with r near 1
+      // would otherwise round away, in the float32 tile sum, the rows of tiny r
+      // that carry a collapsed component's whole variance
+      bf16x8 bbig[NT], bsmall[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const __bf16 rh = (__bf16)__builtin_amdgcn_exp2f(lg[q][nt] - lse[q]);
+          const float rf = (float)rh;
+          const bool big = rf >= kBigR;
+          bbig[nt][q] = big ? rh : (__bf16)0.f;
+          bsmall[nt][q] = big ? (__bf16)0.f : rh;
+          lg[q][nt] = rf;
+        }
+#pragma unroll
+      for (int mt = 0; mt < (STATS ? GM : 1); ++mt) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (mt * 16 + (lane & 15)) * XTS + 8 * (lane >> 4));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const floatx4 t1 =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          ssmall[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bsmall[nt], ssmall[mt][nt], 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sbig[mt][nt][v] += (double)t1[v];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const double xs = xsq[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          nk[nt] += (double)lg[q][nt];
+          qs[nt] += (double)lg[q][nt] * xs;
+        }
+      }
+    }
+  };
+
+  // tiles g, g + G, g + 2G, ...: tile i is staged from registers loaded PF
+  // tiles earlier, and its slot then starts loading tile i + PF
+  int it = 0;
+  for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)PF * A.G) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int64_t t = t0 + (int64_t)u * A.G;
+      if (t >= ntiles) break;
+      __syncthreads();
+      stage_piece<STATS>(A, pf[u], t * LT, slice, rows, xt, xsq);
+      pf[u] = fetch_piece<STATS>(A, t + (int64_t)PF * A.G, ntiles);
+      __syncthreads();
+      if constexpr (PASS == 0) {
+        if (it > 0 && wv == (it & (LNW - 1))) combine((t - A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
+      }
+      process(t * LT, it);
+      ++it;
+    }
+  }
+  if constexpr (PASS == 0) {
+    __syncthreads();
+    if (it > 0 && wv == 0) combine((g + (int64_t)(it - 1) * A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
+  }
+
+  if constexpr (STATS) {
+    // ---- this workgroup's float64 partial for its slice: part[g][k][2 + DP]
+    constexpr int PR = 2 + DP;
+    double* part = A.part + (size_t)g * A.KP * PR;
+#pragma unroll
+    for (int mt = 0; mt < GM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = mt * 16 + 4 * (lane >> 4) + v;
+          double* dst = part + (size_t)k * PR + 2 + row;
+          *dst = (A.accumulate ? *dst : 0.0) + (sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
+        }
+      }
+    __syncthreads();
+    double* red64 = reinterpret_cast<double*>(lds);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int kl = (wv * NT + nt) * 16 + (lane & 15);
+      red64[(kl * 4 + (lane >> 4)) * 2 + 0] = nk[nt];
+      red64[(kl * 4 + (lane >> 4)) * 2 + 1] = qs[nt];
+    }
+    __syncthreads();
+    for (int kl = threadIdx.x; kl < KSL; kl += blockDim.x) {
+      double s0 = 0.0, s1 = 0.0;
+      for (int q = 0; q < 4; ++q) {
+        s0 += red64[(kl * 4 + q) * 2 + 0];
+        s1 += red64[(kl * 4 + q) * 2 + 1];
+      }
+      double* dst = part + (size_t)(slice * KSL + kl) * PR;
+      dst[0] = (A.accumulate ? dst[0] : 0.0) + s0;
+      dst[1] = (A.accumulate ? dst[1] : 0.0) + s1;
+    }
+  }
+}
+
+// Pass B: per row, combine the slices' (max, sum) into the LSE (log2 units);
+// each workgroup also sums its rows' LSE (natural log) into its LL partial.
+__global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
+  constexpr double LN2 = 0.69314718055994530942;
+  __shared__ double red[256];
+  double ll = 0.0;
+  for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < A.N;
+       row += (int64_t)gridDim.x * blockDim.x) {
+    const float2* P = A.P + (size_t)row * A.S;
+    float M = P[0].x;
+    for (int s = 1; s < A.S; ++s) M = fmaxf(M, P[s].x);
+    double S = 0.0;
+    for (int s = 0; s < A.S; ++s) S += (double)P[s].y * exp2((double)P[s].x - (double)M);
+    const double l2 = (double)M + log2(S);
+    A.lse[row] = (float)l2;
+    ll += l2 * LN2;
+  }
+  red[threadIdx.x] = ll;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int i = 0; i < (int)blockDim.x; ++i) s += red[i];
+    A.llpart[blockIdx.x] = (A.accumulate ? A.llpart[blockIdx.x] : 0.0) + s;
+  }
+}
+
+// Prologue: weights w = lambda mu log2(e) split into bf16 hi + lo in the
+// B-fragment order of v_mfma_f32_16x16x32_bf16 (16-component tiles), the
+// constants c, a, c0, lambda (float64) and the sharp-component error bounds.
+// grid: KP blocks of 64 threads.
+__global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int DP, const float* __restrict__ w,
+                                                             const float* __restrict__ mu,
+                                                             const float* __restrict__ cv, __bf16* __restrict__ W,
+                                                             double* __restrict__ c, double* __restrict__ a,
+                                                             double* __restrict__ c0, double* __restrict__ lamk,
+                                                             float* __restrict__ esh) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  constexpr double kLog2Pi = 1.8378770664093454836;
+  const int k = blockIdx.x, tid = threadIdx.x;
+  const int KSTEP = DP / 32;
+  const int kt = k / 16, col = k % 16;
+  const bool live = k < K;
+  const double var = live ? (double)cv[k] : 1.0;
+  const bool ok = live && var > 0.0 && !isinf(var);
+  const double lam = 1.0 / var;
+  for (int f = tid; f < DP; f += blockDim.x) {
+    const double val = (ok && f < D) ? lam * (double)mu[(size_t)k * D + f] * kLog2e : 0.0;
+    const __bf16 hi = (__bf16)val;
+    const __bf16 lo = (__bf16)(val - (double)(float)hi);
+    const int ks = f / 32, j = f % 32, grp = j / 8, e = j % 8;
+    const int lane = grp * 16 + col;
+    for (int h = 0; h < 2; ++h) {
+      const size_t idx = ((size_t)kt * 2 + h) * KSTEP + ks;
+      W[(idx * 64 + lane) * 8 + e] = h == 0 ? hi : lo;
+    }
+  }
+  if (tid == 0) {
+    if (!ok) {
+      c[k] = c0[k] = kDead;
+      a[k] = lamk[k] = 0.0;
+      esh[2 * k] = esh[2 * k + 1] = 0.f;
+      return;
+    }
+    double mm = 0.0;
+    for (int d = 0; d < D; ++d) mm += (double)mu[(size_t)k * D + d] * (double)mu[(size_t)k * D + d];
+    c0[k] = (log((double)w[k]) - 0.5 * (D * kLog2Pi + D * log(var))) * kLog2e;
+    c[k] = c0[k] - 0.5 * lam * mm * kLog2e;
+    a[k] = -0.5 * lam * kLog2e;
+    lamk[k] = lam;
+    // the expanded score's terms reach lambda (|mu|^2 + |x|^2) log2(e); the
+    // bf16 split of the weights and the float32 sums leave an error below
+    // 2^-14 of that.  Components whose terms exceed kSharpLowp are rescored.
+    const bool sharp = lam * (mm + D * var) > kSharpLowp;
+    const double eb = sharp ? ldexp(lam * kLog2e, -14) : 0.0;
+    esh[2 * k] = (float)eb;
+    esh[2 * k + 1] = (float)(eb * mm);
+  }
+}
+
+hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, const float* mu, const float* cv,
+                         hipStream_t s) {
+  LargeKArgs a = a0;
+  hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
+                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)), const_cast<double*>(a.c),
+                     const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
+                     const_cast<float*>(a.esh));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto kA = largek_kernel<128, 0>;
+  auto kC = largek_kernel<128, 2>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)kC, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    attr_set = true;
+  }
+  const int64_t N = a.N;
+  const unsigned char* x0 = reinterpret_cast<const unsigned char*>(a.x);
+  for (int64_t r0 = 0, chunk = 0; r0 < N || (N == 0 && chunk == 0); r0 += p.chunk_rows, ++chunk) {
+    LargeKArgs ac = a;
+    ac.N = std::min<int64_t>(p.chunk_rows, N - r0);
+    ac.x = x0 + (size_t)r0 * p.ld_x * 2;
+    ac.accumulate = chunk > 0;
+    if (ac.N > 0) {
+      ac.G = p.GbA;
+      hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ac.G = p.Gb;
+    hipLaunchKernelGGL(kC, dim3((unsigned)(p.SC * p.Gb)), dim3(64 * LNW), p.lds_c, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (N == 0) break;
+  }
+  return hipSuccess;
+}
+
+}  // namespace gmm

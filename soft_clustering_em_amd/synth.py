@@ -17,6 +17,8 @@ the Flash-GMM paper evaluates on (Section 4); no public dataset is read.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -180,52 +182,74 @@ def full_large(N=2_000_000, D=16, K=32, seed=0, iters=20) -> Workload:
                     mu0[None], cv0[None], iters)
 
 
-def ivf_rows(n_rows: int, start: int, D=128, K=4096, seed=0, noise=0.10, chunk=1 << 18):
+def _ivf_blobs(D, K, seed):
+    crng = np.random.default_rng([seed, 0])
+    centers = crng.standard_normal((K, D))
+    centers /= np.linalg.norm(centers, axis=1, keepdims=True)
+    stds = crng.uniform(0.05, 0.2, (K, D))
+    return centers.astype(np.float32), stds.astype(np.float32)
+
+
+def _ivf_chunk(c, chunk, D, K, seed, noise, centers, stds):
+    """All rows of chunk c (float32), from the chunk's own seed."""
+    rng = np.random.default_rng([seed, 1, c])
+    labels = rng.integers(0, K, chunk)
+    is_noise = rng.random(chunk) < noise
+    z = rng.standard_normal((chunk, D), dtype=np.float32)
+    rows = centers[labels]
+    rows += stds[labels] * z
+    rows[is_noise] = rng.standard_normal((int(is_noise.sum()), D), dtype=np.float32)
+    rows /= np.linalg.norm(rows, axis=1, keepdims=True)
+    return rows
+
+
+def _workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def ivf_rows(n_rows: int, start: int, D=128, K=4096, seed=0, noise=0.10, chunk=1 << 16):
     """Rows [start, start+n_rows) of the IVF workload as float32 (before bf16).
 
     Rows are drawn in independent chunks of `chunk` rows, each from its own
     seed, so any range can be regenerated without the rows before it.
     Blob centres are uniform on the unit sphere with per-(blob, dim) std
-    U[0.05,0.2]; `noise` of the rows are uniform on the sphere; every row is
-    normalised to unit length.
+    U[0.05,0.2]; `noise` of the rows are standard normal (uniform direction);
+    every row is normalised to unit length.
     """
-    crng = np.random.default_rng([seed, 0])
-    centers = crng.standard_normal((K, D))
-    centers /= np.linalg.norm(centers, axis=1, keepdims=True)
-    stds = crng.uniform(0.05, 0.2, (K, D))
+    centers, stds = _ivf_blobs(D, K, seed)
     out = np.empty((n_rows, D), np.float32)
     c0, c1 = start // chunk, (start + n_rows - 1) // chunk
-    for c in range(c0, c1 + 1):
-        rng = np.random.default_rng([seed, 1, c])
+
+    def one(c):
         lo = c * chunk
-        labels = rng.integers(0, K, chunk)
-        is_noise = rng.random(chunk) < noise
         a, b = max(lo, start), min(lo + chunk, start + n_rows)
-        sl = slice(a - lo, b - lo)
-        lab = labels[sl]
-        z = rng.standard_normal((chunk, D))[sl]
-        rows = centers[lab] + stds[lab] * z
-        nz = rng.standard_normal((chunk, D))[sl]
-        rows = np.where(is_noise[sl, None], nz, rows)
-        rows /= np.linalg.norm(rows, axis=1, keepdims=True)
-        out[a - start:b - start] = rows
+        out[a - start:b - start] = _ivf_chunk(c, chunk, D, K, seed, noise, centers, stds)[a - lo:b - lo]
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(c0, c1 + 1)))
     return out
 
 
-def ivf_bf16(N=10_000_000, D=128, K=4096, seed=0, iters=10, chunk=1 << 18) -> Workload:
+def ivf_bf16(N=10_000_000, D=128, K=4096, seed=0, iters=10, chunk=1 << 16) -> Workload:
     """Unit-normalised mixture of K anisotropic blobs plus 10% uniform-on-sphere
     noise, stored as bf16 (round-to-nearest-even).  Init: K distinct random
     rows, variance = global mean per-dimension variance, weights 1/K."""
+    centers, stds = _ivf_blobs(D, K, seed)
     X = np.empty((N, D), np.uint16)
-    s1 = np.zeros(D)
-    s2 = np.zeros(D)
-    for s in range(0, N, chunk):
+    nchunks = (N + chunk - 1) // chunk
+
+    def one(c):
+        s = c * chunk
         n = min(chunk, N - s)
-        bits = f32_to_bf16_bits(ivf_rows(n, s, D, K, seed, chunk=chunk))
+        bits = f32_to_bf16_bits(_ivf_chunk(c, chunk, D, K, seed, 0.10, centers, stds)[:n])
         X[s:s + n] = bits
         v = bf16_bits_to_f32(bits).astype(np.float64)
-        s1 += v.sum(0)
-        s2 += (v * v).sum(0)
+        return v.sum(0), (v * v).sum(0)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        parts = list(ex.map(one, range(nchunks)))
+    s1 = np.sum([p[0] for p in parts], axis=0)   # chunk order: independent of the thread count
+    s2 = np.sum([p[1] for p in parts], axis=0)
     mean = s1 / N
     var = float((s2 / N - mean * mean).mean())
     rng = np.random.default_rng([seed, 2])
