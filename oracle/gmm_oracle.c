@@ -484,8 +484,10 @@ int oracle_responsibilities(int cov, int64_t N, int D, int K, const void* X, int
  * first), keep the first always and ranks 2..m whose responsibility is at
  * least `thr`.  Single problem.
  *   idx (N,m) int32, -1 padded;  resp (N,m);  count (N);  logp (N) = LSE_i
- *   margin (N): smallest gap that decides the output -- between consecutive
- *   ranks 1..m+1 and between ranks 2..m and the threshold.
+ *   margin (N): smallest gap that decides the output.  With c kept ranks,
+ *   the output is fixed by the order of ranks 1..c+1 (the gaps between
+ *   consecutive ones) and by the threshold tests of ranks 2..min(c+1, m);
+ *   the order of the ranks after c+1 does not show in it.
  */
 int oracle_topm(int cov, int64_t N, int D, int K, const void* X, int xtype,
                 const double* w, const double* mu, const double* cv, int m, double thr,
@@ -534,11 +536,11 @@ int oracle_topm(int cov, int64_t N, int D, int K, const void* X, int xtype,
       }
       count[i] = cnt;
       double mg = INFINITY;
-      for (int j = 0; j + 1 < nr && j < m; ++j) {
+      for (int j = 0; j < cnt && j + 1 < nr; ++j) {
         double g = r[rank[j]] - r[rank[j + 1]];
         if (g < mg) mg = g;
       }
-      for (int j = 1; j < nr && j < m; ++j) {
+      for (int j = 1; j <= cnt && j < nr && j < m; ++j) {
         double g = fabs(r[rank[j]] - thr);
         if (g < mg) mg = g;
       }

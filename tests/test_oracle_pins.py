@@ -250,8 +250,11 @@ def test_topm_matches_sorted_responsibilities(cov):
         np.testing.assert_array_equal(idx[i, :len(keep)], keep)
         assert (idx[i, len(keep):] == -1).all()
         np.testing.assert_allclose(resp[i, :len(keep)], r[i, keep], rtol=1e-10)
-        gaps = [r[i, order[j]] - r[i, order[j + 1]] for j in range(m)]
-        gaps += [abs(r[i, order[j]] - thr) for j in range(1, m)]
+        # the output depends on the order of ranks 1..c+1 and on the
+        # threshold tests of ranks 2..min(c+1, m), c = number kept
+        c = len(keep)
+        gaps = [r[i, order[j]] - r[i, order[j + 1]] for j in range(c)]
+        gaps += [abs(r[i, order[j]] - thr) for j in range(1, min(c + 1, m))]
         assert margin[i] == pytest.approx(min(gaps), rel=1e-8, abs=1e-15)
 
 
