@@ -217,6 +217,22 @@ def main():
         },
         "mean_loglik_last": float(mll.mean().item()),
     }
+    if wl.topm is not None:
+        # soft multi-assignment under the fitted model: one pass, timed apart
+        m, thr = wl.topm
+        idx = torch.empty((wl.B, wl.N, m), dtype=torch.int32, device=dev)
+        resp = torch.empty((wl.B, wl.N, m), dtype=torch.float32, device=dev)
+        cnt = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+        tws = torch.empty(g.gmm_workspace_bytes(X, wl.K, wl.cov, op=g.OP_TOPM, m=m), dtype=torch.uint8,
+                          device=dev)
+        g.gmm_predict_proba_topm(X, w, mu, cv, wl.cov, m, thr, idx, resp, cnt, ws=tws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.gmm_predict_proba_topm(X, w, mu, cv, wl.cov, m, thr, idx, resp, cnt, ws=tws)
+        torch.cuda.synchronize()
+        t_topm = time.perf_counter() - t0
+        res["topm"] = {"m": m, "threshold": thr, "ms": t_topm * 1e3, "rows_per_s": wl.B * wl.N / t_topm,
+                       "mean_kept": float(cnt.float().mean().item())}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

@@ -77,9 +77,18 @@ static void largek_layout(Plan& q, int64_t chunk) {
   q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.KP);
   q.off_prec = o; o = align_up(o + sizeof(double) * (size_t)q.KP);
   q.off_sharp = o; o = align_up(o + sizeof(float) * 2 * (size_t)q.KP);
+  q.off_eall = o; o = align_up(o + sizeof(float) * 2 * (size_t)q.KP);
+  q.off_mmk = o;  o = align_up(o + sizeof(double) * (size_t)q.KP);
+  q.off_kconst = o; o = align_up(o + sizeof(double) * 2 * (size_t)q.KP);
   q.off_P = o;    o = align_up(o + sizeof(float) * 2 * (size_t)chunk * q.S);
   q.off_lse = o;  o = align_up(o + sizeof(float) * (size_t)chunk);
   q.off_xsq = o;  o = align_up(o + sizeof(double) * (size_t)chunk);
+  if (q.op == GMM_OP_TOPM) {
+    q.off_mrow = o; o = align_up(o + sizeof(float) * (size_t)chunk);
+    q.off_cnt = o;  o = align_up(o + sizeof(int32_t) * (size_t)chunk);
+    q.off_cand = o; o = align_up(o + sizeof(int32_t) * (size_t)chunk * kLargeKCap);
+    q.off_prem = o; o = align_up(o + sizeof(float) * (size_t)chunk * q.S);
+  }
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
   q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.llG);
   q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.KP * q.PR);
@@ -110,7 +119,6 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   if (d->dtype == GMM_DT_BF16) {
     // bf16 rows: spherical components through the slice-parallel three-pass E-step
     if (cov != SPH) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows are supported for spherical components only");
-    if (op == GMM_OP_TOPM) return fail(GMM_ERR_UNSUPPORTED, "top-m over bf16 rows is not supported");
     if (d->B != 1) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: one problem per call (B = 1)");
     if (d->D > 128) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: D <= 128");
     q.largek = true;
@@ -131,10 +139,11 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     q.llG = q.lse_blocks;
     q.ntiles = (q.N + 31) / 32;
     q.lds_a = largek_lds_bytes(q.DP, 0);
+    q.lds_t = largek_lds_bytes(q.DP, 1);
     q.lds_c = largek_lds_bytes(q.DP, 2);
     q.prec_stride = 1;
     q.op = op;
-    largek_layout(q, std::min<int64_t>((q.N + 31) / 32 * 32, kLargeKChunk));
+    largek_layout(q, std::min<int64_t>((q.N + 31) / 32 * 32, op == GMM_OP_TOPM ? kLargeKTopmChunk : kLargeKChunk));
     *p = q;
     return GMM_OK;
   }
@@ -234,7 +243,8 @@ static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
     Plan q = p;
     largek_layout(q, 32);
     if (ws_bytes >= q.ws_bytes) {
-      const size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
+      size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
+      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (1 + p.S) + sizeof(int32_t) * (1 + kLargeKCap);
       int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
       chunk = std::min<int64_t>(chunk, p.chunk_rows);
       for (largek_layout(q, chunk); q.ws_bytes > ws_bytes && chunk > 32; largek_layout(q, chunk)) chunk -= 32;
@@ -254,11 +264,9 @@ static gmm_status hip_fail(hipError_t e, const char* where) {
 }
 
 // prologue + fused E-step + reduction; statistics to the given buffers
-static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk,
-                                   double* sx, double* sxx, double* ll, double* mean_ll, int accumulate,
-                                   const gmm_options* opts, hipStream_t s) {
+static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws) {
   char* w = static_cast<char*>(ws);
-  LargeKArgs A;
+  LargeKArgs A{};
   A.x = d->x;
   A.N = p.N;
   A.D = p.D;
@@ -281,6 +289,23 @@ static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_p
   A.llpart = reinterpret_cast<double*>(w + p.off_llp);
   A.part = reinterpret_cast<double*>(w + p.off_part);
   A.accumulate = 0;
+  A.eall = reinterpret_cast<float*>(w + p.off_eall);
+  A.mmk = reinterpret_cast<double*>(w + p.off_mmk);
+  A.kconst = reinterpret_cast<double2*>(w + p.off_kconst);
+  if (p.op == GMM_OP_TOPM) {
+    A.mrow = reinterpret_cast<float*>(w + p.off_mrow);
+    A.cnt = reinterpret_cast<int32_t*>(w + p.off_cnt);
+    A.cand = reinterpret_cast<int32_t*>(w + p.off_cand);
+    A.prem = reinterpret_cast<float*>(w + p.off_prem);
+  }
+  return A;
+}
+
+static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk,
+                                   double* sx, double* sxx, double* ll, double* mean_ll, int accumulate,
+                                   const gmm_options* opts, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  LargeKArgs A = largek_args(p, d, prm, ws);
   hipError_t e;
   if (opts && opts->event_begin && (e = hipEventRecord((hipEvent_t)opts->event_begin, s)) != hipSuccess)
     return hip_fail(e, "event record");
@@ -444,6 +469,19 @@ gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params
   if (st != GMM_OK) return st;
   if (p.N == 0) return GMM_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (p.largek) {
+    LargeKArgs A = largek_args(p, data, params, ws);
+    A.topm = 1;
+    A.m = m;
+    A.thr = threshold;
+    A.idx = idx;
+    A.resp = resp;
+    A.count = count;
+    A.logp = logp;
+    hipError_t e = launch_largek_topm(p, A, params->weights, params->means, params->covars, s);
+    if (e != hipSuccess) return hip_fail(e, "large-K top-m launch");
+    return GMM_OK;
+  }
   char* w = static_cast<char*>(ws);
   float* W = reinterpret_cast<float*>(w + p.off_W);
   double* prec = reinterpret_cast<double*>(w + p.off_prec);

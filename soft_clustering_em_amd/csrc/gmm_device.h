@@ -1,6 +1,7 @@
-// gmm_device.h -- device helpers shared by the fused E-step kernel and the
-// top-m kernel: 16-lane DPP reductions, the product-feature index map, and
-// the float64 log-score by direct differences.
+// gmm_device.h -- device helpers shared by the fused E-step kernel, the
+// top-m kernels and the large-K kernels: 16-lane DPP reductions, wave-wide
+// reductions and ranking order, the product-feature index map, and the
+// float64 log-score by direct differences.
 #pragma once
 
 #include "gmm_internal.h"
@@ -73,6 +74,28 @@ __device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D
     }
   }
   return A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;
+}
+
+// ranking order of (log-score, component): higher score first, lower index on ties
+__device__ __forceinline__ bool before(double la, int ka, double lb, int kb) {
+  return la > lb || (la == lb && ka < kb);
+}
+
+// wave-wide (64-lane) reductions through ds_bpermute, fixed butterfly order
+__device__ __forceinline__ double wave_max(double v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ void wave_best(double& l, int& k) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double l2 = __shfl_xor(l, off);
+    const int k2 = __shfl_xor(k, off);
+    if (before(l2, k2, l, k)) { l = l2; k = k2; }
+  }
 }
 
 }  // namespace gmm

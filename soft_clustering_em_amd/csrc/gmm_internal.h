@@ -46,8 +46,8 @@ struct Plan {
   int GbA = 0;              // row groups of pass A (pass C uses Gb)
   int64_t chunk_rows = 0;   // rows per chunk (large K)
   int lse_blocks = 0;       // blocks of the large-K LSE pass
-  size_t lds_a = 0, lds_c = 0;
-  size_t off_P = 0, off_lse = 0, off_xsq = 0;
+  size_t lds_a = 0, lds_t = 0, lds_c = 0;
+  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cnt = 0, off_cand = 0;
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
@@ -99,7 +99,26 @@ struct LargeKArgs {
   double* llpart;       // (lse blocks)
   double* part;         // (G, KP, 2 + DP)
   int accumulate;       // add to part / llpart (every chunk after the first)
+  // top-m
+  const float* eall;    // (KP, 2) error bound of every component's expanded score
+  const double* mmk;    // (KP) |mu_k|^2
+  const double2* kconst; // (KP) (c0 - lambda |mu|^2 log2(e) / 2, lambda log2(e)) for exact scores
+  float* prem;          // (chunk, S) below-band mass of each slice, relative to mrow
+  float* mrow;          // (chunk) row maximum of the log-scores (pass B)
+  int32_t* cnt;         // (chunk) candidate count of each row (pass B clears it)
+  int32_t* cand;        // (chunk, kLargeKCap) candidate components
+  int topm;             // pass B: write mrow and clear cnt
+  int m;
+  float thr;
+  int32_t* idx;         // outputs of the chunk's rows
+  float* resp;
+  int32_t* count;
+  float* logp;
 };
+constexpr int kLargeKCap = 1024;        // candidates kept per row before the all-K fallback
+constexpr int64_t kLargeKTopmChunk = 1 << 15;
+hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,
+                              hipStream_t s);
 hipError_t launch_largek(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,
                          hipStream_t s);
 size_t largek_lds_bytes(int DP, int pass);  // dynamic LDS of pass A (0) / C (2)

@@ -62,6 +62,12 @@ constexpr float kBigR = 0x1p-8f;
 // log-score constant of padded and dead components: finite, so that maxima
 // and differences stay finite, and far enough down that 2^(l - max) is 0
 constexpr float kDead = -1.0e30f;
+// top-m: components scored within this many log2 units of a row's maximum
+// are rescored exactly; the others (each below 2^-20 of the maximum's mass)
+// enter the row's LSE with their expanded-form scores
+constexpr float kTopmBand = 20.f;
+// candidates of one row in one slice held in LDS before they go to the row's list
+constexpr int kCandL = 40;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
@@ -175,16 +181,17 @@ __device__ __forceinline__ float largek_exact_score(const float* __restrict__ mu
 }  // namespace
 
 size_t largek_lds_bytes(int DP, int pass) {
-  const int ksl = pass == 0 ? KSA : KSC;
+  const int ksl = pass != 2 ? KSA : KSC;
   size_t b = (size_t)(ksl / 16) * 2 * (DP / 32) * 64 * 16;  // weights
   b += (size_t)LT * LRS * 2;                                // row tile
-  if (pass != 0) b += (size_t)DP * XTS * 2;                 // transposed tile
+  if (pass == 2) b += (size_t)DP * XTS * 2;                 // transposed tile
   b += (size_t)LT * 8;                                      // |x|^2
-  if (pass == 0) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
+  if (pass != 2) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
+  if (pass == 1) b += (size_t)2 * LT * (1 + kCandL) * 4;    // candidate lists, two tiles
   return b;
 }
 
-// PASS: 0 = A (slice max/sum), 2 = C (statistics).
+// PASS: 0 = A (slice max/sum), 1 = T (top-m candidates), 2 = C (statistics).
 // Weights in global memory: 16-component tiles, [tile][hi/lo][kstep][lane] x 16 bytes.
 template <int DP, int PASS>
 __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
@@ -210,6 +217,11 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   unsigned short* xt = rows + LT * LRS;
   double* xsq = reinterpret_cast<double*>(xt + (STATS ? DP * XTS : 0));
   float* red = reinterpret_cast<float*>(xsq + LT);   // pass A: 2 buffers of LNW * LT * 2
+  int* lcnt = reinterpret_cast<int*>(red + 2 * LNW * LT * 2);  // pass T: 2 x LT counts
+  int* lcand = lcnt + 2 * LT;                                  // pass T: 2 x LT x kCandL
+  if constexpr (PASS == 1) {
+    if (threadIdx.x < 2 * LT) lcnt[threadIdx.x] = 0;
+  }
 
   // the first row tiles start loading before the weights are staged
   Piece pf[PF];
@@ -222,6 +234,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   }
   float creg[NT], areg[NT];
   float eb[NT], e0[NT];  // error bound of a sharp component's expanded score: eb |x|^2 + e0 (0: not sharp)
+  float ea[NT], ea0[NT]; // pass T: the same bound for every component
   bool any_sharp = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -230,6 +243,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     areg[nt] = (float)A.a[k];
     eb[nt] = A.esh[2 * k];
     e0[nt] = A.esh[2 * k + 1];
+    if constexpr (PASS == 1) {
+      ea[nt] = A.eall[2 * k];
+      ea0[nt] = A.eall[2 * k + 1];
+    }
     any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(eb[nt] > 0.f) != 0);
   }
   // pass C: statistics of the r >= 2^-8 class in float64 (one tile at a
@@ -250,11 +267,31 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 
   // pass A: combine the waves' (max, sum) of a finished tile into P; run by
   // one wave (rotating) while the others go on with the next tile
+  // pass T: sum the waves' below-band mass of a finished tile into Prem
   auto combine = [&](int64_t prow0, const float* rb) {
     if (lane < LT) {
       const int p = lane;
       const int64_t row = prow0 + p;
-      if (row < nrows) {
+      if (PASS == 1) {
+        // this slice's candidates of the row go to the row's list (a count
+        // past kCandL sends the row to the all-components path)
+        const int buf = (rb - red) / (LNW * LT * 2);
+        int* lc = lcnt + buf * LT;
+        const int n = lc[p];
+        lc[p] = 0;
+        if (row < nrows) {
+          float S = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < LNW; ++w2) S += rb[(w2 * LT + p) * 2 + 1];
+          A.prem[(size_t)row * A.S + slice] = S;
+          if (n > 0) {
+            const int base = atomicAdd(A.cnt + row, n > kCandL ? kLargeKCap + 1 : n);
+            const int* src = lcand + (buf * LT + p) * kCandL;
+            for (int i = 0; i < n && i < kCandL && base + i < kLargeKCap; ++i)
+              A.cand[(size_t)row * kLargeKCap + base + i] = src[i];
+          }
+        }
+      } else if (row < nrows) {
         float M = rb[p * 2];
 #pragma unroll
         for (int w2 = 1; w2 < LNW; ++w2) M = fmaxf(M, rb[(w2 * LT + p) * 2]);
@@ -316,7 +353,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-          ref[q] = row < nrows ? A.lse[row] : INFINITY;
+          ref[q] = row < nrows ? (PASS == 1 ? A.mrow[row] : A.lse[row]) : INFINITY;
         }
       }
 #pragma unroll
@@ -333,7 +370,49 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       }
     }
 
-    if constexpr (PASS == 0) {
+    if constexpr (PASS == 1) {
+      // ---- candidates: every component whose score may lie within kTopmBand
+      // of the row's maximum (its expanded-form error counted twice); the
+      // mass 2^(l - max) of the others, per row, for the LSE
+      float rem[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+        const int64_t row = row0 + p;
+        rem[q] = 0.f;
+        if (row < nrows) {
+          const float mr = A.mrow[row];
+          const float floor_l = mr - kTopmBand;
+          const float xs = (float)xsq[p];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if (lg[q][nt] + 2.f * fmaf(ea[nt], xs, ea0[nt]) >= floor_l) {
+              const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+              const int slot = atomicAdd(lcnt + (it & 1) * LT + p, 1);
+              if (slot < kCandL) lcand[((it & 1) * LT + p) * kCandL + slot] = k;
+            } else {
+              rem[q] += __builtin_amdgcn_exp2f(lg[q][nt] - mr);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rem[q] += dpp_mov<0xB1>(rem[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rem[q] += dpp_mov<0x4E>(rem[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rem[q] += dpp_mov<0x141>(rem[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rem[q] += dpp_mov<0x140>(rem[q]);
+      float* rbuf = red + (it & 1) * (LNW * LT * 2);
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+          rbuf[(wv * LT + p) * 2 + 1] = rem[q];
+        }
+      }
+    } else if constexpr (PASS == 0) {
       // ---- per-row max and sum over this wave's components (the eight rows'
       // reductions interleaved); the waves are combined one tile later
       float m[8], sm[8];
@@ -432,14 +511,14 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       stage_piece<STATS>(A, pf[u], t * LT, slice, rows, xt, xsq);
       pf[u] = fetch_piece<STATS>(A, t + (int64_t)PF * A.G, ntiles);
       __syncthreads();
-      if constexpr (PASS == 0) {
+      if constexpr (PASS != 2) {
         if (it > 0 && wv == (it & (LNW - 1))) combine((t - A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
       }
       process(t * LT, it);
       ++it;
     }
   }
-  if constexpr (PASS == 0) {
+  if constexpr (PASS != 2) {
     __syncthreads();
     if (it > 0 && wv == 0) combine((g + (int64_t)(it - 1) * A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
   }
@@ -498,6 +577,10 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
     const double l2 = (double)M + log2(S);
     A.lse[row] = (float)l2;
     ll += l2 * LN2;
+    if (A.topm) {
+      A.mrow[row] = M;
+      A.cnt[row] = 0;
+    }
   }
   red[threadIdx.x] = ll;
   __syncthreads();
@@ -517,7 +600,8 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
                                                              const float* __restrict__ cv, __bf16* __restrict__ W,
                                                              double* __restrict__ c, double* __restrict__ a,
                                                              double* __restrict__ c0, double* __restrict__ lamk,
-                                                             float* __restrict__ esh) {
+                                                             float* __restrict__ esh, float* __restrict__ eall,
+                                                             double* __restrict__ mmk, double2* __restrict__ kconst) {
   constexpr double kLog2e = 1.4426950408889634074;
   constexpr double kLog2Pi = 1.8378770664093454836;
   const int k = blockIdx.x, tid = threadIdx.x;
@@ -543,6 +627,9 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
       c[k] = c0[k] = kDead;
       a[k] = lamk[k] = 0.0;
       esh[2 * k] = esh[2 * k + 1] = 0.f;
+      eall[2 * k] = eall[2 * k + 1] = 0.f;
+      mmk[k] = 0.0;
+      kconst[k] = double2{(double)kDead, 0.0};
       return;
     }
     double mm = 0.0;
@@ -555,9 +642,14 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
     // bf16 split of the weights and the float32 sums leave an error below
     // 2^-14 of that.  Components whose terms exceed kSharpLowp are rescored.
     const bool sharp = lam * (mm + D * var) > kSharpLowp;
-    const double eb = sharp ? ldexp(lam * kLog2e, -14) : 0.0;
+    const double ea = ldexp(lam * kLog2e, -14);
+    const double eb = sharp ? ea : 0.0;
     esh[2 * k] = (float)eb;
     esh[2 * k + 1] = (float)(eb * mm);
+    eall[2 * k] = (float)ea;
+    eall[2 * k + 1] = (float)(ea * mm);
+    mmk[k] = mm;
+    kconst[k] = double2{c0[k] - 0.5 * lam * mm * kLog2e, lam * kLog2e};
   }
 }
 
@@ -567,7 +659,8 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
                      cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)), const_cast<double*>(a.c),
                      const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
-                     const_cast<float*>(a.esh));
+                     const_cast<float*>(a.esh), const_cast<float*>(a.eall),
+                     const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kA = largek_kernel<128, 0>;
@@ -596,6 +689,242 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
     hipLaunchKernelGGL(kC, dim3((unsigned)(p.SC * p.Gb)), dim3(64 * LNW), p.lds_c, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N == 0) break;
+  }
+  return hipSuccess;
+}
+
+
+// Top-m, last step: one wave per row.  The row's candidates (all K
+// components, in batches, when it has more than kLargeKCap) are scored 16
+// lanes to a candidate (lane i of a group holds dims 8i..8i+7 of the row),
+// sixteen at a time, exactly in float64: c0 - (lambda/2) log2(e) (|x|^2 -
+// 2 x . mu + |mu|^2), every product of a bf16 x and a float32 mu being exact
+// in float64, so the expanded form loses nothing at float64 precision.  The
+// scores go to LDS; each batch updates the row's running (max, sum) and its
+// best m (kept in LDS ahead of the next batch's scores), chosen by m rounds
+// of a wave-wide best.  The LSE adds pass T's below-band mass.  Rank 1 is
+// always kept, ranks 2..m while r >= thr.
+constexpr int kTopmMaxM = 16;
+constexpr int kBatch = 512;                       // scores per batch
+constexpr int kSlots = kTopmMaxM + kBatch;        // running best m, then the batch
+constexpr int kPer = (kSlots + 63) / 64;          // slots per lane in the selection
+
+// 2^d for d <= 0 to about 1e-7 relative: float exp2 of the float part and a
+// first-order correction for the rest of d
+__device__ __forceinline__ double exp2_acc(double d) {
+  const float h = (float)d;
+  const double l = d - (double)h;
+  return (double)__builtin_amdgcn_exp2f(h) * (1.0 + l * 0.69314718055994530942);
+}
+
+__global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  constexpr double LN2 = 0.69314718055994530942;
+  __shared__ double sl[4][kSlots];
+  __shared__ int skk[4][kSlots];
+  const int lane = threadIdx.x & 63;
+  const int wq = threadIdx.x >> 6;
+  const int grp = lane >> 4, li = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wq;
+  if (row >= A.N) return;  // uniform across the wave; the block has no barrier
+  double* L = sl[wq];
+  int* KK = skk[wq];
+  const int m = A.m;
+  const int D = (int)A.D;
+  const int n = A.cnt[row];
+  const bool all = n > kLargeKCap;
+  const int total = all ? A.K : n;
+  // this lane's 8 dims of the row
+  const unsigned short* xr = reinterpret_cast<const unsigned short*>(A.x) + row * A.ld_x;
+  double xv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * li + e;
+    xv[e] = d < D ? (double)__uint_as_float((unsigned)xr[d] << 16) : 0.0;
+  }
+  const bool vec = (D & 7) == 0 && ((uintptr_t)A.mu & 15) == 0;
+  const double xsq = A.xsq[row];
+  if (lane < kTopmMaxM) {
+    L[lane] = -INFINITY;
+    KK[lane] = 0x7fffffff;
+  }
+  double Mrun = -INFINITY, Srun = 0.0;
+  for (int b0 = 0; b0 < total; b0 += kBatch) {
+    const int nb = min(kBatch, total - b0);
+    // 16 candidates per step (four per 16-lane group), their loads issued
+    // together and unconditionally (indices past the batch repeat its last
+    // entry; lanes past D read inside the row and hold x = 0)
+    constexpr int U = 4;
+    const int doff = vec ? min(8 * li, D - 8) : 0;
+    for (int i0 = 0; i0 < nb; i0 += 4 * U) {
+      int ku[U];
+      if (all) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) ku[u] = b0 + min(i0 + 4 * u + grp, nb - 1);
+      } else {
+        const int* cl = A.cand + (size_t)row * kLargeKCap + b0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) ku[u] = cl[min(i0 + 4 * u + grp, nb - 1)];
+      }
+      double2 cu[U];
+      float4 m0[U], m1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cu[u] = A.kconst[ku[u]];
+        const float* mu = A.mu + (size_t)ku[u] * D;
+        if (vec) {
+          m0[u] = *reinterpret_cast<const float4*>(mu + doff);
+          m1[u] = *reinterpret_cast<const float4*>(mu + doff + 4);
+        } else {
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = (8 * li + e < D) ? mu[8 * li + e] : 0.f;
+          m0[u] = float4{t[0], t[1], t[2], t[3]};
+          m1[u] = float4{t[4], t[5], t[6], t[7]};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double dot = xv[0] * (double)m0[u].x + xv[1] * (double)m0[u].y + xv[2] * (double)m0[u].z +
+                     xv[3] * (double)m0[u].w + xv[4] * (double)m1[u].x + xv[5] * (double)m1[u].y +
+                     xv[6] * (double)m1[u].z + xv[7] * (double)m1[u].w;
+        dot = row16_sum_f64(dot);
+        const int i = i0 + 4 * u + grp;
+        if (li == 0 && i < nb) {
+          // score = (c0 - lambda log2(e) |mu|^2 / 2) + lambda log2(e) (x . mu - |x|^2 / 2)
+          L[kTopmMaxM + i] = cu[u].x + cu[u].y * (dot - 0.5 * xsq);
+          KK[kTopmMaxM + i] = ku[u];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // this batch's slots (and the running best m) into registers; only the
+    // first tcnt of each lane's kPer slots can hold entries
+    const int tcnt = (kTopmMaxM + nb + 63) / 64;
+    double vl[kPer];
+    int vk[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      vl[t] = -INFINITY;
+      vk[t] = 0x7fffffff;
+      if (t < tcnt) {
+        const int j = lane + 64 * t;
+        if (j < kTopmMaxM + nb) {
+          vl[t] = L[j];
+          vk[t] = KK[j];
+        }
+      }
+    }
+    // running max and sum over the batch's scores
+    double lmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+      if (t < tcnt && lane + 64 * t >= kTopmMaxM) lmax = fmax(lmax, vl[t]);
+    const double Mb = wave_max(lmax);
+    double ssum = 0.0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+      if (t < tcnt && lane + 64 * t >= kTopmMaxM && vl[t] > -INFINITY) ssum += exp2_acc(vl[t] - Mb);
+    const double Sb = wave_sum(ssum);
+    const double Mn = fmax(Mrun, Mb);
+    Srun = (Mrun > -INFINITY ? Srun * exp2(Mrun - Mn) : 0.0) + Sb * exp2(Mb - Mn);
+    Mrun = Mn;
+    // the best m of the running list and the batch
+    double rl = -INFINITY;
+    int rk = 0x7fffffff;
+    for (int j = 0; j < m; ++j) {
+      double bl = -INFINITY;
+      int bk = 0x7fffffff;
+      int bt = -1;
+#pragma unroll
+      for (int t = 0; t < kPer; ++t)
+        if (t < tcnt && before(vl[t], vk[t], bl, bk)) {
+          bl = vl[t];
+          bk = vk[t];
+          bt = t;
+        }
+      double wl = bl;
+      int wk = bk;
+      wave_best(wl, wk);
+#pragma unroll
+      for (int t = 0; t < kPer; ++t)
+        if (t < tcnt && bt == t && bk == wk && bl == wl) vl[t] = -INFINITY, vk[t] = 0x7fffffff;
+      if (lane == j) {
+        rl = wl;
+        rk = wk;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < kTopmMaxM) {
+      L[lane] = rl;
+      KK[lane] = rk;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  double S = Srun;
+  if (!all) {
+    // below-band mass of every slice, relative to the expanded-form maximum
+    const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
+    S += rem * exp2((double)A.mrow[row] - Mrun);
+  }
+  const double lse = Mrun + log2(S);
+  if (lane == 0) {
+    int c = 0;
+    for (int j = 0; j < m; ++j) {
+      const double bl = L[j];
+      const int bk = KK[j];
+      const double r = bk < A.K ? exp2(bl - lse) : 0.0;
+      const bool keep = bk < A.K && (j == 0 || r >= (double)A.thr) && c == j;
+      A.idx[row * m + j] = keep ? bk : -1;
+      A.resp[row * m + j] = keep ? (float)r : 0.f;
+      if (keep) ++c;
+    }
+    if (A.count) A.count[row] = c;
+    if (A.logp) A.logp[row] = (float)(lse * LN2);
+  }
+}
+
+hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* w, const float* mu, const float* cv,
+                              hipStream_t s) {
+  LargeKArgs a = a0;
+  hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
+                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)), const_cast<double*>(a.c),
+                     const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
+                     const_cast<float*>(a.esh), const_cast<float*>(a.eall),
+                     const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto kA = largek_kernel<128, 0>;
+  auto kT = largek_kernel<128, 1>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)kT, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    attr_set = true;
+  }
+  const int64_t N = a.N;
+  const unsigned char* x0 = reinterpret_cast<const unsigned char*>(a.x);
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk_rows) {
+    LargeKArgs ac = a;
+    ac.N = std::min<int64_t>(p.chunk_rows, N - r0);
+    ac.x = x0 + (size_t)r0 * p.ld_x * 2;
+    ac.idx = a.idx + r0 * a.m;
+    ac.resp = a.resp + r0 * a.m;
+    ac.count = a.count ? a.count + r0 : nullptr;
+    ac.logp = a.logp ? a.logp + r0 : nullptr;
+    ac.G = p.GbA;
+    hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(largek_topm_final_kernel, dim3((unsigned)((ac.N + 3) / 4)), dim3(256), 0, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -22,32 +22,6 @@
 
 namespace gmm {
 
-namespace {
-
-// (score, index) order: larger score first, then smaller index
-__device__ __forceinline__ bool before(double la, int ka, double lb, int kb) {
-  return la > lb || (la == lb && ka < kb);
-}
-
-// wave-wide (64-lane) reductions through ds_bpermute, fixed butterfly order
-__device__ __forceinline__ double wave_max(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-__device__ __forceinline__ void wave_best(double& l, int& k) {
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double l2 = __shfl_xor(l, off);
-    const int k2 = __shfl_xor(k, off);
-    if (before(l2, k2, l, k)) { l = l2; k = k2; }
-  }
-}
-
-}  // namespace
-
 template <int COV, int DP, int KW>
 __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
   constexpr int T = kTopmRows;

@@ -149,3 +149,84 @@ def test_estep_stats_match_oracle(torch_cuda):
     assert (np.abs(sx - rsx)[big] / scale[big]).max() <= TOL_LOWP
     np.testing.assert_allclose(to_np(st["sxx"])[0][big], rsxx[big], rtol=TOL_LOWP)
     np.testing.assert_allclose(to_np(st["loglik"])[0], ref["ll"][0], rtol=1e-5)
+
+
+# ------------------------------------------------------------------ top-m
+def gpu_topm(torch, X, w, mu, cv, m, thr, ws=None):
+    import soft_clustering_em_amd as g
+    B, N = X.shape[0], X.shape[1]
+    wd, mud, cvd = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda") for a in (w, mu, cv))
+    idx = torch.full((B, N, m), -7, dtype=torch.int32, device="cuda")
+    resp = torch.full((B, N, m), -7.0, dtype=torch.float32, device="cuda")
+    cnt = torch.full((B, N), -7, dtype=torch.int32, device="cuda")
+    logp = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+    g.gmm_predict_proba_topm(X, wd, mud, cvd, "spherical", m, thr, idx, resp, cnt, logp, ws=ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()[0], resp.cpu().numpy()[0], cnt.cpu().numpy()[0], logp.cpu().numpy()[0]
+
+
+def check_topm_bf16(torch, bits, w, mu, cv, m, thr, label, ws=None):
+    """bits (1,N,D) uint16; parameters (1,K[,D]) float32.  Ranks and counts
+    exact where the oracle's margin exceeds 1e-6; responsibilities and log p
+    to float32 rounding (they are decided in float64 on both sides)."""
+    X = bf16_tensor(torch, bits)
+    gi, gr, gc, gl = gpu_topm(torch, X, w, mu, cv, m, thr, ws)
+    thr32 = float(np.float32(thr))
+    oi, orr, oc, ol, om = oracle.topm("spherical", (bits[0], "bf16"), w[0].astype(np.float64),
+                                      mu[0].astype(np.float64), cv[0].astype(np.float64), m, thr32)
+    ok = om > 1e-6
+    bad = np.nonzero(ok & ((gi != oi).any(1) | (gc != oc)))[0]
+    assert bad.size == 0, (label, bad[:5], gi[bad[:5]], oi[bad[:5]], om[bad[:5]])
+    kept = oi >= 0
+    np.testing.assert_allclose(gr[ok[:, None] & kept], orr[ok[:, None] & kept], rtol=1e-6, atol=1e-7)
+    assert (gr[~kept & ok[:, None]] == 0).all()
+    np.testing.assert_allclose(gl, ol, rtol=2e-6, atol=1e-5)
+    print(f"{label}: rows={bits.shape[1]} excluded(margin<=1e-6)={int((~ok).sum())} "
+          f"mean kept={gc.mean():.2f}", flush=True)
+
+
+def test_topm_ivf_trained(torch_cuda):
+    """The IVF workload's soft multi-assignment (m = 4, threshold 0.1) under
+    the model after two EM steps, on its first 30,000 rows."""
+    wl = synth.ivf_bf16(N=30_000)
+    thetas, _ = oracle_trajectory(wl, 2)
+    w, mu, cv = thetas[2]
+    check_topm_bf16(torch_cuda, wl.X, w, mu, cv, 4, 0.1, "ivf N=30000 K=4096")
+
+
+@pytest.mark.parametrize("m,thr", [(1, 0.1), (3, 0.05), (16, 0.001)])
+def test_topm_shapes(torch_cuda, m, thr):
+    wl = bf16_workload(4001, 100, 300, seed=m)
+    thetas, _ = oracle_trajectory(wl, 1)
+    w, mu, cv = thetas[1]
+    check_topm_bf16(torch_cuda, wl.X, w, mu, cv, m, thr, f"K=300 D=100 m={m}")
+
+
+def test_topm_all_components_path(torch_cuda):
+    """Every component within the band of every row's maximum (wide
+    components, means spread over a few units): more than 64 candidates per
+    row, so each row is rescored over all K components; the responsibilities
+    still differ enough to rank."""
+    rng = np.random.default_rng(8)
+    K, D, N = 520, 16, 1500
+    bits = synth.f32_to_bf16_bits((0.1 * rng.standard_normal((N, D))).astype(np.float32))[None]
+    mu = rng.standard_normal((1, K, D)).astype(np.float32)
+    w = np.full((1, K), 1.0 / K, np.float32)
+    cv = np.full((1, K), 4.0, np.float32)
+    check_topm_bf16(torch_cuda, bits, w, mu, cv, 4, 0.001, "flat K=520")
+
+
+def test_topm_short_chunks(torch_cuda):
+    import soft_clustering_em_amd as g
+    torch = torch_cuda
+    wl = synth.ivf_bf16(N=5_000, K=512)
+    thetas, _ = oracle_trajectory(wl, 1)
+    w, mu, cv = thetas[1]
+    X = bf16_tensor(torch, wl.X)
+    full = g.gmm_workspace_bytes(X, wl.K, "spherical", op=g.OP_TOPM, m=4)
+    # per row: slice pairs, LSE, |x|^2, row maximum and slice remainders,
+    # candidate count and list
+    per_row = 4 * (2 * 2 + 1) + 8 + 4 * (1 + 2) + 4 * (1 + 1024)
+    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    check_topm_bf16(torch, wl.X, w, mu, cv, 4, 0.1, "ivf K=512 chunks of about 1000 rows",
+                    ws=ws[:full - 4000 * per_row])

@@ -114,12 +114,13 @@ def test_topm_widths(torch_cuda, m, K):
 
 
 def test_topm_many_candidates_path(torch_cuda):
-    """Every component close to every row: more than 64 candidates per row, so
-    the all-components path runs."""
+    """Every component close to every row (wide components, means spread over
+    a few units): more than 64 candidates per row, so the all-components path
+    runs; the responsibilities still differ enough to rank."""
     rng = np.random.default_rng(5)
     K, D, N = 200, 4, 2000
     X = (0.1 * rng.standard_normal((1, N, D))).astype(np.float32)
-    mu = (0.01 * rng.standard_normal((1, K, D))).astype(np.float32)
+    mu = rng.standard_normal((1, K, D)).astype(np.float32)
     w = np.full((1, K), 1 / K, np.float32)
     cv = np.full((1, K), 4.0, np.float32)
     check_topm(torch_cuda, X, "spherical", w, mu, cv, m=4, thr=0.001, label="flat")
