@@ -25,10 +25,11 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# per-file additions: the large-K kernels take maxima of finite values only
-# (dead components carry a finite floor), so min/max need no NaN quieting and
-# fold with their DPP operands
-EXTRA = {"gmm_largek.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# per-file additions: the E-step kernels never form a NaN (dead components
+# carry -inf or a finite floor, and every exponent of a difference is guarded),
+# so min/max need no NaN quieting and fold with their DPP operands
+_NONAN = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+EXTRA = {"gmm_largek.hip": _NONAN, "gmm_estep.hip": _NONAN}
 
 
 def _compile(src: str) -> str:
