@@ -85,8 +85,7 @@ static void largek_layout(Plan& q, int64_t chunk) {
   q.off_xsq = o;  o = align_up(o + sizeof(double) * (size_t)chunk);
   if (q.op == GMM_OP_TOPM) {
     q.off_mrow = o; o = align_up(o + sizeof(float) * (size_t)chunk);
-    q.off_cnt = o;  o = align_up(o + sizeof(int32_t) * (size_t)chunk);
-    q.off_cand = o; o = align_up(o + sizeof(int32_t) * (size_t)chunk * kLargeKCap);
+    q.off_cmask = o; o = align_up(o + sizeof(uint32_t) * (size_t)chunk * (q.KP / 32));
     q.off_prem = o; o = align_up(o + sizeof(float) * (size_t)chunk * q.S);
   }
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
@@ -121,6 +120,7 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     if (cov != SPH) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows are supported for spherical components only");
     if (d->B != 1) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: one problem per call (B = 1)");
     if (d->D > 128) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: D <= 128");
+    if (K > kLargeKMaxK) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: K <= %d", kLargeKMaxK);
     q.largek = true;
     q.DP = 128;
     q.F = q.G = q.DP;
@@ -244,7 +244,7 @@ static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
     largek_layout(q, 32);
     if (ws_bytes >= q.ws_bytes) {
       size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
-      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (1 + p.S) + sizeof(int32_t) * (1 + kLargeKCap);
+      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (1 + p.S) + sizeof(uint32_t) * (p.KP / 32);
       int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
       chunk = std::min<int64_t>(chunk, p.chunk_rows);
       for (largek_layout(q, chunk); q.ws_bytes > ws_bytes && chunk > 32; largek_layout(q, chunk)) chunk -= 32;
@@ -294,8 +294,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
   A.kconst = reinterpret_cast<double2*>(w + p.off_kconst);
   if (p.op == GMM_OP_TOPM) {
     A.mrow = reinterpret_cast<float*>(w + p.off_mrow);
-    A.cnt = reinterpret_cast<int32_t*>(w + p.off_cnt);
-    A.cand = reinterpret_cast<int32_t*>(w + p.off_cand);
+    A.cmask = reinterpret_cast<uint32_t*>(w + p.off_cmask);
     A.prem = reinterpret_cast<float*>(w + p.off_prem);
   }
   return A;

@@ -47,7 +47,7 @@ struct Plan {
   int64_t chunk_rows = 0;   // rows per chunk (large K)
   int lse_blocks = 0;       // blocks of the large-K LSE pass
   size_t lds_a = 0, lds_t = 0, lds_c = 0;
-  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cnt = 0, off_cand = 0;
+  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
@@ -105,9 +105,8 @@ struct LargeKArgs {
   const double2* kconst; // (KP) (c0 - lambda |mu|^2 log2(e) / 2, lambda log2(e)) for exact scores
   float* prem;          // (chunk, S) below-band mass of each slice, relative to mrow
   float* mrow;          // (chunk) row maximum of the log-scores (pass B)
-  int32_t* cnt;         // (chunk) candidate count of each row (pass B clears it)
-  int32_t* cand;        // (chunk, kLargeKCap) candidate components
-  int topm;             // pass B: write mrow and clear cnt
+  uint32_t* cmask;      // (chunk, KP/32) candidate components of each row, one bit per component
+  int topm;             // pass B: write mrow
   int m;
   float thr;
   int32_t* idx;         // outputs of the chunk's rows
@@ -115,8 +114,8 @@ struct LargeKArgs {
   int32_t* count;
   float* logp;
 };
-constexpr int kLargeKCap = 1024;        // candidates kept per row before the all-K fallback
-constexpr int64_t kLargeKTopmChunk = 1 << 15;
+constexpr int64_t kLargeKTopmChunk = 1 << 18;
+constexpr int kLargeKMaxK = 16384;     // components of one large-K problem at most
 hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,
                               hipStream_t s);
 hipError_t launch_largek(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,

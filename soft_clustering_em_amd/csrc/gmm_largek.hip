@@ -66,8 +66,7 @@ constexpr float kDead = -1.0e30f;
 // are rescored exactly; the others (each below 2^-20 of the maximum's mass)
 // enter the row's LSE with their expanded-form scores
 constexpr float kTopmBand = 20.f;
-// candidates of one row in one slice held in LDS before they go to the row's list
-constexpr int kCandL = 40;
+
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
@@ -187,7 +186,7 @@ size_t largek_lds_bytes(int DP, int pass) {
   if (pass == 2) b += (size_t)DP * XTS * 2;                 // transposed tile
   b += (size_t)LT * 8;                                      // |x|^2
   if (pass != 2) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
-  if (pass == 1) b += (size_t)2 * LT * (1 + kCandL) * 4;    // candidate lists, two tiles
+  if (pass == 1) b += (size_t)2 * LT * LNW * 4;             // candidate masks, two tiles
   return b;
 }
 
@@ -217,11 +216,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   unsigned short* xt = rows + LT * LRS;
   double* xsq = reinterpret_cast<double*>(xt + (STATS ? DP * XTS : 0));
   float* red = reinterpret_cast<float*>(xsq + LT);   // pass A: 2 buffers of LNW * LT * 2
-  int* lcnt = reinterpret_cast<int*>(red + 2 * LNW * LT * 2);  // pass T: 2 x LT counts
-  int* lcand = lcnt + 2 * LT;                                  // pass T: 2 x LT x kCandL
-  if constexpr (PASS == 1) {
-    if (threadIdx.x < 2 * LT) lcnt[threadIdx.x] = 0;
-  }
+  // pass T: 2 buffers of (LT rows, LNW waves) candidate masks, bit j of word
+  // (row, w) = component w * 32 + j of the slice
+  uint32_t* lmask = reinterpret_cast<uint32_t*>(red + 2 * LNW * LT * 2);
 
   // the first row tiles start loading before the weights are staged
   Piece pf[PF];
@@ -273,23 +270,17 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       const int p = lane;
       const int64_t row = prow0 + p;
       if (PASS == 1) {
-        // this slice's candidates of the row go to the row's list (a count
-        // past kCandL sends the row to the all-components path)
+        // this slice's below-band mass and its 8 candidate words of the row
         const int buf = (rb - red) / (LNW * LT * 2);
-        int* lc = lcnt + buf * LT;
-        const int n = lc[p];
-        lc[p] = 0;
         if (row < nrows) {
           float S = 0.f;
 #pragma unroll
           for (int w2 = 0; w2 < LNW; ++w2) S += rb[(w2 * LT + p) * 2 + 1];
           A.prem[(size_t)row * A.S + slice] = S;
-          if (n > 0) {
-            const int base = atomicAdd(A.cnt + row, n > kCandL ? kLargeKCap + 1 : n);
-            const int* src = lcand + (buf * LT + p) * kCandL;
-            for (int i = 0; i < n && i < kCandL && base + i < kLargeKCap; ++i)
-              A.cand[(size_t)row * kLargeKCap + base + i] = src[i];
-          }
+          const uint32_t* src = lmask + (buf * LT + p) * LNW;
+          uint4* dst = reinterpret_cast<uint4*>(A.cmask + (size_t)row * (A.KP / 32) + slice * LNW);
+          dst[0] = uint4{src[0], src[1], src[2], src[3]};
+          dst[1] = uint4{src[4], src[5], src[6], src[7]};
         }
       } else if (row < nrows) {
         float M = rb[p * 2];
@@ -375,26 +366,25 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // of the row's maximum (its expanded-form error counted twice); the
       // mass 2^(l - max) of the others, per row, for the LSE
       float rem[8];
+      uint32_t* mbuf = lmask + (it & 1) * (LT * LNW);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
         const int64_t row = row0 + p;
         rem[q] = 0.f;
-        if (row < nrows) {
-          const float mr = A.mrow[row];
-          const float floor_l = mr - kTopmBand;
-          const float xs = (float)xsq[p];
+        const float mr = row < nrows ? A.mrow[row] : 0.f;
+        const float floor_l = mr - kTopmBand;
+        const float xs = (float)xsq[p];
+        uint32_t word = 0;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            if (lg[q][nt] + 2.f * fmaf(ea[nt], xs, ea0[nt]) >= floor_l) {
-              const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
-              const int slot = atomicAdd(lcnt + (it & 1) * LT + p, 1);
-              if (slot < kCandL) lcand[((it & 1) * LT + p) * kCandL + slot] = k;
-            } else {
-              rem[q] += __builtin_amdgcn_exp2f(lg[q][nt] - mr);
-            }
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          const bool cand = row < nrows && lg[q][nt] + 2.f * fmaf(ea[nt], xs, ea0[nt]) >= floor_l;
+          if (!cand && row < nrows) rem[q] += __builtin_amdgcn_exp2f(lg[q][nt] - mr);
+          // lanes 16g..16g+15 hold row (q, g): their 16 bits are this row's components nt*16 .. +15
+          const uint64_t b = __builtin_amdgcn_ballot_w64(cand);
+          word |= (uint32_t)((b >> (16 * (lane >> 4))) & 0xFFFFu) << (16 * nt);
         }
+        if ((lane & 15) == 0) mbuf[p * LNW + wv] = word;
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) rem[q] += dpp_mov<0xB1>(rem[q]);
@@ -577,10 +567,7 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
     const double l2 = (double)M + log2(S);
     A.lse[row] = (float)l2;
     ll += l2 * LN2;
-    if (A.topm) {
-      A.mrow[row] = M;
-      A.cnt[row] = 0;
-    }
+    if (A.topm) A.mrow[row] = M;
   }
   red[threadIdx.x] = ll;
   __syncthreads();
@@ -694,20 +681,21 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
 }
 
 
-// Top-m, last step: one wave per row.  The row's candidates (all K
-// components, in batches, when it has more than kLargeKCap) are scored 16
-// lanes to a candidate (lane i of a group holds dims 8i..8i+7 of the row),
-// sixteen at a time, exactly in float64: c0 - (lambda/2) log2(e) (|x|^2 -
-// 2 x . mu + |mu|^2), every product of a bf16 x and a float32 mu being exact
-// in float64, so the expanded form loses nothing at float64 precision.  The
-// scores go to LDS; each batch updates the row's running (max, sum) and its
-// best m (kept in LDS ahead of the next batch's scores), chosen by m rounds
-// of a wave-wide best.  The LSE adds pass T's below-band mass.  Rank 1 is
-// always kept, ranks 2..m while r >= thr.
+// Top-m, last step: one wave per row.  The row's candidates (the set bits of
+// its mask, in increasing component order) are scored in batches, 16 lanes to
+// a candidate (lane i of a group holds dims 8i..8i+7 of the row), sixteen at a
+// time, exactly in float64: c0 - (lambda/2) log2(e) (|x|^2 - 2 x . mu +
+// |mu|^2), every product of a bf16 x and a float32 mu being exact in float64,
+// so the expanded form loses nothing at float64 precision.  The scores go to
+// LDS; each batch updates the row's running (max, sum) and its best m (kept
+// in LDS ahead of the next batch's scores), chosen by m rounds of a
+// wave-wide best.  The LSE adds pass T's below-band mass.  Rank 1 is always
+// kept, ranks 2..m while r >= thr.  Every step runs in a fixed order.
 constexpr int kTopmMaxM = 16;
 constexpr int kBatch = 512;                       // scores per batch
 constexpr int kSlots = kTopmMaxM + kBatch;        // running best m, then the batch
 constexpr int kPer = (kSlots + 63) / 64;          // slots per lane in the selection
+constexpr int kMaskSlots = kLargeKMaxK / 32 / 64;  // mask words per lane at the largest K
 
 // 2^d for d <= 0 to about 1e-7 relative: float exp2 of the float part and a
 // first-order correction for the rest of d
@@ -717,11 +705,22 @@ __device__ __forceinline__ double exp2_acc(double d) {
   return (double)__builtin_amdgcn_exp2f(h) * (1.0 + l * 0.69314718055994530942);
 }
 
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  total = __shfl(x, 63, 64);
+  return x - v;
+}
+
 __global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
-  constexpr double kLog2e = 1.4426950408889634074;
   constexpr double LN2 = 0.69314718055994530942;
   __shared__ double sl[4][kSlots];
   __shared__ int skk[4][kSlots];
+  __shared__ unsigned short slist[4][kBatch];
   const int lane = threadIdx.x & 63;
   const int wq = threadIdx.x >> 6;
   const int grp = lane >> 4, li = lane & 15;
@@ -729,11 +728,22 @@ __global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
   if (row >= A.N) return;  // uniform across the wave; the block has no barrier
   double* L = sl[wq];
   int* KK = skk[wq];
+  unsigned short* LST = slist[wq];
   const int m = A.m;
   const int D = (int)A.D;
-  const int n = A.cnt[row];
-  const bool all = n > kLargeKCap;
-  const int total = all ? A.K : n;
+  const int nwords = A.KP / 32;
+  // this lane's words of the row's candidate mask: lanes cover words lane*wpl .. +wpl-1
+  const int wpl = (nwords + 63) / 64;
+  uint32_t mw[kMaskSlots];
+  int mycount = 0;
+#pragma unroll
+  for (int t = 0; t < kMaskSlots; ++t) {
+    const int wi = lane * wpl + t;
+    mw[t] = (t < wpl && wi < nwords) ? A.cmask[(size_t)row * nwords + wi] : 0u;
+    mycount += __popc(mw[t]);
+  }
+  int total;
+  const int mybase = wave_excl_scan(mycount, lane, total);
   // this lane's 8 dims of the row
   const unsigned short* xr = reinterpret_cast<const unsigned short*>(A.x) + row * A.ld_x;
   double xv[8];
@@ -743,6 +753,7 @@ __global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
     xv[e] = d < D ? (double)__uint_as_float((unsigned)xr[d] << 16) : 0.0;
   }
   const bool vec = (D & 7) == 0 && ((uintptr_t)A.mu & 15) == 0;
+  const int doff = vec ? min(8 * li, D - 8) : 0;
   const double xsq = A.xsq[row];
   if (lane < kTopmMaxM) {
     L[lane] = -INFINITY;
@@ -751,21 +762,32 @@ __global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
   double Mrun = -INFINITY, Srun = 0.0;
   for (int b0 = 0; b0 < total; b0 += kBatch) {
     const int nb = min(kBatch, total - b0);
+    // the batch's component list, in increasing component order
+    {
+      int r = mybase;
+#pragma unroll
+      for (int t = 0; t < kMaskSlots; ++t) {
+        uint32_t w = mw[t];
+        const int kbase = (lane * wpl + t) * 32;
+        while (w) {
+          const int bit = __builtin_ctz(w);
+          w &= w - 1;
+          if (r >= b0 && r < b0 + nb) LST[r - b0] = (unsigned short)(kbase + bit);
+          ++r;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // 16 candidates per step (four per 16-lane group), their loads issued
-    // together and unconditionally (indices past the batch repeat its last
-    // entry; lanes past D read inside the row and hold x = 0)
+    // together (indices past the batch repeat its last entry; lanes past D
+    // read inside the row and hold x = 0)
     constexpr int U = 4;
-    const int doff = vec ? min(8 * li, D - 8) : 0;
     for (int i0 = 0; i0 < nb; i0 += 4 * U) {
       int ku[U];
-      if (all) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) ku[u] = b0 + min(i0 + 4 * u + grp, nb - 1);
-      } else {
-        const int* cl = A.cand + (size_t)row * kLargeKCap + b0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) ku[u] = cl[min(i0 + 4 * u + grp, nb - 1)];
-      }
+      for (int u = 0; u < U; ++u) ku[u] = LST[min(i0 + 4 * u + grp, nb - 1)];
       double2 cu[U];
       float4 m0[U], m1[U];
 #pragma unroll
@@ -865,12 +887,9 @@ __global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  double S = Srun;
-  if (!all) {
-    // below-band mass of every slice, relative to the expanded-form maximum
-    const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
-    S += rem * exp2((double)A.mrow[row] - Mrun);
-  }
+  // below-band mass of every slice, relative to the expanded-form maximum
+  const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
+  const double S = Srun + rem * exp2((double)A.mrow[row] - Mrun);
   const double lse = Mrun + log2(S);
   if (lane == 0) {
     int c = 0;

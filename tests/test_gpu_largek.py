@@ -225,8 +225,8 @@ def test_topm_short_chunks(torch_cuda):
     X = bf16_tensor(torch, wl.X)
     full = g.gmm_workspace_bytes(X, wl.K, "spherical", op=g.OP_TOPM, m=4)
     # per row: slice pairs, LSE, |x|^2, row maximum and slice remainders,
-    # candidate count and list
-    per_row = 4 * (2 * 2 + 1) + 8 + 4 * (1 + 2) + 4 * (1 + 1024)
+    # candidate mask (one bit per component)
+    per_row = 4 * (2 * 2 + 1) + 8 + 4 * (1 + 2) + 512 // 8
     ws = torch.empty(full, dtype=torch.uint8, device="cuda")
     check_topm_bf16(torch, wl.X, w, mu, cv, 4, 0.1, "ivf K=512 chunks of about 1000 rows",
                     ws=ws[:full - 4000 * per_row])
