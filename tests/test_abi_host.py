@@ -139,3 +139,55 @@ def test_mstep_validation():
     assert L.gmm_mstep(1, 8, ctypes.byref(st), 0, ctypes.byref(p), None, None, None) == _abi.GMM_ERR_INVALID_ARG
     st.nk = None
     assert L.gmm_mstep(1, 8, ctypes.byref(st), 100, ctypes.byref(p), None, None, None) == _abi.GMM_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ bf16 rows (large-K path)
+def _bf16(N, D=128, B=1):
+    return _data(N, D=D, B=B, dtype=_abi.DT_BF16)
+
+
+@pytest.mark.parametrize("cov,B,D,K,ok", [
+    (_abi.COV_SPHERICAL, 1, 128, 4096, True),
+    (_abi.COV_SPHERICAL, 1, 100, 300, True),
+    (_abi.COV_SPHERICAL, 1, 128, 16384, True),
+    (_abi.COV_SPHERICAL, 1, 128, 16385, False),   # above the large-K window
+    (_abi.COV_SPHERICAL, 1, 129, 64, False),      # D > 128
+    (_abi.COV_SPHERICAL, 2, 64, 64, False),       # one problem per call
+    (_abi.COV_DIAG, 1, 64, 64, False),            # bf16 rows: spherical only
+    (_abi.COV_FULL, 1, 8, 8, False),
+])
+def test_bf16_support_window(cov, B, D, K, ok):
+    L = _abi.lib()
+    n = L.gmm_workspace_bytes(ctypes.byref(_bf16(10_000, D=D, B=B)), K, cov, _abi.OP_FIT, 0)
+    assert (n > 0) == ok
+    f16 = _data(10_000, D=D, dtype=_abi.DT_F16)
+    assert L.gmm_workspace_bytes(ctypes.byref(f16), K, cov, _abi.OP_FIT, 0) == 0
+
+
+def test_bf16_workspace_stops_growing_after_one_chunk():
+    """The large-K scratch is O(rows per chunk): constant once N exceeds a chunk
+    (2^20 rows for the fit, 2^18 for top-m)."""
+    L = _abi.lib()
+    for op, chunk in ((_abi.OP_FIT, 1 << 20), (_abi.OP_TOPM, 1 << 18)):
+        sizes = [L.gmm_workspace_bytes(ctypes.byref(_bf16(n)), 4096, _abi.COV_SPHERICAL, op, 4)
+                 for n in (chunk, 2 * chunk, 10 ** 7, 10 ** 9)]
+        assert len(set(sizes)) == 1, (op, sizes)
+        small = L.gmm_workspace_bytes(ctypes.byref(_bf16(chunk // 4)), 4096, _abi.COV_SPHERICAL, op, 4)
+        assert 0 < small < sizes[0]
+        # far below the float32 N x K responsibility matrix of one chunk
+        assert sizes[0] < chunk * 4096 * 4
+
+
+def test_bf16_small_workspace_is_accepted_down_to_one_tile():
+    """A workspace below the preferred size streams shorter chunks; below the
+    size for a single 32-row tile the call is rejected before any device work."""
+    L = _abi.lib()
+    d = _bf16(100_000)
+    p = _params(K=4096, cov=_abi.COV_SPHERICAL)
+    full = L.gmm_workspace_bytes(ctypes.byref(d), 4096, _abi.COV_SPHERICAL, _abi.OP_FIT, 0)
+    tiny = L.gmm_workspace_bytes(ctypes.byref(_bf16(32)), 4096, _abi.COV_SPHERICAL, _abi.OP_FIT, 0)
+    opts = _abi.GmmOptions(1e-6, 0, None, None)
+    ws = ctypes.c_void_p(1 << 20)
+    st = L.gmm_fit_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(opts), None, None, ws, tiny - 256, None)
+    assert st == _abi.GMM_ERR_WORKSPACE, L.gmm_last_error()
+    assert tiny < full
