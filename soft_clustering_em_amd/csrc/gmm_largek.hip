@@ -70,23 +70,6 @@ constexpr float kTopmBand = 20.f;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
-// 16-lane all-reduce of a double (the two halves moved by the DPP patterns of
-// row16_sum)
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const long long b = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffLL), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-__device__ __forceinline__ double row16_sum_f64(double v) {
-  v += dpp_f64<0xB1>(v);
-  v += dpp_f64<0x4E>(v);
-  v += dpp_f64<0x141>(v);
-  v += dpp_f64<0x140>(v);
-  return v;
-}
-
 // The 16-byte piece of a row tile that thread j loads: pass A takes row
 // j / 16, dims 8 (j % 16) .. +7 (a row's pieces in 16 consecutive lanes);
 // pass C takes row j % 32, dims 8 (j / 32) .. +7 (a piece's 32 rows in
