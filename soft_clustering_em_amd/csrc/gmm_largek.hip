@@ -21,12 +21,12 @@
 // itself is exact in bf16); the statistics contraction X^T R runs on the same
 // instruction with r rounded to bf16.  Every statistic (N_k, sum r x,
 // sum r |x|^2) uses that same rounded r, so the M-step sees the exact moments
-// of one set of weights.  Each tile's MFMA results (32 rows: exact bf16
-// products) are added into float64 accumulators, and the responsibilities of
-// a tile are summed in two magnitude classes (r >= 2^-8 and below) by
-// separate MFMAs: a component collapsed onto a row far from the origin has a
-// variance many orders below |mu|^2, carried by rows of tiny r that a
-// float32 sum with its own row, or float32 sums over many tiles, would bury.  The logit accumulator layout
+// of one set of weights.  The responsibilities are summed in two magnitude
+// classes (r >= 2^-8 and below) by separate MFMAs into separate float32
+// accumulators, added in float64 at the chunk's partial: a component
+// collapsed onto a row far from the origin has a variance many orders below
+// |mu|^2, carried by rows of tiny r that a float32 sum with its own row
+// (r near 1) would bury; within a class the terms are of like magnitude.  The logit accumulator layout
 // (lane l: component l%16, rows 4(l/16)+v of a 16-row block) provides R as
 // the B operand of the statistics MFMA directly when the 32 rows of a tile
 // are ordered k = 8g + j <-> row 4g + j (j < 4), 16 + 4g + (j - 4) (j >= 4);
@@ -229,9 +229,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     }
     any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(eb[nt] > 0.f) != 0);
   }
-  // pass C: statistics of the r >= 2^-8 class in float64 (one tile at a
-  // time), of the small class in the MFMA's float32 accumulator
-  double sbig[STATS ? GM : 1][NT][4];
+  // pass C: statistics of the r >= 2^-8 and r < 2^-8 classes, each in its
+  // own float32 MFMA accumulator (float64 at the chunk's partial)
+  floatx4 sbig[STATS ? GM : 1][NT];
   floatx4 ssmall[STATS ? GM : 1][NT];
   double nk[NT], qs[NT];
 #pragma unroll
@@ -239,8 +239,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       ssmall[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sbig[mt][nt][v] = 0.0;
+      sbig[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) nk[nt] = qs[nt] = 0.0;
@@ -453,11 +452,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (mt * 16 + (lane & 15)) * XTS + 8 * (lane >> 4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const floatx4 t1 =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          sbig[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], sbig[mt][nt], 0, 0, 0);
           ssmall[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bsmall[nt], ssmall[mt][nt], 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sbig[mt][nt][v] += (double)t1[v];
         }
       }
 #pragma unroll
@@ -509,7 +505,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         for (int v = 0; v < 4; ++v) {
           const int row = mt * 16 + 4 * (lane >> 4) + v;
           double* dst = part + (size_t)k * PR + 2 + row;
-          *dst = (A.accumulate ? *dst : 0.0) + (sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
+          *dst = (A.accumulate ? *dst : 0.0) + ((double)sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
         }
       }
     __syncthreads();
