@@ -112,15 +112,15 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   double ll = 0.0;
   // statistic feature held by this lane in row tile mt: f = 16 mt + lane%16,
   // as (fd, fe): fe < 0 -> x_fd (or 0 when fd < 0); else x_fd * x_fe
-  int fd[GM], fe[GM];
+  // (spherical and diagonal: x_f, or x_{f-DP}^2 in the diagonal's second
+  // half, which starts at a 16-row tile boundary -- known per tile at compile time)
+  int fd[QUAD ? GM : 1], fe[QUAD ? GM : 1];
+  if constexpr (QUAD) {
 #pragma unroll
-  for (int mt = 0; mt < GM; ++mt) {
-    const int f = mt * 16 + (lane & 15);
-    fd[mt] = f;
-    fe[mt] = -1;
-    if constexpr (COV == DIAG) {
-      if (f >= DP) { fd[mt] = f - DP; fe[mt] = f - DP; }
-    } else if constexpr (QUAD) {
+    for (int mt = 0; mt < GM; ++mt) {
+      const int f = mt * 16 + (lane & 15);
+      fd[mt] = f;
+      fe[mt] = -1;
       if (f >= DP) {
         if (f - DP < NQ) {
           const int de = quad_pair<DP>(f - DP);
@@ -378,14 +378,17 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 #pragma unroll
         for (int mt = 0; mt < GM; ++mt) {
           double av;
-          if constexpr (COV == SPH) {
-            av = (double)phi[prow * FS + fd[mt]];
-          } else {
+          if constexpr (QUAD) {
             if (fe[mt] < 0) {
               av = fd[mt] >= 0 ? (double)phi[prow * FS + fd[mt]] : 0.0;
             } else {
               av = (double)phi[prow * FS + fd[mt]] * (double)phi[prow * FS + fe[mt]];
             }
+          } else if (COV == DIAG && mt * 16 >= DP) {
+            const double xv = (double)phi[prow * FS + mt * 16 - DP + (lane & 15)];
+            av = xv * xv;
+          } else {
+            av = (double)phi[prow * FS + mt * 16 + (lane & 15)];
           }
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
