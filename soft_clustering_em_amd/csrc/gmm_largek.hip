@@ -30,7 +30,8 @@
 // (lane l: component l%16, rows 4(l/16)+v of a 16-row block) provides R as
 // the B operand of the statistics MFMA directly when the 32 rows of a tile
 // are ordered k = 8g + j <-> row 4g + j (j < 4), 16 + 4g + (j - 4) (j >= 4);
-// the A operand X^T is kept in LDS in that order.  Workgroups of one row
+// the A operand X^T is kept in LDS in that order (its feature rows permuted
+// against bank conflicts, see xt_row).  Workgroups of one row
 // group and different slices have ids that differ by multiples of 8, so they
 // share an XCD and its L2 copy of the rows.
 #include "gmm_device.h"
@@ -39,11 +40,16 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gmm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -57,8 +63,11 @@ constexpr int XTS = 40;                // LDS row stride of the transposed tile,
 // lambda (|mu|^2 + D sigma^2) > kSharpLowp: with bf16 weights (two-term
 // split) their rounding would reach about 1% of a responsibility.
 constexpr double kSharpLowp = 2.0e3;
-// responsibilities at or above this go to the "big" class of the statistics MFMA
+// responsibilities at or above this go to the "big" class of the statistics
+// MFMA; r >= 0, so the class test compares bf16 bit patterns
 constexpr float kBigR = 0x1p-8f;
+constexpr short kBigRBits = 0x3B80;
+static_assert(__builtin_bit_cast(unsigned, kBigR) == (unsigned)kBigRBits << 16, "bf16 pattern of kBigR");
 // log-score constant of padded and dead components: finite, so that maxima
 // and differences stay finite, and far enough down that 2^(l - max) is 0
 constexpr float kDead = -1.0e30f;
@@ -70,79 +79,110 @@ constexpr float kTopmBand = 20.f;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
-// The 16-byte piece of a row tile that thread j loads: pass A takes row
-// j / 16, dims 8 (j % 16) .. +7 (a row's pieces in 16 consecutive lanes);
-// pass C takes row j % 32, dims 8 (j / 32) .. +7 (a piece's 32 rows in
-// consecutive lanes, for the transposed copy).
-template <bool STATS>
+// The 16-byte piece of a row tile that thread j loads: row j / 16, dims
+// 8 (j % 16) .. +7 -- a row's 256 bytes come from 16 consecutive lanes, so a
+// wave's load touches 8 cache lines.
 __device__ __forceinline__ void piece_of(int j, int& r, int& c8) {
-  if constexpr (STATS) {
-    r = j % LT;
-    c8 = (j / LT) * 8;
-  } else {
-    r = j / 16;
-    c8 = (j % 16) * 8;
-  }
+  r = j / 16;
+  c8 = (j % 16) * 8;
 }
+
+// Pass C's transposed copy X^T keeps feature f = 8 m + e in LDS row
+// 16 e + m: the eight 2-byte stores of a piece (one per e) from the 16 lanes
+// of a row (m = 0..15) then fall on rows 80 bytes apart, spread over the
+// banks, where rows 8 features apart (640 bytes) would share one bank.  The
+// statistics tile mt (LDS rows 16 mt .. +15) thus holds features 8 i + mt.
+__device__ __forceinline__ int xt_row(int f) { return (f & 7) * 16 + (f >> 3); }
 
 struct Piece {
   u16x8 v;
   double xs;  // pass C: |x|^2 of row j (threads j < LT), computed by pass A
+  float ls;   // threads j < LT, row j: its LSE (pass C) or its maximum score (pass T)
+  int nv;     // dims of v that belong to the row (the rest is zeroed when staged)
 };
 
-template <bool STATS>
+// Loads without branches: every address is clamped into the chunk (N >= 1),
+// and what lies outside it is zeroed when the piece is staged.  Each call
+// then issues the same loads in the same order, so the wait before a tile's
+// staging covers only that tile's loads, not the later tiles' in flight.
+// VEC: rows 16-byte aligned with a stride that is a multiple of 8.
+template <int PASS, bool VEC, bool STATS = (PASS == 2)>
 __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, int64_t ntiles) {
   const unsigned short* xb = reinterpret_cast<const unsigned short*>(A.x);
   const int j = threadIdx.x;
   int r, c8;
-  piece_of<STATS>(j, r, c8);
+  piece_of(j, r, c8);
   const int64_t row = tile * LT + r;
+  const int64_t rc = row < A.N ? row : A.N - 1;
+  const int D = (int)A.D;
   Piece pc;
-  pc.v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  pc.xs = 0.0;
-  if (tile < ntiles && row < A.N) {
-    if (c8 + 8 <= A.D && A.vec16) {
-      pc.v = *reinterpret_cast<const u16x8*>(xb + row * A.ld_x + c8);
-    } else {
-      for (int e = 0; e < 8; ++e) pc.v[e] = (c8 + e < A.D) ? xb[row * A.ld_x + c8 + e] : (unsigned short)0;
-    }
+  pc.nv = (tile < ntiles && row < A.N) ? min(max(D - c8, 0), 8) : 0;
+  if constexpr (VEC) {
+    pc.v = *reinterpret_cast<const u16x8*>(xb + rc * A.ld_x + min(c8, (int)A.ld_x - 8));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pc.v[e] = xb[rc * A.ld_x + min(c8 + e, D - 1)];
   }
+  pc.xs = 0.0;
+  pc.ls = 0.f;
+  const int64_t xrow = tile * LT + (j & (LT - 1));  // every wave: the tile's 32 rows (threads j < LT keep theirs)
   if constexpr (STATS) {
-    const int64_t xrow = tile * LT + j;
-    if (j < LT && tile < ntiles && xrow < A.N) pc.xs = A.xsq[xrow];
+    // pass B padded the LSE with +inf to whole tiles (ntiles * LT rows)
+    pc.xs = A.xsq[xrow < A.N ? xrow : A.N - 1];
+    pc.ls = A.lse[xrow < ntiles * LT ? xrow : ntiles * LT - 1];
+  } else if constexpr (PASS == 1) {
+    pc.ls = A.mrow[xrow < A.N ? xrow : A.N - 1];
   }
   return pc;
 }
 
 // Write a thread's piece into the LDS tile.  Pass A also forms |x|^2 of each
-// row (each bf16 square is exact in float32, their sum exact in float64) and,
-// in the workgroups of slice 0, stores it for pass C; pass C writes the
+// row: in the workgroups of slice 0 exactly (each bf16 square is exact in
+// float32, their sum exact in float64), stored for pass C and the top-m
+// rescoring; elsewhere in float32; pass C writes the
 // transposed copy X^T[d][k] with the k order of the statistics MFMA.
 template <bool STATS>
 __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc, int64_t row0, int slice,
-                                            unsigned short* rows, unsigned short* xt, double* xsq) {
+                                            unsigned short* rows, unsigned short* xt, double* xsq, float* ls) {
   const int j = threadIdx.x;
   int r, c8;
-  piece_of<STATS>(j, r, c8);
-  *reinterpret_cast<u16x8*>(rows + r * LRS + c8) = pc.v;
+  piece_of(j, r, c8);
+  u16x8 v = pc.v;
+  if (pc.nv < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < pc.nv ? v[e] : (unsigned short)0;
+  }
+  *reinterpret_cast<u16x8*>(rows + r * LRS + c8) = v;
+  const bool live = row0 + j < A.N;  // threads j < LT: row j of the tile
+  if (j < LT) ls[j] = live ? pc.ls : (STATS ? INFINITY : 0.f);
   if constexpr (STATS) {
     const int g = (r & 15) >> 2, j4 = r & 3;
     const int kpos = 8 * g + (r < 16 ? j4 : 4 + j4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xt[(c8 + e) * XTS + kpos] = pc.v[e];
-    if (j < LT) xsq[j] = pc.xs;
-  } else {
+    for (int e = 0; e < 8; ++e) xt[xt_row(c8 + e) * XTS + kpos] = v[e];
+    if (j < LT) xsq[j] = live ? pc.xs : 0.0;
+  } else if (slice == 0) {
     double sq = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = bf16_to_f32(pc.v[e]);
+      const float f = bf16_to_f32(v[e]);
       sq += (double)(f * f);
     }
     sq = row16_sum_f64(sq);
     if ((j & 15) == 0) {
       xsq[r] = sq;
-      if (slice == 0 && row0 + r < A.N) A.xsq[row0 + r] = sq;
+      if (row0 + r < A.N) A.xsq[row0 + r] = sq;
     }
+  } else {
+    // the other slices use |x|^2 only in the float32 logits
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf16_to_f32(v[e]);
+      sq = fmaf(f, f, sq);
+    }
+    sq = row16_sum(sq);
+    if ((j & 15) == 0) xsq[r] = (double)sq;
   }
 }
 
@@ -163,11 +203,12 @@ __device__ __forceinline__ float largek_exact_score(const float* __restrict__ mu
 }  // namespace
 
 size_t largek_lds_bytes(int DP, int pass) {
-  const int ksl = pass != 2 ? KSA : KSC;
-  size_t b = (size_t)(ksl / 16) * 2 * (DP / 32) * 64 * 16;  // weights
-  b += (size_t)LT * LRS * 2;                                // row tile
-  if (pass == 2) b += (size_t)DP * XTS * 2;                 // transposed tile
-  b += (size_t)LT * 8;                                      // |x|^2
+  // weights (pass C keeps them in registers)
+  size_t b = pass != 2 ? (size_t)(KSA / 16) * 2 * (DP / 32) * 64 * 16 : 0;
+  size_t tile = (size_t)LT * LRS * 2;                       // row tile
+  if (pass == 2) tile += (size_t)DP * XTS * 2;              // transposed tile
+  tile += (size_t)LT * 8 + LT * 4;                          // |x|^2, LSE or maximum
+  b += (pass == 2 ? 3 : 1) * tile;                          // buffers
   if (pass != 2) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
   if (pass == 1) b += (size_t)2 * LT * LNW * 4;             // candidate masks, two tiles
   return b;
@@ -183,6 +224,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   constexpr int KSTEP = DP / 32;          // MFMA k-steps over the features
   constexpr int GM = DP / 16;             // statistic row tiles (dimensions)
   constexpr int WFRAG = (KSL / 16) * 2 * KSTEP * 64;
+  // pass C holds its wave's logit weights in registers for the whole kernel
+  // (NT * 2 * KSTEP fragments); passes A and T read them from LDS
+  constexpr bool WREG = STATS;
+  constexpr int WLDS = WREG ? 0 : WFRAG;  // 16-byte fragments in LDS
   constexpr int PF = 3;                   // row tiles in flight (registers)
   static_assert(DP == 128 && LT * DP / 8 == 64 * LNW, "one 16-byte piece per thread");
 
@@ -193,21 +238,35 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   const int64_t nrows = A.N;
   const int64_t ntiles = (nrows + LT - 1) / LT;
 
+  // row-tile buffers (rows, pass C's transposed copy, |x|^2, per-row LSE or
+  // maximum): pass C keeps
+  // three -- tile i's X^T for its statistics, tile i + 1's rows for its
+  // logits, tile i + 2 being staged -- and passes A and T one
+  constexpr int NB = STATS ? 3 : 1;
+  constexpr int BUFB = LT * LRS * 2 + (STATS ? DP * XTS * 2 : 0) + LT * 8 + LT * 4;  // bytes per buffer
+  static_assert(BUFB % 16 == 0, "16-byte aligned buffers");
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
-  unsigned short* rows = reinterpret_cast<unsigned short*>(Wl + WFRAG);
-  unsigned short* xt = rows + LT * LRS;
-  double* xsq = reinterpret_cast<double*>(xt + (STATS ? DP * XTS : 0));
-  float* red = reinterpret_cast<float*>(xsq + LT);   // pass A: 2 buffers of LNW * LT * 2
+  unsigned char* bufs = reinterpret_cast<unsigned char*>(Wl + WLDS);
+  auto rows_of = [&](int bi) { return reinterpret_cast<unsigned short*>(bufs + bi * BUFB); };
+  auto xt_of = [&](int bi) { return rows_of(bi) + LT * LRS; };
+  auto xsq_of = [&](int bi) { return reinterpret_cast<double*>(xt_of(bi) + (STATS ? DP * XTS : 0)); };
+  auto ls_of = [&](int bi) { return reinterpret_cast<float*>(xsq_of(bi) + LT); };
+  float* red = reinterpret_cast<float*>(bufs + NB * BUFB);  // pass A: 2 buffers of LNW * LT * 2
   // pass T: 2 buffers of (LT rows, LNW waves) candidate masks, bit j of word
   // (row, w) = component w * 32 + j of the slice
   uint32_t* lmask = reinterpret_cast<uint32_t*>(red + 2 * LNW * LT * 2);
 
-  // the first row tiles start loading before the weights are staged
-  Piece pf[PF];
+  bf16x8 wreg[WREG ? NT : 1][2][WREG ? KSTEP : 1];
+  if constexpr (WREG) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(A.W) + (size_t)slice * WFRAG;
 #pragma unroll
-  for (int u = 0; u < PF; ++u) pf[u] = fetch_piece<STATS>(A, g + (int64_t)u * A.G, ntiles);
-  {
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks) wreg[nt][h][ks] = src[(((wv * NT + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
+  } else {
     const uint4* src = reinterpret_cast<const uint4*>(A.W) + (size_t)slice * WFRAG;
     uint4* dst = reinterpret_cast<uint4*>(Wl);
     for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
@@ -277,13 +336,20 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     }
   };
 
-  auto process = [&](int64_t row0, int it) {
-    // ---- logits (log2 units): c + a |x|^2 + x . w_hi + x . w_lo
-    floatx4 acc[2][NT];
+  // ---- logits (log2 units) of the tile in buffer bi: c + a |x|^2 +
+  // x . w_hi + x . w_lo, the MFMA chain starting from the constant part.
+  // Lane's rows: q = rb * 4 + v <-> tile row rb * 16 + 4 (lane / 16) + v.
+  auto logits = [&](int bi, floatx4 (&acc)[2][NT]) {
+    const unsigned short* rows = rows_of(bi);
+    const double* xsq = xsq_of(bi);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < 4; ++v) {
+        const float xs = (float)xsq[rb * 16 + 4 * (lane >> 4) + v];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rb][nt][v] = fmaf(areg[nt], xs, creg[nt]);
+      }
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
       bf16x8 av[2];
@@ -294,21 +360,37 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 bw = Wl[(((wv * NT + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
+          bf16x8 bw;
+          if constexpr (WREG) bw = wreg[nt][h][ks];
+          else bw = Wl[(((wv * NT + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bw, acc[rb][nt], 0, 0, 0);
         }
     }
-    // lane's rows: q = rb * 4 + v <-> tile row rb * 16 + 4 (lane / 16) + v
+  };
+
+  // ---- the rest of a tile (row0: its first row, it: its ordinal in this
+  // workgroup, acc: its logits, bi: its buffer); SHARP (a compile-time
+  // constant): this wave holds a sharp component
+  auto finish = [&](int64_t row0, int it, auto sharp_c, const floatx4 (&acc)[2][NT], int bi) {
+    constexpr bool SHARP = decltype(sharp_c)::value;
+    const unsigned short* rows = rows_of(bi);
+    const unsigned short* xt = xt_of(bi);
+    const double* xsq = xsq_of(bi);
+    const float* lsb = ls_of(bi);
+    floatx4 lse4[2];
+    if constexpr (STATS) {
+      // four consecutive rows per load; rows past N hold +inf (r = 0)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) lse4[rb] = *reinterpret_cast<const floatx4*>(lsb + rb * 16 + 4 * (lane >> 4));
+    }
     float lg[8][NT];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float xs = (float)xsq[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)];
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) lg[q][nt] = fmaf(areg[nt], xs, creg[nt]) + acc[q >> 2][nt][q & 3];
-    }
-    if (any_sharp) {
+      for (int nt = 0; nt < NT; ++nt) lg[q][nt] = acc[q >> 2][nt][q & 3];
+    if constexpr (SHARP) {
       // sharp components: every score that may come within 60 (log2 units)
       // of the row's top, recomputed from direct differences in float64.
       // The reference is the row LSE in pass C and, in pass A, the best
@@ -326,7 +408,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-          ref[q] = row < nrows ? (PASS == 1 ? A.mrow[row] : A.lse[row]) : INFINITY;
+          ref[q] = row < nrows ? lsb[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)] : INFINITY;
         }
       }
 #pragma unroll
@@ -354,7 +436,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
         const int64_t row = row0 + p;
         rem[q] = 0.f;
-        const float mr = row < nrows ? A.mrow[row] : 0.f;
+        const float mr = lsb[p];  // 0 for rows past N, which have no candidates
         const float floor_l = mr - kTopmBand;
         const float xs = (float)xsq[p];
         uint32_t word = 0;
@@ -426,27 +508,32 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       }
     } else {
       // ---- responsibilities r = 2^(l - LSE), rounded to bf16 once; statistics
-      float lse[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-        lse[q] = row < nrows ? A.lse[row] : INFINITY;  // rows past N: r = 0
-      }
       // two magnitude classes, summed by separate MFMAs: a row with r near 1
       // would otherwise round away, in the float32 tile sum, the rows of tiny r
-      // that carry a collapsed component's whole variance
+      // that carry a collapsed component's whole variance.  Pairs of r are
+      // rounded to bf16 together (B-operand elements 2i, 2i + 1 = rows q = 2i,
+      // 2i + 1) and split by 16-bit integer arithmetic: kBigRBits - bits is
+      // negative exactly for the big class, and its sign fills the mask.
       bf16x8 bbig[NT], bsmall[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt) {
+        u32x4 pb, ps;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const __bf16 rh = (__bf16)__builtin_amdgcn_exp2f(lg[q][nt] - lse[q]);
-          const float rf = (float)rh;
-          const bool big = rf >= kBigR;
-          bbig[nt][q] = big ? rh : (__bf16)0.f;
-          bsmall[nt][q] = big ? (__bf16)0.f : rh;
-          lg[q][nt] = rf;
+        for (int i = 0; i < 4; ++i) {
+          const int q0 = 2 * i, q1 = 2 * i + 1;
+          const float r0 = __builtin_amdgcn_exp2f(lg[q0][nt] - lse4[q0 >> 2][q0 & 3]);
+          const float r1 = __builtin_amdgcn_exp2f(lg[q1][nt] - lse4[q1 >> 2][q1 & 3]);
+          const unsigned P = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+          const i16x2 d = (i16x2{kBigRBits - 1, kBigRBits - 1} - __builtin_bit_cast(i16x2, P)) >> 15;
+          const unsigned big = P & __builtin_bit_cast(unsigned, d);
+          pb[i] = big;
+          ps[i] = P ^ big;
+          lg[q0][nt] = __uint_as_float(P << 16);
+          lg[q1][nt] = __uint_as_float(P & 0xFFFF0000u);
         }
+        bbig[nt] = __builtin_bit_cast(bf16x8, pb);
+        bsmall[nt] = __builtin_bit_cast(bf16x8, ps);
+      }
 #pragma unroll
       for (int mt = 0; mt < (STATS ? GM : 1); ++mt) {
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (mt * 16 + (lane & 15)) * XTS + 8 * (lane >> 4));
@@ -469,23 +556,80 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   };
 
   // tiles g, g + G, g + 2G, ...: tile i is staged from registers loaded PF
-  // tiles earlier, and its slot then starts loading tile i + PF
-  int it = 0;
-  for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)PF * A.G) {
+  // tiles earlier, and its slot then starts loading tile i + PF.  Waves with
+  // and without sharp components run their own copy of the loop (the same
+  // barriers in the same order), so the common one has no exact-score
+  // branch; so do 16-byte and element-wise row loads (vec_c).
+  auto run = [&](auto sharp_c, auto vec_c) {
+    constexpr bool VEC = decltype(vec_c)::value;
+    int it = 0;
+    Piece pf[PF];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int64_t t = t0 + (int64_t)u * A.G;
-      if (t >= ntiles) break;
-      __syncthreads();
-      stage_piece<STATS>(A, pf[u], t * LT, slice, rows, xt, xsq);
-      pf[u] = fetch_piece<STATS>(A, t + (int64_t)PF * A.G, ntiles);
-      __syncthreads();
-      if constexpr (PASS != 2) {
-        if (it > 0 && wv == (it & (LNW - 1))) combine((t - A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
+    for (int u = 0; u < PF; ++u) pf[u] = fetch_piece<PASS, VEC>(A, g + (int64_t)u * A.G, ntiles);
+    if constexpr (!STATS) {
+      for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)PF * A.G) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int64_t t = t0 + (int64_t)u * A.G;
+          if (t >= ntiles) break;
+          __syncthreads();
+          stage_piece<STATS>(A, pf[u], t * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
+          pf[u] = fetch_piece<PASS, VEC>(A, t + (int64_t)PF * A.G, ntiles);
+          __syncthreads();
+          if (it > 0 && wv == (it & (LNW - 1))) combine((t - A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
+          floatx4 acc[2][NT];
+          logits(0, acc);
+          finish(t * LT, it, sharp_c, acc, 0);
+          ++it;
+        }
       }
-      process(t * LT, it);
-      ++it;
+    } else {
+      // Software-pipelined: iteration i stages tile i + 2, runs the logit
+      // MFMAs of tile i + 1 and finishes tile i, with one barrier.  Tile i
+      // (= g + i G) lives in buffer i % 3 and was loaded into pf[i % 3].  The
+      // buffer staged in iteration i was last read by tile i - 1's statistics,
+      // which every wave finished before the barrier that closed iteration
+      // i - 1.  Staging and logits past the workgroup's last tile touch only
+      // a free buffer and are never used.
+      static_assert(PF == NB, "prefetch slots follow the buffers");
+      const int64_t nmine = ntiles > g ? (ntiles - 1 - g) / A.G + 1 : 0;
+      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
+      pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)3 * A.G, ntiles);
+      stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xt_of(1), xsq_of(1), ls_of(1));
+      pf[1] = fetch_piece<PASS, VEC>(A, g + (int64_t)4 * A.G, ntiles);
+      __syncthreads();
+      floatx4 acc[2][NT];
+      logits(0, acc);
+      for (int64_t i0 = 0; i0 < nmine; i0 += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int64_t i = i0 + u;
+          if (i >= nmine) break;
+          const int bn = (u + 1) % 3, bs = (u + 2) % 3;
+          stage_piece<STATS>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xt_of(bs), xsq_of(bs),
+                             ls_of(bs));
+          pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 5) * A.G, ntiles);
+          floatx4 accn[2][NT];
+          logits(bn, accn);
+          finish((g + i * A.G) * LT, (int)i, sharp_c, acc, u);
+          __syncthreads();
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = accn[rb][nt];
+          ++it;
+        }
+      }
     }
+    return it;
+  };
+  // (an empty chunk -- pass C only -- just writes its zero partial)
+  int it = 0;
+  if (nrows > 0) {
+    if (A.vec16)
+      it = any_sharp ? run(std::true_type{}, std::true_type{}) : run(std::false_type{}, std::true_type{});
+    else
+      it = any_sharp ? run(std::true_type{}, std::false_type{}) : run(std::false_type{}, std::false_type{});
   }
   if constexpr (PASS != 2) {
     __syncthreads();
@@ -503,7 +647,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = mt * 16 + 4 * (lane >> 4) + v;
+          const int row = 8 * (4 * (lane >> 4) + v) + mt;  // feature of LDS row 16 mt + 4 (lane / 16) + v
           double* dst = part + (size_t)k * PR + 2 + row;
           *dst = (A.accumulate ? *dst : 0.0) + ((double)sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
         }
@@ -532,12 +676,19 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 
 // Pass B: per row, combine the slices' (max, sum) into the LSE (log2 units);
 // each workgroup also sums its rows' LSE (natural log) into its LL partial.
+// The rows from N up to the next multiple of the row tile get LSE = +inf, so
+// that pass C reads a tile's LSE values unguarded and gets r = 0 for them.
 __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
   constexpr double LN2 = 0.69314718055994530942;
   __shared__ double red[256];
   double ll = 0.0;
-  for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < A.N;
+  const int64_t npad = (A.N + LT - 1) / LT * LT;
+  for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < npad;
        row += (int64_t)gridDim.x * blockDim.x) {
+    if (row >= A.N) {
+      A.lse[row] = INFINITY;
+      continue;
+    }
     const float2* P = A.P + (size_t)row * A.S;
     float M = P[0].x;
     for (int s = 1; s < A.S; ++s) M = fmaxf(M, P[s].x);
