@@ -34,6 +34,23 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// all-reduce across the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48) with the gfx950 row swaps: v_permlane16_swap exchanges rows 1 and 0
+// and rows 3 and 2 between its two operands, v_permlane32_swap rows 2-3 and
+// 0-1; given the same value twice, the two results hold the two halves.
+__device__ __forceinline__ float rows4_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 16-lane all-reduce of a double (the two halves moved by the DPP patterns of
 // row16_sum)
 template <int CTRL>

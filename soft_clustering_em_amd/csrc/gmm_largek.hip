@@ -208,7 +208,7 @@ size_t largek_lds_bytes(int DP, int pass) {
   size_t tile = (size_t)LT * LRS * 2;                       // row tile
   if (pass == 2) tile += (size_t)DP * XTS * 2;              // transposed tile
   tile += (size_t)LT * 8 + LT * 4;                          // |x|^2, LSE or maximum
-  b += (pass == 2 ? 3 : 1) * tile;                          // buffers
+  b += (pass == 2 ? 3 : 2) * tile;                          // buffers
   if (pass != 2) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
   if (pass == 1) b += (size_t)2 * LT * LNW * 4;             // candidate masks, two tiles
   return b;
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   // (NT * 2 * KSTEP fragments); passes A and T read them from LDS
   constexpr bool WREG = STATS;
   constexpr int WLDS = WREG ? 0 : WFRAG;  // 16-byte fragments in LDS
-  constexpr int PF = 3;                   // row tiles in flight (registers)
+  constexpr int PF = STATS ? 3 : 2;       // row tiles in flight (registers)
   static_assert(DP == 128 && LT * DP / 8 == 64 * LNW, "one 16-byte piece per thread");
 
   const int lane = threadIdx.x & 63;
@@ -239,10 +239,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   const int64_t ntiles = (nrows + LT - 1) / LT;
 
   // row-tile buffers (rows, pass C's transposed copy, |x|^2, per-row LSE or
-  // maximum): pass C keeps
-  // three -- tile i's X^T for its statistics, tile i + 1's rows for its
-  // logits, tile i + 2 being staged -- and passes A and T one
-  constexpr int NB = STATS ? 3 : 1;
+  // maximum): pass C keeps three -- tile i's X^T for its statistics, tile
+  // i + 1's rows for its logits, tile i + 2 being staged -- and passes A and T
+  // two (tile i, tile i + 1 being staged)
+  constexpr int NB = STATS ? 3 : 2;
   constexpr int BUFB = LT * LRS * 2 + (STATS ? DP * XTS * 2 : 0) + LT * 8 + LT * 4;  // bytes per buffer
   static_assert(BUFB % 16 == 0, "16-byte aligned buffers");
   extern __shared__ float lds[];
@@ -271,22 +271,37 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     uint4* dst = reinterpret_cast<uint4*>(Wl);
     for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
   }
-  float creg[NT], areg[NT];
-  float eb[NT], e0[NT];  // error bound of a sharp component's expanded score: eb |x|^2 + e0 (0: not sharp)
-  float ea[NT], ea0[NT]; // pass T: the same bound for every component
+  // Pass A computes the logits transposed (weights as the MFMA's A operand):
+  // lane l then holds rows rb * 16 + l % 16 against components
+  // nt * 16 + 4 (l / 16) + v, so a row's max and sum over the wave's
+  // components are an in-lane fold over (nt, v) plus two cross-row swaps.
+  // Passes T and C keep rows 4 (l / 16) + v against component l % 16 (the
+  // layout the statistics MFMA takes as its B operand).
+  constexpr bool TR = (PASS == 0);
+  constexpr int CV = TR ? 4 : 1;  // components per lane and 16-column tile
+  auto comp_of = [&](int nt, int v) {
+    return slice * KSL + (wv * NT + nt) * 16 + (TR ? 4 * (lane >> 4) + v : (lane & 15));
+  };
+  float creg[NT][CV], areg[NT][CV];
+  float eb[NT][CV], e0[NT][CV];  // error bound of a sharp component's expanded score: eb |x|^2 + e0 (0: not sharp)
+  float ea[NT], ea0[NT];         // pass T: the same bound for every component
   bool any_sharp = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
-    creg[nt] = (float)A.c[k];
-    areg[nt] = (float)A.a[k];
-    eb[nt] = A.esh[2 * k];
-    e0[nt] = A.esh[2 * k + 1];
+#pragma unroll
+    for (int v = 0; v < CV; ++v) {
+      const int k = comp_of(nt, v);
+      creg[nt][v] = (float)A.c[k];
+      areg[nt][v] = (float)A.a[k];
+      eb[nt][v] = A.esh[2 * k];
+      e0[nt][v] = A.esh[2 * k + 1];
+      any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(eb[nt][v] > 0.f) != 0);
+    }
     if constexpr (PASS == 1) {
+      const int k = comp_of(nt, 0);
       ea[nt] = A.eall[2 * k];
       ea0[nt] = A.eall[2 * k + 1];
     }
-    any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(eb[nt] > 0.f) != 0);
   }
   // pass C: statistics of the r >= 2^-8 and r < 2^-8 classes, each in its
   // own float32 MFMA accumulator (float64 at the chunk's partial)
@@ -346,9 +361,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float xs = (float)xsq[rb * 16 + 4 * (lane >> 4) + v];
+        const float xs = (float)xsq[rb * 16 + (TR ? (lane & 15) : 4 * (lane >> 4) + v)];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[rb][nt][v] = fmaf(areg[nt], xs, creg[nt]);
+        for (int nt = 0; nt < NT; ++nt) acc[rb][nt][v] = fmaf(areg[nt][TR ? v : 0], xs, creg[nt][TR ? v : 0]);
       }
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
@@ -365,7 +380,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           else bw = Wl[(((wv * NT + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bw, acc[rb][nt], 0, 0, 0);
+            acc[rb][nt] = TR ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, av[rb], acc[rb][nt], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bw, acc[rb][nt], 0, 0, 0);
         }
     }
   };
@@ -379,6 +395,70 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     const unsigned short* xt = xt_of(bi);
     const double* xsq = xsq_of(bi);
     const float* lsb = ls_of(bi);
+    if constexpr (PASS == 0) {
+      // ---- per-row max and sum of 2^(l - max) over this wave's components
+      float lg[2][NT][4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) lg[rb][nt][v] = acc[rb][nt][v];
+      if constexpr (SHARP) {
+        // sharp components: every score that may come within 60 (log2 units)
+        // of the best score of this wave's other components (accurate in
+        // expanded form) is recomputed from direct differences in float64
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float ref = kDead;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ref = fmaxf(ref, eb[nt][v] > 0.f ? kDead : lg[rb][nt][v]);
+          ref = rows4_max(ref);
+          const int p = rb * 16 + (lane & 15);
+          const float xs = (float)xsq[p];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (eb[nt][v] > 0.f && row0 + p < nrows && lg[rb][nt][v] + eb[nt][v] * xs + e0[nt][v] >= ref - 60.f) {
+                const int k = comp_of(nt, v);
+                lg[rb][nt][v] =
+                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + p * LRS);
+              }
+            }
+        }
+      }
+      float m[2], sm[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        m[rb] = lg[rb][0][0];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) m[rb] = fmaxf(m[rb], lg[rb][nt][v]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) m[rb] = rows4_max(m[rb]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        sm[rb] = __builtin_amdgcn_exp2f(lg[rb][0][0] - m[rb]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = (nt == 0 ? 1 : 0); v < 4; ++v) sm[rb] += __builtin_amdgcn_exp2f(lg[rb][nt][v] - m[rb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sm[rb] = rows4_sum(sm[rb]);
+      float* rbuf = red + (it & 1) * (LNW * LT * 2);
+      if (lane < 16) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          *reinterpret_cast<float2*>(rbuf + (wv * LT + rb * 16 + lane) * 2) = float2{m[rb], sm[rb]};
+      }
+      return;
+    }
     floatx4 lse4[2];
     if constexpr (STATS) {
       // four consecutive rows per load; rows past N hold +inf (r = 0)
@@ -396,20 +476,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // The reference is the row LSE in pass C and, in pass A, the best
       // score of this wave's other components (accurate in expanded form).
       float ref[8];
-      if constexpr (PASS == 0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          float m = kDead;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) m = fmaxf(m, eb[nt] > 0.f ? kDead : lg[q][nt]);
-          ref[q] = row16_max(m);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-          ref[q] = row < nrows ? lsb[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)] : INFINITY;
-        }
+      for (int q = 0; q < 8; ++q) {
+        const int64_t row = row0 + (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
+        ref[q] = row < nrows ? lsb[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)] : INFINITY;
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -417,8 +487,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const float xs = (float)xsq[p];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if (eb[nt] > 0.f && row0 + p < nrows && lg[q][nt] + eb[nt] * xs + e0[nt] >= ref[q] - 60.f) {
-            const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+          if (eb[nt][0] > 0.f && row0 + p < nrows && lg[q][nt] + eb[nt][0] * xs + e0[nt][0] >= ref[q] - 60.f) {
+            const int k = comp_of(nt, 0);
             lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + p * LRS);
           }
         }
@@ -464,46 +534,6 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         for (int q = 0; q < 8; ++q) {
           const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
           rbuf[(wv * LT + p) * 2 + 1] = rem[q];
-        }
-      }
-    } else if constexpr (PASS == 0) {
-      // ---- per-row max and sum over this wave's components (the eight rows'
-      // reductions interleaved); the waves are combined one tile later
-      float m[8], sm[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        m[q] = lg[q][0];
-#pragma unroll
-        for (int nt = 1; nt < NT; ++nt) m[q] = fmaxf(m[q], lg[q][nt]);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0xB1>(m[q]));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x4E>(m[q]));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x141>(m[q]));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], dpp_mov<0x140>(m[q]));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        sm[q] = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sm[q] += __builtin_amdgcn_exp2f(lg[q][nt] - m[q]);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0xB1>(sm[q]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x4E>(sm[q]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x141>(sm[q]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sm[q] += dpp_mov<0x140>(sm[q]);
-      float* rbuf = red + (it & 1) * (LNW * LT * 2);
-      if ((lane & 15) == 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-          *reinterpret_cast<float2*>(rbuf + (wv * LT + p) * 2) = float2{m[q], sm[q]};
         }
       }
     } else {
@@ -566,20 +596,33 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     Piece pf[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u) pf[u] = fetch_piece<PASS, VEC>(A, g + (int64_t)u * A.G, ntiles);
+    const int64_t nmine = ntiles > g ? (ntiles - 1 - g) / A.G + 1 : 0;
     if constexpr (!STATS) {
-      for (int64_t t0 = g; t0 < ntiles; t0 += (int64_t)PF * A.G) {
+      // One barrier per tile: iteration i stages tile i + 1 (= g + (i + 1) G,
+      // buffer and prefetch slot (i + 1) % 2) while it computes tile i.  That
+      // buffer was last read by tile i - 1, finished before the barrier that
+      // closed iteration i - 1.  The rotating wave combines tile i - 1's
+      // per-wave results, written before that barrier; tile i writes the
+      // other half of the double buffer, last read by the combine of tile
+      // i - 2 in iteration i - 1.
+      static_assert(PF == NB, "prefetch slots follow the buffers");
+      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
+      pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)2 * A.G, ntiles);
+      __syncthreads();
+      for (int64_t i0 = 0; i0 < nmine; i0 += 2) {
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          const int64_t t = t0 + (int64_t)u * A.G;
-          if (t >= ntiles) break;
-          __syncthreads();
-          stage_piece<STATS>(A, pf[u], t * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
-          pf[u] = fetch_piece<PASS, VEC>(A, t + (int64_t)PF * A.G, ntiles);
-          __syncthreads();
-          if (it > 0 && wv == (it & (LNW - 1))) combine((t - A.G) * LT, red + ((it - 1) & 1) * (LNW * LT * 2));
+        for (int u = 0; u < 2; ++u) {
+          const int64_t i = i0 + u;
+          if (i >= nmine) break;
+          const int bs = 1 - u;
+          stage_piece<STATS>(A, pf[bs], (g + (i + 1) * A.G) * LT, slice, rows_of(bs), xt_of(bs), xsq_of(bs),
+                             ls_of(bs));
+          pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 3) * A.G, ntiles);
+          if (i > 0 && wv == (i & (LNW - 1))) combine((g + (i - 1) * A.G) * LT, red + ((i - 1) & 1) * (LNW * LT * 2));
           floatx4 acc[2][NT];
-          logits(0, acc);
-          finish(t * LT, it, sharp_c, acc, 0);
+          logits(u, acc);
+          finish((g + i * A.G) * LT, (int)i, sharp_c, acc, u);
+          __syncthreads();
           ++it;
         }
       }
@@ -592,7 +635,6 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // i - 1.  Staging and logits past the workgroup's last tile touch only
       // a free buffer and are never used.
       static_assert(PF == NB, "prefetch slots follow the buffers");
-      const int64_t nmine = ntiles > g ? (ntiles - 1 - g) / A.G + 1 : 0;
       stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
       pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)3 * A.G, ntiles);
       stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xt_of(1), xsq_of(1), ls_of(1));
