@@ -212,7 +212,8 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   // workspace
   size_t o = 0;
   q.off_W = o;    o = align_up(o + sizeof(float) * (size_t)q.B * q.KP * q.F);
-  q.prec_stride = (cov == SPH) ? 1 : (cov == DIAG) ? (int)q.D : (int)(q.D * q.D);
+  // full / tied: L^{-1} as DP x DP, zero past D (the exact score runs over DP)
+  q.prec_stride = (cov == SPH) ? 1 : (cov == DIAG) ? (int)q.D : q.DP * q.DP;
   q.off_prec = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.prec_stride);
   q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);

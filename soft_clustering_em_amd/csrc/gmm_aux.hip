@@ -179,7 +179,10 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       c0[(size_t)b * KP + k] = (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e;
       sharp[(size_t)b * KP + k] = trp * scale > kSharp ? 1 : 0;
     }
-    for (int i = tid; i < D * D; i += blockDim.x) precb[i] = sm_Li[i];
+    for (int i = tid; i < DP * DP; i += blockDim.x) {
+      const int d = i / DP, e = i % DP;
+      precb[i] = (d < D && e < D) ? sm_Li[d * D + e] : 0.0;
+    }
   }
   __syncthreads();
   for (int f = tid; f < F; f += blockDim.x) {

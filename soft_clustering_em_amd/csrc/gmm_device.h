@@ -79,11 +79,15 @@ __device__ __forceinline__ int quad_pair(int q) {
   return (d << 16) | (d + (q - base));
 }
 
-// log2 of pi_k N(x | mu_k, Sigma_k) for one row x (float32 values in LDS), by
-// direct differences in float64: c0_k - 1/2 log2(e) (x - mu)^T P (x - mu).
-// prec holds 1/sigma^2 (spherical: one value; diag: D values) or, for
-// full/tied, the lower-triangular L^{-1} of Sigma = L L^T (D x D).
-template <int COV, int DP, class Args>
+// log2 of pi_k N(x | mu_k, Sigma_k) for one row x (float32 values in LDS,
+// zero past D), by direct differences in float64:
+// c0_k - 1/2 log2(e) (x - mu)^T P (x - mu).  prec holds 1/sigma^2
+// (spherical: one value; diag: D values) or, for full/tied, the
+// lower-triangular L^{-1} of Sigma = L L^T as DP x DP, zero past D.  UNROLL:
+// that product runs fully unrolled over DP (the padding contributes 0), so
+// its loads are issued together rather than one per loop trip -- for callers
+// with the registers to spare.
+template <int COV, int DP, bool UNROLL = true, class Args>
 __device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D, const float* x) {
   constexpr double kLog2e = 1.4426950408889634074;
   const float* mu = A.mu + ((size_t)b * A.K + k) * D;
@@ -100,11 +104,22 @@ __device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D
       const double t = (double)x[d] - (double)mu[d];
       q += P[d] * t * t;
     }
-  } else {
+  } else if constexpr (!UNROLL) {
     for (int i = 0; i < D; ++i) {
       double z = 0.0;
-      for (int j = 0; j <= i; ++j) z += P[i * D + j] * ((double)x[j] - (double)mu[j]);
-      q += z * z;
+      for (int j = 0; j <= i; ++j) z = fma(P[i * DP + j], (double)x[j] - (double)mu[j], z);
+      q = fma(z, z, q);
+    }
+  } else {
+    double t[DP];
+#pragma unroll
+    for (int j = 0; j < DP; ++j) t[j] = j < D ? (double)x[j] - (double)mu[j < D ? j : 0] : 0.0;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      double z = 0.0;
+#pragma unroll
+      for (int j = 0; j <= i; ++j) z = fma(P[i * DP + j], t[j], z);
+      q = fma(z, z, q);
     }
   }
   return A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;

@@ -268,6 +268,47 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
         }
     }
 
+    // ---- sharp components: every score that may come within 60 (log2 units)
+    // of its row's top, again exactly.  Full and tied (a D x D product per
+    // score): each lane lists its own (row block, component tile, row) items
+    // and the wave loops only as often as its busiest lane needs, not once per
+    // row position with any such lane.  Spherical and diagonal (D terms per
+    // score): inline below, per row position.
+    if (QUAD && any_sharp) {
+      uint32_t todo = 0;  // bit (rb NT + nt) 4 + v
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float m = (float)lg[rb][0][v];
+#pragma unroll
+          for (int nt = 1; nt < NT; ++nt) m = fmaxf(m, (float)lg[rb][nt][v]);
+          m = row16_max(m);
+          const int p = rb * 16 + 4 * (lane >> 4) + v;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            if (sharp[nt] && (float)lg[rb][nt][v] >= m - 60.f && row0 + p < N) todo |= 1u << ((rb * NT + nt) * 4 + v);
+        }
+      static_assert(RB * NT * 4 <= 32, "one bit per item");
+      while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
+        if (todo != 0) {
+          const int bit = __builtin_ctz(todo);
+          todo &= todo - 1;
+          const int v = bit & 3, nt = (bit >> 2) % NT, rb = (bit >> 2) / NT;
+          const int p = rb * 16 + 4 * (lane >> 4) + v;
+          const int k = wv * KW + nt * 16 + (lane & 15);
+          const double e = exact_score<COV, DP>(A, b, k, D, phi + p * FS);
+#pragma unroll
+          for (int rb2 = 0; rb2 < RB; ++rb2)
+#pragma unroll
+            for (int nt2 = 0; nt2 < NT; ++nt2)
+#pragma unroll
+              for (int v2 = 0; v2 < 4; ++v2)
+                if ((rb2 * NT + nt2) * 4 + v2 == bit) lg[rb2][nt2][v2] = e;
+        }
+      }
+    }
+
     // ---- per-wave row max and sum of exponentials over this wave's components
     float mrow[RB][4], srow[RB][4];
 #pragma unroll
@@ -278,8 +319,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 #pragma unroll
         for (int nt = 1; nt < NT; ++nt) m = fmaxf(m, (float)lg[rb][nt][v]);
         m = row16_max(m);
-        if (any_sharp) {
-          // sharp components: scores near the top of the row again, exactly
+        if (!QUAD && any_sharp) {
           const int p = rb * 16 + 4 * (lane >> 4) + v;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {

@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
         const float lv = (float)lg[nt][v];
         if (valid && lv >= Mt[v] - DELTA) {
           const int k = wv * KW + nt * 16 + (lane & 15);
-          const double ex = exact_score<COV, DP>(A, b, k, D, raw + p * DP);
+          const double ex = exact_score<COV, DP, false>(A, b, k, D, raw + p * DP);
           const int slot = atomicAdd(&cnt[p], 1);
           if (slot < CAP) {
             cl[p * CAP + slot] = ex;
@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
           const int k = lane + 64 * i;
-          ls[i] = k < K ? exact_score<COV, DP>(A, b, k, D, raw + p * DP) : -INFINITY;
+          ls[i] = k < K ? exact_score<COV, DP, false>(A, b, k, D, raw + p * DP) : -INFINITY;
           mx = fmax(mx, ls[i]);
         }
         const double M = wave_max(mx);
