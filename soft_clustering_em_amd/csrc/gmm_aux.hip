@@ -72,6 +72,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
   __shared__ double sm_v[128];                // diag precisions / P mu
   __shared__ double sm_S[16 * 16], sm_L[16 * 16], sm_Li[16 * 16], sm_P[16 * 16];
   __shared__ double sm_c;
+  __shared__ double sm_red[64];               // one partial per thread (blockDim.x == 64)
   __shared__ int sm_ok;
 
   if (k >= K) {  // padding component: never responsible
@@ -166,18 +167,32 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       for (int e = 0; e < D; ++e) s += sm_P[d * D + e] * sm_mu[e];
       sm_v[d] = s;
     }
+    // lambda_max(P) <= ||P^2||_F^(1/2) = (sum_i lambda_i^4)^(1/4) (P symmetric
+    // positive definite): an upper bound far tighter than tr P when the
+    // eigenvalues are spread
+    {
+      double s4 = 0.0;
+      for (int i = tid; i < D * D; i += blockDim.x) {
+        const int d = i / D, e = i % D;
+        double s = 0.0;
+        for (int p = 0; p < D; ++p) s += sm_P[d * D + p] * sm_P[p * D + e];
+        s4 += s * s;
+      }
+      sm_red[tid] = s4;
+    }
     __syncthreads();
     if (tid == 0) {
-      double logdet = 0.0, quad = 0.0, trp = 0.0, scale = 0.0;
+      double logdet = 0.0, quad = 0.0, scale = 0.0, f4 = 0.0;
       for (int d = 0; d < D; ++d) {
         logdet += 2.0 * log(sm_L[d * D + d]);
         quad += sm_mu[d] * sm_v[d];
-        trp += sm_P[d * D + d];
         scale += sm_mu[d] * sm_mu[d] + sm_S[d * D + d];
       }
+      for (int q = 0; q < (int)blockDim.x; ++q) f4 += sm_red[q];
+      const double lmax = sqrt(sqrt(f4));
       sm_c = (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e;
       c0[(size_t)b * KP + k] = (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e;
-      sharp[(size_t)b * KP + k] = trp * scale > kSharp ? 1 : 0;
+      sharp[(size_t)b * KP + k] = lmax * scale > kSharp ? 1 : 0;
     }
     for (int i = tid; i < DP * DP; i += blockDim.x) {
       const int d = i / DP, e = i % DP;
