@@ -183,3 +183,45 @@ def fit_step(cov, X, w, mu, cv, eps=1e-6, nthreads=0):
     wo, mo, co, fl = mstep(cov, st, n, np.asarray(w).reshape(B, -1),
                            np.asarray(mu).reshape(st["sx"].shape), np.asarray(cv).reshape(st["sxx"].shape), eps)
     return dict(w=wo, mu=mo, cv=co, mean_ll=st["ll"] / n, stats=st, flags=fl)
+
+
+def ivf_lists(idx, resp, K):
+    """Inverted lists (IVF posting lists) of a soft multi-assignment.
+
+    "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft Clustering",
+    Section 4 (GMM as the IVF coarse quantizer, the multi-assignment scheme of
+    Section 4.3) and Conclusion (boundary vectors are stored in several posting
+    lists): row i of problem b goes into the list of every component that its
+    multi-assignment kept.  idx (B,N,m) int32: a row's entries are its leading
+    values in [0, K); the first value outside that range ends the row.  resp
+    (B,N,m) float or None.  Lists hold rows in increasing row order (the pages
+    fix no order; this is the plainest deterministic one).
+
+    Returns offsets (B,K+1) int64 (list k of problem b is rows[b, offsets[b,k]
+    : offsets[b,k+1]]), rows (B,N*m) int32 and list_resp (B,N*m) float32 (or
+    None), both -1 / 0 past offsets[b,K].  Written as the definition, one row
+    at a time: small inputs only.
+    """
+    idx = np.asarray(idx)
+    B, N, m = idx.shape
+    offsets = np.zeros((B, K + 1), np.int64)
+    rows = np.full((B, N * m), -1, np.int32)
+    lr = None if resp is None else np.zeros((B, N * m), np.float32)
+    for b in range(B):
+        lists = [[] for _ in range(K)]
+        for i in range(N):
+            for j in range(m):
+                k = int(idx[b, i, j])
+                if k < 0 or k >= K:
+                    break
+                lists[k].append((i, 0.0 if resp is None else float(resp[b, i, j])))
+        pos = 0
+        for k in range(K):
+            offsets[b, k] = pos
+            for i, r in lists[k]:
+                rows[b, pos] = i
+                if lr is not None:
+                    lr[b, pos] = r
+                pos += 1
+        offsets[b, K] = pos
+    return offsets, rows, lr

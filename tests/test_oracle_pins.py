@@ -415,3 +415,54 @@ def test_bf16_input_is_decoded_exactly():
     b = oracle.estep("spherical", Xd, w, mu, cv, nthreads=1)
     for key in ("nk", "sx", "sxx", "ll"):
         np.testing.assert_array_equal(a[key], b[key])
+
+
+# ---------------------------------------------------------------- IVF lists
+def _ivf_random(rng, B, N, m, K):
+    """Top-m-like rows: a count in 1..m (some rows end early with -1) and
+    distinct components per row."""
+    idx = np.full((B, N, m), -1, np.int32)
+    resp = np.zeros((B, N, m), np.float32)
+    for b in range(B):
+        cnt = rng.integers(1, m + 1, size=N)
+        for i in range(N):
+            ks = rng.choice(K, size=cnt[i], replace=False)
+            idx[b, i, :cnt[i]] = ks
+            resp[b, i, :cnt[i]] = np.sort(rng.random(cnt[i]))[::-1]
+    return idx, resp
+
+
+@pytest.mark.parametrize("B,N,m,K", [(1, 500, 4, 37), (2, 300, 1, 5), (1, 200, 6, 300)])
+def test_ivf_lists_match_a_stable_sort(B, N, m, K):
+    """The definition against a stable library sort of the (component, row)
+    pairs in row-major order, plus bincount for the offsets."""
+    rng = np.random.default_rng(B * 1000 + N + m)
+    idx, resp = _ivf_random(rng, B, N, m, K)
+    off, rows, lr = oracle.ivf_lists(idx, resp, K)
+    for b in range(B):
+        valid = np.cumprod((idx[b] >= 0) & (idx[b] < K), axis=1).astype(bool)
+        keys = idx[b][valid]
+        rid = np.broadcast_to(np.arange(N)[:, None], (N, m))[valid]
+        rr = resp[b][valid]
+        order = np.argsort(keys, kind="stable")
+        n = keys.size
+        assert off[b, K] == n
+        assert np.array_equal(off[b], np.concatenate([[0], np.cumsum(np.bincount(keys, minlength=K))]))
+        assert np.array_equal(rows[b, :n], rid[order])
+        assert np.array_equal(lr[b, :n], rr[order])
+        assert (rows[b, n:] == -1).all()
+        # every list is increasing in row
+        for k in range(K):
+            seg = rows[b, off[b, k]:off[b, k + 1]]
+            assert (np.diff(seg) > 0).all()
+
+
+def test_ivf_lists_hand_case():
+    """A case small enough to check by eye: rows 0..3 with m = 3."""
+    idx = np.array([[[2, 0, -1], [1, -1, 5], [0, 2, 1], [3, 7, 0]]], np.int32)  # K = 4: 7 ends row 3
+    resp = np.array([[[.6, .4, 0], [1., 0, 0], [.5, .3, .2], [.9, .1, 0]]], np.float32)
+    off, rows, lr = oracle.ivf_lists(idx, resp, 4)
+    assert off[0].tolist() == [0, 2, 4, 6, 7]
+    assert rows[0, :7].tolist() == [0, 2, 1, 2, 0, 2, 3]
+    assert np.allclose(lr[0, :7], [.4, .5, 1., .2, .6, .3, .9])
+    assert rows[0, 7:].tolist() == [-1] * 5
