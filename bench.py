@@ -233,6 +233,26 @@ def main():
         t_topm = time.perf_counter() - t0
         res["topm"] = {"m": m, "threshold": thr, "ms": t_topm * 1e3, "rows_per_s": wl.B * wl.N / t_topm,
                        "mean_kept": float(cnt.float().mean().item())}
+        # the IVF posting lists of that assignment (CSR per component), timed apart
+        off = torch.empty((wl.B, wl.K + 1), dtype=torch.int64, device=dev)
+        rows = torch.empty((wl.B, wl.N * m), dtype=torch.int32, device=dev)
+        lresp = torch.empty((wl.B, wl.N * m), dtype=torch.float32, device=dev)
+        lws = torch.empty(max(256, g.gmm_ivf_workspace_bytes(wl.B, wl.N, m, wl.K)), dtype=torch.uint8, device=dev)
+        g.gmm_ivf_lists(idx, wl.K, resp=resp, offsets=off, rows=rows, list_resp=lresp, ws=lws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            g.gmm_ivf_lists(idx, wl.K, resp=resp, offsets=off, rows=rows, list_resp=lresp, ws=lws)
+        e1.record()
+        torch.cuda.synchronize()
+        t_lists = e0.elapsed_time(e1) / reps
+        entries = int(off[:, wl.K].sum().item())
+        # bytes each build moves at the least: idx read twice (count and place),
+        # resp read once, rows and responsibilities written once per entry
+        lbytes = wl.B * wl.N * m * 4 * 3 + entries * 8
+        res["topm"]["ivf_lists"] = {"ms": t_lists, "entries": entries, "entries_per_s": entries / (t_lists * 1e-3),
+                                    "algorithmic_bytes": lbytes, "achieved_GBs": lbytes / (t_lists * 1e-3) / 1e9}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

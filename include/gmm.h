@@ -167,6 +167,27 @@ gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params
                                   float threshold, int32_t* idx, float* resp, int32_t* count,
                                   float* logp, void* ws, size_t ws_bytes, void* stream);
 
+/* Inverted lists (IVF posting lists) from a soft multi-assignment
+ * (Flash-GMM Section 4 -- the GMM as the IVF coarse quantizer, with the
+ * multi-assignment of Section 4.3 -- and Conclusion: boundary vectors are
+ * stored in several posting lists).  For every problem b and component k, the
+ * rows whose assignment kept k, in increasing row order, as CSR.
+ *   idx  (B,N,m) int32, as written by gmm_predict_proba_topm: a row's entries
+ *        are its leading values in [0, K); the first value outside ends the row
+ *        (-1 padding does); values within a row are expected distinct
+ *   resp (B,N,m) float32, nullable: copied to list_resp when that is non-NULL
+ *   offsets   (B,K+1) int64: list k of problem b is
+ *             rows[b, offsets[b,k] .. offsets[b,k+1]-1]; offsets[b,K] = its entries
+ *   rows      (B,N*m) int32: row indices; entries past offsets[b,K] untouched
+ *   list_resp (B,N*m) float32, nullable: the responsibility of each entry
+ * 1 <= m <= 16, 1 <= K <= 16384, N*m < 2^31.  Workspace:
+ * gmm_ivf_workspace_bytes (4 bytes per (problem, 4096-row block, component)).
+ * Deterministic (no atomics), bit-identical across runs. */
+size_t gmm_ivf_workspace_bytes(int64_t B, int64_t N, int32_t m, int32_t K);
+gmm_status gmm_ivf_lists(int64_t B, int64_t N, int32_t m, int32_t K, const int32_t* idx, const float* resp,
+                         int64_t* offsets, int32_t* rows, float* list_resp, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Static description of a status code. */
 const char* gmm_status_str(int32_t status);
 

@@ -9,6 +9,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_mstep(stats, n_total, w, mu, cv, reg_covar=1e-6, comp_status=None)
   gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
   gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
+  gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
 
 X is (N, D) or (B, N, D) with unit stride along D; w (B,K), mu (B,K,D) and the
 covariance parameters are float32 and are updated in place by the M-step.
@@ -22,7 +23,8 @@ from ._abi import (COV_CODES, GmmError, GmmData, GmmOptions, GmmParams, GmmStats
                    OP_TOPM)
 
 __all__ = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
-           "gmm_predict_proba_topm", "new_stats", "GmmError", "cov_shape"]
+           "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "new_stats", "GmmError",
+           "cov_shape"]
 
 
 def _torch():
@@ -143,3 +145,37 @@ def gmm_predict_proba_topm(X, w, mu, cv, cov, m, threshold, idx, resp, count=Non
     _abi.check(_abi.lib().gmm_predict_proba_topm(ctypes.byref(d), ctypes.byref(p), int(m), float(threshold),
                                                  _ptr(idx), _ptr(resp), _ptr(count), _ptr(logp), _ptr(ws),
                                                  ws.numel(), _stream(stream)))
+
+
+def gmm_ivf_workspace_bytes(B, N, m, K) -> int:
+    return int(_abi.lib().gmm_ivf_workspace_bytes(int(B), int(N), int(m), int(K)))
+
+
+def gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None, stream=None):
+    """Posting lists of a multi-assignment idx ((N, m) or (B, N, m) int32 on the GPU).
+
+    Returns (offsets (B, K+1) int64, rows (B, N*m) int32, list_resp (B, N*m) float32 or None);
+    outputs not given are allocated here (rows and list_resp past offsets[b, K] are left as
+    allocated)."""
+    torch = _torch()
+    if idx.dim() == 2:
+        idx = idx.unsqueeze(0)
+        resp = resp.unsqueeze(0) if resp is not None else None
+    if not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be a contiguous int32 tensor")
+    if resp is not None and (not resp.is_contiguous() or resp.dtype != torch.float32 or resp.shape != idx.shape):
+        raise ValueError("resp must be a contiguous float32 tensor shaped like idx")
+    B, N, m = idx.shape
+    dev = idx.device
+    if offsets is None:
+        offsets = torch.empty(B, K + 1, dtype=torch.int64, device=dev)
+    if rows is None:
+        rows = torch.empty(B, N * m, dtype=torch.int32, device=dev)
+    if list_resp is None and resp is not None:
+        list_resp = torch.empty(B, N * m, dtype=torch.float32, device=dev)
+    if ws is None:
+        n = gmm_ivf_workspace_bytes(B, N, m, K)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _abi.check(_abi.lib().gmm_ivf_lists(int(B), int(N), int(m), int(K), _ptr(idx), _ptr(resp), _ptr(offsets),
+                                        _ptr(rows), _ptr(list_resp), _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, rows, list_resp

@@ -521,6 +521,58 @@ gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params
   return GMM_OK;
 }
 
+// ---- IVF posting lists
+static gmm_status ivf_check(int64_t B, int64_t N, int32_t m, int32_t K) {
+  if (B < 1 || N < 0) return fail(GMM_ERR_INVALID_ARG, "need B >= 1 and N >= 0");
+  if (m < 1 || m > 16) return fail(GMM_ERR_INVALID_ARG, "m must be in [1, 16] (got %d)", m);
+  if (K < 1) return fail(GMM_ERR_INVALID_ARG, "K must be >= 1");
+  if (K > kIvfMaxK) return fail(GMM_ERR_UNSUPPORTED, "IVF lists: K <= %d", kIvfMaxK);
+  if (N * (int64_t)m > INT32_MAX) return fail(GMM_ERR_UNSUPPORTED, "IVF lists: N * m must fit in int32");
+  if (B > INT32_MAX / 64) return fail(GMM_ERR_UNSUPPORTED, "IVF lists: B too large");
+  return GMM_OK;
+}
+
+static size_t ivf_ws(int64_t B, int64_t N, int32_t K) {
+  const int64_t nblk = (N + kIvfBlock - 1) / kIvfBlock;
+  return align_up(sizeof(int32_t) * (size_t)B * (size_t)nblk * (size_t)K);
+}
+
+size_t gmm_ivf_workspace_bytes(int64_t B, int64_t N, int32_t m, int32_t K) {
+  if (ivf_check(B, N, m, K) != GMM_OK) return 0;
+  return std::max<size_t>(ivf_ws(B, N, K), kAlign);
+}
+
+gmm_status gmm_ivf_lists(int64_t B, int64_t N, int32_t m, int32_t K, const int32_t* idx, const float* resp,
+                         int64_t* offsets, int32_t* rows, float* list_resp, void* ws, size_t ws_bytes,
+                         void* stream) {
+  g_err.clear();
+  gmm_status st = ivf_check(B, N, m, K);
+  if (st != GMM_OK) return st;
+  if (!offsets) return fail(GMM_ERR_INVALID_ARG, "offsets must be non-NULL");
+  if (N > 0 && (!idx || !rows)) return fail(GMM_ERR_INVALID_ARG, "idx and rows must be non-NULL");
+  if (list_resp && !resp) return fail(GMM_ERR_INVALID_ARG, "list_resp needs resp");
+  if (!ws || ((uintptr_t)ws) % kAlign != 0) return fail(GMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < ivf_ws(B, N, K))
+    return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, ivf_ws(B, N, K));
+  IvfArgs A;
+  A.idx = idx;
+  A.resp = list_resp ? resp : nullptr;
+  A.N = N;
+  A.B = (int)B;
+  A.m = m;
+  A.K = K;
+  A.KB = 0;
+  while ((1 << A.KB) < K) ++A.KB;
+  A.nblk = (int)((N + kIvfBlock - 1) / kIvfBlock);
+  A.cnt = static_cast<int32_t*>(ws);
+  A.offsets = offsets;
+  A.rows = rows;
+  A.lresp = list_resp;
+  hipError_t e = launch_ivf_lists(A, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "IVF list launch");
+  return GMM_OK;
+}
+
 const char* gmm_status_str(int32_t status) {
   switch (status) {
     case GMM_OK: return "ok";

@@ -148,6 +148,22 @@ struct TopmArgs {
 };
 hipError_t launch_topm(const Plan& p, const TopmArgs& a, hipStream_t s);
 
+// IVF posting lists from a soft multi-assignment (gmm_ivf.hip)
+constexpr int kIvfBlock = 4096;     // rows per walking wave
+constexpr int kIvfMaxK = 16384;     // components (one int of LDS each per wave)
+struct IvfArgs {
+  const int32_t* idx;  // (B,N,m)
+  const float* resp;   // (B,N,m) or null
+  int64_t N;
+  int B, m, K, KB;     // KB: bits of the largest component index
+  int nblk;            // row blocks per problem
+  int32_t* cnt;        // workspace (B,nblk,K): block counts, then their prefixes
+  int64_t* offsets;    // (B,K+1)
+  int32_t* rows;       // (B,N*m)
+  float* lresp;        // (B,N*m) or null
+};
+hipError_t launch_ivf_lists(const IvfArgs& a, hipStream_t s);
+
 // fused E-step + statistics (gmm_estep.hip)
 hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);

@@ -191,3 +191,36 @@ def test_bf16_small_workspace_is_accepted_down_to_one_tile():
     st = L.gmm_fit_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(opts), None, None, ws, tiny - 256, None)
     assert st == _abi.GMM_ERR_WORKSPACE, L.gmm_last_error()
     assert tiny < full
+
+
+# ---------------------------------------------------------------- IVF lists
+def test_ivf_workspace_sizes():
+    L = _abi.lib()
+    n = L.gmm_ivf_workspace_bytes(1, 10_000_000, 4, 4096)
+    # one int32 per (4096-row block, component), rounded up to 256 bytes
+    nblk = (10_000_000 + 4095) // 4096
+    assert n == -(-nblk * 4096 * 4 // 256) * 256
+    assert L.gmm_ivf_workspace_bytes(3, 0, 4, 17) == 256  # N = 0: the minimum
+    for bad in [(0, 10, 4, 8), (1, 10, 0, 8), (1, 10, 17, 8), (1, 10, 4, 0), (1, 10, 4, 16385),
+                (1, 2 ** 29, 16, 8), (1, -1, 4, 8)]:
+        assert L.gmm_ivf_workspace_bytes(*bad) == 0, bad
+
+
+def test_ivf_lists_rejects_bad_arguments_before_the_device():
+    L = _abi.lib()
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    ok = L.gmm_ivf_workspace_bytes(1, 100, 4, 8)
+    cases = {
+        "m": ((1, 100, 0, 8, p, None, p, p, None, ws, ok, None), _abi.GMM_ERR_INVALID_ARG),
+        "K": ((1, 100, 4, 20000, p, None, p, p, None, ws, ok, None), _abi.GMM_ERR_UNSUPPORTED),
+        "offsets": ((1, 100, 4, 8, p, None, None, p, None, ws, ok, None), _abi.GMM_ERR_INVALID_ARG),
+        "idx": ((1, 100, 4, 8, None, None, p, p, None, ws, ok, None), _abi.GMM_ERR_INVALID_ARG),
+        "list_resp": ((1, 100, 4, 8, p, None, p, p, p, ws, ok, None), _abi.GMM_ERR_INVALID_ARG),
+        "ws align": ((1, 100, 4, 8, p, None, p, p, None, ctypes.c_void_p(4100), ok, None),
+                     _abi.GMM_ERR_WORKSPACE),
+        "ws size": ((1, 100, 4, 8, p, None, p, p, None, ws, 0, None), _abi.GMM_ERR_WORKSPACE),
+    }
+    for name, (args, want) in cases.items():
+        assert L.gmm_ivf_lists(*args) == want, name
+        assert L.gmm_last_error() != b"", name
