@@ -11,6 +11,9 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
   gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
 
+The estimator calls (score_samples, predict, score, aic, bic, fit with
+restarts) are in soft_clustering_em_amd.estimator.
+
 X is (N, D) or (B, N, D) with unit stride along D; w (B,K), mu (B,K,D) and the
 covariance parameters are float32 and are updated in place by the M-step.
 """

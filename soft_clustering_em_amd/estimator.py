@@ -1,0 +1,164 @@
+"""Estimator-level calls over the C ABI: per-row log-likelihood, hard
+assignment, mean log-likelihood, information criteria, and a fit loop with
+restarts -- the estimator surface the GMMXX README lists under "Highlights"
+(fit, predict, score, score_samples, aic, bic; restarts as in its estimator).
+
+Every per-row and per-component number comes from the HIP library:
+score_samples and predict from gmm_predict_proba_topm (m = 1: the best
+component and log p(x_i)), score from gmm_estep_stats (sum_i log p(x_i)),
+fit from gmm_fit_step.  What runs here is argument handling, the stopping
+rule and the AIC/BIC arithmetic on B returned scalars.
+
+  n_parameters(cov, K, D)                       -> int
+  score_samples(X, w, mu, cv, cov)              -> (B, N) float32 log p(x_i)
+  predict(X, w, mu, cv, cov)                    -> (B, N) int32 argmax_k r_ik
+  score(X, w, mu, cv, cov)                      -> (B,) float64 mean log p(x_i)
+  information_criteria(mean_ll, N, p)           -> (aic, bic), numpy
+  aic(...), bic(...)                            -> (B,) float64
+  fit(X, K, cov, ...)                           -> FitResult (the restart with the best mean LL)
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import gmm_estep_stats, gmm_fit_step, gmm_predict_proba_topm, new_stats
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _batched(X):
+    return X if X.dim() == 3 else X.unsqueeze(0)
+
+
+def n_parameters(cov: str, K: int, D: int) -> int:
+    """Free parameters of a K-component mixture in D dimensions: K - 1 weights,
+    K D means, and the covariance parameters (spherical K, diag K D, tied
+    D (D + 1) / 2, full K D (D + 1) / 2)."""
+    covp = {"spherical": K, "diag": K * D, "tied": D * (D + 1) // 2, "full": K * D * (D + 1) // 2}[cov]
+    return (K - 1) + K * D + covp
+
+
+def information_criteria(mean_ll, N: int, p: int):
+    """AIC = -2 N mean_ll + 2 p and BIC = -2 N mean_ll + p log N (Akaike;
+    Schwarz), per problem."""
+    total = -2.0 * np.asarray(mean_ll, dtype=np.float64) * N
+    return total + 2.0 * p, total + p * math.log(N)
+
+
+def _topm1(X, w, mu, cv, cov):
+    torch = _torch()
+    Xb = _batched(X)
+    B, N = Xb.shape[0], Xb.shape[1]
+    idx = torch.empty(B, N, 1, dtype=torch.int32, device=X.device)
+    resp = torch.empty(B, N, 1, dtype=torch.float32, device=X.device)
+    logp = torch.empty(B, N, dtype=torch.float32, device=X.device)
+    gmm_predict_proba_topm(X, w, mu, cv, cov, 1, 0.0, idx, resp, logp=logp)
+    return idx[..., 0], logp
+
+
+def score_samples(X, w, mu, cv, cov):
+    """log p(x_i) (natural log) of every row, (B, N) float32."""
+    return _topm1(X, w, mu, cv, cov)[1]
+
+
+def predict(X, w, mu, cv, cov):
+    """The component of largest responsibility of every row (ties: lower
+    index), (B, N) int32."""
+    return _topm1(X, w, mu, cv, cov)[0]
+
+
+def score(X, w, mu, cv, cov):
+    """(1/N) sum_i log p(x_i) per problem, (B,) float64 on the host."""
+    Xb = _batched(X)
+    B, N, D = Xb.shape
+    st = new_stats(B, w.shape[-1], D, cov, X.device)
+    gmm_estep_stats(X, w, mu, cv, cov, st)
+    return (st["loglik"] / N).cpu().numpy()
+
+
+def aic(X, w, mu, cv, cov):
+    Xb = _batched(X)
+    return information_criteria(score(X, w, mu, cv, cov), Xb.shape[1], n_parameters(cov, w.shape[-1], Xb.shape[2]))[0]
+
+
+def bic(X, w, mu, cv, cov):
+    Xb = _batched(X)
+    return information_criteria(score(X, w, mu, cv, cov), Xb.shape[1], n_parameters(cov, w.shape[-1], Xb.shape[2]))[1]
+
+
+@dataclass
+class FitResult:
+    weights: object        # (B, K) float32, device
+    means: object          # (B, K, D) float32, device
+    covars: object         # covariance parameters, device
+    mean_ll: np.ndarray    # (B,) mean log-likelihood of the returned parameters' last E-step
+    n_iter: int
+    converged: bool
+    restart: int           # which restart was kept
+    history: list          # per restart: list of per-iteration mean LL (problem-averaged)
+
+
+def random_init(X, K, cov, generator):
+    """K distinct rows of each problem as means, equal weights, and the
+    problem's sample variance (spherical: its mean over dimensions; diag: per
+    dimension; tied/full: the sample covariance) as every component's."""
+    torch = _torch()
+    Xb = _batched(X).float()
+    B, N, D = Xb.shape
+    if K > N:
+        raise ValueError("K exceeds the number of rows")
+    sel = torch.stack([torch.randperm(N, generator=generator, device="cpu")[:K] for _ in range(B)]).to(X.device)
+    mu = torch.gather(Xb, 1, sel[..., None].expand(B, K, D)).contiguous()
+    w = torch.full((B, K), 1.0 / K, dtype=torch.float32, device=X.device)
+    xm = Xb.mean(dim=1, keepdim=True)
+    var = ((Xb - xm) ** 2).mean(dim=1)  # (B, D)
+    if cov == "spherical":
+        cv = var.mean(dim=1, keepdim=True).expand(B, K).contiguous()
+    elif cov == "diag":
+        cv = var[:, None, :].expand(B, K, D).contiguous()
+    else:
+        Xc = (Xb - xm).contiguous()
+        C = torch.bmm(Xc.transpose(1, 2).contiguous(), Xc) / N
+        cv = C.contiguous() if cov == "tied" else C[:, None].expand(B, K, D, D).contiguous()
+    if X.dim() == 2:
+        w, mu, cv = w[0].contiguous(), mu[0].contiguous(), cv[0].contiguous()
+    return w, mu, cv
+
+
+def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=None):
+    """EM from n_init starts (random_init with a seeded generator, or the
+    given init = (w, mu, cv) for the first start); each runs until the change
+    of the problem-averaged mean log-likelihood falls below tol or n_iter
+    iterations.  Keeps the start whose last mean log-likelihood is highest."""
+    torch = _torch()
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    Xb = _batched(X)
+    B = Xb.shape[0]
+    best, history = None, []
+    for r in range(n_init):
+        if r == 0 and init is not None:
+            w, mu, cv = (t.clone().contiguous() for t in init)
+        else:
+            w, mu, cv = random_init(X, K, cov, gen)
+        mll = torch.zeros(B, dtype=torch.float64, device=X.device)
+        hist, prev, converged, it = [], None, False, 0
+        for it in range(1, n_iter + 1):
+            gmm_fit_step(X, w, mu, cv, cov, reg_covar=reg_covar, mean_loglik=mll)
+            cur = float(mll.mean().item())  # the LL of the parameters that entered this step
+            hist.append(cur)
+            if prev is not None and abs(cur - prev) < tol:
+                converged = True
+                break
+            prev = cur
+        history.append(hist)
+        final = score(X, w, mu, cv, cov)
+        if best is None or final.mean() > best.mean_ll.mean():
+            best = FitResult(w, mu, cv, final, it, converged, r, history)
+    best.history = history
+    return best

@@ -466,3 +466,45 @@ def test_ivf_lists_hand_case():
     assert rows[0, :7].tolist() == [0, 2, 1, 2, 0, 2, 3]
     assert np.allclose(lr[0, :7], [.4, .5, 1., .2, .6, .3, .9])
     assert rows[0, 7:].tolist() == [-1] * 5
+
+
+# ---------------------------------------------------------------- estimator arithmetic
+@pytest.mark.parametrize("cov", ["spherical", "diag", "tied", "full"])
+def test_information_criteria_match_sklearn(cov):
+    """AIC/BIC from the oracle's mean log-likelihood and the parameter count,
+    against sklearn's GaussianMixture.aic/bic on the same parameters (its
+    score is the mean log-likelihood; only the arithmetic around it is pinned
+    here)."""
+    from sklearn.mixture import GaussianMixture
+    from soft_clustering_em_amd.estimator import information_criteria, n_parameters
+    rng = np.random.default_rng(3)
+    N, D, K = 400, 3, 4
+    X = rng.normal(size=(N, D)) + rng.integers(0, 3, size=(N, 1))
+    w = np.full(K, 1.0 / K)
+    mu = X[rng.choice(N, K, replace=False)]
+    if cov == "spherical":
+        cv = np.full(K, 1.3)
+    elif cov == "diag":
+        cv = rng.uniform(0.5, 2.0, size=(K, D))
+    elif cov == "tied":
+        A = rng.normal(size=(D, D))
+        cv = A @ A.T + np.eye(D)
+    else:
+        A = rng.normal(size=(K, D, D))
+        cv = A @ A.transpose(0, 2, 1) + np.eye(D)
+    gm = GaussianMixture(K, covariance_type=cov)
+    gm.weights_, gm.means_, gm.covariances_ = w, mu, cv
+    if cov == "spherical":
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(cv)
+    elif cov == "diag":
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(cv)
+    elif cov == "tied":
+        gm.precisions_cholesky_ = np.linalg.inv(np.linalg.cholesky(cv)).T
+    else:
+        gm.precisions_cholesky_ = np.stack([np.linalg.inv(np.linalg.cholesky(c)).T for c in cv])
+    st = oracle.estep(cov, X[None], w[None], mu[None], cv[None])
+    mean_ll = st["ll"][0] / N
+    a, b = information_criteria(mean_ll, N, n_parameters(cov, K, D))
+    assert abs(mean_ll - gm.score(X)) <= 1e-10 * abs(mean_ll)
+    assert abs(a - gm.aic(X)) <= 1e-9 * abs(a)
+    assert abs(b - gm.bic(X)) <= 1e-9 * abs(b)
