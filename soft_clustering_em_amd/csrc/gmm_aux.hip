@@ -242,38 +242,58 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
                                                      const float* __restrict__ mu, double* __restrict__ raw,
                                                      double* nk, double* sx, double* sxx, double* ll,
                                                      double* mean_ll, int accumulate, int B) {
-  const int tid = threadIdx.x;
-  if ((int64_t)blockIdx.x >= (int64_t)B * K) {
-    const int b = blockIdx.x - B * K;
-    if (tid == 0) {
-      double s = 0.0;
-      for (int g = 0; g < llG; ++g) s += llpart[(size_t)b * llG + g];
-      ll[b] = accumulate ? ll[b] + s : s;
-      if (mean_ll) mean_ll[b] = s / (double)N;
-    }
-    return;
-  }
-  const int b = blockIdx.x / K, k = blockIdx.x % K;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   extern __shared__ double sm[];
-  double* r = sm;            // PR
-  double* m = sm + PR;       // D
-  const size_t stride = (size_t)KP * PR;
-  for (int j = tid; j < PR; j += blockDim.x) {
-    // workgroup order 0..Gb-1; eight loads in flight, additions still in order
+  // fixed-order sum of n values v(g), g = 0..n-1, split into nseg contiguous
+  // segments (segment q: thread-local sum, eight loads in flight), the
+  // segment sums then added in segment order
+  auto seg_sum = [&](const double* src, size_t stride, int n, int nseg, int q) {
+    const int g0 = (int)((int64_t)n * q / nseg), g1 = (int)((int64_t)n * (q + 1) / nseg);
     double s = 0.0;
-    const double* src = part + ((size_t)b * Gb * KP + k) * PR + j;
-    int g = 0;
-    for (; g + 8 <= Gb; g += 8) {
+    int g = g0;
+    for (; g + 8 <= g1; g += 8) {
       double v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(g + u) * stride];
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += v[u];
     }
-    for (; g < Gb; ++g) s += src[(size_t)g * stride];
-    r[j] = s;
-    raw[((size_t)b * KP + k) * PR + j] = s;
+    for (; g < g1; ++g) s += src[(size_t)g * stride];
+    return s;
+  };
+  if ((int64_t)blockIdx.x >= (int64_t)B * K) {
+    const int b = blockIdx.x - B * K;
+    sm[tid] = seg_sum(llpart + (size_t)b * llG, 1, llG, nthr, tid);
+    __syncthreads();
+    if (tid == 0) {
+      double s = 0.0;
+      for (int q = 0; q < nthr; ++q) s += sm[q];
+      ll[b] = accumulate ? ll[b] + s : s;
+      if (mean_ll) mean_ll[b] = s / (double)N;
+    }
+    return;
   }
+  const int b = blockIdx.x / K, k = blockIdx.x % K;
+  double* r = sm;            // PR
+  double* m = sm + PR;       // D
+  double* segs = m + D;      // PR * nseg <= nthr
+  const size_t stride = (size_t)KP * PR;
+  // each statistic over the workgroups 0..Gb-1: in nseg segments when the
+  // statistics are fewer than the threads
+  const int nseg = std::max(1, nthr / PR);
+  const double* src0 = part + ((size_t)b * Gb * KP + k) * PR;
+  if (nseg == 1) {
+    for (int j = tid; j < PR; j += nthr) r[j] = seg_sum(src0 + j, stride, Gb, 1, 0);
+  } else {
+    if (tid < PR * nseg) segs[tid] = seg_sum(src0 + tid / nseg, stride, Gb, nseg, tid % nseg);
+    __syncthreads();
+    for (int j = tid; j < PR; j += nthr) {
+      double s = 0.0;
+      for (int q = 0; q < nseg; ++q) s += segs[j * nseg + q];
+      r[j] = s;
+    }
+  }
+  for (int j = tid; j < PR; j += nthr) raw[((size_t)b * KP + k) * PR + j] = r[j];
   for (int d = tid; d < D; d += blockDim.x) m[d] = (double)mu[((size_t)b * K + k) * D + d];
   __syncthreads();
   if (cov == TIED) return;
@@ -343,8 +363,8 @@ __global__ void __launch_bounds__(256) centre_tied_kernel(int D, int K, int KP, 
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s) {
-  const size_t lds = sizeof(double) * (size_t)(p.PR + p.D);
-  const unsigned threads = (unsigned)std::min(256, std::max(64, (p.PR + 63) / 64 * 64));
+  const unsigned threads = 256;
+  const size_t lds = sizeof(double) * (size_t)(p.PR + p.D + threads);
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(threads), lds, s, p.cov, (int)p.D,
                      (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.llG, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
                      accumulate, (int)p.B);
