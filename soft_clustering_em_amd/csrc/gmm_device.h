@@ -51,6 +51,19 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+__device__ __forceinline__ double rows4_sum_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  v = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0])) +
+      __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+  const unsigned long long w = (unsigned long long)__double_as_longlong(v);
+  auto lo2 = __builtin_amdgcn_permlane32_swap((unsigned)w, (unsigned)w, false, false);
+  auto hi2 = __builtin_amdgcn_permlane32_swap((unsigned)(w >> 32), (unsigned)(w >> 32), false, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi2[0] << 32) | lo2[0])) +
+         __longlong_as_double((long long)(((unsigned long long)hi2[1] << 32) | lo2[1]));
+}
+
 // 16-lane all-reduce of a double (the two halves moved by the DPP patterns of
 // row16_sum)
 template <int CTRL>

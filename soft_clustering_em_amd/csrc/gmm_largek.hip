@@ -716,6 +716,178 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   }
 }
 
+// Pass A without per-tile barriers, for full-width rows (D = 128, 16-byte
+// aligned): the slice's weights and constants go to LDS once; then each wave
+// streams its own row tiles (tile g + G (8 i + w) for wave w), reading a tile's
+// rows from memory straight into registers as the B operand of the transposed
+// logit MFMA (lane l: rows l % 16 (+16), dims 8 (l / 16) .. +7 of each 32-dim
+// step), the next tile's loads in flight while it works.  It covers all 256
+// components of the slice in 32-component chunks with a running per-row max
+// and a per-lane running sum rescaled to it, so a row's (max, sum) for the
+// slice needs no other wave and the waves never wait for each other.
+__global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
+  constexpr int DP = 128, KSTEP = DP / 32, NCH = KSA / 32;
+  constexpr int WFRAG = (KSA / 16) * 2 * KSTEP * 64;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int slice = blockIdx.x / A.G;
+  const int g = blockIdx.x % A.G;
+  const int64_t nrows = A.N;
+  const int64_t ntiles = (nrows + LT - 1) / LT;
+
+  extern __shared__ float lds[];
+  bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
+  float* cst = reinterpret_cast<float*>(Wl + WFRAG);  // c, a, eb, e0 of the slice's components
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(A.W) + (size_t)slice * WFRAG;
+    uint4* dst = reinterpret_cast<uint4*>(Wl);
+    for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
+    for (int i = threadIdx.x; i < KSA; i += blockDim.x) {
+      const int k = slice * KSA + i;
+      cst[i] = (float)A.c[k];
+      cst[KSA + i] = (float)A.a[k];
+      cst[2 * KSA + i] = A.esh[2 * k];
+      cst[3 * KSA + i] = A.esh[2 * k + 1];
+    }
+  }
+  __syncthreads();
+  bool any_sharp = false;
+  for (int i = lane; i < KSA; i += 64) any_sharp = any_sharp || cst[2 * KSA + i] > 0.f;
+  any_sharp = __builtin_amdgcn_ballot_w64(any_sharp) != 0;
+
+  const unsigned short* xb = reinterpret_cast<const unsigned short*>(A.x);
+  auto load_rows = [&](int64_t t, bf16x8 (&rv)[2][KSTEP]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      int64_t row = t * LT + rb * 16 + (lane & 15);
+      row = row < nrows ? row : nrows - 1;
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ++ks)
+        rv[rb][ks] = *reinterpret_cast<const bf16x8*>(xb + row * A.ld_x + ks * 32 + 8 * (lane >> 4));
+    }
+  };
+  int64_t t = g + (int64_t)A.G * wv;
+  bf16x8 nxt[2][KSTEP];
+  if (t < ntiles) load_rows(t, nxt);
+  for (; t < ntiles; t += (int64_t)A.G * LNW) {
+    bf16x8 rv[2][KSTEP];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ++ks) rv[rb][ks] = nxt[rb][ks];
+    if (t + (int64_t)A.G * LNW < ntiles) load_rows(t + (int64_t)A.G * LNW, nxt);
+    // |x|^2 of the lane's two rows: exact (float64) in slice 0, which stores
+    // it for pass C and the top-m rescoring; float32 elsewhere
+    float xs[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (slice == 0) {
+        double q = 0.0;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = (float)rv[rb][ks][e];
+            q += (double)(f * f);
+          }
+        q = rows4_sum_f64(q);
+        xs[rb] = (float)q;
+        const int64_t row = t * LT + rb * 16 + lane;
+        if (lane < 16 && row < nrows) A.xsq[row] = q;
+      } else {
+        float q = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = (float)rv[rb][ks][e];
+            q = fmaf(f, f, q);
+          }
+        xs[rb] = rows4_sum(q);
+      }
+    }
+    float M[2] = {kDead, kDead}, Sl[2] = {0.f, 0.f}, R[2] = {kDead, kDead};
+#pragma unroll 1
+    for (int cc = 0; cc < NCH; ++cc) {
+      // components cc 32 + nt 16 + 4 (lane / 16) + v of the slice
+      floatx4 acc[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
+          const float c = cst[kl], a = cst[KSA + kl];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) acc[rb][nt][v] = fmaf(a, xs[rb], c);
+        }
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const bf16x8 bw = Wl[(((cc * 2 + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, rv[rb][ks], acc[rb][nt], 0, 0, 0);
+          }
+      if (any_sharp) {
+        // sharp components: scores that may come within 60 (log2 units) of the
+        // best other score of the row seen so far in the slice, again exactly
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float r = R[rb];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (!(cst[2 * KSA + cc * 32 + nt * 16 + 4 * (lane >> 4) + v] > 0.f)) r = fmaxf(r, acc[rb][nt][v]);
+          R[rb] = rows4_max(r);
+          const int64_t row = t * LT + rb * 16 + (lane & 15);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
+              const float eb = cst[2 * KSA + kl], e0 = cst[3 * KSA + kl];
+              if (eb > 0.f && row < nrows && acc[rb][nt][v] + eb * xs[rb] + e0 >= R[rb] - 60.f) {
+                const int k = slice * KSA + kl;
+                acc[rb][nt][v] =
+                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, xb + row * A.ld_x);
+              }
+            }
+        }
+      }
+      // running max per row, and the lane's sum rescaled to it
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float cm = acc[rb][0][0];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cm = fmaxf(cm, acc[rb][nt][v]);
+        cm = rows4_max(cm);
+        const float Mn = fmaxf(M[rb], cm);
+        float s = Sl[rb] * __builtin_amdgcn_exp2f(M[rb] - Mn);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s += __builtin_amdgcn_exp2f(acc[rb][nt][v] - Mn);
+        Sl[rb] = s;
+        M[rb] = Mn;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float S = rows4_sum(Sl[rb]);
+      const int64_t row = t * LT + rb * 16 + lane;
+      if (lane < 16 && row < nrows) A.P[(size_t)row * A.S + slice] = float2{M[rb], S};
+    }
+  }
+}
+
+size_t largek_pass_a_lds_bytes() { return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + 4 * KSA * sizeof(float); }
+
 // Pass B: per row, combine the slices' (max, sum) into the LSE (log2 units);
 // each workgroup also sums its rows' LSE (natural log) into its LL partial.
 // The rows from N up to the next multiple of the row tile get LSE = +inf, so
@@ -828,6 +1000,8 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kC, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
     attr_set = true;
   }
   const int64_t N = a.N;
@@ -839,7 +1013,11 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
     ac.accumulate = chunk > 0;
     if (ac.N > 0) {
       ac.G = p.GbA;
-      hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
+      if (p.D == 128 && ac.vec16)
+        hipLaunchKernelGGL(largek_pass_a_kernel, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                           largek_pass_a_lds_bytes(), s, ac);
+      else
+        hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
@@ -1095,6 +1273,8 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kT, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
     attr_set = true;
   }
   const int64_t N = a.N;
@@ -1108,7 +1288,11 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     ac.count = a.count ? a.count + r0 : nullptr;
     ac.logp = a.logp ? a.logp + r0 : nullptr;
     ac.G = p.GbA;
-    hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
+    if (p.D == 128 && ac.vec16)
+      hipLaunchKernelGGL(largek_pass_a_kernel, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(), s, ac);
+    else
+      hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
