@@ -30,8 +30,9 @@
 // (lane l: component l%16, rows 4(l/16)+v of a 16-row block) provides R as
 // the B operand of the statistics MFMA directly when the 32 rows of a tile
 // are ordered k = 8g + j <-> row 4g + j (j < 4), 16 + 4g + (j - 4) (j >= 4);
-// the A operand X^T is kept in LDS in that order (its feature rows permuted
-// against bank conflicts, see xt_row).  Workgroups of one row
+// the A operand X^T comes straight from the row tile in LDS by the
+// transposing 64-bit LDS load (ds_read_b64_tr_b16), two per 16-feature
+// block, one for each half of that row order.  Workgroups of one row
 // group and different slices have ids that differ by multiples of 8, so they
 // share an XCD and its L2 copy of the rows.
 #include "gmm_device.h"
@@ -50,6 +51,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 namespace {
 
@@ -58,7 +61,6 @@ constexpr int KSC = kLargeKSlice / 2;  // components per workgroup in pass C (12
 constexpr int LNW = 8;                 // waves per workgroup
 constexpr int LT = 32;                 // rows per tile
 constexpr int LRS = 136;               // LDS row stride of the row tile, in bf16 (272 bytes)
-constexpr int XTS = 40;                // LDS row stride of the transposed tile, in bf16 (80 bytes)
 // A component is "sharp" when the terms of its expanded log-score reach
 // lambda (|mu|^2 + D sigma^2) > kSharpLowp: with bf16 weights (two-term
 // split) their rounding would reach about 1% of a responsibility.
@@ -87,12 +89,6 @@ __device__ __forceinline__ void piece_of(int j, int& r, int& c8) {
   c8 = (j % 16) * 8;
 }
 
-// Pass C's transposed copy X^T keeps feature f = 8 m + e in LDS row
-// 16 e + m: the eight 2-byte stores of a piece (one per e) from the 16 lanes
-// of a row (m = 0..15) then fall on rows 80 bytes apart, spread over the
-// banks, where rows 8 features apart (640 bytes) would share one bank.  The
-// statistics tile mt (LDS rows 16 mt .. +15) thus holds features 8 i + mt.
-__device__ __forceinline__ int xt_row(int f) { return (f & 7) * 16 + (f >> 3); }
 
 struct Piece {
   u16x8 v;
@@ -139,11 +135,10 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
 // Write a thread's piece into the LDS tile.  Pass A also forms |x|^2 of each
 // row: in the workgroups of slice 0 exactly (each bf16 square is exact in
 // float32, their sum exact in float64), stored for pass C and the top-m
-// rescoring; elsewhere in float32; pass C writes the
-// transposed copy X^T[d][k] with the k order of the statistics MFMA.
+// rescoring; elsewhere in float32.
 template <bool STATS>
 __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc, int64_t row0, int slice,
-                                            unsigned short* rows, unsigned short* xt, double* xsq, float* ls) {
+                                            unsigned short* rows, double* xsq, float* ls) {
   const int j = threadIdx.x;
   int r, c8;
   piece_of(j, r, c8);
@@ -156,10 +151,6 @@ __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc
   const bool live = row0 + j < A.N;  // threads j < LT: row j of the tile
   if (j < LT) ls[j] = live ? pc.ls : (STATS ? INFINITY : 0.f);
   if constexpr (STATS) {
-    const int g = (r & 15) >> 2, j4 = r & 3;
-    const int kpos = 8 * g + (r < 16 ? j4 : 4 + j4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xt[xt_row(c8 + e) * XTS + kpos] = v[e];
     if (j < LT) xsq[j] = live ? pc.xs : 0.0;
   } else if (slice == 0) {
     double sq = 0.0;
@@ -206,7 +197,6 @@ size_t largek_lds_bytes(int DP, int pass) {
   // weights (pass C keeps them in registers)
   size_t b = pass != 2 ? (size_t)(KSA / 16) * 2 * (DP / 32) * 64 * 16 : 0;
   size_t tile = (size_t)LT * LRS * 2;                       // row tile
-  if (pass == 2) tile += (size_t)DP * XTS * 2;              // transposed tile
   tile += (size_t)LT * 8 + LT * 4;                          // |x|^2, LSE or maximum
   b += (pass == 2 ? 3 : 2) * tile;                          // buffers
   if (pass != 2) b += (size_t)2 * LNW * LT * 2 * 4;         // per-wave (max, sum), two tiles
@@ -238,19 +228,18 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   const int64_t nrows = A.N;
   const int64_t ntiles = (nrows + LT - 1) / LT;
 
-  // row-tile buffers (rows, pass C's transposed copy, |x|^2, per-row LSE or
-  // maximum): pass C keeps three -- tile i's X^T for its statistics, tile
-  // i + 1's rows for its logits, tile i + 2 being staged -- and passes A and T
+  // row-tile buffers (rows, |x|^2, per-row LSE or maximum): pass C keeps
+  // three -- tile i's rows for its statistics, tile i + 1's for its logits,
+  // tile i + 2 being staged -- and passes A and T
   // two (tile i, tile i + 1 being staged)
   constexpr int NB = STATS ? 3 : 2;
-  constexpr int BUFB = LT * LRS * 2 + (STATS ? DP * XTS * 2 : 0) + LT * 8 + LT * 4;  // bytes per buffer
+  constexpr int BUFB = LT * LRS * 2 + LT * 8 + LT * 4;  // bytes per buffer
   static_assert(BUFB % 16 == 0, "16-byte aligned buffers");
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
   unsigned char* bufs = reinterpret_cast<unsigned char*>(Wl + WLDS);
   auto rows_of = [&](int bi) { return reinterpret_cast<unsigned short*>(bufs + bi * BUFB); };
-  auto xt_of = [&](int bi) { return rows_of(bi) + LT * LRS; };
-  auto xsq_of = [&](int bi) { return reinterpret_cast<double*>(xt_of(bi) + (STATS ? DP * XTS : 0)); };
+  auto xsq_of = [&](int bi) { return reinterpret_cast<double*>(rows_of(bi) + LT * LRS); };
   auto ls_of = [&](int bi) { return reinterpret_cast<float*>(xsq_of(bi) + LT); };
   float* red = reinterpret_cast<float*>(bufs + NB * BUFB);  // pass A: 2 buffers of LNW * LT * 2
   // pass T: 2 buffers of (LT rows, LNW waves) candidate masks, bit j of word
@@ -392,7 +381,6 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   auto finish = [&](int64_t row0, int it, auto sharp_c, const floatx4 (&acc)[2][NT], int bi) {
     constexpr bool SHARP = decltype(sharp_c)::value;
     const unsigned short* rows = rows_of(bi);
-    const unsigned short* xt = xt_of(bi);
     const double* xsq = xsq_of(bi);
     const float* lsb = ls_of(bi);
     if constexpr (PASS == 0) {
@@ -566,7 +554,12 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       }
 #pragma unroll
       for (int mt = 0; mt < (STATS ? GM : 1); ++mt) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (mt * 16 + (lane & 15)) * XTS + 8 * (lane >> 4));
+        // lane 16 g + i: features 16 mt + i of rows 4 g + e (read 1) and
+        // 16 + 4 g + e (read 2), e = 0..3 -- k = 8 g + e and 8 g + 4 + e
+        const unsigned short* src = rows + (lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * LRS));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           sbig[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], sbig[mt][nt], 0, 0, 0);
@@ -606,7 +599,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // other half of the double buffer, last read by the combine of tile
       // i - 2 in iteration i - 1.
       static_assert(PF == NB, "prefetch slots follow the buffers");
-      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
+      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
       pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)2 * A.G, ntiles);
       __syncthreads();
       for (int64_t i0 = 0; i0 < nmine; i0 += 2) {
@@ -615,7 +608,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           const int64_t i = i0 + u;
           if (i >= nmine) break;
           const int bs = 1 - u;
-          stage_piece<STATS>(A, pf[bs], (g + (i + 1) * A.G) * LT, slice, rows_of(bs), xt_of(bs), xsq_of(bs),
+          stage_piece<STATS>(A, pf[bs], (g + (i + 1) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
                              ls_of(bs));
           pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 3) * A.G, ntiles);
           if (i > 0 && wv == (i & (LNW - 1))) combine((g + (i - 1) * A.G) * LT, red + ((i - 1) & 1) * (LNW * LT * 2));
@@ -635,9 +628,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // i - 1.  Staging and logits past the workgroup's last tile touch only
       // a free buffer and are never used.
       static_assert(PF == NB, "prefetch slots follow the buffers");
-      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xt_of(0), xsq_of(0), ls_of(0));
+      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
       pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)3 * A.G, ntiles);
-      stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xt_of(1), xsq_of(1), ls_of(1));
+      stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xsq_of(1), ls_of(1));
       pf[1] = fetch_piece<PASS, VEC>(A, g + (int64_t)4 * A.G, ntiles);
       __syncthreads();
       floatx4 acc[2][NT];
@@ -648,7 +641,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           const int64_t i = i0 + u;
           if (i >= nmine) break;
           const int bn = (u + 1) % 3, bs = (u + 2) % 3;
-          stage_piece<STATS>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xt_of(bs), xsq_of(bs),
+          stage_piece<STATS>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
                              ls_of(bs));
           pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 5) * A.G, ntiles);
           floatx4 accn[2][NT];
@@ -689,8 +682,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = 8 * (4 * (lane >> 4) + v) + mt;  // feature of LDS row 16 mt + 4 (lane / 16) + v
-          double* dst = part + (size_t)k * PR + 2 + row;
+          const int f = 16 * mt + 4 * (lane >> 4) + v;  // the feature of accumulator row 4 (lane / 16) + v
+          double* dst = part + (size_t)k * PR + 2 + f;
           *dst = (A.accumulate ? *dst : 0.0) + ((double)sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
         }
       }
