@@ -16,6 +16,7 @@ rule and the AIC/BIC arithmetic on B returned scalars.
   information_criteria(mean_ll, N, p)           -> (aic, bic), numpy
   aic(...), bic(...)                            -> (B,) float64
   fit(X, K, cov, ...)                           -> FitResult (the restart with the best mean LL)
+  GaussianMixture(n_components, covariance_type, ...)  the same calls as a scikit-learn style class
 """
 from __future__ import annotations
 
@@ -162,3 +163,84 @@ def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=
             best = FitResult(w, mu, cv, final, it, converged, r, history)
     best.history = history
     return best
+
+
+class GaussianMixture:
+    """The estimator in the scikit-learn style of the GMMXX README (its Python
+    usage example): fit / predict / predict_proba_topm / score_samples /
+    score / aic / bic, with the fitted state in means_, weights_,
+    covariances_ (spherical (K,) variances, diag (K, D), tied (D, D), full
+    (K, D, D)), lower_bound_ (the last E-step's mean log-likelihood),
+    lower_bound_history_ (per iteration, kept restart), n_iter_ and
+    converged_.  X is one problem, (N, D), on the GPU; the state stays on
+    the GPU as float32 tensors.  Every computation runs in the HIP library."""
+
+    def __init__(self, n_components, covariance_type="full", max_iter=100, tol=1e-3, reg_covar=1e-6, n_init=1,
+                 random_state=0, weights_init=None, means_init=None, covariances_init=None):
+        if covariance_type not in ("spherical", "diag", "tied", "full"):
+            raise ValueError(f"unknown covariance_type {covariance_type!r}")
+        self.n_components = int(n_components)
+        self.covariance_type = covariance_type
+        self.max_iter = int(max_iter)
+        self.tol = float(tol)
+        self.reg_covar = float(reg_covar)
+        self.n_init = int(n_init)
+        self.random_state = random_state
+        self.weights_init, self.means_init, self.covariances_init = weights_init, means_init, covariances_init
+
+    def _init(self, X):
+        given = (self.weights_init, self.means_init, self.covariances_init)
+        if all(t is None for t in given):
+            return None
+        if any(t is None for t in given):
+            raise ValueError("weights_init, means_init and covariances_init are given together")
+        torch = _torch()
+        return tuple(torch.as_tensor(t, dtype=torch.float32, device=X.device).contiguous() for t in given)
+
+    def fit(self, X):
+        if X.dim() != 2:
+            raise ValueError("X is (N, D)")
+        res = fit(X, self.n_components, self.covariance_type, n_iter=self.max_iter, tol=self.tol,
+                  n_init=self.n_init, reg_covar=self.reg_covar, seed=self.random_state or 0, init=self._init(X))
+        self.weights_, self.means_, self.covariances_ = res.weights, res.means, res.covars
+        self.lower_bound_ = float(res.mean_ll[0])
+        self.lower_bound_history_ = list(res.history[res.restart])
+        self.n_iter_, self.converged_ = res.n_iter, res.converged
+        self.n_features_in_ = int(X.shape[1])
+        return self
+
+    def _theta(self):
+        if not hasattr(self, "means_"):
+            raise RuntimeError("call fit first")
+        return self.weights_, self.means_, self.covariances_, self.covariance_type
+
+    def fit_predict(self, X):
+        return self.fit(X).predict(X)
+
+    def predict(self, X):
+        return predict(X, *self._theta())[0]
+
+    def score_samples(self, X):
+        return score_samples(X, *self._theta())[0]
+
+    def score(self, X):
+        return float(score(X, *self._theta())[0])
+
+    def aic(self, X):
+        return float(aic(X, *self._theta())[0])
+
+    def bic(self, X):
+        return float(bic(X, *self._theta())[0])
+
+    def predict_proba_topm(self, X, m=4, threshold=0.1):
+        """Soft multi-assignment: per row the components of the m largest
+        responsibilities that reach threshold (the largest always kept),
+        in descending order with ties to the lower index.  Returns idx (N, m)
+        int32 (-1 past count), resp (N, m) float32, count (N,) int32."""
+        torch = _torch()
+        N = X.shape[0]
+        idx = torch.empty(N, m, dtype=torch.int32, device=X.device)
+        resp = torch.empty(N, m, dtype=torch.float32, device=X.device)
+        count = torch.empty(N, dtype=torch.int32, device=X.device)
+        gmm_predict_proba_topm(X, *self._theta(), m, threshold, idx, resp, count=count)
+        return idx, resp, count

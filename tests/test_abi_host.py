@@ -224,3 +224,20 @@ def test_ivf_lists_rejects_bad_arguments_before_the_device():
     for name, (args, want) in cases.items():
         assert L.gmm_ivf_lists(*args) == want, name
         assert L.gmm_last_error() != b"", name
+
+
+def test_gaussian_mixture_host_checks():
+    """The class rejects an unknown covariance type, a partial init and use
+    before fit, on the host."""
+    import numpy as np
+    import torch
+    from soft_clustering_em_amd.estimator import GaussianMixture
+    with pytest.raises(ValueError):
+        GaussianMixture(4, covariance_type="isotropic")
+    gm = GaussianMixture(4, covariance_type="diag", means_init=np.zeros((4, 3), np.float32))
+    with pytest.raises(ValueError):
+        gm._init(torch.zeros(10, 3))
+    with pytest.raises(RuntimeError):
+        gm.predict(torch.zeros(10, 3))
+    with pytest.raises(ValueError):
+        gm.fit(torch.zeros(2, 10, 3))
