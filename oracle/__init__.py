@@ -9,7 +9,7 @@ Sources it follows: "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
 Clustering", Section 2 (E-step score, log-sum-exp responsibilities, M-step
 eqs. 1-3) and Section 4 / Conclusion (multi-assignment by a threshold on the
 final responsibilities); "ML0094 GMM vs K-Means", Mathematical Formulation
-(responsibility-weighted covariance); GMMXX README, Covariance Coverage (the
+(responsibility-weighted covariance) and its k-means limit (kmeans_step); GMMXX README, Covariance Coverage (the
 four covariance types and their shapes).
 """
 from __future__ import annotations
@@ -52,8 +52,9 @@ def _load():
         lib.oracle_mstep_twopass.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, f64, P, P, P]
         lib.oracle_responsibilities.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, P, P, P]
         lib.oracle_topm.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, i32, f64, P, P, P, P, P, i32]
+        lib.oracle_kmeans_step.argtypes = [i64, i32, i32, P, i32, P, P, P, P, P, P, i32]
         for f in (lib.oracle_estep, lib.oracle_mstep, lib.oracle_mstep_twopass,
-                  lib.oracle_responsibilities, lib.oracle_topm):
+                  lib.oracle_responsibilities, lib.oracle_topm, lib.oracle_kmeans_step):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -183,6 +184,27 @@ def fit_step(cov, X, w, mu, cv, eps=1e-6, nthreads=0):
     wo, mo, co, fl = mstep(cov, st, n, np.asarray(w).reshape(B, -1),
                            np.asarray(mu).reshape(st["sx"].shape), np.asarray(cv).reshape(st["sxx"].shape), eps)
     return dict(w=wo, mu=mo, cv=co, mean_ll=st["ll"] / n, stats=st, flags=fl)
+
+
+def kmeans_step(X, C, nthreads=0):
+    """One k-means (Lloyd) iteration for one problem from centroids C (K, D):
+    (labels (N) int32, gap (N), new centroids (K, D), counts (K) int64,
+    inertia).  gap = second smallest minus smallest squared distance of the
+    row, the margin its label depends on."""
+    Xa, xt = _x_and_type(X)
+    N, D = Xa.shape
+    C = np.ascontiguousarray(C, dtype=np.float64).reshape(-1, D)
+    K = C.shape[0]
+    labels = np.zeros(N, dtype=np.int32)
+    gap = np.zeros(N)
+    newC = np.zeros((K, D))
+    counts = np.zeros(K, dtype=np.int64)
+    inertia = np.zeros(1)
+    rc = _load().oracle_kmeans_step(N, D, K, _ptr(Xa), xt, _ptr(C), _ptr(labels), _ptr(gap), _ptr(newC),
+                                    _ptr(counts), _ptr(inertia), int(nthreads))
+    if rc:
+        raise ValueError("oracle_kmeans_step rejected its arguments")
+    return labels, gap, newC, counts, float(inertia[0])
 
 
 def ivf_lists(idx, resp, K):

@@ -552,4 +552,71 @@ int oracle_topm(int cov, int64_t N, int D, int K, const void* X, int xtype,
   return 0;
 }
 
+/*
+ * One k-means (Lloyd) iteration: the hard-assignment limit of EM ("ML0094
+ * GMM vs K-Means": k-means assigns each point to the centroid at the smallest
+ * distance and is the limit of a GMM with one shared spherical variance going
+ * to zero, where the posterior collapses to an argmax; the mean update with
+ * 0/1 responsibilities is the mean of the cluster's points).  Flash-GMM
+ * Section 4: k-means is the usual coarse quantizer of an IVF index.
+ * Single problem, centroids C (K,D).
+ *   labels (N): argmin_k |x_i - c_k|^2 by direct differences, ties to the
+ *     lower k;  gap (N): second smallest minus smallest distance (INFINITY
+ *     when K == 1) -- the margin that decides the label;
+ *   newC (K,D): mean of the rows labelled k (summed in row order); a cluster
+ *     with no rows keeps its centroid;  counts (K);
+ *   inertia: sum over rows of the smallest distance, in row order.
+ */
+int oracle_kmeans_step(int64_t N, int D, int K, const void* X, int xtype, const double* C,
+                       int32_t* labels, double* gap, double* newC, int64_t* counts, double* inertia,
+                       int nthreads) {
+  if (K < 1 || D < 1 || N < 0) return -1;
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+  double* qmin = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* x = (double*)malloc(sizeof(double) * D);
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+      for (int d = 0; d < D; ++d) x[d] = x_at(X, xtype, i * D + d);
+      double best = INFINITY, second = INFINITY;
+      int arg = 0;
+      for (int k = 0; k < K; ++k) {
+        double q = 0.0;
+        for (int d = 0; d < D; ++d) {
+          const double t = x[d] - C[(size_t)k * D + d];
+          q += t * t;
+        }
+        if (q < best) {
+          second = best;
+          best = q;
+          arg = k;
+        } else if (q < second) {
+          second = q;
+        }
+      }
+      labels[i] = arg;
+      qmin[i] = best;
+      gap[i] = second - best;
+    }
+    free(x);
+  }
+  double* sum = (double*)calloc((size_t)K * D, sizeof(double));
+  for (int k = 0; k < K; ++k) counts[k] = 0;
+  double in = 0.0;
+  for (int64_t i = 0; i < N; ++i) {
+    const int k = labels[i];
+    for (int d = 0; d < D; ++d) sum[(size_t)k * D + d] += x_at(X, xtype, i * D + d);
+    counts[k] += 1;
+    in += qmin[i];
+  }
+  for (int k = 0; k < K; ++k)
+    for (int d = 0; d < D; ++d)
+      newC[(size_t)k * D + d] = counts[k] > 0 ? sum[(size_t)k * D + d] / (double)counts[k] : C[(size_t)k * D + d];
+  *inertia = in;
+  free(sum);
+  free(qmin);
+  return 0;
+}
+
 int oracle_version(void) { return 1; }

@@ -508,3 +508,93 @@ def test_information_criteria_match_sklearn(cov):
     assert abs(mean_ll - gm.score(X)) <= 1e-10 * abs(mean_ll)
     assert abs(a - gm.aic(X)) <= 1e-9 * abs(a)
     assert abs(b - gm.bic(X)) <= 1e-9 * abs(b)
+
+
+# ---------------------------------------------------------------- k-means (the hard-assignment limit)
+def test_kmeans_labels_minimise_the_objective_by_enumeration():
+    """Over all K^N labelings of a tiny set, the smallest sum of squared
+    distances to the given centroids is the oracle's inertia, reached by its
+    labels (the objective separates over rows: a nearest centroid per row)."""
+    rng = np.random.default_rng(11)
+    for N, K, D in [(5, 3, 2), (6, 2, 3), (4, 3, 1)]:
+        X = rng.normal(size=(N, D))
+        C = rng.normal(size=(K, D))
+        lab, gap, _, cnt, inertia = oracle.kmeans_step(X, C)
+        best, arg = np.inf, None
+        for z in itertools.product(range(K), repeat=N):
+            s = sum(float(np.sum((X[i] - C[z[i]]) ** 2)) for i in range(N))
+            if s < best:
+                best, arg = s, z
+        assert np.array_equal(lab, np.array(arg)) and abs(inertia - best) <= 1e-12 * best
+        assert (gap > 0).all() and cnt.sum() == N
+
+
+def test_kmeans_update_is_the_cluster_mean_and_minimises_its_sse():
+    """The new centroid of a cluster is the mean of its rows, and moving it
+    in any direction raises the cluster's sum of squared distances."""
+    rng = np.random.default_rng(12)
+    X = rng.normal(size=(400, 5)) + 3.0 * rng.integers(0, 4, size=(400, 1))
+    C = X[rng.choice(400, 6, replace=False)]
+    lab, _, newC, cnt, _ = oracle.kmeans_step(X, C)
+    for k in range(6):
+        rows = X[lab == k]
+        assert cnt[k] == len(rows)
+        if len(rows) == 0:
+            continue
+        np.testing.assert_allclose(newC[k], rows.mean(axis=0), rtol=1e-13, atol=1e-13)
+        sse = np.sum((rows - newC[k]) ** 2)
+        for _ in range(5):
+            dlt = 1e-3 * rng.normal(size=5)
+            assert np.sum((rows - newC[k] - dlt) ** 2) > sse
+
+
+def test_kmeans_is_the_shared_variance_limit_of_em():
+    """With equal weights and one shared spherical variance the GMM's most
+    responsible component is the nearest centroid for any variance, and as
+    the variance goes to zero the EM mean update becomes the k-means update
+    (the GMM oracle's code, not the k-means one, computes the right side)."""
+    rng = np.random.default_rng(13)
+    K, D = 5, 4
+    X = rng.normal(size=(600, D)) * 2.0
+    C = X[:K].copy()
+    lab, gap, newC, cnt, _ = oracle.kmeans_step(X, C)
+    w = np.full(K, 1.0 / K)
+    for s2 in (3.0, 0.3):
+        idx, _, _, _, _ = oracle.topm("spherical", X, w, C, np.full(K, s2), 1, 0.0)
+        assert np.array_equal(idx[:, 0], lab)
+    s2 = 1e-3 * gap.min()
+    out = oracle.fit_step("spherical", X, w, C, np.full(K, s2), eps=0.0)
+    keep = cnt > 0
+    np.testing.assert_allclose(out["mu"][0][keep], newC[keep], rtol=0, atol=1e-9)
+
+
+def test_kmeans_step_matches_sklearn_lloyd():
+    """One Lloyd iteration from given centroids equals sklearn's KMeans
+    (init = those centroids, one iteration) on its cluster centres."""
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(14)
+    X = rng.normal(size=(3000, 6)) + 4.0 * rng.integers(0, 5, size=(3000, 1)) * rng.normal(size=(1, 6))
+    C = X[rng.choice(3000, 8, replace=False)]
+    lab, _, newC, cnt, _ = oracle.kmeans_step(X, C)
+    assert (cnt > 0).all()
+    km = KMeans(n_clusters=8, init=C, n_init=1, max_iter=1, tol=0.0, algorithm="lloyd").fit(X)
+    np.testing.assert_allclose(newC, km.cluster_centers_, rtol=1e-10, atol=1e-10)
+
+
+def test_kmeans_empty_cluster_keeps_its_centroid():
+    rng = np.random.default_rng(15)
+    X = rng.normal(size=(200, 3))
+    C = np.vstack([X[:3], np.full((1, 3), 1e3)])
+    lab, _, newC, cnt, _ = oracle.kmeans_step(X, C)
+    assert cnt[3] == 0 and np.array_equal(newC[3], C[3]) and (lab != 3).all()
+
+
+def test_kmeans_bf16_rows_are_decoded_exactly():
+    rng = np.random.default_rng(16)
+    Xf = rng.normal(size=(300, 7)).astype(np.float32)
+    bits = (Xf.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 pattern will do
+    Xd = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    C = Xd[:4].copy()
+    a = oracle.kmeans_step((bits, "bf16"), C)
+    b = oracle.kmeans_step(Xd, C)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]) and a[4] == b[4]
