@@ -188,6 +188,30 @@ gmm_status gmm_ivf_lists(int64_t B, int64_t N, int32_t m, int32_t K, const int32
                          int64_t* offsets, int32_t* rows, float* list_resp, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* One k-means (Lloyd) iteration: the hard-assignment limit of EM ("ML0094
+ * GMM vs K-Means": k-means gives each point to the centroid at the smallest
+ * distance, the limit of a GMM with one shared spherical variance going to
+ * zero, where the posterior collapses to an argmax; Flash-GMM Section 4: the
+ * usual IVF coarse quantizer).  For each problem b of `data`:
+ *   labels (B,N) int32 out: argmin_k |x_i - c_k|^2 under the centroids that
+ *     enter the call, decided on float64 distances, ties to the lower k;
+ *   centroids (B,K,D) float32 in/out: replaced by the mean of the rows
+ *     labelled k (summed in float64, in increasing row order); a cluster with
+ *     no rows keeps its centroid;
+ *   counts (B,K) int64 out, nullable: rows per cluster;
+ *   inertia (B) float64 out, nullable: sum_i min_k |x_i - c_k|^2 under the
+ *     entering centroids.
+ * Same row types and shape window as gmm_predict_proba_topm with spherical
+ * components (float32 rows: K <= 256, any B; bf16 rows: B = 1, any K), and
+ * N < 2^31.  Workspace: gmm_kmeans_workspace_bytes (it grows with N: the
+ * labels' posting lists and a responsibility per row).  The assignment is the
+ * library's exact top-1 under equal weights and one shared variance, so its
+ * labels agree with a float64 nearest-centroid search wherever the two
+ * smallest distances differ by more than their rounding.  Deterministic. */
+size_t gmm_kmeans_workspace_bytes(const gmm_data* data, int32_t K);
+gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, int32_t* labels, int64_t* counts,
+                           double* inertia, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gmm_status_str(int32_t status);
 

@@ -10,6 +10,8 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
   gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
   gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
+  gmm_kmeans_workspace_bytes(X, K)            -> int
+  gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=None)
 
 The estimator calls (score_samples, predict, score, aic, bic, fit with
 restarts) are in soft_clustering_em_amd.estimator.
@@ -26,7 +28,8 @@ from ._abi import (COV_CODES, GmmError, GmmData, GmmOptions, GmmParams, GmmStats
                    OP_TOPM)
 
 __all__ = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
-           "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "new_stats", "GmmError",
+           "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
+           "gmm_kmeans_step", "new_stats", "GmmError",
            "cov_shape"]
 
 
@@ -182,3 +185,34 @@ def gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws
     _abi.check(_abi.lib().gmm_ivf_lists(int(B), int(N), int(m), int(K), _ptr(idx), _ptr(resp), _ptr(offsets),
                                         _ptr(rows), _ptr(list_resp), _ptr(ws), ws.numel(), _stream(stream)))
     return offsets, rows, list_resp
+
+
+def gmm_kmeans_workspace_bytes(X, K) -> int:
+    d = _data(X)
+    return int(_abi.lib().gmm_kmeans_workspace_bytes(ctypes.byref(d), int(K)))
+
+
+def gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=None, stream=None):
+    """One k-means (Lloyd) iteration; centroids ((K, D) or (B, K, D) float32)
+    are replaced by the cluster means.  Returns (labels (B, N) int32 under the
+    entering centroids, counts (B, K) int64, inertia (B,) float64); outputs
+    not given are allocated here."""
+    torch = _torch()
+    d = _data(X)
+    B, N = int(d.B), int(d.N)
+    K = centroids.shape[-2]
+    if centroids.dtype != torch.float32 or not centroids.is_contiguous() or centroids.numel() != B * K * d.D:
+        raise ValueError("centroids must be a contiguous float32 tensor of B*K*D elements")
+    dev = centroids.device
+    if labels is None:
+        labels = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, K, dtype=torch.int64, device=dev)
+    if inertia is None:
+        inertia = torch.empty(B, dtype=torch.float64, device=dev)
+    if ws is None:
+        n = gmm_kmeans_workspace_bytes(X, K)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _abi.check(_abi.lib().gmm_kmeans_step(ctypes.byref(d), int(K), _ptr(centroids), _ptr(labels), _ptr(counts),
+                                          _ptr(inertia), _ptr(ws), ws.numel(), _stream(stream)))
+    return labels, counts, inertia

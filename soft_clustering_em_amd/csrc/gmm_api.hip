@@ -373,6 +373,62 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   return GMM_OK;
 }
 
+// The top-m launch sequence of a planned call (N >= 1, workspace checked).
+static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
+                           int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, hipStream_t s) {
+  if (p.largek) {
+    LargeKArgs A = largek_args(p, data, params, ws);
+    A.topm = 1;
+    A.m = m;
+    A.thr = threshold;
+    A.idx = idx;
+    A.resp = resp;
+    A.count = count;
+    A.logp = logp;
+    hipError_t e = launch_largek_topm(p, A, params->weights, params->means, params->covars, s);
+    if (e != hipSuccess) return hip_fail(e, "large-K top-m launch");
+    return GMM_OK;
+  }
+  char* w = static_cast<char*>(ws);
+  float* W = reinterpret_cast<float*>(w + p.off_W);
+  double* prec = reinterpret_cast<double*>(w + p.off_prec);
+  double* c0 = reinterpret_cast<double*>(w + p.off_c0);
+  double* c = reinterpret_cast<double*>(w + p.off_c);
+  double* a = reinterpret_cast<double*>(w + p.off_a);
+  int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
+  int32_t* sharp = reinterpret_cast<int32_t*>(w + p.off_sharp);
+  hipError_t e = launch_prologue(p, params->weights, params->means, params->covars, W, prec, c0, c, a, flag, sharp, s);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  TopmArgs A;
+  A.x = data->x;
+  A.N = p.N;
+  A.D = p.D;
+  A.ld_x = p.ld_x;
+  A.stride_b = p.stride_b;
+  A.K = (int)p.K;
+  A.KP = p.KP;
+  A.NW = p.NW;
+  A.Gb = p.Gb;
+  A.ntiles = p.ntiles;
+  A.W = W;
+  A.c = c;
+  A.a = a;
+  A.mu = params->means;
+  A.prec = prec;
+  A.c0 = c0;
+  A.prec_stride = p.prec_stride;
+  A.m = m;
+  A.thr = threshold;
+  A.idx = idx;
+  A.resp = resp;
+  A.count = count;
+  A.logp = logp;
+  e = launch_topm(p, A, s);
+  if (e != hipSuccess) return hip_fail(e, "top-m launch");
+  return GMM_OK;
+}
+
+
 }  // namespace gmm
 
 using namespace gmm;
@@ -468,57 +524,7 @@ gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params
   st = check_ws(p, ws, ws_bytes);
   if (st != GMM_OK) return st;
   if (p.N == 0) return GMM_OK;
-  hipStream_t s = (hipStream_t)stream;
-  if (p.largek) {
-    LargeKArgs A = largek_args(p, data, params, ws);
-    A.topm = 1;
-    A.m = m;
-    A.thr = threshold;
-    A.idx = idx;
-    A.resp = resp;
-    A.count = count;
-    A.logp = logp;
-    hipError_t e = launch_largek_topm(p, A, params->weights, params->means, params->covars, s);
-    if (e != hipSuccess) return hip_fail(e, "large-K top-m launch");
-    return GMM_OK;
-  }
-  char* w = static_cast<char*>(ws);
-  float* W = reinterpret_cast<float*>(w + p.off_W);
-  double* prec = reinterpret_cast<double*>(w + p.off_prec);
-  double* c0 = reinterpret_cast<double*>(w + p.off_c0);
-  double* c = reinterpret_cast<double*>(w + p.off_c);
-  double* a = reinterpret_cast<double*>(w + p.off_a);
-  int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
-  int32_t* sharp = reinterpret_cast<int32_t*>(w + p.off_sharp);
-  hipError_t e = launch_prologue(p, params->weights, params->means, params->covars, W, prec, c0, c, a, flag, sharp, s);
-  if (e != hipSuccess) return hip_fail(e, "prologue launch");
-  TopmArgs A;
-  A.x = data->x;
-  A.N = p.N;
-  A.D = p.D;
-  A.ld_x = p.ld_x;
-  A.stride_b = p.stride_b;
-  A.K = (int)p.K;
-  A.KP = p.KP;
-  A.NW = p.NW;
-  A.Gb = p.Gb;
-  A.ntiles = p.ntiles;
-  A.W = W;
-  A.c = c;
-  A.a = a;
-  A.mu = params->means;
-  A.prec = prec;
-  A.c0 = c0;
-  A.prec_stride = p.prec_stride;
-  A.m = m;
-  A.thr = threshold;
-  A.idx = idx;
-  A.resp = resp;
-  A.count = count;
-  A.logp = logp;
-  e = launch_topm(p, A, s);
-  if (e != hipSuccess) return hip_fail(e, "top-m launch");
-  return GMM_OK;
+  return run_topm(p, data, params, m, threshold, idx, resp, count, logp, ws, (hipStream_t)stream);
 }
 
 // ---- IVF posting lists
@@ -570,6 +576,88 @@ gmm_status gmm_ivf_lists(int64_t B, int64_t N, int32_t m, int32_t K, const int32
   A.lresp = list_resp;
   hipError_t e = launch_ivf_lists(A, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "IVF list launch");
+  return GMM_OK;
+}
+
+// ---- k-means (Lloyd) iteration: exact top-1 under equal weights and one
+// shared variance, posting lists of the labels, list-ordered cluster means
+struct KmLayout {
+  Plan p;
+  size_t off_w, off_cv, off_resp, off_cnt, off_offsets, off_rows, off_ip, bytes;
+};
+
+static gmm_status kmeans_plan(const gmm_data* d, int32_t K, KmLayout* L) {
+  Plan p;
+  gmm_status st = make_plan(d, K, SPH, GMM_OP_TOPM, &p);
+  if (st != GMM_OK) return st;
+  st = ivf_check(p.B, p.N, 1, K);
+  if (st != GMM_OK) return st;
+  const size_t B = (size_t)p.B, N = (size_t)p.N, k = (size_t)K;
+  size_t o = align_up(p.ws_bytes);
+  L->off_w = o;       o = align_up(o + sizeof(float) * B * k);
+  L->off_cv = o;      o = align_up(o + sizeof(float) * B * k);
+  L->off_resp = o;    o = align_up(o + sizeof(float) * B * N);
+  L->off_cnt = o;     o = align_up(o + ivf_ws(p.B, p.N, K));
+  L->off_offsets = o; o = align_up(o + sizeof(int64_t) * B * (k + 1));
+  L->off_rows = o;    o = align_up(o + sizeof(int32_t) * B * N);
+  L->off_ip = o;      o = align_up(o + sizeof(double) * B * k);
+  L->bytes = o;
+  L->p = p;
+  return GMM_OK;
+}
+
+size_t gmm_kmeans_workspace_bytes(const gmm_data* data, int32_t K) {
+  KmLayout L;
+  if (kmeans_plan(data, K, &L) != GMM_OK) return 0;
+  return L.bytes;
+}
+
+gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, int32_t* labels, int64_t* counts,
+                           double* inertia, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KmLayout L;
+  gmm_status st = kmeans_plan(data, K, &L);
+  if (st != GMM_OK) return st;
+  const Plan& p = L.p;
+  if (!centroids) return fail(GMM_ERR_INVALID_ARG, "centroids must be non-NULL");
+  if (p.N > 0 && !labels) return fail(GMM_ERR_INVALID_ARG, "labels must be non-NULL");
+  if (!ws || ((uintptr_t)ws) % kAlign != 0) return fail(GMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.bytes) return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  float* wk = reinterpret_cast<float*>(w + L.off_w);
+  float* cv = reinterpret_cast<float*>(w + L.off_cv);
+  hipError_t e = launch_kmeans_params(p.B, K, (int)p.D, centroids, wk, cv, s);
+  if (e != hipSuccess) return hip_fail(e, "k-means parameter launch");
+  if (p.N > 0) {
+    gmm_params prm;
+    prm.K = K;
+    prm.cov = SPH;
+    prm.weights = wk;
+    prm.means = centroids;
+    prm.covars = cv;
+    st = run_topm(p, data, &prm, 1, 0.0f, labels, reinterpret_cast<float*>(w + L.off_resp), nullptr, nullptr, ws, s);
+    if (st != GMM_OK) return st;
+  }
+  IvfArgs A;
+  A.idx = labels;
+  A.resp = nullptr;
+  A.N = p.N;
+  A.B = (int)p.B;
+  A.m = 1;
+  A.K = K;
+  A.KB = 0;
+  while ((1 << A.KB) < K) ++A.KB;
+  A.nblk = (int)((p.N + kIvfBlock - 1) / kIvfBlock);
+  A.cnt = reinterpret_cast<int32_t*>(w + L.off_cnt);
+  A.offsets = reinterpret_cast<int64_t*>(w + L.off_offsets);
+  A.rows = reinterpret_cast<int32_t*>(w + L.off_rows);
+  A.lresp = nullptr;
+  e = launch_ivf_lists(A, s);
+  if (e != hipSuccess) return hip_fail(e, "k-means list launch");
+  e = launch_kmeans_update(data->x, data->dtype == GMM_DT_BF16 ? 1 : 0, p.B, p.N, p.ld_x, p.stride_b, K, (int)p.D,
+                           A.offsets, A.rows, centroids, counts, reinterpret_cast<double*>(w + L.off_ip), inertia, s);
+  if (e != hipSuccess) return hip_fail(e, "k-means update launch");
   return GMM_OK;
 }
 

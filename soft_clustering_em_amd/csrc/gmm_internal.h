@@ -164,6 +164,12 @@ struct IvfArgs {
 };
 hipError_t launch_ivf_lists(const IvfArgs& a, hipStream_t s);
 
+// k-means (Lloyd) iteration pieces (gmm_kmeans.hip)
+hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* w, float* cv, hipStream_t s);
+hipError_t launch_kmeans_update(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
+                                int D, const int64_t* offsets, const int32_t* rows, float* C, int64_t* counts,
+                                double* ip, double* inertia, hipStream_t s);
+
 // fused E-step + statistics (gmm_estep.hip)
 hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);

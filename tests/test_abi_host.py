@@ -241,3 +241,41 @@ def test_gaussian_mixture_host_checks():
         gm.predict(torch.zeros(10, 3))
     with pytest.raises(ValueError):
         gm.fit(torch.zeros(2, 10, 3))
+
+
+def test_kmeans_workspace_and_window():
+    """The k-means step takes the top-m window (float32 rows: K <= 256; bf16
+    rows: one problem, any K) and a workspace that grows with N (posting
+    lists and one responsibility per row); sizes are 256-byte multiples."""
+    L = _abi.lib()
+    for N, D, K in [(10_000, 8, 16), (1_000_000, 64, 256), (5003, 7, 1)]:
+        n = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(N, D)), K)
+        assert n > 0 and n % 256 == 0
+        assert n >= N * 8
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 257) == 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 0) == 0
+    bf = _data(100_000, 128, dtype=_abi.DT_BF16)
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(bf), 4096) > 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 64) == 0
+    a = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(100_000, 32)), 64)
+    b = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(200_000, 32)), 64)
+    assert b > a
+
+
+def test_kmeans_rejects_bad_arguments_before_the_device():
+    L = _abi.lib()
+    d = _data(1000, 16)
+    n = L.gmm_kmeans_workspace_bytes(ctypes.byref(d), 8)
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    cases = {
+        "centroids": ((ctypes.byref(d), 8, None, p, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "labels": ((ctypes.byref(d), 8, p, None, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "K": ((ctypes.byref(d), 0, p, p, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "K window": ((ctypes.byref(d), 300, p, p, None, None, ws, n, None), _abi.GMM_ERR_UNSUPPORTED),
+        "ws align": ((ctypes.byref(d), 8, p, p, None, None, ctypes.c_void_p(4100), n, None), _abi.GMM_ERR_WORKSPACE),
+        "ws size": ((ctypes.byref(d), 8, p, p, None, None, ws, n - 256, None), _abi.GMM_ERR_WORKSPACE),
+    }
+    for name, (args, want) in cases.items():
+        assert L.gmm_kmeans_step(*args) == want, name
+        assert L.gmm_last_error() != b"", name
