@@ -253,6 +253,24 @@ def main():
         lbytes = wl.B * wl.N * m * 4 * 3 + entries * 8
         res["topm"]["ivf_lists"] = {"ms": t_lists, "entries": entries, "entries_per_s": entries / (t_lists * 1e-3),
                                     "algorithmic_bytes": lbytes, "achieved_GBs": lbytes / (t_lists * 1e-3) / 1e9}
+        # the hard-assignment baseline: Lloyd steps from the fitted means
+        # (nearest centroid, posting lists of the labels, cluster means)
+        if wl.B == 1:
+            C = mu.clone().contiguous()
+            kws = torch.empty(g.gmm_kmeans_workspace_bytes(X, wl.K), dtype=torch.uint8, device=dev)
+            lab = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+            kcnt = torch.empty((wl.B, wl.K), dtype=torch.int64, device=dev)
+            kin = torch.empty((wl.B,), dtype=torch.float64, device=dev)
+            g.gmm_kmeans_step(X, C, lab, kcnt, kin, ws=kws)
+            reps = 3
+            e0.record()
+            for _ in range(reps):
+                g.gmm_kmeans_step(X, C, lab, kcnt, kin, ws=kws)
+            e1.record()
+            torch.cuda.synchronize()
+            t_km = e0.elapsed_time(e1) / reps
+            res["topm"]["kmeans_step"] = {"ms": t_km, "points_components_per_s": wl.N * wl.K / (t_km * 1e-3),
+                                          "inertia_last": float(kin[0].item())}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

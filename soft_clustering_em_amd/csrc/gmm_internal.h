@@ -116,6 +116,11 @@ struct LargeKArgs {
 };
 constexpr int64_t kLargeKTopmChunk = 1 << 18;
 constexpr int kLargeKMaxK = 16384;     // components of one large-K problem at most
+// A component is "sharp" on the large-K path when the terms of its expanded
+// log-score reach lambda (|mu|^2 + D sigma^2) > kLargeKSharp: with bf16
+// weights (two-term split) their rounding would reach about 1% of a
+// responsibility, so its scores near a row's top are recomputed in float64.
+constexpr double kLargeKSharp = 2.0e3;
 hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,
                               hipStream_t s);
 hipError_t launch_largek(const Plan& p, const LargeKArgs& a, const float* w, const float* mu, const float* cv,

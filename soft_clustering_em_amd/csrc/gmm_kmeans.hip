@@ -16,9 +16,11 @@
 // variance, so the labels come from the library's exact top-1 assignment
 // (float32 / bf16 MFMA scores, a candidate band, float64 rescoring, ties to
 // the lower index).  The variance only sets how wide the candidate band is in
-// distance units; kmeans_params_kernel takes 2^-12 max_k |c_k|^2, which keeps
-// the band at about 1% of the centroid scale and the score rounding far below
-// it.  The labels then go through the posting-list kernels (rows of each
+// distance units; kmeans_params_kernel takes 2^-10 max_k |c_k|^2: then
+// lambda (|c_k|^2 + D sigma^2) <= 2^10 + D, below the large-K path's sharp
+// threshold for every D it takes, so no component needs the direct-difference
+// rescoring there, and the candidate band is a few percent of the centroid
+// scale.  The labels then go through the posting-list kernels (rows of each
 // cluster in increasing order), and kmeans_update_kernel sums each cluster's
 // rows in that fixed order in float64: no atomics, the same bits every run.
 #include "gmm_internal.h"
@@ -31,7 +33,10 @@ namespace gmm {
 
 namespace {
 
-// Per problem: w_k = 1/K and the shared variance 2^-12 max(max_k |c_k|^2, 1e-20).
+constexpr int kVarShift = 10;  // shared variance = 2^-kVarShift max_k |c_k|^2
+static_assert((1 << kVarShift) + 128 < kLargeKSharp, "k-means components must stay below the sharp threshold");
+
+// Per problem: w_k = 1/K and the shared variance 2^-kVarShift max(max_k |c_k|^2, 1e-20).
 __global__ void __launch_bounds__(256) kmeans_params_kernel(int K, int D, const float* __restrict__ C,
                                                             float* __restrict__ w, float* __restrict__ cv) {
   __shared__ double red[256];
@@ -52,7 +57,7 @@ __global__ void __launch_bounds__(256) kmeans_params_kernel(int K, int D, const 
     if (t < h) red[t] = fmax(red[t], red[t + h]);
     __syncthreads();
   }
-  const float s2 = (float)(fmax(red[0], 1e-20) * 0x1p-12);
+  const float s2 = (float)ldexp(fmax(red[0], 1e-20), -kVarShift);
   const float wk = 1.0f / (float)K;
   for (int k = t; k < K; k += 256) {
     w[(size_t)b * K + k] = wk;

@@ -61,10 +61,7 @@ constexpr int KSC = kLargeKSlice / 2;  // components per workgroup in pass C (12
 constexpr int LNW = 8;                 // waves per workgroup
 constexpr int LT = 32;                 // rows per tile
 constexpr int LRS = 136;               // LDS row stride of the row tile, in bf16 (272 bytes)
-// A component is "sharp" when the terms of its expanded log-score reach
-// lambda (|mu|^2 + D sigma^2) > kSharpLowp: with bf16 weights (two-term
-// split) their rounding would reach about 1% of a responsibility.
-constexpr double kSharpLowp = 2.0e3;
+constexpr double kSharpLowp = kLargeKSharp;
 // responsibilities at or above this go to the "big" class of the statistics
 // MFMA; r >= 0, so the class test compares bf16 bit patterns
 constexpr float kBigR = 0x1p-8f;

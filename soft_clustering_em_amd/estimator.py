@@ -17,6 +17,7 @@ rule and the AIC/BIC arithmetic on B returned scalars.
   aic(...), bic(...)                            -> (B,) float64
   fit(X, K, cov, ...)                           -> FitResult (the restart with the best mean LL)
   GaussianMixture(n_components, covariance_type, ...)  the same calls as a scikit-learn style class
+  KMeans(n_clusters, ...)                       Lloyd iterations over gmm_kmeans_step (the hard limit)
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import gmm_estep_stats, gmm_fit_step, gmm_predict_proba_topm, new_stats
+from . import gmm_estep_stats, gmm_fit_step, gmm_kmeans_step, gmm_predict_proba_topm, new_stats
 
 
 def _torch():
@@ -176,9 +177,12 @@ class GaussianMixture:
     the GPU as float32 tensors.  Every computation runs in the HIP library."""
 
     def __init__(self, n_components, covariance_type="full", max_iter=100, tol=1e-3, reg_covar=1e-6, n_init=1,
-                 random_state=0, weights_init=None, means_init=None, covariances_init=None):
+                 random_state=0, weights_init=None, means_init=None, covariances_init=None, init_params="random"):
         if covariance_type not in ("spherical", "diag", "tied", "full"):
             raise ValueError(f"unknown covariance_type {covariance_type!r}")
+        if init_params not in ("random", "kmeans"):
+            raise ValueError(f"unknown init_params {init_params!r}")
+        self.init_params = init_params
         self.n_components = int(n_components)
         self.covariance_type = covariance_type
         self.max_iter = int(max_iter)
@@ -191,11 +195,23 @@ class GaussianMixture:
     def _init(self, X):
         given = (self.weights_init, self.means_init, self.covariances_init)
         if all(t is None for t in given):
-            return None
+            return self._kmeans_init(X) if self.init_params == "kmeans" else None
         if any(t is None for t in given):
             raise ValueError("weights_init, means_init and covariances_init are given together")
         torch = _torch()
         return tuple(torch.as_tensor(t, dtype=torch.float32, device=X.device).contiguous() for t in given)
+
+    def _kmeans_init(self, X):
+        """Means from Lloyd iterations (KMeans with this seed), weights from the
+        cluster sizes (at least one row each), and the covariance of
+        random_init (the data's variance) for every component."""
+        torch = _torch()
+        km = KMeans(self.n_components, max_iter=20, random_state=self.random_state).fit(X)
+        gen = torch.Generator(device="cpu").manual_seed(int(self.random_state or 0))
+        _, _, cv = random_init(X, self.n_components, self.covariance_type, gen)
+        cnt = km.counts_.to(torch.float64).clamp_min(1.0)
+        w = (cnt / cnt.sum()).to(torch.float32).contiguous()
+        return w, km.cluster_centers_.clone().contiguous(), cv
 
     def fit(self, X):
         if X.dim() != 2:
@@ -244,3 +260,64 @@ class GaussianMixture:
         count = torch.empty(N, dtype=torch.int32, device=X.device)
         gmm_predict_proba_topm(X, *self._theta(), m, threshold, idx, resp, count=count)
         return idx, resp, count
+
+
+class KMeans:
+    """k-means by Lloyd iterations, each one gmm_kmeans_step (nearest
+    centroid on float64 distances, cluster means summed in float64): the
+    hard-assignment, shared-variance-to-zero limit of the GMM, and the usual
+    IVF coarse quantizer the GMM replaces.  X is one problem, (N, D) float32
+    or bfloat16, on the GPU.  Starts from K distinct rows drawn with the seed
+    (or init, (K, D)); stops when the inertia falls by less than tol of
+    itself, or after max_iter steps.  Fitted state (scikit-learn names):
+    cluster_centers_ (K, D) float32, labels_ (N,) int32 and inertia_ under
+    the final centres, counts_ (K,) int64, n_iter_, inertia_history_ (the
+    inertia under the centres entering each step)."""
+
+    def __init__(self, n_clusters, max_iter=100, tol=1e-4, random_state=0, init=None):
+        self.n_clusters = int(n_clusters)
+        self.max_iter = int(max_iter)
+        self.tol = float(tol)
+        self.random_state = random_state
+        self.init = init
+
+    def _start(self, X):
+        torch = _torch()
+        N, K = X.shape[0], self.n_clusters
+        if self.init is not None:
+            return torch.as_tensor(self.init, dtype=torch.float32, device=X.device).clone().contiguous()
+        if K > N:
+            raise ValueError("n_clusters exceeds the number of rows")
+        gen = torch.Generator(device="cpu").manual_seed(int(self.random_state or 0))
+        sel = torch.randperm(N, generator=gen)[:K].to(X.device)
+        return X.index_select(0, sel).float().contiguous()
+
+    def fit(self, X):
+        if X.dim() != 2:
+            raise ValueError("X is (N, D)")
+        C = self._start(X)
+        hist, it = [], 0
+        for it in range(1, self.max_iter + 1):
+            _, counts, inertia = gmm_kmeans_step(X, C)
+            cur = float(inertia[0].item())
+            hist.append(cur)
+            if len(hist) > 1 and hist[-2] - cur <= self.tol * hist[-2]:
+                break
+        self.cluster_centers_ = C
+        self.n_iter_ = it
+        self.inertia_history_ = hist
+        self.labels_, self.counts_, self.inertia_ = self._assign(X)
+        return self
+
+    def _assign(self, X):
+        if not hasattr(self, "cluster_centers_"):
+            raise RuntimeError("call fit first")
+        labels, counts, inertia = gmm_kmeans_step(X, self.cluster_centers_.clone())
+        return labels[0], counts[0], float(inertia[0].item())
+
+    def predict(self, X):
+        """The nearest centre of every row (ties: lower index), (N,) int32."""
+        return self._assign(X)[0]
+
+    def fit_predict(self, X):
+        return self.fit(X).labels_

@@ -241,6 +241,13 @@ def test_gaussian_mixture_host_checks():
         gm.predict(torch.zeros(10, 3))
     with pytest.raises(ValueError):
         gm.fit(torch.zeros(2, 10, 3))
+    with pytest.raises(ValueError):
+        GaussianMixture(4, init_params="kmeans++")
+    from soft_clustering_em_amd.estimator import KMeans
+    with pytest.raises(RuntimeError):
+        KMeans(3).predict(torch.zeros(10, 3))
+    with pytest.raises(ValueError):
+        KMeans(20)._start(torch.zeros(10, 3))
 
 
 def test_kmeans_workspace_and_window():
