@@ -230,3 +230,57 @@ def test_topm_short_chunks(torch_cuda):
     ws = torch.empty(full, dtype=torch.uint8, device="cuda")
     check_topm_bf16(torch, wl.X, w, mu, cv, 4, 0.1, "ivf K=512 chunks of about 1000 rows",
                     ws=ws[:full - 4000 * per_row])
+
+
+def test_full_size_ivf_step_properties(torch_cuda):
+    """The full IVF workload (10,000,000 bf16 rows, D = 128, K = 4096) at its
+    initial parameters, in the launch configuration the bench times (2^20-row
+    chunks for the E-step, 2^18 for the top-m).  What holds at any size:
+    sum_k N_k = N and sum_k sum_i r_ik x_i = sum_i x_i (each row's
+    responsibilities sum to one, up to their single bf16 rounding, within
+    2^-9); the E-step's log-likelihood equals the
+    sum of the top-m path's per-row log p (two different code paths: slice
+    maxima and sums of approximate scores, against float64 rescoring); and on
+    2,000 sampled rows the top-4 assignment, its responsibilities and log p
+    match the oracle row by row."""
+    import soft_clustering_em_amd as g
+    torch = torch_cuda
+    wl = synth.ivf_bf16()
+    N, D, K, m = wl.N, wl.D, wl.K, 4
+    X = bf16_tensor(torch, wl.X)
+    w, mu, cv = (torch.from_numpy(a.copy()).cuda() for a in (wl.w0, wl.mu0, wl.cv0))
+    st = g.new_stats(1, K, D, "spherical", "cuda")
+    g.gmm_estep_stats(X, w, mu, cv, "spherical", st)
+    colsum = X.float().sum(dim=1, dtype=torch.float64)[0]
+    idx = torch.empty(1, N, m, dtype=torch.int32, device="cuda")
+    resp = torch.empty(1, N, m, dtype=torch.float32, device="cuda")
+    cnt = torch.empty(1, N, dtype=torch.int32, device="cuda")
+    logp = torch.empty(1, N, dtype=torch.float32, device="cuda")
+    g.gmm_predict_proba_topm(X, w, mu, cv, "spherical", m, 0.1, idx, resp, cnt, logp)
+    torch.cuda.synchronize()
+    nk = st["nk"][0].cpu().numpy()
+    sx = st["sx"][0].cpu().numpy()
+    ll = float(st["loglik"][0].item())
+    ll_rows = float(logp[0].double().sum().item())
+    cs = colsum.cpu().numpy()
+    absx = float(X.float().abs().sum(dtype=torch.float64).item())
+    print(f"full size: sum N_k / N - 1 = {nk.sum() / N - 1:.2e}, LL {ll:.6e} vs rows {ll_rows:.6e}, "
+          f"max |sum_k S1 - sum x| = {np.abs(sx.sum(axis=0) - cs).max():.3e} (sum |x| = {absx:.3e})", flush=True)
+    # each r is rounded once to bf16 (relative error <= 2^-9), so a row's
+    # responsibilities sum to one within 2^-9; the rounding of a dominant
+    # r = 1 - eps up to 1.0 makes the N_k sum lean above N
+    assert abs(nk.sum() / N - 1) <= 2.0 ** -9
+    assert np.abs(sx.sum(axis=0) - cs).max() <= 2.0 ** -9 * absx
+    assert abs(ll - ll_rows) <= 1e-5 * abs(ll)
+    rng = np.random.default_rng(4)
+    pick = np.sort(rng.choice(N, 2000, replace=False))
+    gi, gr, gc, gl = (t[0].cpu().numpy()[pick] for t in (idx, resp, cnt, logp))
+    oi, orr, oc, ol, om = oracle.topm("spherical", (wl.X[0][pick], "bf16"), wl.w0[0].astype(np.float64),
+                                      wl.mu0[0].astype(np.float64), wl.cv0[0].astype(np.float64), m,
+                                      float(np.float32(0.1)))
+    ok = om > 1e-6
+    assert np.array_equal(gi[ok], oi[ok]) and np.array_equal(gc[ok], oc[ok])
+    kept = oi >= 0
+    np.testing.assert_allclose(gr[ok[:, None] & kept], orr[ok[:, None] & kept], rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(gl, ol, rtol=2e-6, atol=1e-5)
+    print(f"sampled rows: {int(ok.sum())} of 2000 decided, mean kept {gc.mean():.2f}", flush=True)
