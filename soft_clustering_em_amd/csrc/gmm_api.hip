@@ -159,15 +159,6 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.G = feat_G(cov, q.DP);
   q.FS = feat_stride(std::max(q.F, q.G));
   q.PR = 2 + q.G;
-  if ((K + 15) / 16 <= kMaxWaves) {
-    q.KW = 16;
-  } else if ((K + 31) / 32 <= kMaxWaves) {
-    q.KW = 32;
-  } else {
-    return fail(GMM_ERR_UNSUPPORTED, "K=%d is above the single-pass window (<= %d)", K, 32 * kMaxWaves);
-  }
-  q.NW = (K + q.KW - 1) / q.KW;
-  q.KP = q.KW * q.NW;
   const bool direct_ok =
       (((uintptr_t)d->x) % 16 == 0) && (q.ld_x == q.D) && (q.D % 4 == 0) && (q.stride_b % 4 == 0);
   auto lds_for = [&](int T, int nraw) {
@@ -175,30 +166,49 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     return sizeof(float) * ((size_t)q.KP * q.F + (size_t)T * q.FS + (size_t)nraw * T * q.DP + 2 * (size_t)T +
                             2 * (size_t)q.NW * T + q.F);
   };
-  q.T = 0;
-  if (op == GMM_OP_TOPM) {
-    if (K > kTopmMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m supports K <= %d", kTopmMaxK);
-    const size_t T = kTopmRows, C = kTopmCap;
-    q.T = (int)T;
-    q.direct = false;
-    q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F) +
-            sizeof(double) * (T + (size_t)q.NW * T + T * C);
-    if (q.lds > kLdsBytes) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K,
-                                       (long long)d->D);
+  // Components per wave: 16 gives more waves per workgroup; from K = 64 on,
+  // spherical and diagonal E-steps take 32 where a tile fits, so each feature
+  // operand read from LDS feeds two MFMA column tiles (diag_batched: 1.65 ->
+  // 1.34 ms per E-step).  The top-m tiling keeps 16 first.
+  int kws[2] = {16, 32};
+  if (op != GMM_OP_TOPM && K >= 64 && (cov == SPH || cov == DIAG)) {
+    kws[0] = 32;
+    kws[1] = 16;
   }
-  // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
-  for (int nraw : {2, 1}) {
-    if (q.T) break;
-    if (nraw == 2 && !direct_ok) continue;
-    for (int T : {64, 32, 16}) {
-      if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
-        q.T = T;
-        q.direct = nraw == 2;
-        break;
+  q.T = 0;
+  bool waves_ok = false;
+  for (int kw : kws) {
+    if ((K + kw - 1) / kw > kMaxWaves) continue;
+    waves_ok = true;
+    q.KW = kw;
+    q.NW = (K + q.KW - 1) / q.KW;
+    q.KP = q.KW * q.NW;
+    if (op == GMM_OP_TOPM) {
+      if (K > kTopmMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m supports K <= %d", kTopmMaxK);
+      const size_t T = kTopmRows, C = kTopmCap;
+      q.T = (int)T;
+      q.direct = false;
+      q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F) +
+              sizeof(double) * (T + (size_t)q.NW * T + T * C);
+      if (q.lds > kLdsBytes)
+        return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K, (long long)d->D);
+      break;
+    }
+    // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
+    for (int nraw : {2, 1}) {
+      if (nraw == 2 && !direct_ok) continue;
+      for (int T : {64, 32, 16}) {
+        if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
+          q.T = T;
+          q.direct = nraw == 2;
+          break;
+        }
       }
+      if (q.T) break;
     }
     if (q.T) break;
   }
+  if (!waves_ok) return fail(GMM_ERR_UNSUPPORTED, "K=%d is above the single-pass window (<= %d)", K, 32 * kMaxWaves);
   if (!q.T) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld does not fit in LDS", K, (long long)d->D);
   if (op != GMM_OP_TOPM) q.lds = lds_for(q.T, q.direct ? 2 : 1);
   q.ntiles = (q.N + q.T - 1) / q.T;
