@@ -81,6 +81,13 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_a
 // The 16-byte piece of a row tile that thread j loads: row j / 16, dims
 // 8 (j % 16) .. +7 -- a row's 256 bytes come from 16 consecutive lanes, so a
 // wave's load touches 8 cache lines.
+// Row r = 16 b + 8 h + j of a tile sits in LDS slot 16 b + 2 j + h.  With
+// slots 68 dwords apart (4 banks), the 16-byte logit reads of a 16-row block
+// (16 lanes, one row each) still cover all 64 banks once, and each half-wave
+// of pass C's transposing reads -- 8 rows, 32 bytes each -- now takes every
+// other slot, 8 banks apart: no two rows share a bank (next-slot rows would).
+__device__ __forceinline__ int tile_slot(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+
 __device__ __forceinline__ void piece_of(int j, int& r, int& c8) {
   r = j / 16;
   c8 = (j % 16) * 8;
@@ -144,7 +151,7 @@ __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = e < pc.nv ? v[e] : (unsigned short)0;
   }
-  *reinterpret_cast<u16x8*>(rows + r * LRS + c8) = v;
+  *reinterpret_cast<u16x8*>(rows + tile_slot(r) * LRS + c8) = v;
   const bool live = row0 + j < A.N;  // threads j < LT: row j of the tile
   if (j < LT) ls[j] = live ? pc.ls : (STATS ? INFINITY : 0.f);
   if constexpr (STATS) {
@@ -356,7 +363,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       bf16x8 av[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        av[rb] = *reinterpret_cast<const bf16x8*>(rows + (rb * 16 + (lane & 15)) * LRS + ks * 32 + 8 * (lane >> 4));
+        av[rb] = *reinterpret_cast<const bf16x8*>(rows + tile_slot(rb * 16 + (lane & 15)) * LRS + ks * 32 +
+                                                  8 * (lane >> 4));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -410,7 +418,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
               if (eb[nt][v] > 0.f && row0 + p < nrows && lg[rb][nt][v] + eb[nt][v] * xs + e0[nt][v] >= ref - 60.f) {
                 const int k = comp_of(nt, v);
                 lg[rb][nt][v] =
-                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + p * LRS);
+                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + tile_slot(p) * LRS);
               }
             }
         }
@@ -474,7 +482,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         for (int nt = 0; nt < NT; ++nt) {
           if (eb[nt][0] > 0.f && row0 + p < nrows && lg[q][nt] + eb[nt][0] * xs + e0[nt][0] >= ref[q] - 60.f) {
             const int k = comp_of(nt, 0);
-            lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + p * LRS);
+            lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + tile_slot(p) * LRS);
           }
         }
       }
@@ -553,7 +561,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       for (int mt = 0; mt < (STATS ? GM : 1); ++mt) {
         // lane 16 g + i: features 16 mt + i of rows 4 g + e (read 1) and
         // 16 + 4 g + e (read 2), e = 0..3 -- k = 8 g + e and 8 g + 4 + e
-        const unsigned short* src = rows + (lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
+        // (slot(16 + r) = 16 + slot(r): read 2 is 16 slots further)
+        const unsigned short* src = rows + tile_slot(lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * LRS));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
