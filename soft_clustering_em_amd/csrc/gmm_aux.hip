@@ -95,17 +95,37 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     for (int d = tid; d < D; d += blockDim.x)
       sm_v[d] = (cov == SPH) ? 1.0 / (double)cv[(size_t)b * K + k] : 1.0 / (double)cv[((size_t)b * K + k) * D + d];
     __syncthreads();
+    // per-dimension terms on the block's threads (one log per variance;
+    // spherical: one log in all), then summed in thread order by thread 0
+    {
+      double ld = 0.0, qd = 0.0, sd = 0.0, lm = 0.0;
+      int bad = 0;
+      for (int d = tid; d < D; d += blockDim.x) {
+        const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
+        if (!(v > 0.0) || isinf(v)) bad = 1;
+        if (cov == DIAG) ld += log(v);
+        qd += sm_v[d] * sm_mu[d] * sm_mu[d];
+        lm = fmax(lm, sm_v[d]);
+        sd += sm_mu[d] * sm_mu[d] + v;
+      }
+      sm_S[tid] = ld;
+      sm_L[tid] = qd;
+      sm_Li[tid] = sd;
+      sm_P[tid] = lm;
+      sm_red[tid] = bad;
+    }
+    __syncthreads();
     if (tid == 0) {
       bool ok = true;
       double logdet = 0.0, quad = 0.0, lmax = 0.0, scale = 0.0;
-      for (int d = 0; d < D; ++d) {
-        const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
-        if (!(v > 0.0) || isinf(v)) ok = false;
-        logdet += log(v);
-        quad += sm_v[d] * sm_mu[d] * sm_mu[d];
-        lmax = fmax(lmax, sm_v[d]);
-        scale += sm_mu[d] * sm_mu[d] + v;
+      for (int t = 0; t < (int)blockDim.x; ++t) {
+        logdet += sm_S[t];
+        quad += sm_L[t];
+        scale += sm_Li[t];
+        lmax = fmax(lmax, sm_P[t]);
+        if (sm_red[t] != 0.0) ok = false;
       }
+      if (cov == SPH) logdet = D * log((double)cv[(size_t)b * K + k]);
       sm_ok = ok;
       sm_c = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e : -INFINITY;
       c0[(size_t)b * KP + k] = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e : -INFINITY;
