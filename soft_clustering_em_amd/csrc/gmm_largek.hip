@@ -724,15 +724,17 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // components of the slice in 32-component chunks with a running per-row max
 // and a per-lane running sum rescaled to it, so a row's (max, sum) for the
 // slice needs no other wave and the waves never wait for each other.
+template <int RB>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   constexpr int DP = 128, KSTEP = DP / 32, NCH = KSA / 32;
+  constexpr int PT = 16 * RB;  // rows per tile
   constexpr int WFRAG = (KSA / 16) * 2 * KSTEP * 64;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int slice = blockIdx.x / A.G;
   const int g = blockIdx.x % A.G;
   const int64_t nrows = A.N;
-  const int64_t ntiles = (nrows + LT - 1) / LT;
+  const int64_t ntiles = (nrows + PT - 1) / PT;
 
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
@@ -755,10 +757,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   any_sharp = __builtin_amdgcn_ballot_w64(any_sharp) != 0;
 
   const unsigned short* xb = reinterpret_cast<const unsigned short*>(A.x);
-  auto load_rows = [&](int64_t t, bf16x8 (&rv)[2][KSTEP]) {
+  auto load_rows = [&](int64_t t, bf16x8 (&rv)[RB][KSTEP]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      int64_t row = t * LT + rb * 16 + (lane & 15);
+    for (int rb = 0; rb < RB; ++rb) {
+      int64_t row = t * PT + rb * 16 + (lane & 15);
       row = row < nrows ? row : nrows - 1;
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
@@ -766,20 +768,20 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     }
   };
   int64_t t = g + (int64_t)A.G * wv;
-  bf16x8 nxt[2][KSTEP];
+  bf16x8 nxt[RB][KSTEP];
   if (t < ntiles) load_rows(t, nxt);
   for (; t < ntiles; t += (int64_t)A.G * LNW) {
-    bf16x8 rv[2][KSTEP];
+    bf16x8 rv[RB][KSTEP];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks) rv[rb][ks] = nxt[rb][ks];
     if (t + (int64_t)A.G * LNW < ntiles) load_rows(t + (int64_t)A.G * LNW, nxt);
     // |x|^2 of the lane's two rows: exact (float64) in slice 0, which stores
     // it for pass C and the top-m rescoring; float32 elsewhere
-    float xs[2];
+    float xs[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       if (slice == 0) {
         double q = 0.0;
 #pragma unroll
@@ -791,7 +793,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           }
         q = rows4_sum_f64(q);
         xs[rb] = (float)q;
-        const int64_t row = t * LT + rb * 16 + lane;
+        const int64_t row = t * PT + rb * 16 + lane;
         if (lane < 16 && row < nrows) A.xsq[row] = q;
       } else {
         float q = 0.f;
@@ -805,11 +807,17 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         xs[rb] = rows4_sum(q);
       }
     }
-    float M[2] = {kDead, kDead}, Sl[2] = {0.f, 0.f}, R[2] = {kDead, kDead};
+    float M[RB], Sl[RB], R[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      M[rb] = kDead;
+      Sl[rb] = 0.f;
+      R[rb] = kDead;
+    }
 #pragma unroll 1
     for (int cc = 0; cc < NCH; ++cc) {
       // components cc 32 + nt 16 + 4 (lane / 16) + v of the slice
-      floatx4 acc[2][2];
+      floatx4 acc[RB][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -817,7 +825,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
           const float c = cst[kl], a = cst[KSA + kl];
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) acc[rb][nt][v] = fmaf(a, xs[rb], c);
+          for (int rb = 0; rb < RB; ++rb) acc[rb][nt][v] = fmaf(a, xs[rb], c);
         }
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
@@ -827,14 +835,14 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           for (int nt = 0; nt < 2; ++nt) {
             const bf16x8 bw = Wl[(((cc * 2 + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
               acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, rv[rb][ks], acc[rb][nt], 0, 0, 0);
           }
       if (any_sharp) {
         // sharp components: scores that may come within 60 (log2 units) of the
         // best other score of the row seen so far in the slice, again exactly
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
           float r = R[rb];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
@@ -842,7 +850,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             for (int v = 0; v < 4; ++v)
               if (!(cst[2 * KSA + cc * 32 + nt * 16 + 4 * (lane >> 4) + v] > 0.f)) r = fmaxf(r, acc[rb][nt][v]);
           R[rb] = rows4_max(r);
-          const int64_t row = t * LT + rb * 16 + (lane & 15);
+          const int64_t row = t * PT + rb * 16 + (lane & 15);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -859,7 +867,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       }
       // running max per row, and the lane's sum rescaled to it
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         float cm = acc[rb][0][0];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -877,13 +885,17 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const float S = rows4_sum(Sl[rb]);
-      const int64_t row = t * LT + rb * 16 + lane;
+      const int64_t row = t * PT + rb * 16 + lane;
       if (lane < 16 && row < nrows) A.P[(size_t)row * A.S + slice] = float2{M[rb], S};
     }
   }
 }
+
+// 16-row blocks per tile of the barrier-free pass A: every weight fragment
+// read from LDS feeds kPassARB MFMAs
+constexpr int kPassARB = 4;
 
 size_t largek_pass_a_lds_bytes() { return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + 4 * KSA * sizeof(float); }
 
@@ -999,7 +1011,7 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kC, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
     attr_set = true;
   }
@@ -1013,7 +1025,7 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
     if (ac.N > 0) {
       ac.G = p.GbA;
       if (p.D == 128 && ac.vec16)
-        hipLaunchKernelGGL(largek_pass_a_kernel, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+        hipLaunchKernelGGL(largek_pass_a_kernel<kPassARB>, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
                            largek_pass_a_lds_bytes(), s, ac);
       else
         hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
@@ -1272,7 +1284,7 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kT, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
     attr_set = true;
   }
@@ -1288,7 +1300,7 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     ac.logp = a.logp ? a.logp + r0 : nullptr;
     ac.G = p.GbA;
     if (p.D == 128 && ac.vec16)
-      hipLaunchKernelGGL(largek_pass_a_kernel, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+      hipLaunchKernelGGL(largek_pass_a_kernel<kPassARB>, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
                          largek_pass_a_lds_bytes(), s, ac);
     else
       hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
