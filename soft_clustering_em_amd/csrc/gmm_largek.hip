@@ -1057,6 +1057,11 @@ constexpr int kBatch = 512;                       // scores per batch
 constexpr int kSlots = kTopmMaxM + kBatch;        // running best m, then the batch
 constexpr int kPer = (kSlots + 63) / 64;          // slots per lane in the selection
 constexpr int kMaskSlots = kLargeKMaxK / 32 / 64;  // mask words per lane at the largest K
+// rows (one wave each) per workgroup of the rescoring kernel: one, so that a
+// row with many candidates holds no other row's slot on the CU (4 rows per
+// workgroup: 141.6 ms per IVF top-m pass; 1 row: 121.0 ms; 1 row at four
+// waves per SIMD, registers capped at 128: 117.7 ms)
+constexpr int kFinalRows = 1;
 
 // 2^d for d <= 0 to about 1e-7 relative: float exp2 of the float part and a
 // first-order correction for the rest of d
@@ -1077,15 +1082,15 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
   return x - v;
 }
 
-__global__ void __launch_bounds__(256) largek_topm_final_kernel(LargeKArgs A) {
+__global__ void __launch_bounds__(64 * kFinalRows, 4) largek_topm_final_kernel(LargeKArgs A) {
   constexpr double LN2 = 0.69314718055994530942;
-  __shared__ double sl[4][kSlots];
-  __shared__ int skk[4][kSlots];
-  __shared__ unsigned short slist[4][kBatch];
+  __shared__ double sl[kFinalRows][kSlots];
+  __shared__ int skk[kFinalRows][kSlots];
+  __shared__ unsigned short slist[kFinalRows][kBatch];
   const int lane = threadIdx.x & 63;
   const int wq = threadIdx.x >> 6;
   const int grp = lane >> 4, li = lane & 15;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wq;
+  const int64_t row = (int64_t)blockIdx.x * kFinalRows + wq;
   if (row >= A.N) return;  // uniform across the wave; the block has no barrier
   double* L = sl[wq];
   int* KK = skk[wq];
@@ -1309,7 +1314,8 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(largek_topm_final_kernel, dim3((unsigned)((ac.N + 3) / 4)), dim3(256), 0, s, ac);
+    hipLaunchKernelGGL(largek_topm_final_kernel, dim3((unsigned)((ac.N + kFinalRows - 1) / kFinalRows)),
+                       dim3(64 * kFinalRows), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
