@@ -51,6 +51,13 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+__device__ __forceinline__ uint32_t rows4_or(uint32_t v) {
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] | b[1];
+}
+
 __device__ __forceinline__ double rows4_sum_f64(double v) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(v);
   auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);

@@ -724,10 +724,16 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // components of the slice in 32-component chunks with a running per-row max
 // and a per-lane running sum rescaled to it, so a row's (max, sum) for the
 // slice needs no other wave and the waves never wait for each other.
-template <int RB>
+// MODE 0: per-row maximum and sum of 2^(l - max) over the slice (pass A of a
+// fit step); 1: candidate marks and below-band mass against the row maximum
+// (pass T of the top-m); 2: the maximum alone (pass A of the top-m, whose
+// last kernel needs only the row maxima and pass T's masses)
+template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
+  constexpr bool MARK = MODE == 1;
   constexpr int DP = 128, KSTEP = DP / 32, NCH = KSA / 32;
   constexpr int PT = 16 * RB;  // rows per tile
+  constexpr int NCST = MARK ? 6 : 4;  // per-component constants in LDS
   constexpr int WFRAG = (KSA / 16) * 2 * KSTEP * 64;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -738,7 +744,9 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
-  float* cst = reinterpret_cast<float*>(Wl + WFRAG);  // c, a, eb, e0 of the slice's components
+  float* cst = reinterpret_cast<float*>(Wl + WFRAG);  // c, a, eb, e0 (and ea, ea0) of the slice's components
+  // pass T: each wave's candidate words of its tile's rows, (row, chunk)
+  uint32_t* wbuf = reinterpret_cast<uint32_t*>(cst + NCST * KSA) + (threadIdx.x >> 6) * PT * NCH;
   {
     const uint4* src = reinterpret_cast<const uint4*>(A.W) + (size_t)slice * WFRAG;
     uint4* dst = reinterpret_cast<uint4*>(Wl);
@@ -749,12 +757,29 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       cst[KSA + i] = (float)A.a[k];
       cst[2 * KSA + i] = A.esh[2 * k];
       cst[3 * KSA + i] = A.esh[2 * k + 1];
+      if constexpr (MARK) {
+        cst[4 * KSA + i] = A.eall[2 * k];
+        cst[5 * KSA + i] = A.eall[2 * k + 1];
+      }
     }
   }
   __syncthreads();
   bool any_sharp = false;
   for (int i = lane; i < KSA; i += 64) any_sharp = any_sharp || cst[2 * KSA + i] > 0.f;
   any_sharp = __builtin_amdgcn_ballot_w64(any_sharp) != 0;
+  // pass T: the largest error bound of the slice's components (slope in |x|^2,
+  // offset), so that a row's candidate threshold is one number: the band it
+  // gives contains every component's own band, a superset that the exact
+  // rescoring sorts out
+  float eam = 0.f, ea0m = 0.f;
+  if constexpr (MARK) {
+    for (int i = lane; i < KSA; i += 64) {
+      eam = fmaxf(eam, cst[4 * KSA + i]);
+      ea0m = fmaxf(ea0m, cst[5 * KSA + i]);
+    }
+    eam = (float)wave_max((double)eam);
+    ea0m = (float)wave_max((double)ea0m);
+  }
 
   const unsigned short* xb = reinterpret_cast<const unsigned short*>(A.x);
   auto load_rows = [&](int64_t t, bf16x8 (&rv)[RB][KSTEP]) {
@@ -794,7 +819,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         q = rows4_sum_f64(q);
         xs[rb] = (float)q;
         const int64_t row = t * PT + rb * 16 + lane;
-        if (lane < 16 && row < nrows) A.xsq[row] = q;
+        if (!MARK && lane < 16 && row < nrows) A.xsq[row] = q;
       } else {
         float q = 0.f;
 #pragma unroll
@@ -813,6 +838,20 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       M[rb] = kDead;
       Sl[rb] = 0.f;
       R[rb] = kDead;
+    }
+    // pass T: the row maximum (pass B) is the reference of the candidate band
+    // and of the sharp rescoring; rows past N have no candidates and no mass
+    float mr[RB], thr[RB];
+    bool live[RB];
+    if constexpr (MARK) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int64_t row = t * PT + rb * 16 + (lane & 15);
+        live[rb] = row < nrows;
+        mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
+        R[rb] = mr[rb];
+        thr[rb] = live[rb] ? mr[rb] - kTopmBand - 2.f * fmaf(eam, xs[rb], ea0m) : INFINITY;
+      }
     }
 #pragma unroll 1
     for (int cc = 0; cc < NCH; ++cc) {
@@ -843,13 +882,15 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         // best other score of the row seen so far in the slice, again exactly
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          float r = R[rb];
+          if constexpr (!MARK) {
+            float r = R[rb];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (!(cst[2 * KSA + cc * 32 + nt * 16 + 4 * (lane >> 4) + v] > 0.f)) r = fmaxf(r, acc[rb][nt][v]);
-          R[rb] = rows4_max(r);
+              for (int v = 0; v < 4; ++v)
+                if (!(cst[2 * KSA + cc * 32 + nt * 16 + 4 * (lane >> 4) + v] > 0.f)) r = fmaxf(r, acc[rb][nt][v]);
+            R[rb] = rows4_max(r);
+          }
           const int64_t row = t * PT + rb * 16 + (lane & 15);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
@@ -865,6 +906,29 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             }
         }
       }
+      if constexpr (MARK) {
+        // candidates: every component whose score may lie within kTopmBand of
+        // the row's maximum (the slice's largest expanded-form error counted
+        // twice); the mass 2^(l - max) of the others; bit j of word (row, cc)
+        // is component cc 32 + j of the slice
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          uint32_t word = 0;
+          float rem = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const bool cand = acc[rb][nt][v] >= thr[rb];  // never for rows past N (thr = +inf)
+              if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][nt][v] - mr[rb]);
+              word |= (cand ? 1u : 0u) << (nt * 16 + 4 * (lane >> 4) + v);
+            }
+          word = rows4_or(word);
+          Sl[rb] += rem;
+          if (lane < 16) wbuf[(rb * 16 + lane) * NCH + cc] = word;
+        }
+        continue;
+      }
       // running max per row, and the lane's sum rescaled to it
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -874,6 +938,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) cm = fmaxf(cm, acc[rb][nt][v]);
         cm = rows4_max(cm);
+        if constexpr (MODE == 2) {
+          M[rb] = fmaxf(M[rb], cm);
+          continue;
+        }
         const float Mn = fmaxf(M[rb], cm);
         float s = Sl[rb] * __builtin_amdgcn_exp2f(M[rb] - Mn);
 #pragma unroll
@@ -888,7 +956,18 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     for (int rb = 0; rb < RB; ++rb) {
       const float S = rows4_sum(Sl[rb]);
       const int64_t row = t * PT + rb * 16 + lane;
-      if (lane < 16 && row < nrows) A.P[(size_t)row * A.S + slice] = float2{M[rb], S};
+      if (lane < 16 && row < nrows) {
+        if constexpr (MARK) {
+          // this slice's below-band mass and its 8 candidate words of the row
+          A.prem[(size_t)row * A.S + slice] = S;
+          const uint32_t* src = wbuf + (rb * 16 + lane) * NCH;
+          uint4* dst = reinterpret_cast<uint4*>(A.cmask + (size_t)row * (A.KP / 32) + slice * NCH);
+          dst[0] = uint4{src[0], src[1], src[2], src[3]};
+          dst[1] = uint4{src[4], src[5], src[6], src[7]};
+        } else {
+          A.P[(size_t)row * A.S + slice] = float2{M[rb], MODE == 2 ? 1.f : S};
+        }
+      }
     }
   }
 }
@@ -897,7 +976,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 // read from LDS feeds kPassARB MFMAs
 constexpr int kPassARB = 4;
 
-size_t largek_pass_a_lds_bytes() { return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + 4 * KSA * sizeof(float); }
+size_t largek_pass_a_lds_bytes(bool mark) {
+  return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + (mark ? 6 : 4) * KSA * sizeof(float) +
+         (mark ? (size_t)LNW * 16 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
+}
 
 // Pass B: per row, combine the slices' (max, sum) into the LSE (log2 units);
 // each workgroup also sums its rows' LSE (natural log) into its LL partial.
@@ -1011,7 +1093,7 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kC, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
     attr_set = true;
   }
@@ -1025,8 +1107,8 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
     if (ac.N > 0) {
       ac.G = p.GbA;
       if (p.D == 128 && ac.vec16)
-        hipLaunchKernelGGL(largek_pass_a_kernel<kPassARB>, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
-                           largek_pass_a_lds_bytes(), s, ac);
+        hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 0>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                           largek_pass_a_lds_bytes(false), s, ac);
       else
         hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1289,7 +1371,9 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)kT, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
     attr_set = true;
   }
@@ -1305,14 +1389,18 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     ac.logp = a.logp ? a.logp + r0 : nullptr;
     ac.G = p.GbA;
     if (p.D == 128 && ac.vec16)
-      hipLaunchKernelGGL(largek_pass_a_kernel<kPassARB>, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
-                         largek_pass_a_lds_bytes(), s, ac);
+      hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 2>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(false), s, ac);
     else
       hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
+    if (p.D == 128 && ac.vec16)
+      hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 1>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(true), s, ac);
+    else
+      hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(largek_topm_final_kernel, dim3((unsigned)((ac.N + kFinalRows - 1) / kFinalRows)),
                        dim3(64 * kFinalRows), 0, s, ac);
