@@ -155,7 +155,23 @@ __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc
   const bool live = row0 + j < A.N;  // threads j < LT: row j of the tile
   if (j < LT) ls[j] = live ? pc.ls : (STATS ? INFINITY : 0.f);
   if constexpr (STATS) {
-    if (j < LT) xsq[j] = live ? pc.xs : 0.0;
+    if (j < LT) {
+      xsq[j] = live ? pc.xs : 0.0;
+      // columns 128.. of the row's slot, the statistics MFMA's features
+      // 128..133: 1 and |x|^2 as five bf16 terms (each remainder exact in
+      // float64; 40 bits, as many as |x|^2 of a bf16 row can need), so N_k and
+      // sum r |x|^2 come out of both magnitude classes like sum r x, and a
+      // component collapsed onto one row gets them exactly
+      u16x8 ext = u16x8{(unsigned short)0x3F80, 0, 0, 0, 0, 0, 0, 0};
+      double q = live ? pc.xs : 0.0;
+#pragma unroll
+      for (int e = 1; e <= 5; ++e) {
+        const __bf16 h = (__bf16)(float)q;
+        ext[e] = __builtin_bit_cast(unsigned short, h);
+        q -= (double)(float)h;
+      }
+      *reinterpret_cast<u16x8*>(rows + tile_slot(j) * LRS + 128) = ext;
+    }
   } else if (slice == 0) {
     double sq = 0.0;
 #pragma unroll
@@ -217,6 +233,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   constexpr int NT = KSL / LNW / 16;      // 16-column tiles per wave (2 in A, 1 in C)
   constexpr int KSTEP = DP / 32;          // MFMA k-steps over the features
   constexpr int GM = DP / 16;             // statistic row tiles (dimensions)
+  constexpr int GMX = GM + 1;             // and one for N_k and sum r |x|^2 (features 128..133)
   constexpr int WFRAG = (KSL / 16) * 2 * KSTEP * 64;
   // pass C holds its wave's logit weights in registers for the whole kernel
   // (NT * 2 * KSTEP fragments); passes A and T read them from LDS
@@ -298,18 +315,15 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   }
   // pass C: statistics of the r >= 2^-8 and r < 2^-8 classes, each in its
   // own float32 MFMA accumulator (float64 at the chunk's partial)
-  floatx4 sbig[STATS ? GM : 1][NT];
-  floatx4 ssmall[STATS ? GM : 1][NT];
-  double nk[NT], qs[NT];
+  floatx4 sbig[STATS ? GMX : 1][NT];
+  floatx4 ssmall[STATS ? GMX : 1][NT];
 #pragma unroll
-  for (int mt = 0; mt < (STATS ? GM : 1); ++mt)
+  for (int mt = 0; mt < (STATS ? GMX : 1); ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       ssmall[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
       sbig[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) nk[nt] = qs[nt] = 0.0;
 
   // pass A: combine the waves' (max, sum) of a finished tile into P; run by
   // one wave (rotating) while the others go on with the next tile
@@ -551,34 +565,25 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           const unsigned big = P & __builtin_bit_cast(unsigned, d);
           pb[i] = big;
           ps[i] = P ^ big;
-          lg[q0][nt] = __uint_as_float(P << 16);
-          lg[q1][nt] = __uint_as_float(P & 0xFFFF0000u);
         }
         bbig[nt] = __builtin_bit_cast(bf16x8, pb);
         bsmall[nt] = __builtin_bit_cast(bf16x8, ps);
       }
 #pragma unroll
-      for (int mt = 0; mt < (STATS ? GM : 1); ++mt) {
+      for (int mt = 0; mt < (STATS ? GMX : 1); ++mt) {
         // lane 16 g + i: features 16 mt + i of rows 4 g + e (read 1) and
         // 16 + 4 g + e (read 2), e = 0..3 -- k = 8 g + e and 8 g + 4 + e
         // (slot(16 + r) = 16 + slot(r): read 2 is 16 slots further)
         const unsigned short* src = rows + tile_slot(lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * LRS));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        // the last block's features 136..143 lie past the slot's 136 columns
+        if (mt == GM && (lane & 15) >= 8) av = bf16x8{};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           sbig[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], sbig[mt][nt], 0, 0, 0);
           ssmall[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bsmall[nt], ssmall[mt][nt], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const double xs = xsq[(q >> 2) * 16 + 4 * (lane >> 4) + (q & 3)];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          nk[nt] += (double)lg[q][nt];
-          qs[nt] += (double)lg[q][nt] * xs;
         }
       }
     }
@@ -693,24 +698,21 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           *dst = (A.accumulate ? *dst : 0.0) + ((double)sbig[mt][nt][v] + (double)ssmall[mt][nt][v]);
         }
       }
-    __syncthreads();
-    double* red64 = reinterpret_cast<double*>(lds);
+    // N_k and sum r |x|^2: features 128 and 129..133 of the last block; lane
+    // l holds features 128 + 4 (l / 16) + v of component l % 16, so lanes
+    // 0..15 take features 132, 133 from lanes 16..31
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int kl = (wv * NT + nt) * 16 + (lane & 15);
-      red64[(kl * 4 + (lane >> 4)) * 2 + 0] = nk[nt];
-      red64[(kl * 4 + (lane >> 4)) * 2 + 1] = qs[nt];
-    }
-    __syncthreads();
-    for (int kl = threadIdx.x; kl < KSL; kl += blockDim.x) {
-      double s0 = 0.0, s1 = 0.0;
-      for (int q = 0; q < 4; ++q) {
-        s0 += red64[(kl * 4 + q) * 2 + 0];
-        s1 += red64[(kl * 4 + q) * 2 + 1];
+      double f[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) f[v] = (double)sbig[GM][nt][v] + (double)ssmall[GM][nt][v];
+      const double f4 = __shfl_down(f[0], 16, 64), f5 = __shfl_down(f[1], 16, 64);
+      if ((lane >> 4) == 0) {
+        const int k = slice * KSL + (wv * NT + nt) * 16 + (lane & 15);
+        double* dst = part + (size_t)k * PR;
+        dst[0] = (A.accumulate ? dst[0] : 0.0) + f[0];
+        dst[1] = (A.accumulate ? dst[1] : 0.0) + (((f[1] + f[2]) + f[3]) + (f4 + f5));
       }
-      double* dst = part + (size_t)(slice * KSL + kl) * PR;
-      dst[0] = (A.accumulate ? dst[0] : 0.0) + s0;
-      dst[1] = (A.accumulate ? dst[1] : 0.0) + s1;
     }
   }
 }
