@@ -21,7 +21,8 @@
 // itself is exact in bf16); the statistics contraction X^T R runs on the same
 // instruction with r rounded to bf16.  Every statistic (N_k, sum r x,
 // sum r |x|^2) uses that same rounded r, so the M-step sees the exact moments
-// of one set of weights.  The responsibilities are summed in two magnitude
+// of one set of weights; N_k and sum r |x|^2 ride on the same MFMAs as extra
+// features (1, and |x|^2 as five bf16 terms).  The responsibilities are summed in two magnitude
 // classes (r >= 2^-8 and below) by separate MFMAs into separate float32
 // accumulators, added in float64 at the chunk's partial: a component
 // collapsed onto a row far from the origin has a variance many orders below
