@@ -49,10 +49,12 @@ def flops_per_pair(cov, D):
 
 
 def largek_roofline(D):
-    """(algorithmic flops, executed flops) per pair of the bf16 large-K E-step:
-    logits 2D (the hi and lo weight terms, in pass A and again in pass C:
-    4 x 2D executed) and statistics 2D, plus N_k and sum r|x|^2."""
-    return 4 * D + 4, 10 * D + 4
+    """(algorithmic flops, executed flops) per pair of the bf16 large-K E-step.
+    Algorithmic: logits 2D and statistics 2D, plus N_k and sum r|x|^2.
+    Executed: logits with the hi and lo weight terms in pass A and again in
+    pass C (4 x 2D), statistics in two magnitude classes over D features plus
+    the 16-feature block that carries 1 and |x|^2 (2 x 2 (D + 16))."""
+    return 4 * D + 4, 8 * D + 4 * (D + 16)
 
 
 def contraction_split(cov, D):
@@ -175,7 +177,8 @@ def main():
         peak = PEAK_BF16_MFMA
         kernel = "large-K E-step (prologue + passes A, B, C)"
         peak_note = (f"bf16 MFMA dense peak; {alg} algorithmic flop/pair (2D logits + 2D statistics); "
-                     f"{executed} flop/pair executed (two-term weights, logits recomputed in pass C)")
+                     f"{executed} flop/pair executed (two-term weights, logits recomputed in pass C, "
+                     f"statistics in two magnitude classes)")
         dtype = "bf16"
     else:
         f32f, f64f = contraction_split(wl.cov, wl.D)
