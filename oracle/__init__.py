@@ -247,3 +247,39 @@ def ivf_lists(idx, resp, K):
                 pos += 1
         offsets[b, K] = pos
     return offsets, rows, lr
+
+
+def fisher_vector(X, w, mu, var, power=True, l2=True):
+    """Fisher vectors of B sets of rows under one diagonal GMM (w (K,), mu
+    (K, D), var (K, D)): the application Flash-GMM's closing discussion names
+    (Fisher Vector encoding, Perronnin et al. 2010), in its improved form.
+    Per set of N rows, with r the responsibilities:
+      G_mu[k, d]  = 1 / (N sqrt(w_k))   sum_i r_ik (x_id - mu_kd) / sigma_kd
+      G_sig[k, d] = 1 / (N sqrt(2 w_k)) sum_i r_ik (((x_id - mu_kd) / sigma_kd)^2 - 1)
+    (the gradients of the mean log-likelihood with respect to mu and sigma,
+    scaled by the diagonal Fisher information), concatenated k-major as
+    [G_mu, G_sig], then optionally a signed square root and L2 normalisation.
+    Returns (B, 2 K D) float64."""
+    X = np.asarray(X, dtype=np.float64)
+    if X.ndim == 2:
+        X = X[None]
+    w = np.asarray(w, dtype=np.float64).reshape(-1)
+    mu = np.asarray(mu, dtype=np.float64).reshape(w.size, -1)
+    var = np.asarray(var, dtype=np.float64).reshape(mu.shape)
+    sig = np.sqrt(var)
+    out = []
+    for Xb in X:
+        N = Xb.shape[0]
+        _, r, _ = responsibilities("diag", Xb, w, mu, var)
+        z = (Xb[:, None, :] - mu[None]) / sig[None]  # (N, K, D)
+        gmu = np.einsum("nk,nkd->kd", r, z) / (N * np.sqrt(w))[:, None]
+        gsig = np.einsum("nk,nkd->kd", r, z * z - 1.0) / (N * np.sqrt(2.0 * w))[:, None]
+        fv = np.concatenate([gmu.ravel(), gsig.ravel()])
+        if power:
+            fv = np.sign(fv) * np.sqrt(np.abs(fv))
+        if l2:
+            n = np.linalg.norm(fv)
+            if n > 0:
+                fv = fv / n
+        out.append(fv)
+    return np.stack(out)

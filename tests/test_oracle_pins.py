@@ -598,3 +598,50 @@ def test_kmeans_bf16_rows_are_decoded_exactly():
     a = oracle.kmeans_step((bits, "bf16"), C)
     b = oracle.kmeans_step(Xd, C)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]) and a[4] == b[4]
+
+
+# ---------------------------------------------------------------- Fisher vectors
+def test_fisher_vector_is_the_scaled_loglik_gradient():
+    """The Fisher vector's blocks are the gradients of the mean log-likelihood
+    (the oracle's E-step, a different code path) with respect to mu and sigma,
+    scaled by sigma / sqrt(w) and sigma / sqrt(2 w): checked by central
+    differences."""
+    rng = np.random.default_rng(21)
+    K, D, N = 3, 2, 40
+    X = rng.normal(size=(N, D)) * 1.5
+    w = rng.dirichlet(np.full(K, 3.0))
+    mu = rng.normal(size=(K, D))
+    sig = rng.uniform(0.7, 1.6, size=(K, D))
+    fv = oracle.fisher_vector(X, w, mu, sig ** 2, power=False, l2=False)[0]
+    gmu, gsig = fv[:K * D].reshape(K, D), fv[K * D:].reshape(K, D)
+
+    def mean_ll(m, s):
+        return oracle.estep("diag", X, w, m, s ** 2)["ll"][0] / N
+
+    h = 1e-5
+    for k in range(K):
+        for d in range(D):
+            e = np.zeros((K, D))
+            e[k, d] = h
+            dmu = (mean_ll(mu + e, sig) - mean_ll(mu - e, sig)) / (2 * h)
+            dsig = (mean_ll(mu, sig + e) - mean_ll(mu, sig - e)) / (2 * h)
+            assert abs(gmu[k, d] - sig[k, d] / np.sqrt(w[k]) * dmu) <= 1e-7, (k, d)
+            assert abs(gsig[k, d] - sig[k, d] / np.sqrt(2 * w[k]) * dsig) <= 1e-7, (k, d)
+
+
+def test_fisher_vector_one_component_and_normalisation():
+    """K = 1 (every r = 1): the blocks are the standardised mean offset and
+    the standardised variance ratio minus one, by numpy moments; the signed
+    square root keeps signs and the L2 step gives unit norm."""
+    rng = np.random.default_rng(22)
+    X = rng.normal(size=(2, 300, 4)) * 2.0 + 1.0
+    mu = rng.normal(size=(1, 4))
+    var = rng.uniform(0.5, 3.0, size=(1, 4))
+    raw = oracle.fisher_vector(X, [1.0], mu, var, power=False, l2=False)
+    for b in range(2):
+        z = (X[b] - mu) / np.sqrt(var)
+        np.testing.assert_allclose(raw[b][:4], z.mean(axis=0), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(raw[b][4:], ((z * z).mean(axis=0) - 1.0) / np.sqrt(2.0), rtol=1e-12, atol=1e-12)
+    full = oracle.fisher_vector(X, [1.0], mu, var)
+    np.testing.assert_allclose(np.linalg.norm(full, axis=1), 1.0, rtol=1e-12)
+    assert (np.sign(full) == np.sign(raw)).all()
