@@ -212,6 +212,24 @@ size_t gmm_kmeans_workspace_bytes(const gmm_data* data, int32_t K);
 gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, int32_t* labels, int64_t* counts,
                            double* inertia, void* ws, size_t ws_bytes, void* stream);
 
+/* Fisher vectors of B sets of N rows (data as (B, N, D) float32) under ONE
+ * diagonal model (model: K, cov = GMM_COV_DIAG, weights (K), means (K, D),
+ * covars (K, D) variances) -- the encoding Flash-GMM's closing discussion
+ * names as the same fused log-sum-exp and weighted-statistics pattern
+ * (Perronnin et al. 2010, improved form).  Per set b, with r the
+ * responsibilities:
+ *   fv[b][k D + d]       = (sum_i r_ik x_id - N_k mu_kd) / (sigma_kd N sqrt(w_k))
+ *   fv[b][K D + k D + d] = (sum_i r_ik (x_id - mu_kd)^2 / sigma_kd^2 - N_k) / (N sqrt(2 w_k))
+ * then, per flags, bit 0: signed square root of every value; bit 1: L2
+ * normalisation of each set's 2 K D values.  fv (B, 2 K D) float32 out.  A
+ * component with w_k <= 0 or a variance <= 0 gives zeros; N = 0 gives zeros.
+ * The statistics are those of gmm_estep_stats (float64); the window is its
+ * diagonal one.  Workspace: gmm_fisher_vector_workspace_bytes (it holds the
+ * model replicated per set and the sets' statistics).  Deterministic. */
+size_t gmm_fisher_vector_workspace_bytes(const gmm_data* data, int32_t K);
+gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint32_t flags, float* fv, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gmm_status_str(int32_t status);
 

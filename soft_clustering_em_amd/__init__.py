@@ -12,6 +12,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
   gmm_kmeans_workspace_bytes(X, K)            -> int
   gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=None)
+  gmm_fisher_vector(X, w, mu, var, power=True, l2=True, fv=None, ws=None)
 
 The estimator calls (score_samples, predict, score, aic, bic, fit with
 restarts) are in soft_clustering_em_amd.estimator.
@@ -29,7 +30,7 @@ from ._abi import (COV_CODES, GmmError, GmmData, GmmOptions, GmmParams, GmmStats
 
 __all__ = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
            "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
-           "gmm_kmeans_step", "new_stats", "GmmError",
+           "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector", "new_stats", "GmmError",
            "cov_shape"]
 
 
@@ -216,3 +217,31 @@ def gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=Non
     _abi.check(_abi.lib().gmm_kmeans_step(ctypes.byref(d), int(K), _ptr(centroids), _ptr(labels), _ptr(counts),
                                           _ptr(inertia), _ptr(ws), ws.numel(), _stream(stream)))
     return labels, counts, inertia
+
+
+def gmm_fisher_vector_workspace_bytes(X, K) -> int:
+    d = _data(X)
+    return int(_abi.lib().gmm_fisher_vector_workspace_bytes(ctypes.byref(d), int(K)))
+
+
+def gmm_fisher_vector(X, w, mu, var, power=True, l2=True, fv=None, ws=None, stream=None):
+    """Fisher vectors of the sets X ((N, D) or (B, N, D) float32) under one
+    diagonal model (w (K,), mu (K, D), var (K, D) float32): (B, 2 K D)
+    float32, [G_mu, G_sigma] per set, optionally with the signed square root
+    (power) and L2 normalisation."""
+    torch = _torch()
+    d = _data(X)
+    B, K, D = int(d.B), int(w.shape[-1]), int(d.D)
+    if mu.numel() != K * D or var.numel() != K * D:
+        raise ValueError("the model is one diagonal GMM: w (K,), mu and var (K, D)")
+    p = GmmParams(K, COV_CODES["diag"], ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(mu.data_ptr()),
+                  ctypes.c_void_p(var.data_ptr()))
+    if fv is None:
+        fv = torch.empty(B, 2 * K * D, dtype=torch.float32, device=w.device)
+    if ws is None:
+        n = gmm_fisher_vector_workspace_bytes(X, K)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=w.device)
+    flags = (1 if power else 0) | (2 if l2 else 0)
+    _abi.check(_abi.lib().gmm_fisher_vector(ctypes.byref(d), ctypes.byref(p), flags, _ptr(fv), _ptr(ws), ws.numel(),
+                                            _stream(stream)))
+    return fv

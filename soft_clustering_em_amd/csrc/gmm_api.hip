@@ -671,6 +671,77 @@ gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, in
   return GMM_OK;
 }
 
+// ---- Fisher vectors: the batched E-step's per-problem statistics under one
+// replicated diagonal model, turned into gradient blocks by fisher_kernel
+struct FvLayout {
+  Plan p;
+  size_t off_w, off_mu, off_var, off_nk, off_sx, off_sxx, off_ll, bytes;
+};
+
+static gmm_status fisher_plan(const gmm_data* d, int32_t K, FvLayout* L) {
+  Plan p;
+  gmm_status st = make_plan(d, K, DIAG, GMM_OP_ESTEP, &p);
+  if (st != GMM_OK) return st;
+  const size_t B = (size_t)p.B, k = (size_t)K, D = (size_t)p.D;
+  size_t o = align_up(p.ws_bytes);
+  L->off_w = o;   o = align_up(o + sizeof(float) * B * k);
+  L->off_mu = o;  o = align_up(o + sizeof(float) * B * k * D);
+  L->off_var = o; o = align_up(o + sizeof(float) * B * k * D);
+  L->off_nk = o;  o = align_up(o + sizeof(double) * B * k);
+  L->off_sx = o;  o = align_up(o + sizeof(double) * B * k * D);
+  L->off_sxx = o; o = align_up(o + sizeof(double) * B * k * D);
+  L->off_ll = o;  o = align_up(o + sizeof(double) * B);
+  L->bytes = o;
+  L->p = p;
+  return GMM_OK;
+}
+
+size_t gmm_fisher_vector_workspace_bytes(const gmm_data* data, int32_t K) {
+  FvLayout L;
+  if (fisher_plan(data, K, &L) != GMM_OK) return 0;
+  return L.bytes;
+}
+
+gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint32_t flags, float* fv, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!model || !model->weights || !model->means || !model->covars)
+    return fail(GMM_ERR_INVALID_ARG, "model parameters must be non-NULL");
+  if (model->cov != DIAG) return fail(GMM_ERR_UNSUPPORTED, "Fisher vectors take a diagonal model");
+  if (flags & ~3u) return fail(GMM_ERR_INVALID_ARG, "flags: bit 0 power, bit 1 L2; other bits must be 0");
+  FvLayout L;
+  gmm_status st = fisher_plan(data, model->K, &L);
+  if (st != GMM_OK) return st;
+  if (!fv) return fail(GMM_ERR_INVALID_ARG, "fv must be non-NULL");
+  if (!ws || ((uintptr_t)ws) % kAlign != 0) return fail(GMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.bytes) return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.bytes);
+  const Plan& p = L.p;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  float* wr = reinterpret_cast<float*>(w + L.off_w);
+  float* mur = reinterpret_cast<float*>(w + L.off_mu);
+  float* varr = reinterpret_cast<float*>(w + L.off_var);
+  double* nk = reinterpret_cast<double*>(w + L.off_nk);
+  double* sx = reinterpret_cast<double*>(w + L.off_sx);
+  double* sxx = reinterpret_cast<double*>(w + L.off_sxx);
+  double* ll = reinterpret_cast<double*>(w + L.off_ll);
+  hipError_t e = launch_fisher_replicate(p.B, model->K, (int)p.D, model->weights, model->means, model->covars, wr,
+                                         mur, varr, s);
+  if (e != hipSuccess) return hip_fail(e, "Fisher model replication launch");
+  gmm_params rep;
+  rep.K = model->K;
+  rep.cov = DIAG;
+  rep.weights = wr;
+  rep.means = mur;
+  rep.covars = varr;
+  st = run_estep(p, data, &rep, ws, nk, sx, sxx, ll, nullptr, 0, nullptr, s);
+  if (st != GMM_OK) return st;
+  e = launch_fisher(p.B, model->K, (int)p.D, p.N, flags, model->weights, model->means, model->covars, nk, sx, sxx, fv,
+                    s);
+  if (e != hipSuccess) return hip_fail(e, "Fisher vector launch");
+  return GMM_OK;
+}
+
 const char* gmm_status_str(int32_t status) {
   switch (status) {
     case GMM_OK: return "ok";

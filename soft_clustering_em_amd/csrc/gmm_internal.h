@@ -171,6 +171,13 @@ hipError_t launch_ivf_lists(const IvfArgs& a, hipStream_t s);
 
 // k-means (Lloyd) iteration pieces (gmm_kmeans.hip)
 hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* w, float* cv, hipStream_t s);
+
+// Fisher vectors (gmm_fisher.hip)
+hipError_t launch_fisher_replicate(int64_t B, int K, int D, const float* w, const float* mu, const float* var,
+                                   float* wr, float* mur, float* varr, hipStream_t s);
+hipError_t launch_fisher(int64_t B, int K, int D, int64_t N, uint32_t flags, const float* w, const float* mu,
+                         const float* var, const double* nk, const double* sx, const double* sxx, float* fv,
+                         hipStream_t s);
 hipError_t launch_kmeans_update(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
                                 int D, const int64_t* offsets, const int32_t* rows, float* C, int64_t* counts,
                                 double* ip, double* inertia, hipStream_t s);

@@ -286,3 +286,25 @@ def test_kmeans_rejects_bad_arguments_before_the_device():
     for name, (args, want) in cases.items():
         assert L.gmm_kmeans_step(*args) == want, name
         assert L.gmm_last_error() != b"", name
+
+
+def test_fisher_vector_rejects_bad_arguments_before_the_device():
+    L = _abi.lib()
+    d = _data(1000, 16, B=4)
+    n = L.gmm_fisher_vector_workspace_bytes(ctypes.byref(d), 8)
+    assert n > 0 and n % 256 == 0
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    good = _abi.GmmParams(8, _abi.COV_DIAG, p, p, p)
+    sph = _abi.GmmParams(8, _abi.COV_SPHERICAL, p, p, p)
+    nul = _abi.GmmParams(8, _abi.COV_DIAG, None, p, p)
+    cases = {
+        "spherical model": ((ctypes.byref(d), ctypes.byref(sph), 3, p, ws, n, None), _abi.GMM_ERR_UNSUPPORTED),
+        "null means": ((ctypes.byref(d), ctypes.byref(nul), 3, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "flags": ((ctypes.byref(d), ctypes.byref(good), 4, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "fv": ((ctypes.byref(d), ctypes.byref(good), 3, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "ws size": ((ctypes.byref(d), ctypes.byref(good), 3, p, ws, n - 256, None), _abi.GMM_ERR_WORKSPACE),
+    }
+    for name, (args, want) in cases.items():
+        assert L.gmm_fisher_vector(*args) == want, name
+        assert L.gmm_last_error() != b"", name
