@@ -283,3 +283,37 @@ def fisher_vector(X, w, mu, var, power=True, l2=True):
                 fv = fv / n
         out.append(fv)
     return np.stack(out)
+
+
+def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6):
+    """One approximate top-k EM iteration for one problem (spherical or
+    diagonal): the training mode the GMMXX README lists as approx_top_k --
+    each row keeps the topk components of largest log-score (ties to the lower
+    index), normalises over that subset only, and only those enter the
+    statistics; the M-step is the usual one.  Returns dict like fit_step:
+    w, mu, cv (each with a leading problem axis), mean_ll = the mean over rows
+    of the log-sum-exp over each row's kept components, the statistics, and
+    keep (N, topk) the kept components, best first, -1 past K."""
+    Xa, _ = _x_and_type(X)
+    N, D = Xa.shape
+    ls, _, _ = responsibilities(cov, X, w, mu, cv)
+    K = ls.shape[1]
+    m = min(int(topk), K)
+    order = np.argsort(-ls, axis=1, kind="stable")[:, :m]  # descending score, ties: lower index first
+    sel = np.take_along_axis(ls, order, axis=1)
+    mx = sel[:, :1]
+    lse = (mx + np.log(np.exp(sel - mx).sum(axis=1, keepdims=True)))[:, 0]
+    r = np.zeros((N, K))
+    np.put_along_axis(r, order, np.exp(sel - lse[:, None]), axis=1)
+    mu0 = np.asarray(mu, dtype=np.float64).reshape(K, D)
+    nk = r.sum(axis=0)
+    sx = r.T @ Xa
+    diff2 = (Xa[:, None, :] - mu0[None]) ** 2  # (N, K, D)
+    sxx = np.einsum("nk,nkd->kd", r, diff2)
+    if cov == "spherical":
+        sxx = sxx.sum(axis=1)
+    st = dict(nk=nk[None], sx=sx[None], sxx=sxx[None], ll=np.array([lse.sum()]))
+    wo, mo, co, fl = mstep(cov, st, N, np.asarray(w).reshape(1, K), mu0[None], np.asarray(cv).reshape(st["sxx"].shape), eps)
+    keep = np.full((N, max(int(topk), 1)), -1, dtype=np.int64)
+    keep[:, :m] = order
+    return dict(w=wo, mu=mo, cv=co, mean_ll=np.array([lse.mean()]), stats=st, flags=fl, keep=keep)

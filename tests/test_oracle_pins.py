@@ -645,3 +645,46 @@ def test_fisher_vector_one_component_and_normalisation():
     full = oracle.fisher_vector(X, [1.0], mu, var)
     np.testing.assert_allclose(np.linalg.norm(full, axis=1), 1.0, rtol=1e-12)
     assert (np.sign(full) == np.sign(raw)).all()
+
+
+# ---------------------------------------------------------------- approximate top-k EM
+@pytest.mark.parametrize("cov", ["spherical", "diag"])
+def test_topk_em_with_every_component_is_exact_em(cov):
+    """Keeping all K components is the exact EM step (the pinned fit_step)."""
+    rng = np.random.default_rng(31)
+    K, D, N = 5, 3, 400
+    w, mu, cv = rand_theta(rng, cov, K, D)
+    X = rng.normal(size=(N, D)) * 3.0
+    a = oracle.topk_fit_step(cov, X, w, mu, cv, K)
+    b = oracle.fit_step(cov, X, w, mu, cv)
+    for key in ("w", "mu", "cv", "mean_ll"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-10, atol=1e-12)
+
+
+def test_topk_em_with_one_component_is_the_kmeans_update():
+    """With k = 1, equal weights and one shared spherical variance the kept
+    component is the nearest centroid, so the new means are the k-means update
+    of the k-means oracle (a different code path)."""
+    rng = np.random.default_rng(32)
+    K, D, N = 6, 4, 700
+    X = rng.normal(size=(N, D)) * 2.0
+    C = X[:K].copy()
+    out = oracle.topk_fit_step("spherical", X, np.full(K, 1.0 / K), C, np.full(K, 0.7), 1, eps=0.0)
+    lab, gap, newC, cnt, _ = oracle.kmeans_step(X, C)
+    keep = cnt > 0
+    assert np.array_equal(out["keep"][:, 0], lab)
+    np.testing.assert_allclose(out["mu"][0][keep], newC[keep], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["stats"]["nk"][0], cnt, rtol=0, atol=1e-12)
+
+
+def test_topk_em_normalises_over_the_kept_set():
+    """Each row's kept responsibilities sum to one, so sum_k N_k = N, and the
+    row's log-sum-exp over the kept set never exceeds its full log p(x)."""
+    rng = np.random.default_rng(33)
+    K, D, N = 8, 2, 300
+    w, mu, cv = rand_theta(rng, "diag", K, D)
+    X = rng.normal(size=(N, D)) * 3.0
+    out = oracle.topk_fit_step("diag", X, w, mu, cv, 3)
+    assert abs(out["stats"]["nk"].sum() - N) <= 1e-9 * N
+    _, _, lse = oracle.responsibilities("diag", X, w, mu, cv)
+    assert out["mean_ll"][0] <= lse.mean() + 1e-12
