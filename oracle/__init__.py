@@ -285,26 +285,30 @@ def fisher_vector(X, w, mu, var, power=True, l2=True):
     return np.stack(out)
 
 
-def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6):
+def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6, floor=2.0 ** -20):
     """One approximate top-k EM iteration for one problem (spherical or
     diagonal): the training mode the GMMXX README lists as approx_top_k --
     each row keeps the topk components of largest log-score (ties to the lower
-    index), normalises over that subset only, and only those enter the
+    index) among those whose full responsibility is at least `floor` (the best
+    one always), normalises over that subset only, and only those enter the
     statistics; the M-step is the usual one.  Returns dict like fit_step:
     w, mu, cv (each with a leading problem axis), mean_ll = the mean over rows
     of the log-sum-exp over each row's kept components, the statistics, and
     keep (N, topk) the kept components, best first, -1 past K."""
     Xa, _ = _x_and_type(X)
     N, D = Xa.shape
-    ls, _, _ = responsibilities(cov, X, w, mu, cv)
+    ls, rfull, _ = responsibilities(cov, X, w, mu, cv)
     K = ls.shape[1]
     m = min(int(topk), K)
     order = np.argsort(-ls, axis=1, kind="stable")[:, :m]  # descending score, ties: lower index first
-    sel = np.take_along_axis(ls, order, axis=1)
+    kept = np.take_along_axis(rfull, order, axis=1) >= floor
+    kept[:, 0] = True
+    sel = np.where(kept, np.take_along_axis(ls, order, axis=1), -np.inf)
     mx = sel[:, :1]
     lse = (mx + np.log(np.exp(sel - mx).sum(axis=1, keepdims=True)))[:, 0]
     r = np.zeros((N, K))
     np.put_along_axis(r, order, np.exp(sel - lse[:, None]), axis=1)
+    order = np.where(kept, order, -1)
     mu0 = np.asarray(mu, dtype=np.float64).reshape(K, D)
     nk = r.sum(axis=0)
     sx = r.T @ Xa

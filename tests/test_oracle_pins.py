@@ -650,12 +650,13 @@ def test_fisher_vector_one_component_and_normalisation():
 # ---------------------------------------------------------------- approximate top-k EM
 @pytest.mark.parametrize("cov", ["spherical", "diag"])
 def test_topk_em_with_every_component_is_exact_em(cov):
-    """Keeping all K components is the exact EM step (the pinned fit_step)."""
+    """Keeping all K components (no floor) is the exact EM step (the pinned
+    fit_step)."""
     rng = np.random.default_rng(31)
     K, D, N = 5, 3, 400
     w, mu, cv = rand_theta(rng, cov, K, D)
     X = rng.normal(size=(N, D)) * 3.0
-    a = oracle.topk_fit_step(cov, X, w, mu, cv, K)
+    a = oracle.topk_fit_step(cov, X, w, mu, cv, K, floor=0.0)
     b = oracle.fit_step(cov, X, w, mu, cv)
     for key in ("w", "mu", "cv", "mean_ll"):
         np.testing.assert_allclose(a[key], b[key], rtol=1e-10, atol=1e-12)
@@ -669,7 +670,7 @@ def test_topk_em_with_one_component_is_the_kmeans_update():
     K, D, N = 6, 4, 700
     X = rng.normal(size=(N, D)) * 2.0
     C = X[:K].copy()
-    out = oracle.topk_fit_step("spherical", X, np.full(K, 1.0 / K), C, np.full(K, 0.7), 1, eps=0.0)
+    out = oracle.topk_fit_step("spherical", X, np.full(K, 1.0 / K), C, np.full(K, 0.7), 1, eps=0.0, floor=0.0)
     lab, gap, newC, cnt, _ = oracle.kmeans_step(X, C)
     keep = cnt > 0
     assert np.array_equal(out["keep"][:, 0], lab)
@@ -686,5 +687,8 @@ def test_topk_em_normalises_over_the_kept_set():
     X = rng.normal(size=(N, D)) * 3.0
     out = oracle.topk_fit_step("diag", X, w, mu, cv, 3)
     assert abs(out["stats"]["nk"].sum() - N) <= 1e-9 * N
+    _, rfull, _ = oracle.responsibilities("diag", X, w, mu, cv)
+    k2 = out["keep"][:, 1:]
+    assert (np.take_along_axis(rfull, np.where(k2 >= 0, k2, 0), axis=1)[k2 >= 0] >= 2.0 ** -20).all()
     _, _, lse = oracle.responsibilities("diag", X, w, mu, cv)
     assert out["mean_ll"][0] <= lse.mean() + 1e-12
