@@ -13,6 +13,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_kmeans_workspace_bytes(X, K)            -> int
   gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=None)
   gmm_fisher_vector(X, w, mu, var, power=True, l2=True, fv=None, ws=None)
+  gmm_topk_fit_step(X, w, mu, cv, cov, topk, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
 
 The estimator calls (score_samples, predict, score, aic, bic, fit with
 restarts) are in soft_clustering_em_amd.estimator.
@@ -30,7 +31,8 @@ from ._abi import (COV_CODES, GmmError, GmmData, GmmOptions, GmmParams, GmmStats
 
 __all__ = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
            "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
-           "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector", "new_stats", "GmmError",
+           "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector",
+           "gmm_topk_fit_workspace_bytes", "gmm_topk_fit_step", "new_stats", "GmmError",
            "cov_shape"]
 
 
@@ -245,3 +247,24 @@ def gmm_fisher_vector(X, w, mu, var, power=True, l2=True, fv=None, ws=None, stre
     _abi.check(_abi.lib().gmm_fisher_vector(ctypes.byref(d), ctypes.byref(p), flags, _ptr(fv), _ptr(ws), ws.numel(),
                                             _stream(stream)))
     return fv
+
+
+def gmm_topk_fit_workspace_bytes(X, K, cov, topk) -> int:
+    d = _data(X)
+    return int(_abi.lib().gmm_topk_fit_workspace_bytes(ctypes.byref(d), int(K), _cov_code(cov), int(topk)))
+
+
+def gmm_topk_fit_step(X, w, mu, cv, cov, topk, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None,
+                      stream=None):
+    """One approximate top-k EM iteration in place (each row keeps its topk
+    best components and normalises over them)."""
+    torch = _torch()
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    o = GmmOptions(float(reg_covar), 0, None, None)
+    if ws is None:
+        n = gmm_topk_fit_workspace_bytes(X, p.K, cov, topk)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=X.device)
+    _abi.check(_abi.lib().gmm_topk_fit_step(ctypes.byref(d), ctypes.byref(p), int(topk), ctypes.byref(o),
+                                            _ptr(mean_loglik), _ptr(comp_status), _ptr(ws), ws.numel(),
+                                            _stream(stream)))

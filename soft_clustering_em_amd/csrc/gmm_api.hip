@@ -742,6 +742,105 @@ gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint
   return GMM_OK;
 }
 
+// ---- approximate top-k EM: the top-m pass with m = k and threshold 2^-20, the
+// posting lists of its entries, weighted statistics per component, M-step
+static constexpr float kTopkFloor = 0x1p-20f;  // smallest responsibility a top-k entry keeps (rank 1 aside)
+
+struct TkLayout {
+  Plan p;
+  size_t off_idx, off_resp, off_logp, off_rinv, off_llrow, off_cnt, off_offsets, off_rows, off_lresp;
+  size_t off_nk, off_sx, off_sxx, off_ll, bytes;
+};
+
+static gmm_status topk_plan(const gmm_data* d, int32_t K, int32_t cov, int32_t topk, TkLayout* L) {
+  if (cov != SPH && cov != DIAG) return fail(GMM_ERR_UNSUPPORTED, "top-k EM takes spherical or diagonal components");
+  if (topk < 1 || topk > 16) return fail(GMM_ERR_INVALID_ARG, "topk must be in [1, 16] (got %d)", topk);
+  Plan p;
+  gmm_status st = make_plan(d, K, cov, GMM_OP_TOPM, &p);
+  if (st != GMM_OK) return st;
+  st = ivf_check(p.B, p.N, topk, K);
+  if (st != GMM_OK) return st;
+  const size_t B = (size_t)p.B, N = (size_t)p.N, k = (size_t)K, D = (size_t)p.D, m = (size_t)topk;
+  size_t o = align_up(p.ws_bytes);
+  L->off_idx = o;     o = align_up(o + sizeof(int32_t) * B * N * m);
+  L->off_resp = o;    o = align_up(o + sizeof(float) * B * N * m);
+  L->off_logp = o;    o = align_up(o + sizeof(float) * B * N);
+  L->off_rinv = o;    o = align_up(o + sizeof(double) * B * N);
+  L->off_llrow = o;   o = align_up(o + sizeof(double) * B * N);
+  L->off_cnt = o;     o = align_up(o + ivf_ws(p.B, p.N, K));
+  L->off_offsets = o; o = align_up(o + sizeof(int64_t) * B * (k + 1));
+  L->off_rows = o;    o = align_up(o + sizeof(int32_t) * B * N * m);
+  L->off_lresp = o;   o = align_up(o + sizeof(float) * B * N * m);
+  L->off_nk = o;      o = align_up(o + sizeof(double) * B * k);
+  L->off_sx = o;      o = align_up(o + sizeof(double) * B * k * D);
+  L->off_sxx = o;     o = align_up(o + sizeof(double) * B * (cov == DIAG ? k * D : k));
+  L->off_ll = o;      o = align_up(o + sizeof(double) * B);
+  L->bytes = o;
+  L->p = p;
+  return GMM_OK;
+}
+
+size_t gmm_topk_fit_workspace_bytes(const gmm_data* data, int32_t K, int32_t cov, int32_t topk) {
+  TkLayout L;
+  if (topk_plan(data, K, cov, topk, &L) != GMM_OK) return 0;
+  return L.bytes;
+}
+
+gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t topk, const gmm_options* opts,
+                             double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  gmm_status st = check_params(inout, 0, 0, true);
+  if (st != GMM_OK) return st;
+  TkLayout L;
+  st = topk_plan(data, inout->K, inout->cov, topk, &L);
+  if (st != GMM_OK) return st;
+  const Plan& p = L.p;
+  if (p.N < 1) return fail(GMM_ERR_INVALID_ARG, "a fit step needs N >= 1");
+  if (opts && opts->flags) return fail(GMM_ERR_INVALID_ARG, "options.flags must be 0");
+  const double reg = opts ? opts->reg_covar : 1e-6;
+  if (!(reg >= 0.0)) return fail(GMM_ERR_INVALID_ARG, "reg_covar must be >= 0");
+  if (!ws || ((uintptr_t)ws) % kAlign != 0) return fail(GMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.bytes) return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + L.off_idx);
+  float* resp = reinterpret_cast<float*>(w + L.off_resp);
+  float* logp = reinterpret_cast<float*>(w + L.off_logp);
+  // kept: the topk best among the components with r >= 2^-20 (the best always):
+  // the top-m rule at that threshold, decided on float64 responsibilities;
+  // every such component lies in the band the top-m rescoring covers
+  st = run_topm(p, data, inout, topk, kTopkFloor, idx, resp, nullptr, logp, ws, s);
+  if (st != GMM_OK) return st;
+  IvfArgs A;
+  A.idx = idx;
+  A.resp = resp;
+  A.N = p.N;
+  A.B = (int)p.B;
+  A.m = topk;
+  A.K = inout->K;
+  A.KB = 0;
+  while ((1 << A.KB) < inout->K) ++A.KB;
+  A.nblk = (int)((p.N + kIvfBlock - 1) / kIvfBlock);
+  A.cnt = reinterpret_cast<int32_t*>(w + L.off_cnt);
+  A.offsets = reinterpret_cast<int64_t*>(w + L.off_offsets);
+  A.rows = reinterpret_cast<int32_t*>(w + L.off_rows);
+  A.lresp = reinterpret_cast<float*>(w + L.off_lresp);
+  hipError_t e = launch_ivf_lists(A, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k list launch");
+  double* nk = reinterpret_cast<double*>(w + L.off_nk);
+  double* sx = reinterpret_cast<double*>(w + L.off_sx);
+  double* sxx = reinterpret_cast<double*>(w + L.off_sxx);
+  e = launch_topk_stats(data->x, data->dtype == GMM_DT_BF16 ? 1 : 0, p.B, p.N, p.ld_x, p.stride_b, inout->K, (int)p.D,
+                        topk, inout->cov, resp, logp, inout->means, A.offsets, A.rows, A.lresp,
+                        reinterpret_cast<double*>(w + L.off_rinv), reinterpret_cast<double*>(w + L.off_llrow), nk, sx,
+                        sxx, reinterpret_cast<double*>(w + L.off_ll), mean_loglik, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k statistics launch");
+  e = launch_mstep_strided(inout->cov, p.B, p.D, inout->K, nk, sx, sxx, p.N, inout->weights, inout->means,
+                           inout->covars, reg, nullptr, 0, comp_status, s);
+  if (e != hipSuccess) return hip_fail(e, "M-step launch");
+  return GMM_OK;
+}
+
 const char* gmm_status_str(int32_t status) {
   switch (status) {
     case GMM_OK: return "ok";

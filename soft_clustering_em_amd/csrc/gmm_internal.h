@@ -172,6 +172,13 @@ hipError_t launch_ivf_lists(const IvfArgs& a, hipStream_t s);
 // k-means (Lloyd) iteration pieces (gmm_kmeans.hip)
 hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* w, float* cv, hipStream_t s);
 
+// approximate top-k EM statistics (gmm_topk.hip)
+hipError_t launch_topk_stats(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
+                             int D, int m, int cov, const float* resp, const float* logp, const float* mu,
+                             const int64_t* offsets, const int32_t* rows, const float* lresp, double* rinv,
+                             double* llrow, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
+                             hipStream_t s);
+
 // Fisher vectors (gmm_fisher.hip)
 hipError_t launch_fisher_replicate(int64_t B, int K, int D, const float* w, const float* mu, const float* var,
                                    float* wr, float* mur, float* varr, hipStream_t s);

@@ -308,3 +308,19 @@ def test_fisher_vector_rejects_bad_arguments_before_the_device():
     for name, (args, want) in cases.items():
         assert L.gmm_fisher_vector(*args) == want, name
         assert L.gmm_last_error() != b"", name
+
+
+def test_topk_fit_step_window_and_arguments():
+    L = _abi.lib()
+    d = _data(5000, 16)
+    assert L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_DIAG, 4) > 0
+    assert L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_FULL, 4) == 0
+    assert L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_DIAG, 0) == 0
+    assert L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_DIAG, 17) == 0
+    a = L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_DIAG, 2)
+    b = L.gmm_topk_fit_workspace_bytes(ctypes.byref(d), 32, _abi.COV_DIAG, 8)
+    assert b > a
+    p = ctypes.c_void_p(4096)
+    prm = _abi.GmmParams(32, _abi.COV_TIED, p, p, p)
+    assert L.gmm_topk_fit_step(ctypes.byref(d), ctypes.byref(prm), 4, None, None, None, ctypes.c_void_p(1 << 20),
+                               1 << 30, None) == _abi.GMM_ERR_UNSUPPORTED

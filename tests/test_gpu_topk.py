@@ -1,0 +1,115 @@
+"""Parity of gmm_topk_fit_step (approximate top-k EM: each row keeps its k
+best components among those with responsibility >= 2^-20, the best always, and
+normalises over them) against the float64 oracle
+(oracle.topk_fit_step, pinned by its k = K and k = 1 special cases), one step
+from identical float32 parameters.  The kept sets are decided on float64
+scores on both sides and the statistics are float64 sums of float32
+responsibilities, so the float32 bar of 1e-4 holds for bf16 rows too."""
+import numpy as np
+import pytest
+
+import oracle
+from parity import TOL_F32, param_errors, to_np
+from soft_clustering_em_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import soft_clustering_em_amd._abi as abi
+    abi.lib()
+    return torch
+
+
+def theta(rng, cov, B, K, D, X):
+    w = np.stack([rng.dirichlet(np.full(K, 3.0)) for _ in range(B)]).astype(np.float32)
+    mu = np.stack([X[b][rng.choice(X.shape[1], K, replace=False)] for b in range(B)]).astype(np.float32)
+    if cov == "spherical":
+        cv = rng.uniform(0.5, 2.0, size=(B, K)).astype(np.float32)
+    else:
+        cv = rng.uniform(0.5, 2.0, size=(B, K, X.shape[2])).astype(np.float32)
+    return w, mu, cv
+
+
+def gpu_step(torch, Xd, th, cov, topk):
+    import soft_clustering_em_amd as g
+    w, mu, cv = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in th)
+    B = w.shape[0]
+    mll = torch.zeros(B, dtype=torch.float64, device="cuda")
+    cs = torch.full(w.shape, -1, dtype=torch.int32, device="cuda")
+    g.gmm_topk_fit_step(Xd, w, mu, cv, cov, topk, mean_loglik=mll, comp_status=cs)
+    torch.cuda.synchronize()
+    return (to_np(w), to_np(mu), to_np(cv)), to_np(mll), cs.cpu().numpy()
+
+
+def check(label, cov, X64, th, got, mll, topk):
+    B, K = th[0].shape
+    D = X64.shape[2]
+    for b in range(B):
+        ref = oracle.topk_fit_step(cov, X64[b], *(a[b].astype(np.float64) for a in th), topk)
+        e = param_errors(cov, 1, K, D, tuple(a[b] for a in got), (ref["w"], ref["mu"], ref["cv"]), ref["stats"]["nk"])
+        e_ll = abs(mll[b] - ref["mean_ll"][0]) / abs(ref["mean_ll"][0])
+        print(f"{label} b={b}: mu={e['mu']:.2e} cv={e['cv']:.2e} w={e['w']:.2e} ll={e_ll:.2e}", flush=True)
+        assert e["mu"] <= TOL_F32 and e["cv"] <= TOL_F32 and e["w"] <= TOL_F32 and e_ll <= 1e-6, (label, b, e, e_ll)
+
+
+@pytest.mark.parametrize("cov", ["spherical", "diag"])
+@pytest.mark.parametrize("B,N,D,K,topk", [(1, 3001, 12, 20, 3), (3, 2000, 7, 33, 1), (2, 1500, 16, 40, 16)])
+def test_topk_step_float32(torch_cuda, cov, B, N, D, K, topk):
+    torch = torch_cuda
+    rng = np.random.default_rng(N + K + topk)
+    X = (rng.normal(size=(B, N, D)) + 3.0 * rng.integers(0, 6, size=(B, N, 1)) * rng.normal(size=(B, 1, D))).astype(np.float32)
+    th = theta(rng, cov, B, K, D, X)
+    got, mll, cs = gpu_step(torch, torch.from_numpy(X).cuda(), th, cov, topk)
+    check(f"{cov} B={B} N={N} D={D} K={K} k={topk}", cov, X.astype(np.float64), th, got, mll, topk)
+    assert (cs >= 0).all()
+
+
+def test_topk_with_every_component_is_the_exact_step(torch_cuda):
+    """k >= K: the GPU top-k step and the GPU exact step agree to float32
+    rounding (what the 2^-20 floor drops is below it here)."""
+    import soft_clustering_em_amd as g
+    torch = torch_cuda
+    rng = np.random.default_rng(41)
+    B, N, D, K = 1, 4000, 10, 12
+    X = rng.normal(size=(B, N, D)).astype(np.float32) * 2.0
+    th = theta(rng, "diag", B, K, D, X)
+    Xd = torch.from_numpy(X).cuda()
+    got, mll, _ = gpu_step(torch, Xd, th, "diag", 16)
+    w, mu, cv = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in th)
+    m2 = torch.zeros(B, dtype=torch.float64, device="cuda")
+    g.gmm_fit_step(Xd, w, mu, cv, "diag", mean_loglik=m2)
+    e = param_errors("diag", B, K, D, got, (to_np(w), to_np(mu), to_np(cv)), np.full((B, K), 10.0))
+    assert e["mu"] <= 1e-5 and e["cv"] <= 1e-5 and e["w"] <= 1e-5, e
+    assert abs(mll[0] - float(m2[0])) <= 1e-6 * abs(float(m2[0]))
+
+
+@pytest.mark.parametrize("N,D,K,topk", [(5003, 128, 512, 4), (3000, 100, 300, 2)])
+def test_topk_step_bf16_rows(torch_cuda, N, D, K, topk):
+    """bf16 rows take the large-K top-m (spherical, any K)."""
+    torch = torch_cuda
+    rng = np.random.default_rng(N + topk)
+    centers = 3.0 * rng.standard_normal((K, D))
+    Xf = (centers[rng.integers(0, K, N)] + rng.standard_normal((N, D))).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(Xf)
+    X64 = synth.bf16_bits_to_f32(bits).astype(np.float64)[None]
+    th = theta(rng, "spherical", 1, K, D, X64.astype(np.float32))
+    Xd = torch.from_numpy(np.ascontiguousarray(bits[None]).view(np.int16)).cuda().view(torch.bfloat16)
+    got, mll, cs = gpu_step(torch, Xd, th, "spherical", topk)
+    check(f"bf16 N={N} D={D} K={K} k={topk}", "spherical", X64, th, got, mll, topk)
+
+
+def test_topk_step_is_deterministic(torch_cuda):
+    torch = torch_cuda
+    rng = np.random.default_rng(42)
+    X = rng.normal(size=(1, 20000, 32)).astype(np.float32)
+    th = theta(rng, "diag", 1, 64, 32, X)
+    Xd = torch.from_numpy(X).cuda()
+    a = gpu_step(torch, Xd, th, "diag", 4)
+    b = gpu_step(torch, Xd, th, "diag", 4)
+    for u, v in zip(a[0], b[0]):
+        assert np.array_equal(u, v)
+    assert np.array_equal(a[1], b[1])
