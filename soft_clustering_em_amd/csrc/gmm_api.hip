@@ -748,8 +748,9 @@ static constexpr float kTopkFloor = 0x1p-20f;  // smallest responsibility a top-
 
 struct TkLayout {
   Plan p;
-  size_t off_idx, off_resp, off_logp, off_rinv, off_llrow, off_cnt, off_offsets, off_rows, off_lresp;
-  size_t off_nk, off_sx, off_sxx, off_ll, bytes;
+  size_t off_idx, off_resp, off_logp, off_rinv, off_llpart, off_cnt, off_offsets, off_rows, off_lresp;
+  size_t off_part, off_nk, off_sx, off_sxx, off_ll, bytes;
+  int S;
 };
 
 static gmm_status topk_plan(const gmm_data* d, int32_t K, int32_t cov, int32_t topk, TkLayout* L) {
@@ -766,11 +767,13 @@ static gmm_status topk_plan(const gmm_data* d, int32_t K, int32_t cov, int32_t t
   L->off_resp = o;    o = align_up(o + sizeof(float) * B * N * m);
   L->off_logp = o;    o = align_up(o + sizeof(float) * B * N);
   L->off_rinv = o;    o = align_up(o + sizeof(double) * B * N);
-  L->off_llrow = o;   o = align_up(o + sizeof(double) * B * N);
+  L->off_llpart = o;  o = align_up(o + sizeof(double) * B * ((N + 255) / 256));
   L->off_cnt = o;     o = align_up(o + ivf_ws(p.B, p.N, K));
   L->off_offsets = o; o = align_up(o + sizeof(int64_t) * B * (k + 1));
   L->off_rows = o;    o = align_up(o + sizeof(int32_t) * B * N * m);
   L->off_lresp = o;   o = align_up(o + sizeof(float) * B * N * m);
+  L->S = topk_parts(p.B, p.N, topk, K);
+  L->off_part = o;    o = align_up(o + sizeof(double) * B * k * (size_t)L->S * (1 + 2 * D));
   L->off_nk = o;      o = align_up(o + sizeof(double) * B * k);
   L->off_sx = o;      o = align_up(o + sizeof(double) * B * k * D);
   L->off_sxx = o;     o = align_up(o + sizeof(double) * B * (cov == DIAG ? k * D : k));
@@ -830,10 +833,33 @@ gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t to
   double* nk = reinterpret_cast<double*>(w + L.off_nk);
   double* sx = reinterpret_cast<double*>(w + L.off_sx);
   double* sxx = reinterpret_cast<double*>(w + L.off_sxx);
-  e = launch_topk_stats(data->x, data->dtype == GMM_DT_BF16 ? 1 : 0, p.B, p.N, p.ld_x, p.stride_b, inout->K, (int)p.D,
-                        topk, inout->cov, resp, logp, inout->means, A.offsets, A.rows, A.lresp,
-                        reinterpret_cast<double*>(w + L.off_rinv), reinterpret_cast<double*>(w + L.off_llrow), nk, sx,
-                        sxx, reinterpret_cast<double*>(w + L.off_ll), mean_loglik, s);
+  TopkStepArgs T;
+  T.x = data->x;
+  T.bf16 = data->dtype == GMM_DT_BF16 ? 1 : 0;
+  T.B = p.B;
+  T.N = p.N;
+  T.ld_x = p.ld_x;
+  T.stride_b = p.stride_b;
+  T.K = inout->K;
+  T.D = (int)p.D;
+  T.m = topk;
+  T.cov = inout->cov;
+  T.S = L.S;
+  T.resp = resp;
+  T.logp = logp;
+  T.mu = inout->means;
+  T.offsets = A.offsets;
+  T.rows = A.rows;
+  T.lresp = A.lresp;
+  T.rinv = reinterpret_cast<double*>(w + L.off_rinv);
+  T.llpart = reinterpret_cast<double*>(w + L.off_llpart);
+  T.part = reinterpret_cast<double*>(w + L.off_part);
+  T.nk = nk;
+  T.sx = sx;
+  T.sxx = sxx;
+  T.ll = reinterpret_cast<double*>(w + L.off_ll);
+  T.mean_ll = mean_loglik;
+  e = launch_topk_stats(T, s);
   if (e != hipSuccess) return hip_fail(e, "top-k statistics launch");
   e = launch_mstep_strided(inout->cov, p.B, p.D, inout->K, nk, sx, sxx, p.N, inout->weights, inout->means,
                            inout->covars, reg, nullptr, 0, comp_status, s);

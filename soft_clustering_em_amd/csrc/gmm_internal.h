@@ -173,11 +173,34 @@ hipError_t launch_ivf_lists(const IvfArgs& a, hipStream_t s);
 hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* w, float* cv, hipStream_t s);
 
 // approximate top-k EM statistics (gmm_topk.hip)
-hipError_t launch_topk_stats(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
-                             int D, int m, int cov, const float* resp, const float* logp, const float* mu,
-                             const int64_t* offsets, const int32_t* rows, const float* lresp, double* rinv,
-                             double* llrow, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
-                             hipStream_t s);
+// approximate top-k EM statistics (gmm_topk.hip)
+struct TopkStepArgs {
+  const void* x;              // rows, float32 or bf16 bits
+  int bf16;
+  int64_t B, N, ld_x, stride_b;
+  int K, D, m, cov, S;        // S: contiguous parts each component's list is split into
+  const float* resp;          // (B, N, m) kept responsibilities, best first
+  const float* logp;          // (B, N) log p(x) of the full mixture
+  const float* mu;            // (B, K, D) means entering the step
+  const int64_t* offsets;     // (B, K+1) list offsets
+  const int32_t* rows;        // (B, N m) list rows
+  const float* lresp;         // (B, N m) list responsibilities
+  double* rinv;               // (B, N) scratch: 1 / sum of the kept responsibilities
+  double* llpart;             // (B, ceil(N / 256)) scratch: per-block row log-likelihoods
+  double* part;               // (B, K, S, 1 + 2 D) scratch: per-part statistics
+  double *nk, *sx, *sxx;      // (B, K), (B, K, D), (B, K) or (B, K, D)
+  double *ll, *mean_ll;       // (B); mean_ll may be null
+};
+// parts per component list: about 512 entries each on average, at most 64,
+// and at most 65536 workgroups over all (problem, component, part)
+inline int topk_parts(int64_t B, int64_t N, int m, int K) {
+  int64_t S = (N * m / K + 511) / 512;
+  if (S > 64) S = 64;
+  const int64_t cap = 65536 / (B * K);
+  if (S > cap) S = cap;
+  return S < 1 ? 1 : (int)S;
+}
+hipError_t launch_topk_stats(const TopkStepArgs& a, hipStream_t s);
 
 // Fisher vectors (gmm_fisher.hip)
 hipError_t launch_fisher_replicate(int64_t B, int K, int D, const float* w, const float* mu, const float* var,
