@@ -8,7 +8,8 @@ this module builds it with gcc and marshals numpy arrays through ctypes.
 Sources it follows: "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
 Clustering", Section 2 (E-step score, log-sum-exp responsibilities, M-step
 eqs. 1-3) and Section 4 / Conclusion (multi-assignment by a threshold on the
-final responsibilities); "ML0094 GMM vs K-Means", Mathematical Formulation
+final responsibilities), and its closing discussion (Fisher vectors, kernel
+density estimation); "ML0094 GMM vs K-Means", Mathematical Formulation
 (responsibility-weighted covariance) and its k-means limit (kmeans_step); GMMXX README, Covariance Coverage (the
 four covariance types and their shapes).
 """
@@ -321,3 +322,29 @@ def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6, floor=2.0 ** -20):
     keep = np.full((N, max(int(topk), 1)), -1, dtype=np.int64)
     keep[:, :m] = order
     return dict(w=wo, mu=mo, cv=co, mean_ll=np.array([lse.mean()]), stats=st, flags=fl, keep=keep)
+
+
+def kde_score(Y, X, h):
+    """Log of the Gaussian kernel density estimate at each query row: the
+    other application Flash-GMM's closing discussion names beside Fisher
+    vectors.  With M reference rows x_j and an isotropic bandwidth h, the
+    estimate is a mixture of M equal-weight spherical Gaussians centred on the
+    references with variance h^2:
+      log p(y) = logsumexp_j(-|y - x_j|^2 / (2 h^2)) - log M - (D / 2) log(2 pi h^2).
+    Squared distances by direct differences in float64.  Y: (N, D) or
+    (B, N, D); X: (M, D).  Returns float64 of Y's leading shape."""
+    from scipy.special import logsumexp
+    Y = np.asarray(Y, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    lead = Y.shape[:-1]
+    Y = Y.reshape(-1, Y.shape[-1])
+    M, D = X.shape
+    h = float(h)
+    const = -np.log(M) - 0.5 * D * np.log(2.0 * np.pi * h * h)
+    out = np.empty(Y.shape[0])
+    step = max(1, int(2e7 // max(1, M * D)))
+    for s in range(0, Y.shape[0], step):
+        diff = Y[s:s + step, None, :] - X[None, :, :]
+        d2 = np.einsum("nmd,nmd->nm", diff, diff)
+        out[s:s + step] = logsumexp(-d2 / (2.0 * h * h), axis=1) + const
+    return out.reshape(lead)

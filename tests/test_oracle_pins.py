@@ -692,3 +692,50 @@ def test_topk_em_normalises_over_the_kept_set():
     assert (np.take_along_axis(rfull, np.where(k2 >= 0, k2, 0), axis=1)[k2 >= 0] >= 2.0 ** -20).all()
     _, _, lse = oracle.responsibilities("diag", X, w, mu, cv)
     assert out["mean_ll"][0] <= lse.mean() + 1e-12
+
+
+# ---- kernel density estimation (Flash-GMM, closing discussion)
+
+def test_kde_matches_sklearn_kernel_density():
+    """sklearn's Gaussian KernelDensity (exact tree traversal: rtol = atol = 0)."""
+    from sklearn.neighbors import KernelDensity
+    rng = np.random.default_rng(71)
+    for (M, N, D, h) in [(57, 40, 3, 0.7), (200, 31, 11, 1.9), (1, 5, 4, 0.3)]:
+        X = rng.normal(size=(M, D)) * 2.0 + 1.0
+        Y = rng.normal(size=(N, D)) * 2.0 + 1.0
+        ref = KernelDensity(kernel="gaussian", bandwidth=h).fit(X).score_samples(Y)
+        got = oracle.kde_score(Y, X, h)
+        assert np.allclose(got, ref, rtol=1e-11, atol=1e-11), np.abs(got - ref).max()
+
+
+def test_kde_single_reference_is_the_gaussian_logpdf():
+    rng = np.random.default_rng(72)
+    D, h = 6, 0.45
+    x = rng.normal(size=(1, D))
+    Y = rng.normal(size=(25, D))
+    ref = multivariate_normal(mean=x[0], cov=h * h * np.eye(D)).logpdf(Y)
+    assert np.allclose(oracle.kde_score(Y, x, h), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_kde_is_the_equal_weight_spherical_mixture():
+    """The estimate is the GMM log-likelihood of weights 1/M, means X, variance
+    h^2 (the C oracle's E-step), batched queries included."""
+    rng = np.random.default_rng(73)
+    M, N, D, h = 23, 17, 5, 0.8
+    X = rng.normal(size=(M, D))
+    Y = rng.normal(size=(2, N, D))
+    got = oracle.kde_score(Y, X, h)
+    assert got.shape == (2, N)
+    for b in range(2):
+        _, _, lse = oracle.responsibilities("spherical", Y[b], np.full(M, 1.0 / M), X, np.full(M, h * h))
+        assert np.allclose(got[b], lse, rtol=1e-12, atol=1e-12)
+
+
+def test_kde_integrates_to_one():
+    """A density: in one dimension its integral over a wide grid is 1."""
+    rng = np.random.default_rng(74)
+    X = rng.normal(size=(9, 1)) * 3.0
+    h = 0.6
+    g = np.linspace(-30.0, 30.0, 60001)
+    p = np.exp(oracle.kde_score(g[:, None], X, h))
+    assert abs(np.trapezoid(p, g) - 1.0) < 1e-9
