@@ -248,6 +248,29 @@ size_t gmm_fisher_vector_workspace_bytes(const gmm_data* data, int32_t K);
 gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint32_t flags, float* fv, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Gaussian kernel density estimate (Flash-GMM's closing discussion names
+ * kernel density estimation as another user of the fused log-sum-exp): for
+ * each query row y (queries as (B, N, D) float32, D <= 128) and the M
+ * reference rows x_j of ref ((M, D) float32, row j at ref[j * ld_ref], any
+ * alignment), with bandwidth h,
+ *   logdens[b N + i] = log( (1/M) sum_j N(y_bi | x_j, h^2 I) )
+ *                    = LSE_j(-|y - x_j|^2 / (2 h^2)) - log M - (D/2) log(2 pi h^2),
+ * float32 out (B, N); the references are shared by every problem.  The
+ * cross terms run in float32 on the matrix cores after the references are
+ * centred at their mean; the terms within 2^-30 of a row's largest are then
+ * recomputed in float64 from direct differences (up to 8 per row), which
+ * makes the log density exact to float32 rounding.  A row with more than 8
+ * such terms keeps the float32 terms: within about
+ *   ln 2 * lam * eps * (2 DP |y - c| |x - c| + |y - c|^2 + |x - c|^2)
+ * of exact (lam = log2(e) / (2 h^2), c the reference mean, DP = D rounded up
+ * to 16, 32, 64 or 128, eps = 2^-24; the |x - c| of the terms that dominate
+ * the sum).  1 <= M <= 2^30, h > 0 with 1 / (2 h^2) finite in float32.  N = 0 returns
+ * GMM_OK and launches nothing.  Workspace: gmm_kde_workspace_bytes (the
+ * centred references, (M rounded up to 64) * (DP + 1) floats).  Deterministic. */
+size_t gmm_kde_workspace_bytes(const gmm_data* queries, int64_t M);
+gmm_status gmm_kde_score(const gmm_data* queries, const float* ref, int64_t M, int64_t ld_ref, double bandwidth,
+                         float* logdens, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gmm_status_str(int32_t status);
 

@@ -254,6 +254,32 @@ def gmm_topk_fit_workspace_bytes(X, K, cov, topk) -> int:
     return int(_abi.lib().gmm_topk_fit_workspace_bytes(ctypes.byref(d), int(K), _cov_code(cov), int(topk)))
 
 
+def gmm_kde_workspace_bytes(Y, M) -> int:
+    d = _data(Y)
+    return int(_abi.lib().gmm_kde_workspace_bytes(ctypes.byref(d), int(M)))
+
+
+def gmm_kde_score(Y, ref, bandwidth, out=None, ws=None, stream=None):
+    """Log of the Gaussian kernel density estimate with bandwidth h over the
+    reference rows ref ((M, D) float32) at the query rows Y ((N, D) or
+    (B, N, D) float32): float32 of Y's leading shape."""
+    torch = _torch()
+    d = _data(Y)
+    if ref.dim() != 2 or ref.shape[1] != d.D or ref.dtype != torch.float32:
+        raise ValueError("ref must be (M, D) float32 with the queries' D")
+    if ref.shape[0] > 0 and ref.stride(1) != 1:
+        raise ValueError("ref needs unit stride along D")
+    M = int(ref.shape[0])
+    if out is None:
+        out = torch.empty(Y.shape[:-1], dtype=torch.float32, device=Y.device)
+    if ws is None:
+        n = gmm_kde_workspace_bytes(Y, M)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=Y.device)
+    _abi.check(_abi.lib().gmm_kde_score(ctypes.byref(d), _ptr(ref), M, int(ref.stride(0)), float(bandwidth), _ptr(out),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def gmm_topk_fit_step(X, w, mu, cv, cov, topk, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None,
                       stream=None):
     """One approximate top-k EM iteration in place (each row keeps its topk

@@ -22,7 +22,8 @@ GMM_OK, GMM_ERR_INVALID_ARG, GMM_ERR_UNSUPPORTED, GMM_ERR_WORKSPACE, GMM_ERR_HIP
 EXPORTED = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
             "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
             "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector",
-            "gmm_topk_fit_workspace_bytes", "gmm_topk_fit_step", "gmm_status_str",
+            "gmm_topk_fit_workspace_bytes", "gmm_topk_fit_step", "gmm_kde_workspace_bytes", "gmm_kde_score",
+            "gmm_status_str",
             "gmm_last_error", "gmm_version"]
 
 
@@ -88,13 +89,17 @@ def lib() -> ctypes.CDLL:
         L.gmm_fisher_vector_workspace_bytes.restype = ctypes.c_size_t
         L.gmm_fisher_vector.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams), ctypes.c_uint32, P, P,
                                         ctypes.c_size_t, P]
+        L.gmm_kde_workspace_bytes.argtypes = [ctypes.POINTER(GmmData), ctypes.c_int64]
+        L.gmm_kde_workspace_bytes.restype = ctypes.c_size_t
+        L.gmm_kde_score.argtypes = [ctypes.POINTER(GmmData), P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, P, P,
+                                    ctypes.c_size_t, P]
         L.gmm_topk_fit_workspace_bytes.argtypes = [ctypes.POINTER(GmmData), ctypes.c_int32, ctypes.c_int32,
                                                    ctypes.c_int32]
         L.gmm_topk_fit_workspace_bytes.restype = ctypes.c_size_t
         L.gmm_topk_fit_step.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams), ctypes.c_int32,
                                         ctypes.POINTER(GmmOptions), P, P, P, ctypes.c_size_t, P]
         for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_predict_proba_topm, L.gmm_ivf_lists,
-                  L.gmm_kmeans_step, L.gmm_fisher_vector, L.gmm_topk_fit_step):
+                  L.gmm_kmeans_step, L.gmm_fisher_vector, L.gmm_topk_fit_step, L.gmm_kde_score):
             f.restype = ctypes.c_int
         L.gmm_status_str.argtypes = [ctypes.c_int32]
         L.gmm_status_str.restype = ctypes.c_char_p

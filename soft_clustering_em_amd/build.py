@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = ["gmm_api.hip", "gmm_aux.hip", "gmm_estep.hip", "gmm_topm.hip", "gmm_largek.hip", "gmm_ivf.hip", "gmm_kmeans.hip", "gmm_fisher.hip", "gmm_topk.hip"]
+SOURCES = ["gmm_api.hip", "gmm_aux.hip", "gmm_estep.hip", "gmm_topm.hip", "gmm_largek.hip", "gmm_ivf.hip", "gmm_kmeans.hip", "gmm_fisher.hip", "gmm_topk.hip", "gmm_kde.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

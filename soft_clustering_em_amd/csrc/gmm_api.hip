@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 namespace gmm {
@@ -864,6 +865,90 @@ gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t to
   e = launch_mstep_strided(inout->cov, p.B, p.D, inout->K, nk, sx, sxx, p.N, inout->weights, inout->means,
                            inout->covars, reg, nullptr, 0, comp_status, s);
   if (e != hipSuccess) return hip_fail(e, "M-step launch");
+  return GMM_OK;
+}
+
+// ---- Gaussian kernel density estimate: centred references, then the
+// streaming log-sum-exp kernel
+struct KdeLayout {
+  int DP;
+  int64_t Mp;
+  size_t off_cen, off_xc, off_bx, bytes;
+};
+
+static gmm_status kde_plan(const gmm_data* q, int64_t M, KdeLayout* L) {
+  gmm_status st = check_data(q);
+  if (st != GMM_OK) return st;
+  if (q->dtype != GMM_DT_F32) return fail(GMM_ERR_UNSUPPORTED, "kernel density: float32 query rows only");
+  if (q->D > 128) return fail(GMM_ERR_UNSUPPORTED, "kernel density: D <= 128 (got %lld)", (long long)q->D);
+  if (M < 1) return fail(GMM_ERR_INVALID_ARG, "kernel density needs M >= 1 reference rows (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 30)) return fail(GMM_ERR_UNSUPPORTED, "kernel density: M <= 2^30");
+  const int64_t nqb = (q->N + kde_query_rows() - 1) / kde_query_rows();
+  if (q->B * nqb >= ((int64_t)1 << 31)) return fail(GMM_ERR_UNSUPPORTED, "kernel density: too many query rows");
+  L->DP = q->D <= 16 ? 16 : q->D <= 32 ? 32 : q->D <= 64 ? 64 : 128;
+  const int64_t T = kde_tile_rows();
+  L->Mp = (M + T - 1) / T * T;
+  size_t o = 0;
+  L->off_cen = o; o = align_up(o + sizeof(float) * (size_t)L->DP);
+  L->off_xc = o;  o = align_up(o + sizeof(float) * (size_t)L->Mp * L->DP);
+  L->off_bx = o;  o = align_up(o + sizeof(float) * (size_t)L->Mp);
+  L->bytes = o;
+  return GMM_OK;
+}
+
+size_t gmm_kde_workspace_bytes(const gmm_data* queries, int64_t M) {
+  KdeLayout L;
+  if (kde_plan(queries, M, &L) != GMM_OK) return 0;
+  return L.bytes;
+}
+
+gmm_status gmm_kde_score(const gmm_data* queries, const float* ref, int64_t M, int64_t ld_ref, double bandwidth,
+                         float* logdens, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KdeLayout L;
+  gmm_status st = kde_plan(queries, M, &L);
+  if (st != GMM_OK) return st;
+  if (!ref) return fail(GMM_ERR_INVALID_ARG, "ref must be non-NULL");
+  if (ld_ref < queries->D)
+    return fail(GMM_ERR_INVALID_ARG, "ld_ref (%lld) < D (%lld)", (long long)ld_ref, (long long)queries->D);
+  if (!(bandwidth > 0.0) || !std::isfinite(bandwidth))
+    return fail(GMM_ERR_INVALID_ARG, "bandwidth must be finite and > 0");
+  const double LOG2E = 1.4426950408889634074;
+  const float lamf = (float)(LOG2E / (2.0 * bandwidth * bandwidth));
+  if (!(lamf > 0.f) || !std::isfinite(lamf))
+    return fail(GMM_ERR_INVALID_ARG, "bandwidth %g is outside the float32 range of 1 / (2 h^2)", bandwidth);
+  const int64_t rows = queries->B * queries->N;
+  if (rows > 0 && !logdens) return fail(GMM_ERR_INVALID_ARG, "logdens must be non-NULL");
+  if (!ws || ((uintptr_t)ws) % kAlign != 0) return fail(GMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.bytes) return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.bytes);
+  if (rows == 0) return GMM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  float* cen = reinterpret_cast<float*>(w + L.off_cen);
+  float* xc = reinterpret_cast<float*>(w + L.off_xc);
+  float* bx = reinterpret_cast<float*>(w + L.off_bx);
+  hipError_t e = launch_kde_prep(ref, M, ld_ref, (int)queries->D, L.DP, L.Mp, (double)lamf, cen, xc, bx, s);
+  if (e != hipSuccess) return hip_fail(e, "kernel density reference launch");
+  KdeArgs a;
+  a.y = static_cast<const float*>(queries->x);
+  a.B = queries->B;
+  a.N = queries->N;
+  a.ld = queries->ld_x;
+  a.stride_b = queries->B > 1 ? queries->stride_b : 0;
+  a.D = (int)queries->D;
+  a.cen = cen;
+  a.xc = xc;
+  a.bx = bx;
+  a.Mp = L.Mp;
+  a.lam = (double)lamf;
+  a.s2 = 2.f * lamf;
+  a.lam_exact = LOG2E / (2.0 * bandwidth * bandwidth);
+  a.ref = ref;
+  a.ld_ref = ld_ref;
+  a.cnst = -std::log((double)M) - 0.5 * (double)queries->D * std::log(2.0 * M_PI * bandwidth * bandwidth);
+  a.out = logdens;
+  e = launch_kde(a, L.DP, s);
+  if (e != hipSuccess) return hip_fail(e, "kernel density launch");
   return GMM_OK;
 }
 

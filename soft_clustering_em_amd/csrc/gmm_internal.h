@@ -202,6 +202,29 @@ inline int topk_parts(int64_t B, int64_t N, int m, int K) {
 }
 hipError_t launch_topk_stats(const TopkStepArgs& a, hipStream_t s);
 
+// Gaussian kernel density estimate (gmm_kde.hip)
+struct KdeArgs {
+  const float* y;            // query rows: problem b, row i, feature d at y[b stride_b + i ld + d]
+  int64_t B, N, ld, stride_b;
+  int D;
+  const float* cen;          // (DP) reference mean, zero past D
+  const float* xc;           // (Mp, DP) centred references, zero-padded
+  const float* bx;           // (Mp) -lam |x - c|^2, -inf past M
+  int64_t Mp;                // references padded to whole tiles
+  double lam;                // log2(e) / (2 h^2), the float32 value widened
+  float s2;                  // 2 lam
+  double lam_exact;          // log2(e) / (2 h^2) in float64, for the exact rescoring
+  const float* ref;          // the caller's references, row j at ref[j ld_ref]
+  int64_t ld_ref;
+  double cnst;               // -log M - (D / 2) log(2 pi h^2)
+  float* out;                // (B, N) log densities
+};
+int kde_query_rows();        // query rows per workgroup
+int kde_tile_rows();         // reference rows per tile (Mp is a multiple)
+hipError_t launch_kde_prep(const float* x, int64_t M, int64_t ld, int D, int DP, int64_t Mp, double lam, float* cen,
+                           float* xc, float* bx, hipStream_t s);
+hipError_t launch_kde(const KdeArgs& a, int DP, hipStream_t s);
+
 // Fisher vectors (gmm_fisher.hip)
 hipError_t launch_fisher_replicate(int64_t B, int K, int D, const float* w, const float* mu, const float* var,
                                    float* wr, float* mur, float* varr, hipStream_t s);

@@ -260,6 +260,27 @@ def ivf_bf16(N=10_000_000, D=128, K=4096, seed=0, iters=10, chunk=1 << 16) -> Wo
                     topm=(4, 0.1), meta=dict(chunk=chunk))
 
 
+def kde_inputs(N=1_000_000, M=65_536, D=64, seed=0, offset=0.0):
+    """Kernel density inputs: N query rows and M reference rows drawn from the
+    same blob mixture as diag_large (means ~ N(0, 4I), per-dimension std
+    U[0.3, 1.5], Dirichlet(2) weights, K = 256 blobs), shifted by `offset` in
+    every dimension; bandwidth by Scott's rule, h = s M^(-1/(D+4)) with s the
+    root mean per-dimension variance of the references.  Returns (Y (N, D),
+    X (M, D)) float32 and h."""
+    rng = np.random.default_rng([seed, 7])
+    K = 256
+    centers = 2.0 * rng.standard_normal((K, D)) + offset
+    stds = rng.uniform(0.3, 1.5, (K, D))
+    pis = rng.dirichlet(np.full(K, 2.0))
+    X = _blobs(rng, centers, stds, rng.choice(K, M, p=pis))
+    Y = np.empty((N, D), np.float32)
+    step = 1 << 18
+    for s0 in range(0, N, step):
+        Y[s0:s0 + step] = _blobs(rng, centers, stds, rng.choice(K, min(step, N - s0), p=pis))
+    s = float(np.sqrt(X.astype(np.float64).var(0).mean()))
+    return Y, X, s * M ** (-1.0 / (D + 4))
+
+
 WORKLOADS = {
     "spherical_small": spherical_small,
     "diag_large": diag_large,

@@ -324,3 +324,39 @@ def test_topk_fit_step_window_and_arguments():
     prm = _abi.GmmParams(32, _abi.COV_TIED, p, p, p)
     assert L.gmm_topk_fit_step(ctypes.byref(d), ctypes.byref(prm), 4, None, None, None, ctypes.c_void_p(1 << 20),
                                1 << 30, None) == _abi.GMM_ERR_UNSUPPORTED
+
+
+def test_kde_workspace_size_and_bad_arguments_before_the_device():
+    L = _abi.lib()
+    d = _data(1000, 5, B=2)
+    # D = 5 -> 16 padded features; M = 65 -> two 64-row tiles: mean (256 B aligned),
+    # centred references 128 x 16 floats, norms 128 floats
+    n = L.gmm_kde_workspace_bytes(ctypes.byref(d), 65)
+    assert n == 256 + 128 * 16 * 4 + 512
+    assert L.gmm_kde_workspace_bytes(ctypes.byref(d), 0) == 0
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    wide = _data(100, 129)
+    half = _data(100, 8, dtype=_abi.DT_BF16)
+    cases = {
+        "M = 0": ((ctypes.byref(d), p, 0, 5, 1.0, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "h = 0": ((ctypes.byref(d), p, 65, 5, 0.0, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "h < 0": ((ctypes.byref(d), p, 65, 5, -1.0, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "h nan": ((ctypes.byref(d), p, 65, 5, float("nan"), p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "h inf": ((ctypes.byref(d), p, 65, 5, float("inf"), p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "1/(2h^2) overflows": ((ctypes.byref(d), p, 65, 5, 1e-30, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "ld_ref < D": ((ctypes.byref(d), p, 65, 4, 1.0, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "null ref": ((ctypes.byref(d), None, 65, 5, 1.0, p, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "null out": ((ctypes.byref(d), p, 65, 5, 1.0, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
+        "ws size": ((ctypes.byref(d), p, 65, 5, 1.0, p, ws, n - 256, None), _abi.GMM_ERR_WORKSPACE),
+        "ws align": ((ctypes.byref(d), p, 65, 5, 1.0, p, ctypes.c_void_p((1 << 20) + 64), n, None),
+                     _abi.GMM_ERR_WORKSPACE),
+        "D > 128": ((ctypes.byref(wide), p, 65, 129, 1.0, p, ws, 1 << 30, None), _abi.GMM_ERR_UNSUPPORTED),
+        "bf16 queries": ((ctypes.byref(half), p, 65, 8, 1.0, p, ws, 1 << 30, None), _abi.GMM_ERR_UNSUPPORTED),
+    }
+    for name, (args, want) in cases.items():
+        assert L.gmm_kde_score(*args) == want, name
+        assert L.gmm_last_error() != b"", name
+    # no query rows: accepted, nothing launched
+    e = _data(0, 5)
+    assert L.gmm_kde_score(ctypes.byref(e), p, 65, 5, 1.0, None, ws, n, None) == _abi.GMM_OK

@@ -1,0 +1,121 @@
+"""Parity of gmm_kde_score (the Gaussian kernel density estimate the closing
+discussion of the Flash-GMM paper names) against the float64 oracle
+(oracle.kde_score, pinned by sklearn's KernelDensity, the one-point Gaussian
+logpdf, the mixture log-likelihood and a 1-D integral), query by query.
+
+Bar: the float32 bar of the library, |error| <= 1e-4 max(1, |log p|), and at
+most twice the rounding bound the header states for the float32 contraction
+(with the largest |x - c| over the references, which over-covers the terms
+that dominate), plus the float32 rounding of the output."""
+import numpy as np
+import pytest
+
+import oracle
+from soft_clustering_em_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import soft_clustering_em_amd._abi as abi
+    abi.lib()
+    return torch
+
+
+def run(torch, Y, X, h):
+    import soft_clustering_em_amd as g
+    out = g.gmm_kde_score(torch.from_numpy(Y).cuda(), torch.from_numpy(X).cuda(), h)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def bound(Y, X, h):
+    """Twice the header's rounding bound, per query (nats)."""
+    D = X.shape[1]
+    DP = 16 if D <= 16 else 32 if D <= 32 else 64 if D <= 64 else 128
+    c = X.astype(np.float64).mean(0)
+    ry = np.linalg.norm(Y.astype(np.float64) - c, axis=-1)
+    rx = np.linalg.norm(X.astype(np.float64) - c, axis=-1).max()
+    lam = np.log2(np.e) / (2.0 * h * h)
+    return 2.0 * np.log(2.0) * lam * EPS * (2 * DP * ry * rx + ry * ry + rx * rx)
+
+
+def check(label, got, ref, Y, X, h):
+    err = np.abs(got - ref)
+    tol = 1e-4 * np.maximum(1.0, np.abs(ref))
+    lim = bound(Y, X, h) + 2 * EPS * np.abs(ref)
+    print(f"{label}: max err {err.max():.2e}, max err/bar {(err / tol).max():.2e}, max err/bound {(err / lim).max():.2e}",
+          flush=True)
+    assert (err <= tol).all(), (label, err.max())
+    assert (err <= lim).all(), (label, (err / lim).max())
+
+
+def blobs(rng, n, D, K=12, spread=3.0, offset=0.0):
+    C = spread * rng.standard_normal((K, D)) + offset
+    return (C[rng.integers(0, K, n)] + rng.standard_normal((n, D))).astype(np.float32)
+
+
+@pytest.mark.parametrize("B,N,M,D,h,offset", [
+    (1, 1000, 777, 5, 0.7, 0.0),     # ragged queries (7 x 128 + 104) and references (12 x 64 + 9)
+    (1, 517, 300, 17, 1.1, 20.0),    # far from the origin: centring at the reference mean
+    (3, 300, 1500, 64, 2.0, 0.0),    # batched queries sharing the references
+    (1, 129, 64, 128, 3.0, -5.0),    # one reference tile, 128 features
+    (1, 2000, 65, 100, 2.5, 0.0),    # a last tile with one reference
+    (1, 64, 1, 8, 0.5, 0.0),         # a single reference: a Gaussian log-density
+    (2, 1, 200, 32, 1.0, 0.0),       # one query per problem
+])
+def test_kde_matches_the_oracle(torch_cuda, B, N, M, D, h, offset):
+    rng = np.random.default_rng(1000 * D + M)
+    X = blobs(rng, M, D, offset=offset)
+    Y = blobs(rng, B * N, D, offset=offset).reshape(B, N, D)
+    Yin = Y[0] if B == 1 else Y
+    got = run(torch_cuda, Yin, X, h)
+    ref = oracle.kde_score(Yin, X, h)
+    assert got.shape == ref.shape
+    check(f"B={B} N={N} M={M} D={D} h={h}", got, ref, Yin, X, h)
+
+
+def test_kde_batched_equals_separate_calls_and_is_deterministic(torch_cuda):
+    torch = torch_cuda
+    rng = np.random.default_rng(5)
+    X = blobs(rng, 333, 24)
+    Y = blobs(rng, 3 * 250, 24).reshape(3, 250, 24)
+    a = run(torch, Y, X, 1.3)
+    b = run(torch, Y, X, 1.3)
+    assert np.array_equal(a, b)
+    for i in range(3):
+        assert np.array_equal(a[i], run(torch, np.ascontiguousarray(Y[i]), X, 1.3))
+
+
+def test_kde_of_the_references_themselves(torch_cuda):
+    """Queries that are reference rows: the dominant term has distance zero."""
+    rng = np.random.default_rng(6)
+    X = blobs(rng, 500, 16, spread=5.0)
+    h = 0.2
+    got = run(torch_cuda, X.copy(), X, h)
+    ref = oracle.kde_score(X, X, h)
+    check("self", got, ref, X, X, h)
+
+
+def test_kde_no_queries(torch_cuda):
+    torch = torch_cuda
+    import soft_clustering_em_amd as g
+    out = g.gmm_kde_score(torch.zeros(0, 8, device="cuda"), torch.ones(10, 8, device="cuda"), 1.0)
+    assert out.shape == (0,)
+
+
+def test_kde_full_size_sampled(torch_cuda):
+    """1M queries against 65,536 references in 64 dimensions (the size the
+    benchmark times), checked on 256 sampled queries."""
+    torch = torch_cuda
+    Y, X, h = synth.kde_inputs()
+    got = run(torch, Y, X, h)
+    assert np.isfinite(got).all()
+    pick = np.sort(np.random.default_rng(9).choice(Y.shape[0], 256, replace=False))
+    ref = oracle.kde_score(Y[pick], X, h)
+    check(f"full N={Y.shape[0]} M={X.shape[0]} h={h:.3f}", got[pick], ref, Y[pick], X, h)
