@@ -112,13 +112,79 @@ def cpu_baseline(wl, budget_s=20.0, max_steps=4, target_macs=2e10):
                       f"{t:.2f} s/iteration"}
 
 
+def run_kde(args, torch, g, synth):
+    """Gaussian kernel density estimate: 1,000,000 query rows against 65,536
+    reference rows, D = 64, float32, bandwidth by Scott's rule.  A step is one
+    gmm_kde_score call (reference centring, then the streaming kernel)."""
+    Y, X, h = synth.kde_inputs()
+    N, D = Y.shape
+    M = X.shape[0]
+    Yd, Xd = torch.from_numpy(Y).cuda(), torch.from_numpy(X).cuda()
+    out = torch.empty(N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(g.gmm_kde_workspace_bytes(Yd, M), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        g.gmm_kde_score(Yd, Xd, h, out=out, ws=ws)
+    torch.cuda.synchronize()
+    # the library launches on torch's current stream, where these events are recorded
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        g.gmm_kde_score(Yd, Xd, h, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = N * M
+    flops = 2 * D * pairs  # the cross-term contraction y . x
+    achieved = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "kernel density: query*reference pairs/s; % of the float32 MFMA peak",
+        "value": pairs / wall,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "kde", "N": N, "M": M, "D": D, "bandwidth": h},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_FP32_MFMA,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA,
+            "traffic": None,
+            "kernel": "kernel density call (centring kernels + streaming kernel)",
+            "kernel_ms": ms,
+            "flops_per_launch": flops,
+            "peak_note": "2 D flops per pair (the cross terms on v_mfma_f32_16x16x4_f32)",
+        },
+        "mean_logdens": float(out.double().mean().item()),
+    }
+    if not args.no_cpu:
+        import oracle
+        q = 2000
+        t0 = time.perf_counter()
+        oracle.kde_score(Y[:q], X, h)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": q * M / t, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle.kde_score (numpy float64, direct differences) on the first {q} "
+                                         f"queries against all {M} references, {t:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="diag_large",
-                    choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16"])
+                    choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (traffic counter calibration)")
@@ -133,6 +199,9 @@ def main():
 
     dev = "cuda"
     torch.cuda.init()
+    if args.workload == "kde":
+        run_kde(args, torch, g, synth)
+        return
     wl = synth.WORKLOADS[args.workload]()
     if wl.xdtype == "bf16":
         X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.bfloat16)
