@@ -13,9 +13,10 @@
 //     distance unchanged and keeps the expanded form below well conditioned)
 //     and stored zero-padded to DP features and whole 64-row tiles, with their
 //     scaled squared norms, by three small kernels;
-//   * a workgroup holds 128 query rows in registers (four waves, two 16-row
-//     blocks each) and walks every reference tile, double-buffered in LDS with
-//     one barrier per tile;
+//   * a workgroup holds 64 query rows in registers (four waves, one 16-row
+//     block each, at most 128 registers so that four waves share a SIMD) and
+//     walks every reference tile, double-buffered in LDS with one barrier per
+//     tile;
 //   * the cross terms y . x run on v_mfma_f32_16x16x4_f32; for the MFMA step
 //     s, lane group g (lane / 16) supplies feature g DP/4 + s of its query row
 //     and of its reference column, so a lane's features are contiguous and its
@@ -50,8 +51,10 @@ namespace gmm {
 namespace {
 
 constexpr int kKdeTile = 64;   // reference rows per LDS tile
-constexpr int kKdeRB = 2;      // 16-row query blocks per wave
-constexpr int kKdeQ = 4 * 16 * kKdeRB;  // query rows per workgroup
+constexpr int kKdeRB = 1;      // 16-row query blocks per wave
+constexpr int kKdeWaves = 4;   // waves per workgroup, sharing each reference tile
+constexpr int kKdeThreads = 64 * kKdeWaves;
+constexpr int kKdeQ = kKdeWaves * 16 * kKdeRB;  // query rows per workgroup
 constexpr float kKdeBand = 30.f;        // log2 units below the running maximum that are rescored
 constexpr int kKdeCap = 8;              // rescored references per row
 
@@ -102,14 +105,15 @@ __global__ void __launch_bounds__(256) kde_norms_kernel(const float* __restrict_
 }
 
 template <int DP>
-__global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
+__global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(KdeArgs A) {
   constexpr int KS = DP / 4;    // MFMA steps; lane group g holds features g KS .. g KS + KS - 1
   constexpr int RS = DP + 4;    // LDS row stride in floats (16-byte aligned rows)
   constexpr int RB = kKdeRB;
   constexpr int NT = kKdeTile / 16;
-  constexpr int PER = kKdeTile * DP / 4 / 256;  // 16-byte pieces of a tile per thread
+  constexpr int NP = kKdeTile * DP / 4;                        // 16-byte pieces of a tile
+  constexpr int PER = (NP + kKdeThreads - 1) / kKdeThreads;    // per thread
   constexpr double LN2 = 0.69314718055994530942;
-  static_assert(PER >= 1 && KS % 4 == 0, "tile shape");
+  static_assert(KS % 4 == 0 && kKdeTile <= kKdeThreads, "tile shape");
   __shared__ float xs[2][kKdeTile * RS];
   __shared__ float bs[2][kKdeTile];
   __shared__ float ays[kKdeQ];
@@ -127,7 +131,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
   float a[RB][KS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = q0 + 32 * wv + 16 * rb + c16;
+    const int64_t row = q0 + 16 * RB * wv + 16 * rb + c16;
     const bool ok = row < A.N;
     double ss = 0.0;
 #pragma unroll
@@ -140,7 +144,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
     // the row's four feature quarters sit in lanes c16, c16 + 16, + 32, + 48
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    if (g == 0) ays[32 * wv + 16 * rb + c16] = (float)(-A.lam * ss);
+    if (g == 0) ays[16 * RB * wv + 16 * rb + c16] = (float)(-A.lam * ss);
   }
 
   // ---- reference tiles: fetched into registers one tile ahead, stored to the idle LDS buffer
@@ -149,18 +153,19 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
   auto fetch = [&](int64_t t) {
     const floatx4* src = reinterpret_cast<const floatx4*>(A.xc + t * kKdeTile * DP);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) pf[i] = src[threadIdx.x + 256 * i];
+    for (int i = 0; i < PER; ++i)
+      if (NP % kKdeThreads == 0 || threadIdx.x + kKdeThreads * i < NP) pf[i] = src[threadIdx.x + kKdeThreads * i];
     if (threadIdx.x < kKdeTile) pb = A.bx[t * kKdeTile + threadIdx.x];
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = (threadIdx.x + 256 * i) * 4;
-      *reinterpret_cast<floatx4*>(&xs[buf][(e / DP) * RS + e % DP]) = pf[i];
+      const int e = (threadIdx.x + kKdeThreads * i) * 4;
+      if (NP % kKdeThreads == 0 || e < 4 * NP) *reinterpret_cast<floatx4*>(&xs[buf][(e / DP) * RS + e % DP]) = pf[i];
     }
     if (threadIdx.x < kKdeTile) bs[buf][threadIdx.x] = pb;
   };
-  for (int i = threadIdx.x; i < kKdeQ; i += 256) cn[i] = 0;
+  for (int i = threadIdx.x; i < kKdeQ; i += kKdeThreads) cn[i] = 0;
   fetch(0);
   stash(0);
   __syncthreads();  // tile 0, the row norms and the list counts visible
@@ -172,7 +177,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      ay[rb][v] = ays[32 * wv + 16 * rb + 4 * g + v];
+      ay[rb][v] = ays[16 * RB * wv + 16 * rb + 4 * g + v];
       mx[rb][v] = -INFINITY;
       sm[rb][v] = 0.f;
       lost[rb][v] = -INFINITY;
@@ -227,7 +232,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
         // terms near the running maximum: listed for the exact rescoring (padding
         // scores are -inf).  A row's list is touched only by its own 16 lanes of
         // this wave, whose LDS operations execute in program order.
-        const int pr = 32 * wv + 16 * rb + 4 * g + v;
+        const int pr = 16 * RB * wv + 16 * rb + 4 * g + v;
         if (mn > mo && c16 == 0) {  // the maximum rose: drop the listed terms now below the band
           const int n = min(cn[pr], kKdeCap);
           int k = 0;
@@ -266,7 +271,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float st = row16_sum(sm[rb][v]);
-      const int pr = 32 * wv + 16 * rb + 4 * g + v;
+      const int pr = 16 * RB * wv + 16 * rb + 4 * g + v;
       const int64_t row = q0 + pr;
       const int cnt = min(cn[pr], kKdeCap);
       const double m = (double)mx[rb][v];
@@ -309,7 +314,7 @@ __global__ void __launch_bounds__(256) kde_kernel(KdeArgs A) {
 template <int DP>
 hipError_t launch_kde_dp(const KdeArgs& a, hipStream_t s) {
   const int64_t nqb = (a.N + kKdeQ - 1) / kKdeQ;
-  hipLaunchKernelGGL(kde_kernel<DP>, dim3((unsigned)(a.B * nqb)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kde_kernel<DP>, dim3((unsigned)(a.B * nqb)), dim3(kKdeThreads), 0, s, a);
   return hipGetLastError();
 }
 
