@@ -113,3 +113,25 @@ def test_topk_step_is_deterministic(torch_cuda):
     for u, v in zip(a[0], b[0]):
         assert np.array_equal(u, v)
     assert np.array_equal(a[1], b[1])
+
+
+def test_topk_step_full_size_properties(torch_cuda):
+    """1M rows x D = 64, K = 256 (the diagonal benchmark workload), k = 4: the
+    weights sum to 1, no component fails, and per row log sum over the kept
+    set lies between log p(x) - log K and log p(x), so the step's mean LL lies
+    between the exact step's minus log K and the exact step's."""
+    import soft_clustering_em_amd as g
+    torch = torch_cuda
+    wl = synth.diag_large()
+    X = torch.from_numpy(wl.X).cuda()
+    th = tuple(np.ascontiguousarray(a) for a in (wl.w0, wl.mu0, wl.cv0))
+    got, mll, cs = gpu_step(torch, X, th, "diag", 4)
+    w, mu, cv = (torch.from_numpy(a).cuda() for a in th)
+    m2 = torch.zeros(1, dtype=torch.float64, device="cuda")
+    g.gmm_fit_step(X, w, mu, cv, "diag", mean_loglik=m2)
+    exact = float(m2[0])
+    print(f"full size: top-k mean LL {mll[0]:.6f}, exact {exact:.6f}", flush=True)
+    assert (cs >= 0).all()
+    assert abs(float(got[0].astype(np.float64).sum()) - 1.0) < 1e-5
+    assert exact - np.log(256) - 1e-6 <= mll[0] <= exact + 1e-6 * abs(exact)
+    assert np.isfinite(got[1]).all() and (got[2] > 0).all()
