@@ -14,7 +14,7 @@
 //   3. per row the candidates are sorted (score descending, index ascending),
 //      and LSE, responsibilities and the kept ranks follow in float64.
 // A row with more than CAP candidates is rescored over all K components by
-// one wave.
+// one wave (the workgroup's waves take such rows in turn).
 #include "gmm_device.h"
 #include "gmm_internal.h"
 
@@ -172,7 +172,10 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       for (int w2 = 0; w2 < NW; ++w2) mx = fmaxf(mx, redm[w2 * T + p]);
       Mt[v] = mx;
     }
-    // ---- candidates: rescored exactly; the rest summed as float32 terms
+    // ---- candidates: first counted (each takes a slot), the rest summed as
+    // float32 terms; then, in rows whose candidates fit the list, rescored
+    // exactly (a row past CAP is rescored over all K below instead)
+    int slotv[NT][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int p = 4 * (lane >> 4) + v;
@@ -181,20 +184,30 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float lv = (float)lg[nt][v];
+        slotv[nt][v] = -1;
         if (valid && lv >= Mt[v] - DELTA) {
-          const int k = wv * KW + nt * 16 + (lane & 15);
-          const double ex = exact_score<COV, DP, false>(A, b, k, D, raw + p * DP);
-          const int slot = atomicAdd(&cnt[p], 1);
-          if (slot < CAP) {
-            cl[p * CAP + slot] = ex;
-            ck[p * CAP + slot] = k;
-          }
+          slotv[nt][v] = atomicAdd(&cnt[p], 1);
         } else if (valid && lv > -INFINITY) {
           nc += __builtin_amdgcn_exp2f(lv - Mt[v]);
         }
       }
       nc = row16_sum(nc);
       if ((lane & 15) == 0) rednc[wv * T + p] = (double)nc;
+    }
+    __syncthreads();  // every row's candidate count is final
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = 4 * (lane >> 4) + v;
+      const bool fits = cnt[p] <= CAP;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int slot = slotv[nt][v];
+        if (slot >= 0 && fits) {
+          const int k = wv * KW + nt * 16 + (lane & 15);
+          cl[p * CAP + slot] = exact_score<COV, DP, false>(A, b, k, D, raw + p * DP);
+          ck[p * CAP + slot] = k;
+        }
+      }
     }
     __syncthreads();
 
@@ -246,9 +259,11 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
     }
     __syncthreads();
 
-    // ---- rows with more than CAP candidates: all K components, one wave
-    if (wv == 0) {
-      for (int p = 0; p < T; ++p) {
+    // ---- rows with more than CAP candidates: all K components, one wave per
+    // row (row p to wave p mod NW); no barrier inside, every wave reaches the
+    // next tile's
+    {
+      for (int p = wv; p < T; p += NW) {
         const int64_t row = row0 + p;
         if (row >= N || cnt[p] <= CAP) continue;  // uniform across the wave
         constexpr int PER = (kTopmMaxK + 63) / 64;
