@@ -113,13 +113,17 @@ __device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D
   const float* mu = A.mu + ((size_t)b * A.K + k) * D;
   const double* P = A.prec + ((size_t)b * A.KP + k) * (size_t)A.prec_stride;
   double q = 0.0;
+  // spherical and diagonal: eight trips per unrolled body so their loads are
+  // in flight together; the sum keeps its order
   if constexpr (COV == SPH) {
+#pragma unroll 8
     for (int d = 0; d < D; ++d) {
       const double t = (double)x[d] - (double)mu[d];
       q += t * t;
     }
     q *= P[0];
   } else if constexpr (COV == DIAG) {
+#pragma unroll 8
     for (int d = 0; d < D; ++d) {
       const double t = (double)x[d] - (double)mu[d];
       q += P[d] * t * t;
