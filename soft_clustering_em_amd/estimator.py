@@ -6,8 +6,10 @@ restarts -- the estimator surface the GMMXX README lists under "Highlights"
 Every per-row and per-component number comes from the HIP library:
 score_samples and predict from gmm_predict_proba_topm (m = 1: the best
 component and log p(x_i)), score from gmm_estep_stats (sum_i log p(x_i)),
-fit from gmm_fit_step.  What runs here is argument handling, the stopping
-rule and the AIC/BIC arithmetic on B returned scalars.
+fit from gmm_fit_step (or gmm_topk_fit_step, the approximate top-k mode of
+the GMMXX README), KernelDensity.score_samples from gmm_kde_score.  What runs
+here is argument handling, the stopping rule and the AIC/BIC arithmetic on B
+returned scalars.
 
   n_parameters(cov, K, D)                       -> int
   score_samples(X, w, mu, cv, cov)              -> (B, N) float32 log p(x_i)
@@ -18,6 +20,7 @@ rule and the AIC/BIC arithmetic on B returned scalars.
   fit(X, K, cov, ...)                           -> FitResult (the restart with the best mean LL)
   GaussianMixture(n_components, covariance_type, ...)  the same calls as a scikit-learn style class
   KMeans(n_clusters, ...)                       Lloyd iterations over gmm_kmeans_step (the hard limit)
+  KernelDensity(bandwidth)                      Gaussian kernel density estimate over gmm_kde_score
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import gmm_estep_stats, gmm_fit_step, gmm_kmeans_step, gmm_predict_proba_topm, new_stats
+from . import (gmm_estep_stats, gmm_fit_step, gmm_kde_score, gmm_kmeans_step, gmm_predict_proba_topm,
+               gmm_topk_fit_step, gmm_topk_fit_workspace_bytes, new_stats)
 
 
 def _torch():
@@ -133,12 +137,19 @@ def random_init(X, K, cov, generator):
     return w, mu, cv
 
 
-def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=None):
+def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=None, topk=None):
     """EM from n_init starts (random_init with a seeded generator, or the
     given init = (w, mu, cv) for the first start); each runs until the change
     of the problem-averaged mean log-likelihood falls below tol or n_iter
-    iterations.  Keeps the start whose last mean log-likelihood is highest."""
+    iterations.  Keeps the start whose last mean log-likelihood is highest.
+    topk: run approximate top-k EM steps instead (each row keeps its topk best
+    components; spherical and diagonal covariance); the history then holds
+    the top-k steps' log-likelihoods, the final score the full mixture's."""
     torch = _torch()
+    tws = None
+    if topk is not None:
+        n = gmm_topk_fit_workspace_bytes(X, K, cov, int(topk))
+        tws = torch.empty(max(n, 256), dtype=torch.uint8, device=X.device)
     gen = torch.Generator(device="cpu").manual_seed(seed)
     Xb = _batched(X)
     B = Xb.shape[0]
@@ -151,7 +162,10 @@ def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=
         mll = torch.zeros(B, dtype=torch.float64, device=X.device)
         hist, prev, converged, it = [], None, False, 0
         for it in range(1, n_iter + 1):
-            gmm_fit_step(X, w, mu, cv, cov, reg_covar=reg_covar, mean_loglik=mll)
+            if topk is None:
+                gmm_fit_step(X, w, mu, cv, cov, reg_covar=reg_covar, mean_loglik=mll)
+            else:
+                gmm_topk_fit_step(X, w, mu, cv, cov, int(topk), reg_covar=reg_covar, mean_loglik=mll, ws=tws)
             cur = float(mll.mean().item())  # the LL of the parameters that entered this step
             hist.append(cur)
             if prev is not None and abs(cur - prev) < tol:
@@ -177,12 +191,14 @@ class GaussianMixture:
     the GPU as float32 tensors.  Every computation runs in the HIP library."""
 
     def __init__(self, n_components, covariance_type="full", max_iter=100, tol=1e-3, reg_covar=1e-6, n_init=1,
-                 random_state=0, weights_init=None, means_init=None, covariances_init=None, init_params="random"):
+                 random_state=0, weights_init=None, means_init=None, covariances_init=None, init_params="random",
+                 topk=None):
         if covariance_type not in ("spherical", "diag", "tied", "full"):
             raise ValueError(f"unknown covariance_type {covariance_type!r}")
         if init_params not in ("random", "kmeans"):
             raise ValueError(f"unknown init_params {init_params!r}")
         self.init_params = init_params
+        self.topk = None if topk is None else int(topk)
         self.n_components = int(n_components)
         self.covariance_type = covariance_type
         self.max_iter = int(max_iter)
@@ -217,7 +233,8 @@ class GaussianMixture:
         if X.dim() != 2:
             raise ValueError("X is (N, D)")
         res = fit(X, self.n_components, self.covariance_type, n_iter=self.max_iter, tol=self.tol,
-                  n_init=self.n_init, reg_covar=self.reg_covar, seed=self.random_state or 0, init=self._init(X))
+                  n_init=self.n_init, reg_covar=self.reg_covar, seed=self.random_state or 0, init=self._init(X),
+                  topk=self.topk)
         self.weights_, self.means_, self.covariances_ = res.weights, res.means, res.covars
         self.lower_bound_ = float(res.mean_ll[0])
         self.lower_bound_history_ = list(res.history[res.restart])
@@ -321,3 +338,32 @@ class KMeans:
 
     def fit_predict(self, X):
         return self.fit(X).labels_
+
+
+class KernelDensity:
+    """Gaussian kernel density estimate in the scikit-learn style
+    (KernelDensity(kernel="gaussian")): fit(X) keeps the reference rows (M, D)
+    float32 on the GPU; score_samples(Y) is log p(y) per query row from
+    gmm_kde_score; score(Y) their sum."""
+
+    def __init__(self, bandwidth=1.0):
+        if not (float(bandwidth) > 0.0):
+            raise ValueError("bandwidth must be > 0")
+        self.bandwidth = float(bandwidth)
+
+    def fit(self, X):
+        torch = _torch()
+        if X.dim() != 2:
+            raise ValueError("X is (M, D)")
+        self.reference_ = X.to(torch.float32).contiguous()
+        self.n_features_in_ = int(X.shape[1])
+        return self
+
+    def score_samples(self, Y):
+        if not hasattr(self, "reference_"):
+            raise RuntimeError("call fit first")
+        return gmm_kde_score(Y.contiguous(), self.reference_, self.bandwidth)
+
+    def score(self, Y):
+        return float(self.score_samples(Y).double().sum().item())
+
