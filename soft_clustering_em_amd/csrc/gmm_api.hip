@@ -965,6 +965,6 @@ const char* gmm_status_str(int32_t status) {
 
 const char* gmm_last_error(void) { return g_err.c_str(); }
 
-int32_t gmm_version(void) { return 100; }
+int32_t gmm_version(void) { return 200; }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = _abi.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.gmm_version() >= 100
+    assert L.gmm_version() >= 200
 
 
 def test_struct_layouts_match_the_header():
