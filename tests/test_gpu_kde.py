@@ -61,7 +61,7 @@ def blobs(rng, n, D, K=12, spread=3.0, offset=0.0):
 
 
 @pytest.mark.parametrize("B,N,M,D,h,offset", [
-    (1, 1000, 777, 5, 0.7, 0.0),     # ragged queries (7 x 128 + 104) and references (12 x 64 + 9)
+    (1, 1000, 777, 5, 0.7, 0.0),     # ragged queries (15 x 64 + 40) and references (12 x 64 + 9)
     (1, 517, 300, 17, 1.1, 20.0),    # far from the origin: centring at the reference mean
     (3, 300, 1500, 64, 2.0, 0.0),    # batched queries sharing the references
     (1, 129, 64, 128, 3.0, -5.0),    # one reference tile, 128 features
@@ -119,3 +119,25 @@ def test_kde_full_size_sampled(torch_cuda):
     pick = np.sort(np.random.default_rng(9).choice(Y.shape[0], 256, replace=False))
     ref = oracle.kde_score(Y[pick], X, h)
     check(f"full N={Y.shape[0]} M={X.shape[0]} h={h:.3f}", got[pick], ref, Y[pick], X, h)
+
+
+def test_kde_padded_row_strides(torch_cuda):
+    """Queries and references as column slices of wider rows (ld > D), batched
+    queries with a problem stride past N * ld: the same values as contiguous
+    copies, and the oracle's."""
+    torch = torch_cuda
+    import soft_clustering_em_amd as g
+    rng = np.random.default_rng(8)
+    D = 20
+    Xw = torch.from_numpy(blobs(rng, 321, 28)).cuda()
+    Ybig = torch.from_numpy(blobs(rng, 2 * 160, 36).reshape(2, 160, 36)).cuda()
+    X = Xw[:, :D]
+    Y = Ybig[:, :150, :D]
+    assert X.stride(0) == 28 and Y.stride(1) == 36 and Y.stride(0) == 160 * 36
+    got = g.gmm_kde_score(Y, X, 1.2)
+    ref_dev = g.gmm_kde_score(Y.contiguous(), X.contiguous(), 1.2)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_dev)
+    ref = oracle.kde_score(Y.cpu().numpy(), X.cpu().numpy(), 1.2)
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= 1e-4 * np.maximum(1.0, np.abs(ref))).all(), err.max()
