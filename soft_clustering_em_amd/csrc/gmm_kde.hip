@@ -22,13 +22,18 @@
 //     and of its reference column, so a lane's features are contiguous and its
 //     reference operands come from LDS as 16-byte reads;
 //   * the log-scores, in log2 units, are l = -lam |y|^2 - lam |x|^2 + 2 lam y.x
-//     with lam = log2(e) / (2 h^2); per row a running maximum (16-lane DPP
-//     reduction per tile) and per lane a running sum of 2^(l - max), combined
-//     across the row's 16 lanes at the end;
+//     with lam = log2(e) / (2 h^2); the row's own -lam |y|^2 is the same for
+//     every reference, so the tiles carry l' = 2 lam y.x - lam |x|^2 and the
+//     row term is added once, in float64, at the end;
+//   * per row a reference maximum and per lane a running sum of
+//     2^(l' - reference), combined across the row's 16 lanes at the end; the
+//     reference moves (16-lane DPP maximum, rescaled sums) only when some score
+//     of the wave's rows passes it by more than 8 log2 units, which after the
+//     first tiles is rare;
 //   * the terms that decide the sum are rescored exactly, as the fused E-step
 //     rescores its sharp components: every reference whose score comes within
-//     30 (log2 units) of the row's running maximum is listed in LDS (up to 8
-//     per row; when the maximum rises, entries that fell below the band are
+//     30 (log2 units) of the row's reference maximum is listed in LDS (up to 8
+//     per row; when the reference moves, entries that fell below the band are
 //     dropped); at the end each listed term's float32 value is taken out of the
 //     sum and its float64 value from direct differences of the caller's rows
 //     put in, the list read in increasing reference order.  A row with more
@@ -57,6 +62,7 @@ constexpr int kKdeThreads = 64 * kKdeWaves;
 constexpr int kKdeQ = kKdeWaves * 16 * kKdeRB;  // query rows per workgroup
 constexpr float kKdeBand = 30.f;        // log2 units below the running maximum that are rescored
 constexpr int kKdeCap = 8;              // rescored references per row
+constexpr float kKdeSlack = 8.f;        // log2 units a score may pass a row's reference maximum before it moves
 
 // c_d = mean of the references' feature d, summed in float64 in a fixed order
 __global__ void __launch_bounds__(256) kde_centre_kernel(const float* __restrict__ x, int64_t M, int64_t ld, int D,
@@ -116,7 +122,7 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
   static_assert(KS % 4 == 0 && kKdeTile <= kKdeThreads, "tile shape");
   __shared__ float xs[2][kKdeTile * RS];
   __shared__ float bs[2][kKdeTile];
-  __shared__ float ays[kKdeQ];
+  __shared__ double ays[kKdeQ];
   __shared__ int cj[kKdeQ * kKdeCap];    // listed references per row
   __shared__ float cl[kKdeQ * kKdeCap];  // their float32 scores
   __shared__ int cn[kKdeQ];              // references that qualified (may exceed kKdeCap)
@@ -144,7 +150,7 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
     // the row's four feature quarters sit in lanes c16, c16 + 16, + 32, + 48
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    if (g == 0) ays[16 * RB * wv + 16 * rb + c16] = (float)(-A.lam * ss);
+    if (g == 0) ays[16 * RB * wv + 16 * rb + c16] = -A.lam * ss;
   }
 
   // ---- reference tiles: fetched into registers one tile ahead, stored to the idle LDS buffer
@@ -170,14 +176,16 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
   stash(0);
   __syncthreads();  // tile 0, the row norms and the list counts visible
 
-  // epilogue layout of a 16x16 block: lane holds rows 4 g + v (v = 0..3) of column c16
-  // lost: the largest score this lane could not list (the row's list was full)
-  float ay[RB][4], mx[RB][4], sm[RB][4], lost[RB][4];
+  // epilogue layout of a 16x16 block: lane holds rows 4 g + v (v = 0..3) of
+  // column c16.  The scores below leave out the row's own -lam |y - c|^2 (added
+  // once at the end in float64); mx is the row's reference maximum, within
+  // kKdeSlack below the largest score seen; lost: the largest score this lane
+  // could not list (the row's list was full)
+  float mx[RB][4], sm[RB][4], lost[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      ay[rb][v] = ays[16 * RB * wv + 16 * rb + 4 * g + v];
       mx[rb][v] = -INFINITY;
       sm[rb][v] = 0.f;
       lost[rb][v] = -INFINITY;
@@ -215,40 +223,47 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float l[NT];
-        float m = -INFINITY;
+        float lm = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          l[nt] = fmaf(A.s2, acc[rb][nt][v], ay[rb][v] + bxv[nt]);
-          m = fmaxf(m, l[nt]);
+          l[nt] = fmaf(A.s2, acc[rb][nt][v], bxv[nt]);
+          lm = fmaxf(lm, l[nt]);
         }
-        m = row16_max(m);  // every tile holds at least one real reference: m is finite
-        const float mo = mx[rb][v];
-        const float mn = fmaxf(mo, m);
-        float s = sm[rb][v] * __builtin_amdgcn_exp2f(mo - mn);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s += __builtin_amdgcn_exp2f(l[nt] - mn);
-        sm[rb][v] = s;
-        mx[rb][v] = mn;
-        // terms near the running maximum: listed for the exact rescoring (padding
-        // scores are -inf).  A row's list is touched only by its own 16 lanes of
-        // this wave, whose LDS operations execute in program order.
         const int pr = 16 * RB * wv + 16 * rb + 4 * g + v;
-        if (mn > mo && c16 == 0) {  // the maximum rose: drop the listed terms now below the band
-          const int n = min(cn[pr], kKdeCap);
-          int k = 0;
-          for (int q = 0; q < n; ++q) {
-            const float lq = cl[pr * kKdeCap + q];
-            if (lq >= mn - kKdeBand) {
-              cj[pr * kKdeCap + k] = cj[pr * kKdeCap + q];
-              cl[pr * kKdeCap + k] = lq;
-              ++k;
+        float mr = mx[rb][v];
+        // the reference moves only when a score passes it by more than
+        // kKdeSlack (a wave-uniform test over the wave's four rows at v; the
+        // first tile always moves it, every tile holding a real reference)
+        if (__builtin_amdgcn_ballot_w64(lm > mr + kKdeSlack) != 0) {
+          const float mn = fmaxf(mr, row16_max(lm));
+          sm[rb][v] *= __builtin_amdgcn_exp2f(mr - mn);
+          // a row's list is touched only by its own 16 lanes of this wave,
+          // whose LDS operations execute in program order
+          if (mn > mr && c16 == 0) {  // drop the listed terms now below the band
+            const int n = min(cn[pr], kKdeCap);
+            int k = 0;
+            for (int q = 0; q < n; ++q) {
+              const float lq = cl[pr * kKdeCap + q];
+              if (lq >= mn - kKdeBand) {
+                cj[pr * kKdeCap + k] = cj[pr * kKdeCap + q];
+                cl[pr * kKdeCap + k] = lq;
+                ++k;
+              }
             }
+            cn[pr] = k;
           }
-          cn[pr] = k;
+          mx[rb][v] = mr = mn;
         }
+        float s = sm[rb][v];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s += __builtin_amdgcn_exp2f(l[nt] - mr);
+        sm[rb][v] = s;
+        // terms within the band of the reference (a superset of those within
+        // the band of the true maximum): listed for the exact rescoring
+        // (padding scores are -inf)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if (l[nt] >= mn - kKdeBand) {
+          if (l[nt] >= mr - kKdeBand) {
             const int slot = atomicAdd(&cn[pr], 1);
             if (slot < kKdeCap) {
               cj[pr * kKdeCap + slot] = (int)(t * kKdeTile + nt * 16 + c16);
@@ -275,6 +290,7 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
       const int64_t row = q0 + pr;
       const int cnt = min(cn[pr], kKdeCap);
       const double m = (double)mx[rb][v];
+      const double mfull = m + ays[pr];  // the reference in the frame of the full scores
       // complete when every term that could not be listed fell below the band
       const bool complete = row16_max(lost[rb][v]) < mx[rb][v] - kKdeBand;
       double S = (double)st;
@@ -303,11 +319,11 @@ __global__ void __launch_bounds__(kKdeThreads, DP >= 128 ? 2 : 4) kde_kernel(Kde
           }
           d2 = row16_sum_f64(d2);
           sub += exp2((double)ln - m);
-          add += exp2(-A.lam_exact * d2 - m);
+          add += exp2(-A.lam_exact * d2 - mfull);
         }
         S = fmax(S - sub, 0.0) + add;
       }
-      if (c16 == 0 && row < A.N) A.out[b * A.N + row] = (float)((m + log2(S)) * LN2 + A.cnst);
+      if (c16 == 0 && row < A.N) A.out[b * A.N + row] = (float)((mfull + log2(S)) * LN2 + A.cnst);
     }
 }
 
