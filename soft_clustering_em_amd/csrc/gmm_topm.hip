@@ -75,21 +75,59 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
   }
   const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)b * A.stride_b;
 
+  // rows of the next tile are fetched into registers while this tile computes,
+  // when a tile is at most PF elements per thread (uniform across the block)
+  constexpr int PF = 4;
+  const bool pre = T * DP <= PF * nthr;
+  float pv[PF];
+  auto fetch_rows = [&](int64_t tile) {
+    const int64_t r0 = tile * T;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int j = threadIdx.x + i * nthr;
+      float v = 0.f;
+      if (j < T * DP) {
+        const int r = j / DP, d = j % DP;
+        if (r0 + r < N && d < D) v = xb[(r0 + r) * A.ld_x + d];
+      }
+      pv[i] = v;
+    }
+  };
+  if (pre && g < A.ntiles) fetch_rows(g);
+
   for (int64_t t = g; t < A.ntiles; t += A.Gb) {
     const int64_t row0 = t * T;
     __syncthreads();  // previous tile fully consumed
-    for (int j = threadIdx.x; j < T * DP; j += nthr) {
-      const int r = j / DP, d = j % DP;
-      const int64_t row = row0 + r;
-      raw[j] = (row < N && d < D) ? xb[row * A.ld_x + d] : 0.f;
+    if (pre) {
+      // the prefetched rows, with their direct features
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int j = threadIdx.x + i * nthr;
+        if (j < T * DP) {
+          const int r = j / DP, d = j % DP;
+          raw[j] = pv[i];
+          phi[r * FS + d] = pv[i];
+          if constexpr (COV == DIAG) phi[r * FS + DP + d] = pv[i] * pv[i];
+        }
+      }
+      if (t + A.Gb < A.ntiles) fetch_rows(t + A.Gb);
+    } else {
+      for (int j = threadIdx.x; j < T * DP; j += nthr) {
+        const int r = j / DP, d = j % DP;
+        const int64_t row = row0 + r;
+        raw[j] = (row < N && d < D) ? xb[row * A.ld_x + d] : 0.f;
+      }
     }
     for (int p = threadIdx.x; p < T; p += nthr) cnt[p] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < T * DP; j += nthr) {
-      const int r = j / DP, d = j % DP;
-      const float v = raw[j];
-      phi[r * FS + d] = v;
-      if constexpr (COV == DIAG) phi[r * FS + DP + d] = v * v;
+    // diagonal features are complete when prefetched; the rest need the whole tile
+    if (!pre || COV != DIAG) __syncthreads();
+    if (!pre) {
+      for (int j = threadIdx.x; j < T * DP; j += nthr) {
+        const int r = j / DP, d = j % DP;
+        const float v = raw[j];
+        phi[r * FS + d] = v;
+        if constexpr (COV == DIAG) phi[r * FS + DP + d] = v * v;
+      }
     }
     if constexpr (COV == SPH) {
       for (int r = threadIdx.x; r < T; r += nthr) {
