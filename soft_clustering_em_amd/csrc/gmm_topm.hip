@@ -233,17 +233,53 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       if ((lane & 15) == 0) rednc[wv * T + p] = (double)nc;
     }
     __syncthreads();  // every row's candidate count is final
+    if constexpr (COV == SPH || COV == DIAG) {
+      // the candidates' components into the lists; then their float64 scores
+      // by direct differences: a wave per row in turn, its four 16-lane groups
+      // four candidates at a time, lane li taking features li, li + 16, ...
+      // (coalesced reads of the means), summed by a 16-lane DPP tree
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int p = 4 * (lane >> 4) + v;
-      const bool fits = cnt[p] <= CAP;
+      for (int v = 0; v < 4; ++v) {
+        const int p = 4 * (lane >> 4) + v;
+        const bool fits = cnt[p] <= CAP;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int slot = slotv[nt][v];
-        if (slot >= 0 && fits) {
-          const int k = wv * KW + nt * 16 + (lane & 15);
-          cl[p * CAP + slot] = exact_score<COV, DP, false>(A, b, k, D, raw + p * DP);
-          ck[p * CAP + slot] = k;
+        for (int nt = 0; nt < NT; ++nt)
+          if (slotv[nt][v] >= 0 && fits) ck[p * CAP + slotv[nt][v]] = wv * KW + nt * 16 + (lane & 15);
+      }
+      __syncthreads();
+      constexpr double kLog2e = 1.4426950408889634074;
+      const int grp = lane >> 4, li = lane & 15;
+      for (int p = wv; p < T; p += NW) {
+        const int n = cnt[p];
+        if (row0 + p >= N || n > CAP) continue;  // uniform across the wave
+        for (int c0i = 0; c0i < n; c0i += 4) {
+          const int c = c0i + grp;
+          const int k = ck[p * CAP + (c < n ? c : n - 1)];
+          const float* mu = A.mu + ((size_t)b * A.K + k) * D;
+          const double* P = A.prec + ((size_t)b * A.KP + k) * (size_t)A.prec_stride;
+          double q = 0.0;
+          for (int d = li; d < D; d += 16) {
+            const double t = (double)raw[p * DP + d] - (double)mu[d];
+            q += (COV == DIAG ? P[d] : 1.0) * t * t;
+          }
+          q = row16_sum_f64(q);
+          if constexpr (COV == SPH) q *= P[0];
+          if (li == 0 && c < n) cl[p * CAP + c] = A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int p = 4 * (lane >> 4) + v;
+        const bool fits = cnt[p] <= CAP;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int slot = slotv[nt][v];
+          if (slot >= 0 && fits) {
+            const int k = wv * KW + nt * 16 + (lane & 15);
+            cl[p * CAP + slot] = exact_score<COV, DP, false>(A, b, k, D, raw + p * DP);
+            ck[p * CAP + slot] = k;
+          }
         }
       }
     }
