@@ -54,6 +54,8 @@ def _load():
         lib.oracle_responsibilities.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, P, P, P]
         lib.oracle_topm.argtypes = [i32, i64, i32, i32, P, i32, P, P, P, i32, f64, P, P, P, P, P, i32]
         lib.oracle_kmeans_step.argtypes = [i64, i32, i32, P, i32, P, P, P, P, P, P, i32]
+        lib.oracle_decode.argtypes = [i32, i64, P, P]
+        lib.oracle_decode.restype = ctypes.c_int
         for f in (lib.oracle_estep, lib.oracle_mstep, lib.oracle_mstep_twopass,
                   lib.oracle_responsibilities, lib.oracle_topm, lib.oracle_kmeans_step):
             f.restype = ctypes.c_int
@@ -77,6 +79,30 @@ def _x_and_type(X):
     if arr.dtype == np.float32:
         return arr, XTYPE["f32"]
     raise TypeError("oracle input must be float32/float64 or (uint16, 'bf16'|'f16')")
+
+
+def decode_rows(X) -> np.ndarray:
+    """The rows as float64, decoded exactly: float32/float64 arrays as they
+    are; (uint16 bits, 'bf16') as bfloat16 (the upper half of a float32);
+    (uint16 bits, 'f16') as IEEE binary16."""
+    if isinstance(X, tuple):
+        arr, kind = X
+        bits = np.ascontiguousarray(arr, dtype=np.uint16)
+        if kind == "bf16":
+            return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        if kind == "f16":
+            return bits.view(np.float16).astype(np.float64)
+        raise TypeError("unknown 16-bit row type %r" % (kind,))
+    return np.asarray(X, dtype=np.float64)
+
+
+def c_decode(X) -> np.ndarray:
+    """The rows as the C oracle decodes them (float64, flattened)."""
+    Xa, xt = _x_and_type(X)
+    out = np.zeros(Xa.size)
+    if _load().oracle_decode(xt, Xa.size, _ptr(Xa), _ptr(out)):
+        raise ValueError("oracle_decode rejected its arguments")
+    return out
 
 
 def cov_len(cov: str, D: int, K: int) -> int:
@@ -286,30 +312,28 @@ def fisher_vector(X, w, mu, var, power=True, l2=True):
     return np.stack(out)
 
 
-def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6, floor=2.0 ** -20):
+def topk_fit_step(cov, X, w, mu, cv, topk, eps=1e-6):
     """One approximate top-k EM iteration for one problem (spherical or
-    diagonal): the training mode the GMMXX README lists as approx_top_k --
-    each row keeps the topk components of largest log-score (ties to the lower
-    index) among those whose full responsibility is at least `floor` (the best
-    one always), normalises over that subset only, and only those enter the
-    statistics; the M-step is the usual one.  Returns dict like fit_step:
-    w, mu, cv (each with a leading problem axis), mean_ll = the mean over rows
-    of the log-sum-exp over each row's kept components, the statistics, and
-    keep (N, topk) the kept components, best first, -1 past K."""
-    Xa, _ = _x_and_type(X)
+    diagonal): the training mode the GMMXX README lists as approx_top_k
+    ("Useful Options" and "CUDA backend (experimental)").  Each row keeps the
+    topk components of largest log-score log pi_k N(x | theta_k) (ties to the
+    lower index), normalises its responsibilities over that subset only, and
+    only those enter the statistics; the M-step is the usual one.  With
+    topk >= K every component is kept, which is the exact EM step.  Returns a
+    dict like fit_step: w, mu, cv (each with a leading problem axis), mean_ll =
+    the mean over rows of the log-sum-exp over each row's kept components, the
+    statistics, and keep (N, topk) the kept components, best first, -1 past K."""
+    Xa = decode_rows(X)
     N, D = Xa.shape
-    ls, rfull, _ = responsibilities(cov, X, w, mu, cv)
+    ls, _, _ = responsibilities(cov, X, w, mu, cv)
     K = ls.shape[1]
     m = min(int(topk), K)
     order = np.argsort(-ls, axis=1, kind="stable")[:, :m]  # descending score, ties: lower index first
-    kept = np.take_along_axis(rfull, order, axis=1) >= floor
-    kept[:, 0] = True
-    sel = np.where(kept, np.take_along_axis(ls, order, axis=1), -np.inf)
+    sel = np.take_along_axis(ls, order, axis=1)
     mx = sel[:, :1]
     lse = (mx + np.log(np.exp(sel - mx).sum(axis=1, keepdims=True)))[:, 0]
     r = np.zeros((N, K))
     np.put_along_axis(r, order, np.exp(sel - lse[:, None]), axis=1)
-    order = np.where(kept, order, -1)
     mu0 = np.asarray(mu, dtype=np.float64).reshape(K, D)
     nk = r.sum(axis=0)
     sx = r.T @ Xa

@@ -619,4 +619,11 @@ int oracle_kmeans_step(int64_t N, int D, int K, const void* X, int xtype, const 
   return 0;
 }
 
+/* The stored input elements as the oracle reads them (exact decoding). */
+int oracle_decode(int xtype, int64_t n, const void* X, double* out) {
+  if (n < 0 || xtype < OX_F64 || xtype > OX_F16) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = x_at(X, xtype, i);
+  return 0;
+}
+
 int oracle_version(void) { return 1; }
