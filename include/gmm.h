@@ -213,19 +213,22 @@ gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, in
                            double* inertia, void* ws, size_t ws_bytes, void* stream);
 
 /* One approximate top-k EM iteration (the approx_top_k training mode of the
- * GMMXX README; statistics and M-step as Flash-GMM Section 2): each row keeps
- * its topk components of largest responsibility among those with r >= 2^-20
- * (the best one always; decided on float64 scores, ties to the lower index, as
- * gmm_predict_proba_topm with m = topk and threshold 2^-20), its
- * responsibilities renormalised over that subset; only those enter N_k,
- * sum r x and sum r (x - mu)^2 (float64, summed per component in increasing
- * row order); then the M-step of gmm_mstep updates `inout` in place.
+ * GMMXX README, "Useful Options" and "CUDA backend (experimental)"; statistics
+ * and M-step as Flash-GMM Section 2): each row keeps the topk components of
+ * largest log-score log pi_k N(x | theta_k) (decided on float64 scores, ties to
+ * the lower index), its responsibilities renormalised over that subset; only
+ * those enter N_k, sum r x and sum r (x - mu)^2 (float64, summed per
+ * component in increasing row order); then the M-step of gmm_mstep updates
+ * `inout` in place.  topk >= K keeps every component: the exact EM step.
  * mean_loglik (B) float64, nullable: the mean over rows of log sum over each
  * row's kept components of pi_k N(x | theta_k), under the entering theta.
  * Spherical and diagonal components; the top-m window (float32 rows: K <=
  * 256, any B; bf16 rows: spherical, B = 1, any K); 1 <= topk <= 16; N * topk
- * < 2^31.  topk >= K is the exact EM step but for the mass of r < 2^-20.  Workspace:
- * gmm_topk_fit_workspace_bytes (it grows with N * topk).  Deterministic. */
+ * < 2^31.  The candidates of a row are the components whose score can reach
+ * a lower bound of its topk-th best score; with bf16 rows of D != 128 (or not
+ * 16-byte aligned) that bound is not formed and every component of the row
+ * is rescored (correct, slower).  Workspace: gmm_topk_fit_workspace_bytes (it
+ * grows with N * topk).  Deterministic. */
 size_t gmm_topk_fit_workspace_bytes(const gmm_data* data, int32_t K, int32_t cov, int32_t topk);
 gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t topk, const gmm_options* opts,
                              double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes, void* stream);

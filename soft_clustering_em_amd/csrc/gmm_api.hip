@@ -88,6 +88,8 @@ static void largek_layout(Plan& q, int64_t chunk) {
     q.off_mrow = o; o = align_up(o + sizeof(float) * (size_t)chunk);
     q.off_cmask = o; o = align_up(o + sizeof(uint32_t) * (size_t)chunk * (q.KP / 32));
     q.off_prem = o; o = align_up(o + sizeof(float) * (size_t)chunk * q.S);
+    q.off_lmx = o;  o = align_up(o + sizeof(float) * 4 * (size_t)chunk * q.S);
+    q.off_kthr = o; o = align_up(o + sizeof(float) * (size_t)chunk);
   }
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
   q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.llG);
@@ -189,7 +191,7 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
       const size_t T = kTopmRows, C = kTopmCap;
       q.T = (int)T;
       q.direct = false;
-      q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F) +
+      q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F + 3 * T) +
               sizeof(double) * (T + (size_t)q.NW * T + T * C);
       if (q.lds > kLdsBytes)
         return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K, (long long)d->D);
@@ -231,6 +233,7 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
   q.off_flag = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
   q.off_sharp = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
+  q.off_err = o;  o = align_up(o + sizeof(float2) * (size_t)q.B * q.KP);
   if (op != GMM_OP_TOPM) {
     q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
     q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
@@ -256,7 +259,7 @@ static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
     largek_layout(q, 32);
     if (ws_bytes >= q.ws_bytes) {
       size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
-      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (1 + p.S) + sizeof(uint32_t) * (p.KP / 32);
+      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (2 + 5 * (size_t)p.S) + sizeof(uint32_t) * (p.KP / 32);
       int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
       chunk = std::min<int64_t>(chunk, p.chunk_rows);
       for (largek_layout(q, chunk); q.ws_bytes > ws_bytes && chunk > 32; largek_layout(q, chunk)) chunk -= 32;
@@ -308,6 +311,8 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
     A.mrow = reinterpret_cast<float*>(w + p.off_mrow);
     A.cmask = reinterpret_cast<uint32_t*>(w + p.off_cmask);
     A.prem = reinterpret_cast<float*>(w + p.off_prem);
+    A.lmx = reinterpret_cast<float4*>(w + p.off_lmx);
+    A.kthr = reinterpret_cast<float*>(w + p.off_kthr);
   }
   return A;
 }
@@ -345,7 +350,7 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   double* part = reinterpret_cast<double*>(w + p.off_part);
   double* llp = reinterpret_cast<double*>(w + p.off_llp);
   double* raw = reinterpret_cast<double*>(w + p.off_aux);
-  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, W, prec, c0, c, a, flag, sharp, s);
+  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, nullptr, W, prec, c0, c, a, flag, sharp, s);
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   EStepArgs A;
   A.x = d->x;
@@ -385,11 +390,15 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
 }
 
 // The top-m launch sequence of a planned call (N >= 1, workspace checked).
+// topk != 0: the top-k mode (every row keeps its m best components, normalised
+// over them; threshold unused).
 static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
-                           int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, hipStream_t s) {
+                           int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, hipStream_t s,
+                           int topk = 0) {
   if (p.largek) {
     LargeKArgs A = largek_args(p, data, params, ws);
     A.topm = 1;
+    A.topk = topk;
     A.m = m;
     A.thr = threshold;
     A.idx = idx;
@@ -408,7 +417,8 @@ static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params
   double* a = reinterpret_cast<double*>(w + p.off_a);
   int32_t* flag = reinterpret_cast<int32_t*>(w + p.off_flag);
   int32_t* sharp = reinterpret_cast<int32_t*>(w + p.off_sharp);
-  hipError_t e = launch_prologue(p, params->weights, params->means, params->covars, W, prec, c0, c, a, flag, sharp, s);
+  float2* err = reinterpret_cast<float2*>(w + p.off_err);
+  hipError_t e = launch_prologue(p, params->weights, params->means, params->covars, err, W, prec, c0, c, a, flag, sharp, s);
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   TopmArgs A;
   A.x = data->x;
@@ -427,9 +437,11 @@ static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params
   A.mu = params->means;
   A.prec = prec;
   A.c0 = c0;
+  A.err = err;
   A.prec_stride = p.prec_stride;
   A.m = m;
   A.thr = threshold;
+  A.topk = topk;
   A.idx = idx;
   A.resp = resp;
   A.count = count;
@@ -743,9 +755,9 @@ gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint
   return GMM_OK;
 }
 
-// ---- approximate top-k EM: the top-m pass with m = k and threshold 2^-20, the
-// posting lists of its entries, weighted statistics per component, M-step
-static constexpr float kTopkFloor = 0x1p-20f;  // smallest responsibility a top-k entry keeps (rank 1 aside)
+// ---- approximate top-k EM: the top-m pass in its top-k mode (m = k, each row's
+// k best normalised over themselves), the posting lists of its entries,
+// weighted statistics per component, M-step
 
 struct TkLayout {
   Plan p;
@@ -810,10 +822,9 @@ gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t to
   int32_t* idx = reinterpret_cast<int32_t*>(w + L.off_idx);
   float* resp = reinterpret_cast<float*>(w + L.off_resp);
   float* logp = reinterpret_cast<float*>(w + L.off_logp);
-  // kept: the topk best among the components with r >= 2^-20 (the best always):
-  // the top-m rule at that threshold, decided on float64 responsibilities;
-  // every such component lies in the band the top-m rescoring covers
-  st = run_topm(p, data, inout, topk, kTopkFloor, idx, resp, nullptr, logp, ws, s);
+  // kept: each row's topk best components, decided on float64 scores, with
+  // their responsibilities and log-sum-exp over those topk only
+  st = run_topm(p, data, inout, topk, 0.0f, idx, resp, nullptr, logp, ws, s, 1);
   if (st != GMM_OK) return st;
   IvfArgs A;
   A.idx = idx;

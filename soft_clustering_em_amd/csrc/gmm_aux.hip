@@ -26,6 +26,13 @@ static constexpr double kLog2e = 1.4426950408889634074;
 // responsibilities need, and the fused kernel evaluates it in float64.
 static constexpr double kSharp = 1.0e4;
 static constexpr double kLog2Pi = 1.8378770664093454836;
+// Error coefficient of the approximate (float32-MFMA) log-score: its float32
+// products and partial sums over each group of 32 features (then added in
+// float64) carry at most about 34 roundings of 2^-24 of the sum of the
+// absolute terms; 2^-18 (64 roundings) leaves a margin.  The sum of absolute
+// terms is bounded per component by L1 |x| + Q |x|^2 (L1 = |linear weights|,
+// Q bounds the quadratic ones), see prologue_kernel.
+static constexpr double kScoreErr = 0x1p-18;
 
 __device__ __forceinline__ size_t wfrag_index(int k, int f, int KW, int F) {
   const int w = k / KW, kk = k % KW, nt = kk / 16, col = kk % 16;
@@ -60,7 +67,8 @@ __device__ bool chol_serial(int D, const double* S, double* L) {
 // grid: B*KP blocks of 64 threads; block (b, k).
 __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int KP, int DP, int F, int KW,
                                                       const float* __restrict__ w, const float* __restrict__ mu,
-                                                      const float* __restrict__ cv, float* __restrict__ W,
+                                                      const float* __restrict__ cv, float2* __restrict__ err,
+                                                      float* __restrict__ W,
                                                       double* __restrict__ prec, int prec_stride,
                                                       double* __restrict__ c0, double* __restrict__ c,
                                                       double* __restrict__ a, int32_t* __restrict__ flag,
@@ -73,11 +81,13 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
   __shared__ double sm_S[16 * 16], sm_L[16 * 16], sm_Li[16 * 16], sm_P[16 * 16];
   __shared__ double sm_c;
   __shared__ double sm_red[64];               // one partial per thread (blockDim.x == 64)
+  __shared__ double sm_l1[64];                // per thread: squared norm of its linear weights
   __shared__ int sm_ok;
 
   if (k >= K) {  // padding component: never responsible
     for (int f = tid; f < F; f += blockDim.x) Wb[wfrag_index(k, f, KW, F)] = 0.f;
     if (tid == 0) {
+      if (err) err[(size_t)b * KP + k] = float2{0.f, 0.f};
       c[(size_t)b * KP + k] = -INFINITY;
       c0[(size_t)b * KP + k] = -INFINITY;
       a[(size_t)b * KP + k] = 0.0;
@@ -98,7 +108,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     // per-dimension terms on the block's threads (one log per variance;
     // spherical: one log in all), then summed in thread order by thread 0
     {
-      double ld = 0.0, qd = 0.0, sd = 0.0, lm = 0.0;
+      double ld = 0.0, qd = 0.0, sd = 0.0, lm = 0.0, l1 = 0.0;
       int bad = 0;
       for (int d = tid; d < D; d += blockDim.x) {
         const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
@@ -107,7 +117,9 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
         qd += sm_v[d] * sm_mu[d] * sm_mu[d];
         lm = fmax(lm, sm_v[d]);
         sd += sm_mu[d] * sm_mu[d] + v;
+        l1 += (sm_v[d] * sm_mu[d]) * (sm_v[d] * sm_mu[d]);
       }
+      sm_l1[tid] = l1;
       sm_S[tid] = ld;
       sm_L[tid] = qd;
       sm_Li[tid] = sd;
@@ -117,14 +129,21 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     __syncthreads();
     if (tid == 0) {
       bool ok = true;
-      double logdet = 0.0, quad = 0.0, lmax = 0.0, scale = 0.0;
+      double logdet = 0.0, quad = 0.0, lmax = 0.0, scale = 0.0, l1 = 0.0;
       for (int t = 0; t < (int)blockDim.x; ++t) {
         logdet += sm_S[t];
         quad += sm_L[t];
         scale += sm_Li[t];
         lmax = fmax(lmax, sm_P[t]);
+        l1 += sm_l1[t];
         if (sm_red[t] != 0.0) ok = false;
       }
+      // spherical: the lambda |x|^2 term is added in float64, only x . (lambda mu)
+      // runs in float32; diagonal: sum_d lambda_d x_d^2 / 2 <= lambda_max |x|^2 / 2
+      if (err)
+        err[(size_t)b * KP + k] = ok ? float2{(float)(kScoreErr * kLog2e * sqrt(l1)),
+                                              (float)(cov == DIAG ? kScoreErr * kLog2e * 0.5 * lmax : 0.0)}
+                                     : float2{0.f, 0.f};
       if (cov == SPH) logdet = D * log((double)cv[(size_t)b * K + k]);
       sm_ok = ok;
       sm_c = ok ? (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e : -INFINITY;
@@ -210,6 +229,12 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       }
       for (int q = 0; q < (int)blockDim.x; ++q) f4 += sm_red[q];
       const double lmax = sqrt(sqrt(f4));
+      // sum over d <= e of |x_d x_e W_de| = |x|^T |P| |x| / 2 <= |P|_F |x|^2 / 2
+      double l1 = 0.0, pf = 0.0;
+      for (int d = 0; d < D; ++d) l1 += sm_v[d] * sm_v[d];
+      for (int i = 0; i < D * D; ++i) pf += sm_P[i] * sm_P[i];
+      if (err)
+        err[(size_t)b * KP + k] = float2{(float)(kScoreErr * kLog2e * sqrt(l1)), (float)(kScoreErr * kLog2e * 0.5 * sqrt(pf))};
       sm_c = (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e;
       c0[(size_t)b * KP + k] = (logpi - 0.5 * (D * kLog2Pi + logdet)) * kLog2e;
       sharp[(size_t)b * KP + k] = lmax * scale > kSharp ? 1 : 0;
@@ -239,15 +264,18 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     c[(size_t)b * KP + k] = ok ? sm_c : -INFINITY;
     a[(size_t)b * KP + k] = 0.0;
     flag[(size_t)b * KP + k] = ok ? 0 : 4;
-    if (!ok) sharp[(size_t)b * KP + k] = 0;
+    if (!ok) {
+      sharp[(size_t)b * KP + k] = 0;
+      if (err) err[(size_t)b * KP + k] = float2{0.f, 0.f};
+    }
   }
 }
 
-hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W,
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float2* err, float* W,
                            double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
                            hipStream_t s) {
   hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(p.B * p.KP)), dim3(64), 0, s, p.cov, (int)p.D, (int)p.K,
-                     p.KP, p.DP, p.F, p.KW, w, mu, cv, W, prec, p.prec_stride, c0, c, a, flag, sharp);
+                     p.KP, p.DP, p.F, p.KW, w, mu, cv, err, W, prec, p.prec_stride, c0, c, a, flag, sharp);
   return hipGetLastError();
 }
 

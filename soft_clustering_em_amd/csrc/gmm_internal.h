@@ -48,6 +48,8 @@ struct Plan {
   int lse_blocks = 0;       // blocks of the large-K LSE pass
   size_t lds_a = 0, lds_t = 0, lds_c = 0;
   size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
+  size_t off_lmx = 0, off_kthr = 0;  // large-K top-k: per-(row, slice) lower-bound maxima, per-row threshold
+  size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
@@ -107,6 +109,10 @@ struct LargeKArgs {
   float* mrow;          // (chunk) row maximum of the log-scores (pass B)
   uint32_t* cmask;      // (chunk, KP/32) candidate components of each row, one bit per component
   int topm;             // pass B: write mrow
+  // top-k mode (topk > 0): each row keeps its topk best components, normalised over them
+  int topk;
+  float4* lmx;          // (chunk, S) per (row, slice): 4 lane-group maxima of (score - error bound), or null
+  float* kthr;          // (chunk) per row: a lower bound of its topk-th best score (candidate threshold)
   int m;
   float thr;
   int32_t* idx;         // outputs of the chunk's rows
@@ -143,9 +149,11 @@ struct TopmArgs {
   const float* mu;
   const double* prec;
   const double* c0;
+  const float2* err;   // (B, KP) error coefficients of the approximate score: err.x |x| + err.y |x|^2
   int prec_stride;
   int m;
   float thr;
+  int topk;            // 1: keep the m best components of every row, normalised over them (no threshold)
   int32_t* idx;
   float* resp;
   int32_t* count;
@@ -179,8 +187,8 @@ struct TopkStepArgs {
   int bf16;
   int64_t B, N, ld_x, stride_b;
   int K, D, m, cov, S;        // S: contiguous parts each component's list is split into
-  const float* resp;          // (B, N, m) kept responsibilities, best first
-  const float* logp;          // (B, N) log p(x) of the full mixture
+  const float* resp;          // (B, N, m) kept responsibilities (normalised over the kept set), best first
+  const float* logp;          // (B, N) log sum over the kept components of pi N(x)
   const float* mu;            // (B, K, D) means entering the step
   const int64_t* offsets;     // (B, K+1) list offsets
   const int32_t* rows;        // (B, N m) list rows
@@ -240,7 +248,7 @@ hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);
 
 // prologue / reduction / M-step (gmm_aux.hip)
-hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float* W,
+hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float2* err, float* W,
                            double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
                            hipStream_t s);
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,

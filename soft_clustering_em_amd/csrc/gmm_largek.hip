@@ -132,7 +132,8 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
     pc.xs = A.xsq[xrow < A.N ? xrow : A.N - 1];
     pc.ls = A.lse[xrow < ntiles * LT ? xrow : ntiles * LT - 1];
   } else if constexpr (PASS == 1) {
-    pc.ls = A.mrow[xrow < A.N ? xrow : A.N - 1];
+    // top-m: the row maximum; top-k: the row's candidate threshold
+    pc.ls = (A.topk ? A.kthr : A.mrow)[xrow < A.N ? xrow : A.N - 1];
   }
   return pc;
 }
@@ -514,14 +515,17 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
         const int64_t row = row0 + p;
         rem[q] = 0.f;
-        const float mr = lsb[p];  // 0 for rows past N, which have no candidates
-        const float floor_l = mr - kTopmBand;
+        // top-m: the row maximum (0 for rows past N, which have no candidates);
+        // top-k: the row's threshold, a lower bound of its top-k-th score
+        const float mr = lsb[p];
+        const float floor_l = A.topk ? mr : mr - kTopmBand;
+        const float emul = A.topk ? 1.f : 2.f;
         const float xs = (float)xsq[p];
         uint32_t word = 0;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bool cand = row < nrows && lg[q][nt] + 2.f * fmaf(ea[nt], xs, ea0[nt]) >= floor_l;
-          if (!cand && row < nrows) rem[q] += __builtin_amdgcn_exp2f(lg[q][nt] - mr);
+          const bool cand = row < nrows && lg[q][nt] + emul * fmaf(ea[nt], xs, ea0[nt]) >= floor_l;
+          if (!cand && row < nrows && !A.topk) rem[q] += __builtin_amdgcn_exp2f(lg[q][nt] - mr);
           // lanes 16g..16g+15 hold row (q, g): their 16 bits are this row's components nt*16 .. +15
           const uint64_t b = __builtin_amdgcn_ballot_w64(cand);
           word |= (uint32_t)((b >> (16 * (lane >> 4))) & 0xFFFFu) << (16 * nt);
@@ -731,12 +735,17 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // fit step); 1: candidate marks and below-band mass against the row maximum
 // (pass T of the top-m); 2: the maximum alone (pass A of the top-m, whose
 // last kernel needs only the row maxima and pass T's masses)
+// MODE: 0 = pass A of the fit (slice max and sum), 1 = pass T of the top-m
+// (candidate masks), 2 = pass A of the top-m (slice max), 3 = pass A of the
+// top-k (slice max, and per lane group the maximum of score - error bound),
+// 4 = pass T of the top-k (candidates against the row's top-k threshold).
 template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
-  constexpr bool MARK = MODE == 1;
+  constexpr bool MARK = MODE == 1 || MODE == 4;
+  constexpr bool KLB = MODE == 3;  // lane-group lower-bound maxima
   constexpr int DP = 128, KSTEP = DP / 32, NCH = KSA / 32;
   constexpr int PT = 16 * RB;  // rows per tile
-  constexpr int NCST = MARK ? 6 : 4;  // per-component constants in LDS
+  constexpr int NCST = (MARK || KLB) ? 6 : 4;  // per-component constants in LDS
   constexpr int WFRAG = (KSA / 16) * 2 * KSTEP * 64;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -760,7 +769,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       cst[KSA + i] = (float)A.a[k];
       cst[2 * KSA + i] = A.esh[2 * k];
       cst[3 * KSA + i] = A.esh[2 * k + 1];
-      if constexpr (MARK) {
+      if constexpr (MARK || KLB) {
         cst[4 * KSA + i] = A.eall[2 * k];
         cst[5 * KSA + i] = A.eall[2 * k + 1];
       }
@@ -835,12 +844,13 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         xs[rb] = rows4_sum(q);
       }
     }
-    float M[RB], Sl[RB], R[RB];
+    float M[RB], Sl[RB], R[RB], Lb[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       M[rb] = kDead;
       Sl[rb] = 0.f;
       R[rb] = kDead;
+      Lb[rb] = kDead;
     }
     // pass T: the row maximum (pass B) is the reference of the candidate band
     // and of the sharp rescoring; rows past N have no candidates and no mass
@@ -853,7 +863,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         live[rb] = row < nrows;
         mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
         R[rb] = mr[rb];
-        thr[rb] = live[rb] ? mr[rb] - kTopmBand - 2.f * fmaf(eam, xs[rb], ea0m) : INFINITY;
+        if constexpr (MODE == 4)
+          thr[rb] = live[rb] ? A.kthr[row] : INFINITY;  // a lower bound of the row's top-k-th score
+        else
+          thr[rb] = live[rb] ? mr[rb] - kTopmBand - 2.f * fmaf(eam, xs[rb], ea0m) : INFINITY;
       }
     }
 #pragma unroll 1
@@ -922,8 +935,15 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const bool cand = acc[rb][nt][v] >= thr[rb];  // never for rows past N (thr = +inf)
-              if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][nt][v] - mr[rb]);
+              bool cand;  // never for rows past N (thr = +inf)
+              if constexpr (MODE == 4) {
+                // top-k: the score's upper end reaches the row's threshold
+                const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
+                cand = acc[rb][nt][v] + fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]) >= thr[rb];
+              } else {
+                cand = acc[rb][nt][v] >= thr[rb];
+                if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][nt][v] - mr[rb]);
+              }
               word |= (cand ? 1u : 0u) << (nt * 16 + 4 * (lane >> 4) + v);
             }
           word = rows4_or(word);
@@ -940,8 +960,20 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) cm = fmaxf(cm, acc[rb][nt][v]);
+        if constexpr (KLB) {
+          // this lane group's largest lower end, score - its error bound
+          float lb = Lb[rb];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
+              lb = fmaxf(lb, acc[rb][nt][v] - fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]));
+            }
+          Lb[rb] = lb;
+        }
         cm = rows4_max(cm);
-        if constexpr (MODE == 2) {
+        if constexpr (MODE == 2 || MODE == 3) {
           M[rb] = fmaxf(M[rb], cm);
           continue;
         }
@@ -953,6 +985,14 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           for (int v = 0; v < 4; ++v) s += __builtin_amdgcn_exp2f(acc[rb][nt][v] - Mn);
         Sl[rb] = s;
         M[rb] = Mn;
+      }
+    }
+    if constexpr (KLB) {
+      // lane group lane / 16 of row rb 16 + lane % 16: entry lane / 16 of (row, slice)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int64_t row = t * PT + rb * 16 + (lane & 15);
+        if (row < nrows) reinterpret_cast<float*>(A.lmx)[((size_t)row * A.S + slice) * 4 + (lane >> 4)] = Lb[rb];
       }
     }
 #pragma unroll
@@ -968,7 +1008,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           dst[0] = uint4{src[0], src[1], src[2], src[3]};
           dst[1] = uint4{src[4], src[5], src[6], src[7]};
         } else {
-          A.P[(size_t)row * A.S + slice] = float2{M[rb], MODE == 2 ? 1.f : S};
+          A.P[(size_t)row * A.S + slice] = float2{M[rb], (MODE == 2 || MODE == 3) ? 1.f : S};
         }
       }
     }
@@ -979,8 +1019,9 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 // read from LDS feeds kPassARB MFMAs
 constexpr int kPassARB = 4;
 
-size_t largek_pass_a_lds_bytes(bool mark) {
-  return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + (mark ? 6 : 4) * KSA * sizeof(float) +
+size_t largek_pass_a_lds_bytes(int mode) {
+  const bool mark = mode == 1 || mode == 4;
+  return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + ((mark || mode == 3) ? 6 : 4) * KSA * sizeof(float) +
          (mark ? (size_t)LNW * 16 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
 }
 
@@ -1008,6 +1049,32 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
     A.lse[row] = (float)l2;
     ll += l2 * LN2;
     if (A.topm) A.mrow[row] = M;
+    if (A.topk) {
+      // the m-th largest of the 4 S lane-group maxima of score - error bound:
+      // m different components reach it, so it bounds the row's m-th best true
+      // score from below (never below the dead-component floor, so padding
+      // never becomes a candidate); without them every live component is one
+      float top[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) top[j] = kDead;
+      if (A.lmx) {
+        const float* lv = reinterpret_cast<const float*>(A.lmx + (size_t)row * A.S);
+        for (int i = 0; i < 4 * A.S; ++i) {
+          float v = lv[i];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {  // insert into the descending list
+            const float hi = fmaxf(top[j], v), lo = fminf(top[j], v);
+            top[j] = hi;
+            v = lo;
+          }
+        }
+      }
+      float th = kDead;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j == A.m - 1) th = top[j];
+      A.kthr[row] = fmaxf(th, 0.5f * kDead);
+    }
   }
   red[threadIdx.x] = ll;
   __syncthreads();
@@ -1111,7 +1178,7 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
       ac.G = p.GbA;
       if (p.D == 128 && ac.vec16)
         hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 0>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
-                           largek_pass_a_lds_bytes(false), s, ac);
+                           largek_pass_a_lds_bytes(0), s, ac);
       else
         hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1190,7 +1257,9 @@ __global__ void __launch_bounds__(64 * kFinalRows, 4) largek_topm_final_kernel(L
 #pragma unroll
   for (int t = 0; t < kMaskSlots; ++t) {
     const int wi = lane * wpl + t;
-    mw[t] = (t < wpl && wi < nwords) ? A.cmask[(size_t)row * nwords + wi] : 0u;
+    uint32_t wd = (t < wpl && wi < nwords) ? A.cmask[(size_t)row * nwords + wi] : 0u;
+    if (wi * 32 + 32 > A.K) wd &= wi * 32 >= A.K ? 0u : (1u << (A.K - wi * 32)) - 1u;  // padding is never a candidate
+    mw[t] = wd;
     mycount += __popc(mw[t]);
   }
   int total;
@@ -1338,17 +1407,26 @@ __global__ void __launch_bounds__(64 * kFinalRows, 4) largek_topm_final_kernel(L
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // below-band mass of every slice, relative to the expanded-form maximum
-  const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
-  const double S = Srun + rem * exp2((double)A.mrow[row] - Mrun);
-  const double lse = Mrun + log2(S);
+  double lse;
+  if (A.topk) {
+    // top-k: the log-sum-exp of the kept m (the best first)
+    double S = 0.0;
+    for (int j = 0; j < m; ++j)
+      if (KK[j] < A.K) S += exp2(L[j] - L[0]);
+    lse = L[0] + log2(S);
+  } else {
+    // below-band mass of every slice, relative to the expanded-form maximum
+    const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
+    const double S = Srun + rem * exp2((double)A.mrow[row] - Mrun);
+    lse = Mrun + log2(S);
+  }
   if (lane == 0) {
     int c = 0;
     for (int j = 0; j < m; ++j) {
       const double bl = L[j];
       const int bk = KK[j];
       const double r = bk < A.K ? exp2(bl - lse) : 0.0;
-      const bool keep = bk < A.K && (j == 0 || r >= (double)A.thr) && c == j;
+      const bool keep = bk < A.K && (A.topk || j == 0 || r >= (double)A.thr) && c == j;
       A.idx[row * m + j] = keep ? bk : -1;
       A.resp[row * m + j] = keep ? (float)r : 0.f;
       if (keep) ++c;
@@ -1378,6 +1456,10 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
                               (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
     attr_set = true;
   }
   const int64_t N = a.N;
@@ -1391,17 +1473,28 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     ac.count = a.count ? a.count + r0 : nullptr;
     ac.logp = a.logp ? a.logp + r0 : nullptr;
     ac.G = p.GbA;
-    if (p.D == 128 && ac.vec16)
+    // the barrier-free passes (rows of 128 bf16, 16-byte aligned); the top-k
+    // threshold needs their lane-group maxima, without them every live
+    // component of a row is a top-k candidate
+    const bool bf = p.D == 128 && ac.vec16;
+    if (!bf) ac.lmx = nullptr;
+    if (bf && ac.topk)
+      hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 3>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(3), s, ac);
+    else if (bf)
       hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 2>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
-                         largek_pass_a_lds_bytes(false), s, ac);
+                         largek_pass_a_lds_bytes(2), s, ac);
     else
       hipLaunchKernelGGL(kA, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_a, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(largek_lse_kernel, dim3((unsigned)p.lse_blocks), dim3(256), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.D == 128 && ac.vec16)
+    if (bf && ac.topk)
+      hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 4>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(4), s, ac);
+    else if (bf)
       hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 1>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
-                         largek_pass_a_lds_bytes(true), s, ac);
+                         largek_pass_a_lds_bytes(1), s, ac);
     else
       hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;

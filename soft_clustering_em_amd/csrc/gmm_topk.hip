@@ -9,15 +9,13 @@
 //   S2_k = sum_i r'_ik (x_i - mu_k)^2 (per dimension; summed for spherical),
 //   LL = sum_i log sum_{j in top_k(i)} pi_j N(x_i | theta_j).
 //
-// The kept set: the k best components among those with r_ik >= 2^-20 (the
-// best one always) -- smaller responsibilities are below the float32
-// resolution of the row's sum, and every component above that floor lies in
-// the band of scores the top-m pass rescores exactly.
+// With k >= K every component is kept: the exact EM step.
 //
-// How: the library's top-m pass with m = k and threshold 2^-20 gives each row
-// that set in float64 order (ties to the lower index) with r_ik and log p(x_i);
-// topk_rows_kernel forms each row's 1 / sum r over the kept set and its
-// log-sum-exp over it (summed per block of 256 rows in a fixed tree); the
+// How: the library's top-m pass in its top-k mode gives each row its k best
+// components in float64 order (ties to the lower index), their
+// responsibilities normalised over those k, and the log-sum-exp over them;
+// topk_rows_kernel forms each row's 1 / sum r' (1 up to float32 rounding) and
+// its log-likelihood term (summed per block of 256 rows in a fixed tree); the
 // posting-list kernels group the entries by component in increasing row order;
 // topk_stats_kernel splits each component's list into S contiguous parts, one
 // workgroup per (problem, component, part), and sums a part's entries in list
@@ -36,8 +34,10 @@ namespace {
 
 constexpr int kRowsPerBlock = 256;
 
-// per row: rinv = 1 / sum of the kept responsibilities; per block of 256 rows
-// of one problem: the sum of log p(x) + log of that sum, in a fixed tree
+// per row: rinv = 1 / sum of the kept responsibilities (they were normalised
+// over the kept set; this removes their float32 rounding from the weights);
+// per block of 256 rows of one problem: the sum of the rows' log-sum-exp over
+// their kept components, in a fixed tree
 __global__ void __launch_bounds__(kRowsPerBlock) topk_rows_kernel(TopkStepArgs A, int64_t nblk) {
   __shared__ double red[kRowsPerBlock];
   const int64_t b = blockIdx.x / nblk, blk = blockIdx.x % nblk;
@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(kRowsPerBlock) topk_rows_kernel(TopkStepArgs A
     double s = 0.0;
     for (int j = 0; j < A.m; ++j) s += (double)A.resp[gi * A.m + j];
     A.rinv[gi] = s > 0.0 ? 1.0 / s : 0.0;
-    v = (double)A.logp[gi] + log(s);
+    v = (double)A.logp[gi];
   }
   red[t] = v;
   __syncthreads();

@@ -5,16 +5,28 @@
 // r >= threshold; ties go to the lower component index.
 //
 // The decisions (order, threshold) are taken on float64 scores:
-//   1. the float32 MFMA logits of the fused E-step give each row an
-//      approximate maximum Mt (exchanged across the waves of the workgroup);
-//   2. every component whose approximate score is within 32 (log2 units) of
-//      Mt is a candidate and is rescored exactly, in float64, by direct
-//      differences; the others carry responsibilities below 2^-32 and enter
-//      the log-sum-exp only as float32 terms;
+//   1. the float32 MFMA logits of the fused E-step give every score s~ with an
+//      error bound E (per component from the prologue: err.x |x| + err.y |x|^2,
+//      plus the float32 rounding of s~ itself), so s~ - E <= s <= s~ + E; each
+//      row's Mt = max (s~ - E) is a lower bound of its true best score
+//      (exchanged across the waves of the workgroup);
+//   2. every component whose s~ + E reaches Mt - 32 (log2 units) is a
+//      candidate and is rescored exactly, in float64, by direct differences:
+//      every component within 32 of the true best is among them; the others
+//      carry responsibilities below 2^-32 and enter the log-sum-exp only as
+//      float32 terms;
 //   3. per row the candidates are sorted (score descending, index ascending),
 //      and LSE, responsibilities and the kept ranks follow in float64.
 // A row with more than CAP candidates is rescored over all K components by
 // one wave (the workgroup's waves take such rows in turn).
+//
+// Top-k mode (the approx_top_k training mode of the GMMXX README: a row keeps
+// its k best log-scores and normalises over them): the candidate threshold is
+// instead a lower bound of the row's k-th best true score -- the k-th largest
+// of the per-lane maxima of s~ - E over the row's components (k different
+// components reach it) -- so every component of the true top k is a
+// candidate; the m = k best after rescoring are kept, with responsibilities
+// and log-sum-exp over those k only.
 #include "gmm_device.h"
 #include "gmm_internal.h"
 
@@ -56,6 +68,10 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
   int* ck = reinterpret_cast<int*>(redm + NW * T);          // T*CAP candidate indices
   int* cnt = ck + T * CAP;                                  // T
   int* qtab = cnt + T;                                      // F
+  float* xnq = reinterpret_cast<float*>(qtab + F);          // T*2: |x|, |x|^2 of each row
+  float* kth = xnq + 2 * T;                                 // T: top-k candidate threshold of each row
+  float* lsc = reinterpret_cast<float*>(cl);                // top-k: T*16*NW per-lane maxima (before cl is used)
+  const bool topk = A.topk != 0;
 
   {
     const float4* src = reinterpret_cast<const float4*>(A.W + (size_t)b * KP * F);
@@ -67,11 +83,15 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       qtab[f] = f < DP ? ((f << 16) | 0xFFFF) : (f - DP < NQ ? quad_pair<DP>(f - DP) : -1);
   }
   double creg[NT], areg[NT];
+  float ex[NT], ey[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int k = wv * KW + nt * 16 + (lane & 15);
     creg[nt] = A.c[(size_t)b * KP + k];
     areg[nt] = (COV == SPH) ? A.a[(size_t)b * KP + k] : 0.0;
+    const float2 e = A.err[(size_t)b * KP + k];
+    ex[nt] = e.x;
+    ey[nt] = e.y;
   }
   const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)b * A.stride_b;
 
@@ -119,8 +139,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       }
     }
     for (int p = threadIdx.x; p < T; p += nthr) cnt[p] = 0;
-    // diagonal features are complete when prefetched; the rest need the whole tile
-    if (!pre || COV != DIAG) __syncthreads();
+    __syncthreads();  // the row norms below read whole rows
     if (!pre) {
       for (int j = threadIdx.x; j < T * DP; j += nthr) {
         const int r = j / DP, d = j % DP;
@@ -129,12 +148,12 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
         if constexpr (COV == DIAG) phi[r * FS + DP + d] = v * v;
       }
     }
-    if constexpr (COV == SPH) {
-      for (int r = threadIdx.x; r < T; r += nthr) {
-        double s = 0.0;
-        for (int d = 0; d < D; ++d) s += (double)raw[r * DP + d] * (double)raw[r * DP + d];
-        xsq[r] = s;
-      }
+    for (int r = threadIdx.x; r < T; r += nthr) {
+      double s = 0.0;
+      for (int d = 0; d < D; ++d) s += (double)raw[r * DP + d] * (double)raw[r * DP + d];
+      xsq[r] = s;
+      xnq[2 * r] = (float)sqrt(s) * (1.f + 0x1p-20f);
+      xnq[2 * r + 1] = (float)s * (1.f + 0x1p-20f);
     }
     if constexpr (QUAD) {
       constexpr int NQP = F - DP;
@@ -190,13 +209,27 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
         for (int nt = 0; nt < NT; ++nt) lg[nt][v] += areg[nt] * xs;
       }
     }
-    // ---- approximate row maximum over all components
+    // ---- error bounds: lo <= true score <= hi; the row maximum of lo
+    float lo[NT][4], hi[NT][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = 4 * (lane >> 4) + v;
+      const float xn = xnq[2 * p], xq = xnq[2 * p + 1];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float lv = (float)lg[nt][v];
+        const float e = lv > -INFINITY ? fmaf(ex[nt], xn, ey[nt] * xq) + 0x1p-22f * fabsf(lv) : 0.f;
+        lo[nt][v] = lv - e;
+        hi[nt][v] = lv + e;
+      }
+    }
     float mw[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float mx = (float)lg[0][v];
+      float mx = lo[0][v];
 #pragma unroll
-      for (int nt = 1; nt < NT; ++nt) mx = fmaxf(mx, (float)lg[nt][v]);
+      for (int nt = 1; nt < NT; ++nt) mx = fmaxf(mx, lo[nt][v]);
+      if (topk) lsc[(4 * (lane >> 4) + v) * (16 * NW) + wv * 16 + (lane & 15)] = mx;
       mw[v] = row16_max(mx);
     }
     if ((lane & 15) == 0)
@@ -210,6 +243,29 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       for (int w2 = 0; w2 < NW; ++w2) mx = fmaxf(mx, redm[w2 * T + p]);
       Mt[v] = mx;
     }
+    if (topk) {
+      // per row (a wave each, in turn): the m-th largest of the 16 NW lane
+      // maxima of lo -- m different components reach it, so the row's m-th
+      // best true score is at least that
+      for (int p = wv; p < T; p += NW) {
+        const int nv = 16 * NW;
+        float a0 = lane < nv ? lsc[p * nv + lane] : -INFINITY;
+        float a1 = lane + 64 < nv ? lsc[p * nv + lane + 64] : -INFINITY;
+        float mx = -INFINITY;
+        for (int j = 0; j < m; ++j) {
+          mx = (float)wave_max((double)fmaxf(a0, a1));
+          const uint64_t b0 = __builtin_amdgcn_ballot_w64(a0 == mx);
+          if (b0) {
+            if (lane == (int)__builtin_ctzll(b0)) a0 = -INFINITY;
+          } else {
+            const uint64_t b1 = __builtin_amdgcn_ballot_w64(a1 == mx);
+            if (b1 && lane == (int)__builtin_ctzll(b1)) a1 = -INFINITY;
+          }
+        }
+        if (lane == 0) kth[p] = mx;
+      }
+      __syncthreads();
+    }
     // ---- candidates: first counted (each takes a slot), the rest summed as
     // float32 terms; then, in rows whose candidates fit the list, rescored
     // exactly (a row past CAP is rescored over all K below instead)
@@ -218,14 +274,16 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
     for (int v = 0; v < 4; ++v) {
       const int p = 4 * (lane >> 4) + v;
       const bool valid = row0 + p < N;
+      const float thc = topk ? kth[p] : Mt[v] - DELTA;
       float nc = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float lv = (float)lg[nt][v];
+        const int k = wv * KW + nt * 16 + (lane & 15);
         slotv[nt][v] = -1;
-        if (valid && lv >= Mt[v] - DELTA) {
+        if (valid && k < K && hi[nt][v] > -INFINITY && hi[nt][v] >= thc) {
           slotv[nt][v] = atomicAdd(&cnt[p], 1);
-        } else if (valid && lv > -INFINITY) {
+        } else if (!topk && valid && lv > -INFINITY) {
           nc += __builtin_amdgcn_exp2f(lv - Mt[v]);
         }
       }
@@ -304,29 +362,43 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
         L[j + 1] = li;
         Kx[j + 1] = ki;
       }
-      float mt = -INFINITY;
-      double ncs = 0.0;
-      for (int w2 = 0; w2 < NW; ++w2) mt = fmaxf(mt, redm[w2 * T + p]);
-      for (int w2 = 0; w2 < NW; ++w2) ncs += rednc[w2 * T + p];
-      const double M = L[0];
-      double S = 0.0;
-      for (int j = 0; j < n; ++j) S += exp2(L[j] - M);
-      S += ncs * exp2((double)mt - M);
-      const double lse = M + log2(S);
+      const double M = n > 0 ? L[0] : -INFINITY;
+      double lse;
       int c = 0;
-      for (int j = 0; j < m; ++j) {
-        int kk = -1;
-        float rr = 0.f;
-        if (j < n) {
-          const double r = exp2(L[j] - lse);
-          if ((j == 0 || r >= (double)A.thr) && c == j) {
-            kk = Kx[j];
-            rr = (float)r;
-            ++c;
-          }
+      if (topk) {
+        // the m best, normalised over themselves
+        const int kept = min(m, n);
+        double S = 0.0;
+        for (int j = 0; j < kept; ++j) S += exp2(L[j] - M);
+        lse = M + log2(S);
+        for (int j = 0; j < m; ++j) {
+          A.idx[((size_t)b * N + row) * m + j] = j < kept ? Kx[j] : -1;
+          A.resp[((size_t)b * N + row) * m + j] = j < kept ? (float)exp2(L[j] - lse) : 0.f;
         }
-        A.idx[((size_t)b * N + row) * m + j] = kk;
-        A.resp[((size_t)b * N + row) * m + j] = rr;
+        c = kept;
+      } else {
+        float mt = -INFINITY;
+        double ncs = 0.0;
+        for (int w2 = 0; w2 < NW; ++w2) mt = fmaxf(mt, redm[w2 * T + p]);
+        for (int w2 = 0; w2 < NW; ++w2) ncs += rednc[w2 * T + p];
+        double S = 0.0;
+        for (int j = 0; j < n; ++j) S += exp2(L[j] - M);
+        S += ncs * exp2((double)mt - M);
+        lse = M + log2(S);
+        for (int j = 0; j < m; ++j) {
+          int kk = -1;
+          float rr = 0.f;
+          if (j < n) {
+            const double r = exp2(L[j] - lse);
+            if ((j == 0 || r >= (double)A.thr) && c == j) {
+              kk = Kx[j];
+              rr = (float)r;
+              ++c;
+            }
+          }
+          A.idx[((size_t)b * N + row) * m + j] = kk;
+          A.resp[((size_t)b * N + row) * m + j] = rr;
+        }
       }
       if (A.count) A.count[(size_t)b * N + row] = c;
       if (A.logp) A.logp[(size_t)b * N + row] = (float)(lse * LN2);
@@ -350,13 +422,17 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
           mx = fmax(mx, ls[i]);
         }
         const double M = wave_max(mx);
-        double s = 0.0;
+        double lse = 0.0;
+        if (!topk) {
+          double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) s += ls[i] > -INFINITY ? exp2(ls[i] - M) : 0.0;
-        const double lse = M + log2(wave_sum(s));
-        int c = 0;
+          for (int i = 0; i < PER; ++i) s += ls[i] > -INFINITY ? exp2(ls[i] - M) : 0.0;
+          lse = M + log2(wave_sum(s));
+        }
+        // the m best (score, index), one per round; lane j keeps round j's
+        double rl = -INFINITY;
+        int rk = 0x7fffffff;
         for (int j = 0; j < m; ++j) {
-          // best remaining (score, index) over the wave
           double bl = -INFINITY;
           int bk = 0x7fffffff;
 #pragma unroll
@@ -368,13 +444,21 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
 #pragma unroll
           for (int i = 0; i < PER; ++i)
             if (lane + 64 * i == bk) ls[i] = -INFINITY;  // taken
-          const double r = exp2(bl - lse);
-          const bool keep = bk < K && (j == 0 || r >= (double)A.thr) && c == j;
-          if (lane == 0) {
-            A.idx[((size_t)b * N + row) * m + j] = keep ? bk : -1;
-            A.resp[((size_t)b * N + row) * m + j] = keep ? (float)r : 0.f;
+          if (lane == j) {
+            rl = bl;
+            rk = bk;
           }
-          if (keep) ++c;
+        }
+        // top-k: the log-sum-exp of the kept ones (round 0 holds the maximum)
+        if (topk) lse = M + log2(wave_sum((lane < m && rk < K) ? exp2(rl - M) : 0.0));
+        // the kept ranks are a prefix: top-k every one found; top-m rank 1, then
+        // the ranks while r >= threshold
+        const double r = rk < K ? exp2(rl - lse) : 0.0;
+        const bool ok = lane < m && rk < K && (topk || lane == 0 || r >= (double)A.thr);
+        const int c = (int)__builtin_ctzll(~__builtin_amdgcn_ballot_w64(ok));
+        if (lane < m) {
+          A.idx[((size_t)b * N + row) * m + lane] = lane < c ? rk : -1;
+          A.resp[((size_t)b * N + row) * m + lane] = lane < c ? (float)r : 0.f;
         }
         if (lane == 0) {
           if (A.count) A.count[(size_t)b * N + row] = c;

@@ -1,10 +1,10 @@
-"""Parity of gmm_topk_fit_step (approximate top-k EM: each row keeps its k
-best components among those with responsibility >= 2^-20, the best always, and
-normalises over them) against the float64 oracle
-(oracle.topk_fit_step, pinned by its k = K and k = 1 special cases), one step
-from identical float32 parameters.  The kept sets are decided on float64
-scores on both sides and the statistics are float64 sums of float32
-responsibilities, so the float32 bar of 1e-4 holds for bf16 rows too."""
+"""Parity of gmm_topk_fit_step (approximate top-k EM, the approx_top_k mode of
+the GMMXX README: each row keeps its k best log-scores and normalises over
+them; k >= K is exact EM) against the float64 oracle (oracle.topk_fit_step,
+pinned by its k >= K, k = 1 and common-kept-set special cases), one step from
+identical float32 parameters.  The kept sets are decided on float64 scores on
+both sides and the statistics are float64 sums of float32 responsibilities,
+so the float32 bar of 1e-4 holds for bf16 rows too."""
 import numpy as np
 import pytest
 
@@ -68,28 +68,74 @@ def test_topk_step_float32(torch_cuda, cov, B, N, D, K, topk):
     assert (cs >= 0).all()
 
 
-def test_topk_with_every_component_is_the_exact_step(torch_cuda):
-    """k >= K: the GPU top-k step and the GPU exact step agree to float32
-    rounding (what the 2^-20 floor drops is below it here)."""
+@pytest.mark.parametrize("cov", ["spherical", "diag"])
+def test_topk_with_every_component_is_the_exact_step(torch_cuda, cov):
+    """k >= K: the GPU top-k step equals the oracle's exact EM step and the GPU
+    exact step (the page: values >= K resolve to exact EM)."""
     import soft_clustering_em_amd as g
     torch = torch_cuda
     rng = np.random.default_rng(41)
     B, N, D, K = 1, 4000, 10, 12
     X = rng.normal(size=(B, N, D)).astype(np.float32) * 2.0
-    th = theta(rng, "diag", B, K, D, X)
+    th = theta(rng, cov, B, K, D, X)
     Xd = torch.from_numpy(X).cuda()
-    got, mll, _ = gpu_step(torch, Xd, th, "diag", 16)
+    got, mll, _ = gpu_step(torch, Xd, th, cov, 16)
+    ref = oracle.fit_step(cov, X[0].astype(np.float64), *(a[0].astype(np.float64) for a in th))
+    e = param_errors(cov, 1, K, D, got, (ref["w"], ref["mu"], ref["cv"]), ref["stats"]["nk"])
+    assert e["mu"] <= TOL_F32 and e["cv"] <= TOL_F32 and e["w"] <= TOL_F32, e
+    assert abs(mll[0] - ref["mean_ll"][0]) <= 1e-6 * abs(ref["mean_ll"][0])
     w, mu, cv = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in th)
     m2 = torch.zeros(B, dtype=torch.float64, device="cuda")
-    g.gmm_fit_step(Xd, w, mu, cv, "diag", mean_loglik=m2)
-    e = param_errors("diag", B, K, D, got, (to_np(w), to_np(mu), to_np(cv)), np.full((B, K), 10.0))
+    g.gmm_fit_step(Xd, w, mu, cv, cov, mean_loglik=m2)
+    e = param_errors(cov, B, K, D, got, (to_np(w), to_np(mu), to_np(cv)), np.full((B, K), 10.0))
     assert e["mu"] <= 1e-5 and e["cv"] <= 1e-5 and e["w"] <= 1e-5, e
     assert abs(mll[0] - float(m2[0])) <= 1e-6 * abs(float(m2[0]))
 
 
-@pytest.mark.parametrize("N,D,K,topk", [(5003, 128, 512, 4), (3000, 100, 300, 2)])
+@pytest.mark.parametrize("cov", ["spherical", "diag"])
+def test_topk_step_float32_far_tail(torch_cuda, cov):
+    """256 well-separated clusters in 64 dimensions, components started at
+    data rows, k = 4: the 2nd-4th kept components of most rows carry
+    responsibilities far below 2^-20, and for components with few rows of
+    their own those tiny weights make much of the scatter (dropping them
+    would change variances by up to 0.5 relative here)."""
+    torch = torch_cuda
+    N, D, K, topk = 5003, 64, 256, 4
+    rng = np.random.default_rng(N + topk)
+    centers = 3.0 * rng.standard_normal((K, D))
+    X = (centers[rng.integers(0, K, N)] + rng.standard_normal((N, D))).astype(np.float32)[None]
+    th = theta(rng, cov, 1, K, D, X)
+    got, mll, cs = gpu_step(torch, torch.from_numpy(X).cuda(), th, cov, topk)
+    check(f"far tail {cov}", cov, X.astype(np.float64), th, got, mll, topk)
+
+
+@pytest.mark.parametrize("cov", ["spherical", "diag"])
+def test_topk_keeps_far_rows_of_a_narrow_component(torch_cuda, cov):
+    """k = 2 of K = 3, the third component far away (every row keeps 0 and 1):
+    component 1 is narrow, so most rows give it a responsibility far below
+    2^-20 that is still kept and still carries its scatter.  Checked against
+    the oracle (which the pins tie to exact EM of the two-component
+    sub-mixture here)."""
+    torch = torch_cuda
+    rng = np.random.default_rng(35)
+    D, N = 2, 6000
+    X = rng.normal(size=(N, D))
+    X[:2] = [[0.5, 0.5], [0.5 + 1e-3, 0.5]]
+    X = X.astype(np.float32)
+    w = np.array([[0.5, 0.3, 0.2]], np.float32)
+    mu = np.array([[[0.0, 0.0], [0.5 + 5e-4, 0.5], [400.0, -400.0]]], np.float32)
+    cv = (np.array([[1.0, 1e-3, 1.0]]) if cov == "spherical" else
+          np.array([[[1.0, 1.2], [1e-3, 2e-3], [1.0, 1.0]]])).astype(np.float32)
+    got, mll, cs = gpu_step(torch, torch.from_numpy(X[None]).cuda(), (w, mu, cv), cov, 2)
+    check(f"narrow {cov}", cov, X[None].astype(np.float64), (w, mu, cv), got, mll, 2)
+
+
+@pytest.mark.parametrize("N,D,K,topk", [(5003, 128, 512, 4), (3000, 100, 300, 2), (4099, 128, 700, 16),
+                                        (2000, 128, 600, 1)])
 def test_topk_step_bf16_rows(torch_cuda, N, D, K, topk):
-    """bf16 rows take the large-K top-m (spherical, any K)."""
+    """bf16 rows take the large-K top-m in its top-k mode (spherical, any K);
+    D = 128 forms the per-row top-k threshold, D = 100 rescores every
+    component of a row."""
     torch = torch_cuda
     rng = np.random.default_rng(N + topk)
     centers = 3.0 * rng.standard_normal((K, D))
@@ -115,11 +161,33 @@ def test_topk_step_is_deterministic(torch_cuda):
     assert np.array_equal(a[1], b[1])
 
 
+def test_topk_step_bf16_collapsed_component(torch_cuda):
+    """bf16 rows, K = 512: one component collapsed (variance 1e-4) onto a
+    tight group of rows, k = 4 -- far rows keep it among their top 4 with
+    tiny responsibilities that carry much of its scatter."""
+    torch = torch_cuda
+    rng = np.random.default_rng(77)
+    N, D, K = 6000, 128, 512
+    centers = rng.standard_normal((K, D)) / np.sqrt(D)
+    Xf = (centers[rng.integers(0, K, N)] + 0.05 * rng.standard_normal((N, D))).astype(np.float32)
+    Xf[:40] = centers[0] + 0.01 * rng.standard_normal((40, D))
+    bits = synth.f32_to_bf16_bits(Xf)
+    X64 = synth.bf16_bits_to_f32(bits).astype(np.float64)[None]
+    w = np.full((1, K), 1.0 / K, np.float32)
+    mu = centers[None].astype(np.float32)
+    cv = np.full((1, K), 0.05 ** 2, np.float32)
+    cv[0, 0] = 1e-4
+    Xd = torch.from_numpy(np.ascontiguousarray(bits[None]).view(np.int16)).cuda().view(torch.bfloat16)
+    got, mll, cs = gpu_step(torch, Xd, (w, mu, cv), "spherical", 4)
+    check("bf16 collapsed K=512 k=4", "spherical", X64, (w, mu, cv), got, mll, 4)
+
+
 def test_topk_step_full_size_properties(torch_cuda):
     """1M rows x D = 64, K = 256 (the diagonal benchmark workload), k = 4: the
-    weights sum to 1, no component fails, and per row log sum over the kept
-    set lies between log p(x) - log K and log p(x), so the step's mean LL lies
-    between the exact step's minus log K and the exact step's."""
+    weights sum to 1, no component fails, and per row the log sum over the kept
+    set lies between log p(x) - log(K / k) (the k largest of K terms hold at
+    least k / K of the mass) and log p(x), so the step's mean LL lies in that
+    range of the exact step's."""
     import soft_clustering_em_amd as g
     torch = torch_cuda
     wl = synth.diag_large()
@@ -133,5 +201,5 @@ def test_topk_step_full_size_properties(torch_cuda):
     print(f"full size: top-k mean LL {mll[0]:.6f}, exact {exact:.6f}", flush=True)
     assert (cs >= 0).all()
     assert abs(float(got[0].astype(np.float64).sum()) - 1.0) < 1e-5
-    assert exact - np.log(256) - 1e-6 <= mll[0] <= exact + 1e-6 * abs(exact)
+    assert exact - np.log(256 / 4) - 1e-6 <= mll[0] <= exact + 1e-6 * abs(exact)
     assert np.isfinite(got[1]).all() and (got[2] > 0).all()
