@@ -33,8 +33,12 @@
  *           previous mu_k and Sigma_k are kept;
  *        4  the input full/tied covariance is not positive definite: the
  *           component gets zero responsibility in this E-step.
- *   - Results are deterministic: no atomics; every reduction runs in a fixed
- *     order for a given shape.
+ *   - Results are deterministic: no global-memory atomics, and every reduction
+ *     runs in a fixed order for a given shape.  Two kernels hand out slots of
+ *     per-row candidate lists with LDS atomic counters (top-m: the waves of a
+ *     workgroup; kernel density: the 16 lanes of one row); the lists are
+ *     sorted by (score, index), or walked in increasing index order, before
+ *     any result depends on them, so the slot order never shows.
  *   - Calls on distinct streams with distinct workspaces may run concurrently.
  */
 #ifndef GMM_H
@@ -65,7 +69,10 @@ typedef enum {
   GMM_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride, ...  */
   GMM_ERR_UNSUPPORTED = 2, /* valid but outside the supported shape/type window */
   GMM_ERR_WORKSPACE = 3,   /* ws is NULL, misaligned or smaller than required   */
-  GMM_ERR_HIP = 4          /* a HIP launch or runtime call failed               */
+  GMM_ERR_HIP = 4,         /* a HIP launch or runtime call failed               */
+  GMM_ERR_NOT_PD = 5       /* a covariance is not positive definite (returned by
+                              gmm_check_components only: the compute calls run
+                              asynchronously and report it per component)      */
 } gmm_status;
 
 /* Operation selector for gmm_workspace_bytes. */
@@ -273,6 +280,17 @@ gmm_status gmm_fisher_vector(const gmm_data* data, const gmm_params* model, uint
 size_t gmm_kde_workspace_bytes(const gmm_data* queries, int64_t M);
 gmm_status gmm_kde_score(const gmm_data* queries, const float* ref, int64_t M, int64_t ld_ref, double bandwidth,
                          float* logdens, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-side summary of a comp_status array that the caller copied to host
+ * memory (count int32 values, as written by gmm_mstep / gmm_fit_step /
+ * gmm_topk_fit_step): GMM_ERR_NOT_PD if any component carries flag 2 (its
+ * updated covariance was not positive definite) or flag 4 (its input
+ * covariance was not), else GMM_OK; GMM_ERR_INVALID_ARG for a NULL array or
+ * count < 0.  *first (nullable) receives the index of the first such
+ * component, or -1.  No HIP call.  The compute calls cannot return
+ * GMM_ERR_NOT_PD themselves: detecting it would need a device-to-host
+ * synchronisation in every call. */
+gmm_status gmm_check_components(const int32_t* comp_status_host, int64_t count, int64_t* first);
 
 /* Static description of a status code. */
 const char* gmm_status_str(int32_t status);

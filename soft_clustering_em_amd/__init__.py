@@ -14,6 +14,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_kmeans_step(X, centroids, labels=None, counts=None, inertia=None, ws=None)
   gmm_fisher_vector(X, w, mu, var, power=True, l2=True, fv=None, ws=None)
   gmm_topk_fit_step(X, w, mu, cv, cov, topk, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
+  gmm_check_components(comp_status)          -> (status, first index or -1); synchronises
 
 The estimator calls (score_samples, predict, score, aic, bic, fit with
 restarts) are in soft_clustering_em_amd.estimator.
@@ -294,3 +295,17 @@ def gmm_topk_fit_step(X, w, mu, cv, cov, topk, reg_covar=1e-6, mean_loglik=None,
     _abi.check(_abi.lib().gmm_topk_fit_step(ctypes.byref(d), ctypes.byref(p), int(topk), ctypes.byref(o),
                                             _ptr(mean_loglik), _ptr(comp_status), _ptr(ws), ws.numel(),
                                             _stream(stream)))
+
+
+def gmm_check_components(comp_status):
+    """Copy comp_status (B, K) to the host (a synchronisation) and summarise it
+    with the library's gmm_check_components: (GMM_ERR_NOT_PD, index of the
+    first component whose input or updated covariance was not positive
+    definite) or (GMM_OK, -1)."""
+    import numpy as np
+    host = np.ascontiguousarray(comp_status.detach().to("cpu").numpy(), dtype=np.int32).reshape(-1)
+    first = ctypes.c_int64(-1)
+    st = _abi.lib().gmm_check_components(host.ctypes.data, host.size, ctypes.byref(first))
+    if st not in (_abi.GMM_OK, _abi.GMM_ERR_NOT_PD):
+        _abi.check(st)
+    return st, first.value

@@ -17,13 +17,13 @@ COV_SPHERICAL, COV_DIAG, COV_TIED, COV_FULL = 0, 1, 2, 3
 COV_CODES = {"spherical": COV_SPHERICAL, "diag": COV_DIAG, "tied": COV_TIED, "full": COV_FULL}
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 OP_FIT, OP_ESTEP, OP_TOPM = 0, 1, 2
-GMM_OK, GMM_ERR_INVALID_ARG, GMM_ERR_UNSUPPORTED, GMM_ERR_WORKSPACE, GMM_ERR_HIP = 0, 1, 2, 3, 4
+GMM_OK, GMM_ERR_INVALID_ARG, GMM_ERR_UNSUPPORTED, GMM_ERR_WORKSPACE, GMM_ERR_HIP, GMM_ERR_NOT_PD = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step",
             "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
             "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector",
             "gmm_topk_fit_workspace_bytes", "gmm_topk_fit_step", "gmm_kde_workspace_bytes", "gmm_kde_score",
-            "gmm_status_str",
+            "gmm_check_components", "gmm_status_str",
             "gmm_last_error", "gmm_version"]
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_predict_proba_topm, L.gmm_ivf_lists,
                   L.gmm_kmeans_step, L.gmm_fisher_vector, L.gmm_topk_fit_step, L.gmm_kde_score):
             f.restype = ctypes.c_int
+        L.gmm_check_components.argtypes = [P, ctypes.c_int64, P]
+        L.gmm_check_components.restype = ctypes.c_int
         L.gmm_status_str.argtypes = [ctypes.c_int32]
         L.gmm_status_str.restype = ctypes.c_char_p
         L.gmm_last_error.argtypes = []

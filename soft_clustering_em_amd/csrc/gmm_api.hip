@@ -970,8 +970,23 @@ const char* gmm_status_str(int32_t status) {
     case GMM_ERR_UNSUPPORTED: return "unsupported shape or type";
     case GMM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case GMM_ERR_HIP: return "HIP runtime error";
+    case GMM_ERR_NOT_PD: return "covariance not positive definite";
     default: return "unknown status";
   }
+}
+
+gmm_status gmm_check_components(const int32_t* comp_status_host, int64_t count, int64_t* first) {
+  g_err.clear();
+  if (first) *first = -1;
+  if (!comp_status_host || count < 0) return fail(GMM_ERR_INVALID_ARG, "comp_status must be non-NULL, count >= 0");
+  for (int64_t i = 0; i < count; ++i) {
+    if (comp_status_host[i] & (2 | 4)) {
+      if (first) *first = i;
+      return fail(GMM_ERR_NOT_PD, "component %lld: covariance not positive definite (flag %d)", (long long)i,
+                  comp_status_host[i]);
+    }
+  }
+  return GMM_OK;
 }
 
 const char* gmm_last_error(void) { return g_err.c_str(); }

@@ -126,9 +126,27 @@ def test_fit_step_validation_happens_before_any_device_work(case, expect):
 
 def test_status_strings():
     L = _abi.lib()
-    for s in range(5):
-        assert L.gmm_status_str(s).decode()
+    for s in range(6):
+        assert L.gmm_status_str(s).decode() != "unknown status"
     assert L.gmm_status_str(99).decode() == "unknown status"
+
+
+def test_check_components_reports_not_positive_definite():
+    """The host-side summary of comp_status: flags 2 and 4 are GMM_ERR_NOT_PD
+    (first such component reported), flag 1 alone is not."""
+    import numpy as np
+    L = _abi.lib()
+    first = ctypes.c_int64(7)
+    ok = np.array([0, 1, 0, 1], np.int32)
+    assert L.gmm_check_components(ok.ctypes.data, ok.size, ctypes.byref(first)) == _abi.GMM_OK
+    assert first.value == -1
+    for flag in (2, 4, 6):
+        bad = np.array([1, 0, flag, 4], np.int32)
+        st = L.gmm_check_components(bad.ctypes.data, bad.size, ctypes.byref(first))
+        assert st == _abi.GMM_ERR_NOT_PD and first.value == 2
+        assert "positive definite" in L.gmm_last_error().decode()
+    assert L.gmm_check_components(None, 3, None) == _abi.GMM_ERR_INVALID_ARG
+    assert L.gmm_check_components(ok.ctypes.data, 0, None) == _abi.GMM_OK
 
 
 def test_mstep_validation():
