@@ -1,16 +1,25 @@
 """Benchmark of the fused EM iteration on one MI355X.
 
-A step is one EM iteration (gmm_fit_step: precision prologue, fused E-step
-with statistics, deterministic reduction, M-step) over the whole synthetic
+A step is one EM iteration (gmm_fit_step: precision prologue, E-step with
+statistics, deterministic reduction, M-step) over the whole synthetic
 workload, with the rows already resident in device memory.  The default
-workload is the diagonal-covariance one (N = 1,000,000 rows, D = 64, K = 256,
-float32); the others are available with --workload.
+workload is the largest configuration that fits one GPU: the IVF coarse
+quantizer (spherical GMM, N = 10,000,000 bf16 rows, D = 128, K = 4096); the
+others are available with --workload.
 
 Prints ONE JSON line (rank 0): value = points*components per second
-(B*N*K / time per iteration), plus the roofline of the fused E-step kernel
-(timed with HIP events that the library records around that kernel on the
-stream it runs on) and the float64 CPU oracle timed on the host cores on a
+(B*N*K / time per iteration), plus the roofline of the E-step (timed with HIP
+events that the library records around it on the stream it runs on) against
+the dense MFMA peak of the type its contractions run in (bf16 for bf16 rows,
+float32 otherwise), and the float64 CPU oracle timed on the host cores on a
 bounded sample of the same workload.
+
+The timed loop is bracketed by two short spin kernels (torch.cuda._sleep),
+outside the timed region, so that a kernel trace of the same command can be
+cut to the timed dispatches:  python bench.py --summarize DIR  prints the
+per-kernel summary of the rocprofv3 kernel trace under DIR between those
+markers (and, with --counters, the per-kernel sums of the counters of a
+rocprofv3 --pmc run, calibrated by the --calib-copy copy kernel).
 """
 from __future__ import annotations
 
@@ -83,12 +92,30 @@ def measured_traffic(workload, source):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def host_threads():
+    """Threads the oracle may use: the cores this process may run on, capped by
+    OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=20.0, max_steps=4, target_macs=2e10):
     """The float64 oracle's EM iteration on the host cores, on the first rows of
     the workload (all of them when one iteration stays near target_macs
     multiply-adds), reported per point*component."""
     import oracle
-    nthreads = os.cpu_count() or 1
+    nthreads = host_threads()
     per_pair = wl.D * (wl.D + 1) if wl.cov in ("full", "tied") else wl.D
     rows = int(min(wl.N, max(1024, target_macs // (wl.B * wl.K * per_pair))))
     Xs = wl.X[:, :rows]
@@ -106,10 +133,113 @@ def cpu_baseline(wl, budget_s=20.0, max_steps=4, target_macs=2e10):
     t = float(np.median(times))
     what = "the full" if rows == wl.N else f"the first {rows} rows of the"
     return {"value": wl.B * rows * wl.K / t, "unit": "points*components/s", "cores": nthreads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(times)} float64 EM iterations of {what} {wl.name} workload "
                       f"(B={wl.B}, N={wl.N}, D={wl.D}, K={wl.K}) from theta_0, median "
                       f"{t:.2f} s/iteration"}
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(root, suffix):
+    out = []
+    for d, _, files in os.walk(root):
+        out += [os.path.join(d, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def _window(rows):
+    """(first, last) dispatch ids strictly between the first two spin-kernel
+    markers, or None when the trace has fewer than two."""
+    marks = sorted(int(r["Dispatch_Id"]) for r in rows if "spin" in r["Kernel_Name"].lower())
+    if len(marks) < 2:
+        return None
+    # the two markers of the timed loop are consecutive spin dispatches
+    return marks[0], marks[1]
+
+
+def _short(name, n=90):
+    name = name.replace("gmm::(anonymous namespace)::", "gmm::")
+    return name if len(name) <= n else name[:n] + "..."
+
+
+def summarize(root, counters, calib_mib):
+    """Markdown summary of rocprofv3 output under root.  Trace: per-kernel
+    calls and durations of the dispatches between the timed-loop markers, then
+    of those after them.  Counters: per kernel in the timed window, the
+    counters' mean per dispatch; FETCH_SIZE / WRITE_SIZE also scaled by what
+    they read on the calibration copy of calib_mib MiB (the last copy kernel
+    before the window)."""
+    if not counters:
+        files = _find(root, "kernel_trace.csv")
+        if not files:
+            sys.exit(f"no kernel_trace.csv under {root}")
+        rows = [r for f in files for r in _read_csv(f)]
+        win = _window(rows)
+
+        def table(sel, title):
+            agg = {}
+            for r in sel:
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                agg.setdefault(r["Kernel_Name"], []).append(d)
+            tot = sum(sum(v) for v in agg.values())
+            print(f"\n{title}\n")
+            print("| kernel | calls | total (us) | average (us) | min (us) | max (us) | share |")
+            print("|---|---|---|---|---|---|---|")
+            for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+                print(f"| `{_short(k)}` | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                      f"{max(v):.1f} | {100 * sum(v) / tot:.1f}% |")
+            print(f"\nSum of kernel durations: {tot:.1f} us.")
+
+        if win is None:
+            table(rows, "All dispatches (no timed-loop markers in this trace):")
+            return
+        lo, hi = win
+        timed = [r for r in rows if lo < int(r["Dispatch_Id"]) < hi]
+        after = [r for r in rows if int(r["Dispatch_Id"]) > hi and "spin" not in r["Kernel_Name"].lower()]
+        table(timed, f"Timed loop (dispatches {lo + 1}..{hi - 1}, between the markers):")
+        if after:
+            table(after, "After the timed loop (top-m pass, posting lists, k-means step where the workload has them):")
+        return
+    files = _find(root, "counter_collection.csv")
+    if not files:
+        sys.exit(f"no counter_collection.csv under {root}")
+    rows = [r for f in files for r in _read_csv(f)]
+    win = _window(rows)
+    per = {}
+    for r in rows:
+        per.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    scale = {}
+    if calib_mib and win is not None:
+        copies = [(d, c) for (d, k), c in per.items() if "copy" in k.lower() and d < win[0]]
+        if copies:
+            kib = calib_mib * 1024.0
+            c = max(copies)[1]
+            for name in ("FETCH_SIZE", "WRITE_SIZE"):
+                if c.get(name):
+                    scale[name] = kib / c[name]
+            print(f"Calibration copy of {calib_mib} MiB ({kib:.0f} KiB read and written): "
+                  + ", ".join(f"{n} reads {c[n]:.1f} KiB (factor {scale[n]:.4f})" for n in scale))
+    agg = {}
+    for (d, k), c in per.items():
+        if win is not None and not (win[0] < d < win[1]):
+            continue
+        a = agg.setdefault(k, {"n": 0})
+        a["n"] += 1
+        for n, v in c.items():
+            a[n] = a.get(n, 0.0) + v
+    names = sorted({n for a in agg.values() for n in a if n != "n"})
+    print("\n| kernel | dispatches | " + " | ".join(f"{n} (mean)" for n in names) + " |")
+    print("|---|---|" + "---|" * len(names))
+    for k, a in sorted(agg.items(), key=lambda kv: kv[0]):
+        print(f"| `{_short(k)}` | {a['n']} | " + " | ".join(f"{a.get(n, 0.0) / a['n']:.4g}" for n in names) + " |")
+    for n in scale:
+        tot = sum(a.get(n, 0.0) for a in agg.values())
+        print(f"\n{n}: {tot:.1f} KiB over the window, {tot * scale[n] * 1024:.4g} bytes scaled")
 
 
 def run_kde(args, torch, g, synth):
@@ -172,7 +302,8 @@ def run_kde(args, torch, g, synth):
         t0 = time.perf_counter()
         oracle.kde_score(Y[:q], X, h)
         t = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": q * M / t, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+        res["cpu_baseline"] = {"value": q * M / t, "unit": "pairs/s", "cores": 1, "cpu_model": cpu_model(),
+                               "kind": "oracle",
                                "sample": f"oracle.kde_score (numpy float64, direct differences) on the first {q} "
                                          f"queries against all {M} references, {t:.1f} s"}
     print(json.dumps(res), flush=True)
@@ -183,12 +314,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="diag_large",
+    ap.add_argument("--workload", default="ivf_bf16",
                     choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (traffic counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="summarise the rocprofv3 output under DIR (no GPU work)")
+    ap.add_argument("--counters", action="store_true", help="with --summarize: counter (--pmc) output")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.counters, args.calib_copy)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -230,34 +367,45 @@ def main():
     for a_, b_ in evs:  # materialise the event handles before handing them to the library
         a_.record(stream)
         b_.record(stream)
+    torch.cuda._sleep(1000)  # trace marker: the timed dispatches follow
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         g.gmm_fit_step(X, w, mu, cv, wl.cov, reg_covar=wl.eps, mean_loglik=mll, ws=ws, events=evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    torch.cuda._sleep(1000)  # trace marker: the timed dispatches ended
     step_s = (t1 - t0) / args.steps
     k_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
 
     pairs = wl.B * wl.N * wl.K
+    extra = {}
     if wl.xdtype == "bf16":
         alg, executed = largek_roofline(wl.D)
         flops = pairs * alg
         peak = PEAK_BF16_MFMA
-        kernel = "large-K E-step (prologue + passes A, B, C)"
-        peak_note = (f"bf16 MFMA dense peak; {alg} algorithmic flop/pair (2D logits + 2D statistics); "
-                     f"{executed} flop/pair executed (two-term weights, logits recomputed in pass C, "
-                     f"statistics in two magnitude classes)")
+        kernel = "large-K E-step (prologue + passes A, B, C over every row chunk)"
+        peak_note = (f"bf16 MFMA dense peak; {alg} algorithmic flop/pair (2D logits + 2D statistics + N_k and "
+                     f"|x|^2 terms)")
+        extra = {"executed_flops_per_launch": pairs * executed,
+                 "executed_frac": pairs * executed / (k_ms * 1e-3) / 1e12 / peak,
+                 "executed_note": (f"{executed} flop/pair executed: two-term weights, logits again in pass C, "
+                                   f"statistics in two magnitude classes")}
         dtype = "bf16"
     else:
         f32f, f64f = contraction_split(wl.cov, wl.D)
         flops = pairs * (f32f + f64f)
-        peak = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
+        peak = PEAK_FP32_MFMA
+        blend = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
         kernel = "fused E-step + statistics"
-        peak_note = (f"float32 MFMA logits ({f32f} flop/pair at {PEAK_FP32_MFMA} TF) + float64 MFMA "
-                     f"statistics ({f64f} flop/pair at {PEAK_FP64_MFMA} TF), time-weighted")
+        peak_note = (f"float32 MFMA dense peak; {f32f + f64f} algorithmic flop/pair (logits and statistics "
+                     f"contractions)")
+        extra = {"frac_vs_fp32_fp64_blend": flops / (k_ms * 1e-3) / 1e12 / blend,
+                 "blend_note": (f"secondary: the statistics half runs on the float64 MFMA; blended peak "
+                                f"{blend:.1f} TF for {f32f} float32 + {f64f} float64 flop/pair")}
         dtype = "f32"
     achieved = flops / (k_ms * 1e-3) / 1e12
+    tr = measured_traffic(wl.name, "gmm_largek.hip" if wl.xdtype == "bf16" else "gmm_estep.hip")
     res = {
         "metric": METRIC,
         "value": pairs / step_s,
@@ -280,12 +428,15 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": measured_traffic(wl.name, "gmm_largek.hip" if wl.xdtype == "bf16" else "gmm_estep.hip"),
-            "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic": tr,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_source": (f"profiles/estep_{wl.name}_traffic.md (taken with the current kernel source)"
+                               if tr is not None else "none for the current kernel source"),
             "kernel": kernel,
             "kernel_ms": k_ms,
             "flops_per_launch": flops,
             "peak_note": peak_note,
+            **extra,
         },
         "mean_loglik_last": float(mll.mean().item()),
     }
@@ -299,10 +450,12 @@ def main():
                           device=dev)
         g.gmm_predict_proba_topm(X, w, mu, cv, wl.cov, m, thr, idx, resp, cnt, ws=tws)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         g.gmm_predict_proba_topm(X, w, mu, cv, wl.cov, m, thr, idx, resp, cnt, ws=tws)
+        e1.record()
         torch.cuda.synchronize()
-        t_topm = time.perf_counter() - t0
+        t_topm = e0.elapsed_time(e1) * 1e-3
         res["topm"] = {"m": m, "threshold": thr, "ms": t_topm * 1e3, "rows_per_s": wl.B * wl.N / t_topm,
                        "mean_kept": float(cnt.float().mean().item())}
         # the IVF posting lists of that assignment (CSR per component), timed apart
@@ -311,7 +464,6 @@ def main():
         lresp = torch.empty((wl.B, wl.N * m), dtype=torch.float32, device=dev)
         lws = torch.empty(max(256, g.gmm_ivf_workspace_bytes(wl.B, wl.N, m, wl.K)), dtype=torch.uint8, device=dev)
         g.gmm_ivf_lists(idx, wl.K, resp=resp, offsets=off, rows=rows, list_resp=lresp, ws=lws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 5
         e0.record()
         for _ in range(reps):
