@@ -162,6 +162,21 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
                         double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* One EM iteration exactly as gmm_fit_step (same kernels, same results), for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace: its scratch is a static device array of 64 MiB per GPU, which
+ * the library holds from its first use on that GPU until the process ends.
+ * A problem whose workspace (gmm_workspace_bytes with GMM_OP_FIT) exceeds
+ * 64 MiB returns GMM_ERR_WORKSPACE before anything is enqueued (bf16 rows
+ * stream in shorter chunks when the part that does not grow with N fits).
+ * The array belongs to the current HIP device; every call on that device
+ * uses the same array, so calls that overlap in time on one GPU (other
+ * streams, other threads) race: serialise them.  Nothing in the array needs
+ * to start at zero.  No hipMalloc, hipFree or allocating library call. */
+gmm_status gmm_fit_step_noalloc(const gmm_data* data, gmm_params* inout, const gmm_options* opts,
+                                double* mean_loglik, int32_t* comp_status, void* stream);
+
 /* Soft multi-assignment (Flash-GMM Section 4 / Conclusion): for every row,
  * components ordered by decreasing responsibility (ties: lower index first);
  * the first is always kept, ranks 2..m are kept while r >= threshold.

@@ -8,6 +8,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_estep_stats(X, w, mu, cv, stats, accumulate=False, ws=None)
   gmm_mstep(stats, n_total, w, mu, cv, reg_covar=1e-6, comp_status=None)
   gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
+  gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None)
   gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
   gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
   gmm_kmeans_workspace_bytes(X, K)            -> int
@@ -145,6 +146,16 @@ def gmm_fit_step(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_statu
     ws = _workspace(X, p.K, cov, OP_FIT, 0, ws)
     _abi.check(_abi.lib().gmm_fit_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o), _ptr(mean_loglik),
                                        _ptr(comp_status), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None, stream=None):
+    """One EM iteration in place, with the library's static scratch array
+    instead of a workspace (nothing is allocated on the device)."""
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    o = GmmOptions(float(reg_covar), 0, None, None)
+    _abi.check(_abi.lib().gmm_fit_step_noalloc(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o),
+                                               _ptr(mean_loglik), _ptr(comp_status), _stream(stream)))
 
 
 def gmm_predict_proba_topm(X, w, mu, cv, cov, m, threshold, idx, resp, count=None, logp=None, ws=None,

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 namespace gmm {
@@ -250,9 +251,9 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   return GMM_OK;
 }
 
-static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
-  if (!ws) return fail(GMM_ERR_WORKSPACE, "workspace is NULL");
-  if (((uintptr_t)ws) % kAlign) return fail(GMM_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+// Whether ws_bytes of workspace hold the plan (the large-K path then streams
+// its rows in chunks that fit); host-only.
+static gmm_status fit_ws(Plan& p, size_t ws_bytes) {
   if (p.largek && ws_bytes < p.ws_bytes) {
     // a smaller workspace streams the rows in shorter chunks (multiples of 32 rows)
     Plan q = p;
@@ -274,8 +275,37 @@ static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
   return GMM_OK;
 }
 
+static gmm_status check_ws(Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(GMM_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws) % kAlign) return fail(GMM_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  return fit_ws(p, ws_bytes);
+}
+
 static gmm_status hip_fail(hipError_t e, const char* where) {
   return fail(GMM_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---- allocation-free fit step: its workspace is this file-scope device array
+// (one copy per GPU, alive until the process ends).  Host code never passes
+// the array's name to a kernel -- on the host that name is a stand-in, not a
+// device address -- but the address hipGetSymbolAddress returns for the
+// current device, fetched once per device.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
 }
 
 // prologue + fused E-step + reduction; statistics to the given buffers
@@ -503,20 +533,24 @@ gmm_status gmm_mstep(int64_t B, int64_t D, const gmm_stats* st_in, int64_t n_tot
   return GMM_OK;
 }
 
-gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_options* opts, double* mean_loglik,
-                        int32_t* comp_status, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+// Host validation of a fit step; fills the plan.
+static gmm_status fit_step_check(const gmm_data* data, const gmm_params* inout, const gmm_options* opts, Plan* p) {
   gmm_status st = check_params(inout, 0, 0, true);
   if (st != GMM_OK) return st;
-  Plan p;
-  st = make_plan(data, inout->K, inout->cov, GMM_OP_FIT, &p);
+  st = make_plan(data, inout->K, inout->cov, GMM_OP_FIT, p);
   if (st != GMM_OK) return st;
-  if (p.N < 1) return fail(GMM_ERR_INVALID_ARG, "a fit step needs N >= 1");
+  if (p->N < 1) return fail(GMM_ERR_INVALID_ARG, "a fit step needs N >= 1");
   if (opts && opts->flags) return fail(GMM_ERR_INVALID_ARG, "options.flags must be 0");
   const double reg = opts ? opts->reg_covar : 1e-6;
   if (!(reg >= 0.0)) return fail(GMM_ERR_INVALID_ARG, "reg_covar must be >= 0");
-  st = check_ws(p, ws, ws_bytes);
-  if (st != GMM_OK) return st;
+  return GMM_OK;
+}
+
+// The launches of one EM iteration on a checked plan and workspace.
+static gmm_status fit_step_run(const Plan& p, const gmm_data* data, gmm_params* inout, const gmm_options* opts,
+                               double* mean_loglik, int32_t* comp_status, void* ws, void* stream) {
+  gmm_status st;
+  const double reg = opts ? opts->reg_covar : 1e-6;
   char* w = static_cast<char*>(ws);
   double* nk = reinterpret_cast<double*>(w + p.off_nk);
   double* sx = reinterpret_cast<double*>(w + p.off_sx);
@@ -530,6 +564,33 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
                                       inout->covars, reg, flag, p.KP, comp_status, s);
   if (e != hipSuccess) return hip_fail(e, "M-step launch");
   return GMM_OK;
+}
+
+gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_options* opts, double* mean_loglik,
+                        int32_t* comp_status, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Plan p;
+  gmm_status st = fit_step_check(data, inout, opts, &p);
+  if (st != GMM_OK) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != GMM_OK) return st;
+  return fit_step_run(p, data, inout, opts, mean_loglik, comp_status, ws, stream);
+}
+
+gmm_status gmm_fit_step_noalloc(const gmm_data* data, gmm_params* inout, const gmm_options* opts,
+                                double* mean_loglik, int32_t* comp_status, void* stream) {
+  g_err.clear();
+  Plan p;
+  gmm_status st = fit_step_check(data, inout, opts, &p);
+  if (st != GMM_OK) return st;
+  if (fit_ws(p, kScratchBytes) != GMM_OK)
+    return fail(GMM_ERR_WORKSPACE,
+                "gmm_fit_step_noalloc: this problem needs %zu bytes of scratch, more than its static %zu-byte "
+                "array; use gmm_fit_step with a workspace",
+                p.ws_bytes, kScratchBytes);
+  void* ws = scratch_ptr();
+  if (!ws) return fail(GMM_ERR_HIP, "gmm_fit_step_noalloc: the device address of the static scratch array");
+  return fit_step_run(p, data, inout, opts, mean_loglik, comp_status, ws, stream);
 }
 
 gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m, float threshold,

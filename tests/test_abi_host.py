@@ -378,3 +378,16 @@ def test_kde_workspace_size_and_bad_arguments_before_the_device():
     # no query rows: accepted, nothing launched
     e = _data(0, 5)
     assert L.gmm_kde_score(ctypes.byref(e), p, 65, 5, 1.0, None, ws, n, None) == _abi.GMM_OK
+
+
+def test_noalloc_rejects_a_problem_above_its_static_scratch():
+    """1M rows x D = 64, K = 256 diagonal needs about 69 MB of workspace, more
+    than the 64 MiB static array: GMM_ERR_WORKSPACE before any device work
+    (the pointers are never touched)."""
+    L = _abi.lib()
+    d = _abi.GmmData(ctypes.c_void_p(4096), _abi.DT_F32, 1, 1_000_000, 64, 64, 0)
+    p = _abi.GmmParams(256, _abi.COV_DIAG, ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096))
+    assert L.gmm_workspace_bytes(ctypes.byref(d), 256, _abi.COV_DIAG, _abi.OP_FIT, 0) > (64 << 20)
+    st = L.gmm_fit_step_noalloc(ctypes.byref(d), ctypes.byref(p), None, None, None, None)
+    assert st == _abi.GMM_ERR_WORKSPACE
+    assert "static" in L.gmm_last_error().decode()
