@@ -177,6 +177,28 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
 gmm_status gmm_fit_step_noalloc(const gmm_data* data, gmm_params* inout, const gmm_options* opts,
                                 double* mean_loglik, int32_t* comp_status, void* stream);
 
+/* One EM iteration (as gmm_fit_step) over rows that stay in HOST memory
+ * (Flash-GMM Section 1: datasets beyond what fits; Section 3: the statistics
+ * are O(K D); GMMXX README, "CUDA backend (experimental)": large-N streaming
+ * of CPU-resident data through the E/M kernels).  host_data describes the
+ * rows exactly as gmm_data does, but host_data->x is a host pointer; for
+ * copies that overlap the compute it must be pinned (hipHostMalloc, or a
+ * torch tensor made with pin_memory=True), pageable memory works but its
+ * copies do not overlap.  The rows go through two device buffers of
+ * chunk_rows rows per problem in the workspace: chunk c is copied on
+ * copy_stream while the E-step of chunk c - 1 runs on stream (events order
+ * them; copy_stream NULL = everything on stream), each chunk's statistics
+ * are added to one float64 set, then one M-step updates `inout`.  Device
+ * memory: gmm_fit_step_streamed_workspace_bytes, which depends on K, D, B
+ * and chunk_rows but not on N.  mean_loglik / comp_status as gmm_fit_step.
+ * The results equal gmm_fit_step's up to the order of the float64 sums.
+ * The host rows must stay unchanged until the call's work on `stream` has
+ * completed. */
+size_t gmm_fit_step_streamed_workspace_bytes(const gmm_data* host_data, int32_t K, int32_t cov, int64_t chunk_rows);
+gmm_status gmm_fit_step_streamed(const gmm_data* host_data, gmm_params* inout, const gmm_options* opts,
+                                 int64_t chunk_rows, double* mean_loglik, int32_t* comp_status, void* ws,
+                                 size_t ws_bytes, void* stream, void* copy_stream);
+
 /* Soft multi-assignment (Flash-GMM Section 4 / Conclusion): for every row,
  * components ordered by decreasing responsibility (ties: lower index first);
  * the first is always kept, ranks 2..m are kept while r >= threshold.

@@ -9,6 +9,8 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_mstep(stats, n_total, w, mu, cv, reg_covar=1e-6, comp_status=None)
   gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
   gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None)
+  gmm_fit_step_streamed(X_host, w, mu, cv, cov, chunk_rows, reg_covar=1e-6, mean_loglik=None,
+                        comp_status=None, ws=None, copy_stream=None)   (rows stay in host memory)
   gmm_predict_proba_topm(X, w, mu, cv, m, threshold, idx, resp, count=None, logp=None, ws=None)
   gmm_ivf_lists(idx, K, resp=None, offsets=None, rows=None, list_resp=None, ws=None)
   gmm_kmeans_workspace_bytes(X, K)            -> int
@@ -156,6 +158,33 @@ def gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, co
     o = GmmOptions(float(reg_covar), 0, None, None)
     _abi.check(_abi.lib().gmm_fit_step_noalloc(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o),
                                                _ptr(mean_loglik), _ptr(comp_status), _stream(stream)))
+
+
+def gmm_fit_step_streamed_workspace_bytes(X_host, K, cov, chunk_rows) -> int:
+    d = _data(X_host)
+    return int(_abi.lib().gmm_fit_step_streamed_workspace_bytes(ctypes.byref(d), int(K), _cov_code(cov),
+                                                                int(chunk_rows)))
+
+
+def gmm_fit_step_streamed(X_host, w, mu, cv, cov, chunk_rows, reg_covar=1e-6, mean_loglik=None, comp_status=None,
+                          ws=None, stream=None, copy_stream=None):
+    """One EM iteration in place over rows in host memory (X_host: a CPU
+    tensor, pinned for overlapped copies), streamed through two device chunk
+    buffers of chunk_rows rows; copy_stream: a torch.cuda.Stream for the
+    copies (None: the compute stream)."""
+    torch = _torch()
+    if X_host.is_cuda:
+        raise ValueError("gmm_fit_step_streamed takes rows in host memory")
+    d = _data(X_host)
+    p = _params(w, mu, cv, cov)
+    o = GmmOptions(float(reg_covar), 0, None, None)
+    if ws is None:
+        n = gmm_fit_step_streamed_workspace_bytes(X_host, p.K, cov, chunk_rows)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=w.device)
+    cs = None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    _abi.check(_abi.lib().gmm_fit_step_streamed(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o), int(chunk_rows),
+                                                _ptr(mean_loglik), _ptr(comp_status), _ptr(ws), ws.numel(),
+                                                _stream(stream), cs))
 
 
 def gmm_predict_proba_topm(X, w, mu, cv, cov, m, threshold, idx, resp, count=None, logp=None, ws=None,

@@ -20,6 +20,7 @@ OP_FIT, OP_ESTEP, OP_TOPM = 0, 1, 2
 GMM_OK, GMM_ERR_INVALID_ARG, GMM_ERR_UNSUPPORTED, GMM_ERR_WORKSPACE, GMM_ERR_HIP, GMM_ERR_NOT_PD = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step", "gmm_fit_step_noalloc",
+            "gmm_fit_step_streamed_workspace_bytes", "gmm_fit_step_streamed",
             "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
             "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector",
             "gmm_topk_fit_workspace_bytes", "gmm_topk_fit_step", "gmm_kde_workspace_bytes", "gmm_kde_score",
@@ -77,6 +78,12 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(GmmOptions), P, P, P, ctypes.c_size_t, P]
         L.gmm_fit_step_noalloc.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams),
                                            ctypes.POINTER(GmmOptions), P, P, P]
+        L.gmm_fit_step_streamed_workspace_bytes.argtypes = [ctypes.POINTER(GmmData), ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int64]
+        L.gmm_fit_step_streamed_workspace_bytes.restype = ctypes.c_size_t
+        L.gmm_fit_step_streamed.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams),
+                                            ctypes.POINTER(GmmOptions), ctypes.c_int64, P, P, P, ctypes.c_size_t,
+                                            P, P]
         L.gmm_predict_proba_topm.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams),
                                              ctypes.c_int32, ctypes.c_float, P, P, P, P, P,
                                              ctypes.c_size_t, P]
@@ -100,7 +107,8 @@ def lib() -> ctypes.CDLL:
         L.gmm_topk_fit_workspace_bytes.restype = ctypes.c_size_t
         L.gmm_topk_fit_step.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams), ctypes.c_int32,
                                         ctypes.POINTER(GmmOptions), P, P, P, ctypes.c_size_t, P]
-        for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_fit_step_noalloc, L.gmm_predict_proba_topm,
+        for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_fit_step_noalloc, L.gmm_fit_step_streamed,
+                  L.gmm_predict_proba_topm,
                   L.gmm_ivf_lists,
                   L.gmm_kmeans_step, L.gmm_fisher_vector, L.gmm_topk_fit_step, L.gmm_kde_score):
             f.restype = ctypes.c_int

@@ -593,6 +593,150 @@ gmm_status gmm_fit_step_noalloc(const gmm_data* data, gmm_params* inout, const g
   return fit_step_run(p, data, inout, opts, mean_loglik, comp_status, ws, stream);
 }
 
+// ---- rows in host memory streamed through two device chunk buffers: the
+// fused E-step of every chunk adds into one set of statistics, then one
+// M-step (Flash-GMM Section 3: the statistics are O(K D); the rows never need
+// to be resident at once)
+struct StreamLayout {
+  Plan p;                 // plan of a full chunk (its workspace is at offset 0)
+  int64_t C = 0;          // rows per chunk
+  size_t esize = 0;       // bytes per element
+  size_t buf_bytes = 0;   // one device chunk buffer: B * C * ld_x elements
+  size_t off_buf[2] = {0, 0}, off_nk = 0, off_sx = 0, off_sxx = 0, off_ll = 0, bytes = 0;
+};
+
+static gmm_data chunk_view(const gmm_data* hd, const StreamLayout& L, const void* dev_x, int64_t rows) {
+  gmm_data cd = *hd;
+  cd.x = dev_x;
+  cd.N = rows;
+  cd.stride_b = L.C * hd->ld_x;
+  return cd;
+}
+
+static gmm_status stream_plan(const gmm_data* hd, int32_t K, int32_t cov, int64_t chunk_rows, StreamLayout* L) {
+  gmm_status st = check_data(hd);
+  if (st != GMM_OK) return st;
+  if (chunk_rows < 1) return fail(GMM_ERR_INVALID_ARG, "chunk_rows must be >= 1");
+  if (hd->N < 1) return fail(GMM_ERR_INVALID_ARG, "a fit step needs N >= 1");
+  L->C = std::min<int64_t>(chunk_rows, hd->N);
+  L->esize = hd->dtype == GMM_DT_F32 ? 4 : 2;
+  // the chunk buffers are 256-byte aligned, so the chunk plan sees aligned rows
+  const gmm_data cd = chunk_view(hd, *L, reinterpret_cast<const void*>(kAlign), L->C);
+  st = make_plan(&cd, K, cov, GMM_OP_FIT, &L->p);
+  if (st != GMM_OK) return st;
+  size_t o = align_up(L->p.ws_bytes);
+  const size_t B = (size_t)hd->B;
+  L->buf_bytes = B * (size_t)L->C * (size_t)hd->ld_x * L->esize;
+  L->off_buf[0] = o; o = align_up(o + L->buf_bytes);
+  L->off_buf[1] = o; o = align_up(o + L->buf_bytes);
+  L->off_nk = o;     o = align_up(o + sizeof(double) * B * K);
+  L->off_sx = o;     o = align_up(o + sizeof(double) * B * K * (size_t)hd->D);
+  L->off_sxx = o;    o = align_up(o + sizeof(double) * B * (size_t)cov_len(cov, hd->D, K));
+  L->off_ll = o;     o = align_up(o + sizeof(double) * B);
+  L->bytes = o;
+  return GMM_OK;
+}
+
+size_t gmm_fit_step_streamed_workspace_bytes(const gmm_data* host_data, int32_t K, int32_t cov, int64_t chunk_rows) {
+  StreamLayout L;
+  if (stream_plan(host_data, K, cov, chunk_rows, &L) != GMM_OK) return 0;
+  return L.bytes;
+}
+
+gmm_status gmm_fit_step_streamed(const gmm_data* host_data, gmm_params* inout, const gmm_options* opts,
+                                 int64_t chunk_rows, double* mean_loglik, int32_t* comp_status, void* ws,
+                                 size_t ws_bytes, void* stream, void* copy_stream) {
+  g_err.clear();
+  gmm_status st = check_params(inout, 0, 0, true);
+  if (st != GMM_OK) return st;
+  StreamLayout L;
+  st = stream_plan(host_data, inout->K, inout->cov, chunk_rows, &L);
+  if (st != GMM_OK) return st;
+  if (opts && opts->flags) return fail(GMM_ERR_INVALID_ARG, "options.flags must be 0");
+  const double reg = opts ? opts->reg_covar : 1e-6;
+  if (!(reg >= 0.0)) return fail(GMM_ERR_INVALID_ARG, "reg_covar must be >= 0");
+  if (!ws) return fail(GMM_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws) % kAlign) return fail(GMM_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < L.bytes) return fail(GMM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.bytes);
+  const int64_t N = host_data->N, B = host_data->B, C = L.C;
+  const int64_t nchunks = (N + C - 1) / C;
+  // every chunk plan fits the full chunk's workspace (it has fewer rows)
+  Plan cp[2];
+  for (int i = 0; i < 2; ++i) {
+    const int64_t rows = i == 0 ? C : N - (nchunks - 1) * C;
+    const gmm_data cd = chunk_view(host_data, L, reinterpret_cast<const void*>(kAlign), rows);
+    st = make_plan(&cd, inout->K, inout->cov, GMM_OP_FIT, &cp[i]);
+    if (st != GMM_OK) return st;
+    st = fit_ws(cp[i], L.p.ws_bytes);
+    if (st != GMM_OK) return st;
+  }
+  char* w = static_cast<char*>(ws);
+  double* nk = reinterpret_cast<double*>(w + L.off_nk);
+  double* sx = reinterpret_cast<double*>(w + L.off_sx);
+  double* sxx = reinterpret_cast<double*>(w + L.off_sxx);
+  double* ll = reinterpret_cast<double*>(w + L.off_ll);
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : s;
+  // start: the copies wait for what the compute stream already holds (an
+  // earlier call may still read the buffers); copied[i]: buffer i is filled;
+  // freed[i]: the E-step that read buffer i is done
+  hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  auto cleanup = [&]() {
+    for (hipEvent_t ev : {start, copied[0], copied[1], freed[0], freed[1]})
+      if (ev) (void)hipEventDestroy(ev);
+  };
+  for (hipEvent_t* ev : {&start, &copied[0], &copied[1], &freed[0], &freed[1]}) {
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "event create");
+    }
+  }
+  const unsigned char* hx = static_cast<const unsigned char*>(host_data->x);
+  const size_t es = L.esize, ld = (size_t)host_data->ld_x;
+  const size_t spitch = (B > 1 ? (size_t)host_data->stride_b : 0) * es;
+  if ((e = hipEventRecord(start, s)) != hipSuccess || (e = hipStreamWaitEvent(cs, start, 0)) != hipSuccess) {
+    cleanup();
+    return hip_fail(e, "stream ordering");
+  }
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int bi = (int)(c & 1);
+    const int64_t r0 = c * C, rows = std::min<int64_t>(C, N - r0);
+    void* buf = w + L.off_buf[bi];
+    if (c >= 2 && (e = hipStreamWaitEvent(cs, freed[bi], 0)) != hipSuccess) break;
+    // rows r0 .. r0 + rows - 1 of every problem (the last row up to its D-th element)
+    const size_t width = ((size_t)(rows - 1) * ld + (size_t)host_data->D) * es;
+    const size_t dpitch = (size_t)C * ld * es;
+    e = hipMemcpy2DAsync(buf, dpitch, hx + (size_t)r0 * ld * es, B > 1 ? spitch : width, width, (size_t)B,
+                         hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) break;
+    if ((e = hipEventRecord(copied[bi], cs)) != hipSuccess || (e = hipStreamWaitEvent(s, copied[bi], 0)) != hipSuccess)
+      break;
+    const gmm_data cd = chunk_view(host_data, L, buf, rows);
+    st = run_estep(c + 1 < nchunks || nchunks == 1 ? cp[0] : cp[1], &cd, inout, ws, nk, sx, sxx, ll, nullptr,
+                   c > 0 ? 1 : 0, nullptr, s);
+    if (st != GMM_OK) {
+      cleanup();
+      return st;
+    }
+    if ((e = hipEventRecord(freed[bi], s)) != hipSuccess) break;
+  }
+  if (e != hipSuccess) {
+    cleanup();
+    return hip_fail(e, "streamed chunk");
+  }
+  if (mean_loglik && (e = launch_mean_ll(B, ll, N, mean_loglik, s)) != hipSuccess) {
+    cleanup();
+    return hip_fail(e, "mean log-likelihood launch");
+  }
+  const int32_t* flag = L.p.largek ? nullptr : reinterpret_cast<const int32_t*>(w + L.p.off_flag);
+  e = launch_mstep_strided(L.p.cov, B, host_data->D, inout->K, nk, sx, sxx, N, inout->weights, inout->means,
+                           inout->covars, reg, flag, L.p.KP, comp_status, s);
+  cleanup();
+  if (e != hipSuccess) return hip_fail(e, "M-step launch");
+  return GMM_OK;
+}
+
 gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
                                   int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, size_t ws_bytes,
                                   void* stream) {

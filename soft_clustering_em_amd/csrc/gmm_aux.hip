@@ -279,6 +279,18 @@ hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const
   return hipGetLastError();
 }
 
+// mean log-likelihood of B problems over n_total rows (the streamed fit step,
+// whose per-chunk reductions add into ll)
+__global__ void mean_ll_kernel(int64_t B, const double* __restrict__ ll, int64_t n_total, double* __restrict__ mean_ll) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) mean_ll[b] = ll[b] / (double)n_total;
+}
+
+hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* mean_ll, hipStream_t s) {
+  hipLaunchKernelGGL(mean_ll_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, B, ll, n_total, mean_ll);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ reduce
 // grid: B*K + B blocks.  Block (b, k) sums the Gb partials of component k in
 // workgroup order (float64) into raw[b][k][:], and (non-tied) writes the

@@ -251,6 +251,7 @@ bool estep_variant_exists(int cov, int dp, int kw, int t);
 hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float2* err, float* W,
                            double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
                            hipStream_t s);
+hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* mean_ll, hipStream_t s);
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s);

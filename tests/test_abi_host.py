@@ -391,3 +391,21 @@ def test_noalloc_rejects_a_problem_above_its_static_scratch():
     st = L.gmm_fit_step_noalloc(ctypes.byref(d), ctypes.byref(p), None, None, None, None)
     assert st == _abi.GMM_ERR_WORKSPACE
     assert "static" in L.gmm_last_error().decode()
+
+
+def test_streamed_workspace_depends_on_the_chunk_not_on_n():
+    """gmm_fit_step_streamed keeps two chunk buffers and one chunk's scratch:
+    its workspace is the same for 10^5 and 10^9 host rows, and grows with the
+    chunk size."""
+    L = _abi.lib()
+
+    def ws(N, C, dtype=_abi.DT_F32, K=256, cov=_abi.COV_DIAG):
+        d = _abi.GmmData(ctypes.c_void_p(4096), dtype, 1, N, 128 if dtype == _abi.DT_BF16 else 64,
+                         128 if dtype == _abi.DT_BF16 else 64, 0)
+        return L.gmm_fit_step_streamed_workspace_bytes(ctypes.byref(d), K, cov, C)
+
+    assert ws(10**5, 1 << 16) == ws(10**9, 1 << 16) > 0
+    assert ws(10**9, 1 << 17) > ws(10**9, 1 << 16)
+    assert ws(10**5, 1 << 16, _abi.DT_BF16, 4096, _abi.COV_SPHERICAL) == ws(10**9, 1 << 16, _abi.DT_BF16, 4096,
+                                                                            _abi.COV_SPHERICAL) > 0
+    assert ws(10**9, 0) == 0  # chunk_rows must be >= 1

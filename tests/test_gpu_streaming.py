@@ -1,0 +1,123 @@
+"""The streamed fit step (rows held in pinned host memory, copied chunk by
+chunk into two device buffers on a copy stream while the E-step of the
+previous chunk runs; Flash-GMM Sections 1 and 3, GMMXX README "CUDA backend
+(experimental)", large-N streaming) against the single-call fit step on
+device-resident rows and against the float64 oracle, one step from identical
+float32 parameters.  The two GPU paths differ only in the order of float64
+sums, so they agree far below the float32 bar."""
+import numpy as np
+import pytest
+
+import oracle
+from parity import TOL_F32, TOL_LOWP, param_errors, to_np
+from soft_clustering_em_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import soft_clustering_em_amd._abi as abi
+    abi.lib()
+    return torch
+
+
+def run_both(torch, Xh, th, cov, chunk):
+    """Streamed step on the pinned host rows Xh and single-call step on a
+    device copy, from the same parameters."""
+    import soft_clustering_em_amd as g
+    B = th[0].shape[0]
+    out = []
+    for streamed in (True, False):
+        w, mu, cv = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in th)
+        mll = torch.zeros(B, dtype=torch.float64, device="cuda")
+        cs = torch.full(w.shape, -1, dtype=torch.int32, device="cuda")
+        if streamed:
+            copy = torch.cuda.Stream()
+            g.gmm_fit_step_streamed(Xh, w, mu, cv, cov, chunk, mean_loglik=mll, comp_status=cs, copy_stream=copy)
+        else:
+            g.gmm_fit_step(Xh.cuda(), w, mu, cv, cov, mean_loglik=mll, comp_status=cs)
+        torch.cuda.synchronize()
+        out.append(((to_np(w), to_np(mu), to_np(cv)), to_np(mll), cs.cpu().numpy()))
+    return out
+
+
+def pinned(torch, a):
+    t = torch.empty(a.shape, dtype={np.float32: torch.float32, np.uint16: torch.int16}[a.dtype.type], pin_memory=True)
+    t.numpy()[...] = a.view(np.int16) if a.dtype == np.uint16 else a
+    return t if a.dtype != np.uint16 else t.view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("cov,B,N,D,K,chunk", [("diag", 1, 100_003, 64, 64, 16384),
+                                               ("spherical", 3, 20_001, 16, 24, 5000),
+                                               ("full", 1, 50_000, 16, 8, 7777),
+                                               ("tied", 2, 30_000, 8, 6, 4096),
+                                               ("diag", 2, 9_000, 32, 40, 20_000)])
+def test_streamed_step_equals_single_call_and_oracle(torch_cuda, cov, B, N, D, K, chunk):
+    torch = torch_cuda
+    rng = np.random.default_rng(N + K)
+    centers = 4.0 * rng.standard_normal((B, K, D))
+    lab = rng.integers(0, K, (B, N))
+    X = (np.take_along_axis(centers, lab[..., None], 1) + rng.standard_normal((B, N, D))).astype(np.float32)
+    w = np.full((B, K), 1.0 / K, np.float32)
+    mu = np.ascontiguousarray(X[:, :K])
+    cv = {"spherical": np.ones((B, K), np.float32), "diag": np.ones((B, K, D), np.float32),
+          "full": np.broadcast_to(np.eye(D, dtype=np.float32), (B, K, D, D)).copy(),
+          "tied": np.broadcast_to(np.eye(D, dtype=np.float32), (B, D, D)).copy()}[cov]
+    (got, ll, cs), (ref, ll_ref, cs_ref) = run_both(torch, pinned(torch, X), (w, mu, cv), cov, chunk)
+    e = param_errors(cov, B, K, D, got, ref, np.full((B, K), 10.0))
+    e_ll = float(np.max(np.abs(ll - ll_ref) / np.abs(ll_ref)))
+    print(f"{cov} B={B} N={N} chunk={chunk}: vs single call mu={e['mu']:.1e} cv={e['cv']:.1e} w={e['w']:.1e} "
+          f"ll={e_ll:.1e}", flush=True)
+    assert max(e["mu"], e["cv"], e["w"], e_ll) <= 1e-6
+    assert np.array_equal(cs, cs_ref)
+    for b in range(B):
+        o = oracle.fit_step(cov, X[b], w[b].astype(np.float64), mu[b].astype(np.float64), cv[b].astype(np.float64))
+        eo = param_errors(cov, 1, K, D, tuple(a[b] for a in got), (o["w"], o["mu"], o["cv"]), o["stats"]["nk"])
+        assert max(eo["mu"], eo["cv"], eo["w"]) <= TOL_F32, (b, eo)
+        assert abs(ll[b] - o["mean_ll"][0]) <= TOL_F32 * abs(o["mean_ll"][0])
+
+
+def test_streamed_bf16_rows_large_k(torch_cuda):
+    """bf16 rows, K = 512 (the large-K path inside every chunk)."""
+    torch = torch_cuda
+    wl = synth.ivf_bf16(N=50_000, K=512)
+    Xh = pinned(torch, wl.X)
+    (got, ll, _), (ref, ll_ref, _) = run_both(torch, Xh, (wl.w0, wl.mu0, wl.cv0), "spherical", 16384)
+    e = param_errors("spherical", 1, wl.K, wl.D, got, ref, np.full((1, wl.K), 10.0))
+    e_ll = abs(ll[0] - ll_ref[0]) / abs(ll_ref[0])
+    print(f"bf16 N=50000 K=512: vs single call mu={e['mu']:.1e} cv={e['cv']:.1e} w={e['w']:.1e} ll={e_ll:.1e}")
+    assert max(e["mu"], e["cv"], e["w"], e_ll) <= 1e-5
+    o = oracle.fit_step("spherical", wl.oracle_x(), *(a[0].astype(np.float64) for a in (wl.w0, wl.mu0, wl.cv0)))
+    eo = param_errors("spherical", 1, wl.K, wl.D, got, (o["w"], o["mu"], o["cv"]), o["stats"]["nk"])
+    assert max(eo["mu"], eo["cv"], eo["w"]) <= TOL_LOWP, eo
+
+
+def test_streamed_device_memory_does_not_grow_with_n(torch_cuda):
+    """The step allocates nothing itself; the caller's workspace is the same
+    for 40,000 and 400,000 rows at one chunk size, and torch sees no other
+    device allocation during the call."""
+    import soft_clustering_em_amd as g
+    torch = torch_cuda
+    rng = np.random.default_rng(9)
+    D, K, C = 32, 16, 8192
+    sizes = []
+    for N in (40_000, 400_000):
+        X = pinned(torch, rng.standard_normal((N, D)).astype(np.float32))
+        w = torch.full((1, K), 1.0 / K, device="cuda")
+        mu = torch.from_numpy(X.numpy()[:K].copy()).cuda()[None]
+        cv = torch.ones((1, K, D), device="cuda")
+        n = g.gmm_fit_step_streamed_workspace_bytes(X, K, "diag", C)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        g.gmm_fit_step_streamed(X, w, mu, cv, "diag", C, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.cuda.max_memory_allocated() == before
+        assert torch.isfinite(mu).all()
+        sizes.append(n)
+    assert sizes[0] == sizes[1]
+    assert sizes[0] < 400_000 * D * 4
