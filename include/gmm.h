@@ -58,10 +58,15 @@ typedef enum {
   GMM_COV_FULL = 3       /* one full Sigma_k per component; (B,K,D,D)      */
 } gmm_cov_type;
 
+/* Row types.  16-bit rows are read exactly (every bf16 and half value is a
+ * float32 value).  bf16 rows of one problem with spherical components take
+ * the large-K path (bf16 MFMA, any K <= 16384, D <= 128); every other 16-bit
+ * case takes the fused path of float32 rows (its K and D window), the rows
+ * decoded to float32 as a tile is staged in LDS. */
 typedef enum {
   GMM_DT_F32 = 0,  /* IEEE float32 rows                                     */
-  GMM_DT_BF16 = 1, /* bfloat16 rows (arithmetic accumulates in float32)     */
-  GMM_DT_F16 = 2   /* IEEE half rows  (arithmetic accumulates in float32)   */
+  GMM_DT_BF16 = 1, /* bfloat16 rows                                         */
+  GMM_DT_F16 = 2   /* IEEE half rows                                        */
 } gmm_dtype;
 
 typedef enum {

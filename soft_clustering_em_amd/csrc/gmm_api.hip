@@ -51,7 +51,6 @@ static gmm_status check_data(const gmm_data* d) {
   if (d->N > 0 && !d->x) return fail(GMM_ERR_INVALID_ARG, "x is NULL");
   if (d->dtype != GMM_DT_F32 && d->dtype != GMM_DT_BF16 && d->dtype != GMM_DT_F16)
     return fail(GMM_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
-  if (d->dtype == GMM_DT_F16) return fail(GMM_ERR_UNSUPPORTED, "float16 rows are not supported");
   if (d->N > ((int64_t)1 << 40)) return fail(GMM_ERR_UNSUPPORTED, "N too large");
   return GMM_OK;
 }
@@ -119,10 +118,10 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.K = K;
   q.ld_x = d->ld_x;
   q.stride_b = d->B > 1 ? d->stride_b : 0;
-  if (d->dtype == GMM_DT_BF16) {
-    // bf16 rows: spherical components through the slice-parallel three-pass E-step
-    if (cov != SPH) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows are supported for spherical components only");
-    if (d->B != 1) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: one problem per call (B = 1)");
+  if (d->dtype == GMM_DT_BF16 && cov == SPH && d->B == 1) {
+    // bf16 rows of one problem with spherical components: the slice-parallel
+    // three-pass E-step (any K; x is exact in the bf16 MFMA operand).  Other
+    // 16-bit cases take the fused path below, the rows decoded to float32.
     if (d->D > 128) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: D <= 128");
     if (K > kLargeKMaxK) return fail(GMM_ERR_UNSUPPORTED, "bf16 rows: K <= %d", kLargeKMaxK);
     q.largek = true;
@@ -163,8 +162,8 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
   q.G = feat_G(cov, q.DP);
   q.FS = feat_stride(std::max(q.F, q.G));
   q.PR = 2 + q.G;
-  const bool direct_ok =
-      (((uintptr_t)d->x) % 16 == 0) && (q.ld_x == q.D) && (q.D % 4 == 0) && (q.stride_b % 4 == 0);
+  const bool direct_ok = d->dtype == GMM_DT_F32 && (((uintptr_t)d->x) % 16 == 0) && (q.ld_x == q.D) &&
+                         (q.D % 4 == 0) && (q.stride_b % 4 == 0);
   auto lds_for = [&](int T, int nraw) {
     // weights, feature tile, raw row tile(s), |x|^2 (float64), per-wave (max, sum), product table
     return sizeof(float) * ((size_t)q.KP * q.F + (size_t)T * q.FS + (size_t)nraw * T * q.DP + 2 * (size_t)T +
@@ -384,6 +383,7 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   EStepArgs A;
   A.x = d->x;
+  A.xtype = p.dtype;
   A.N = p.N;
   A.D = p.D;
   A.ld_x = p.ld_x;
@@ -452,6 +452,7 @@ static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   TopmArgs A;
   A.x = data->x;
+  A.xtype = p.dtype;
   A.N = p.N;
   A.D = p.D;
   A.ld_x = p.ld_x;
@@ -883,7 +884,7 @@ gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, in
   A.lresp = nullptr;
   e = launch_ivf_lists(A, s);
   if (e != hipSuccess) return hip_fail(e, "k-means list launch");
-  e = launch_kmeans_update(data->x, data->dtype == GMM_DT_BF16 ? 1 : 0, p.B, p.N, p.ld_x, p.stride_b, K, (int)p.D,
+  e = launch_kmeans_update(data->x, data->dtype, p.B, p.N, p.ld_x, p.stride_b, K, (int)p.D,
                            A.offsets, A.rows, centroids, counts, reinterpret_cast<double*>(w + L.off_ip), inertia, s);
   if (e != hipSuccess) return hip_fail(e, "k-means update launch");
   return GMM_OK;
@@ -1052,7 +1053,7 @@ gmm_status gmm_topk_fit_step(const gmm_data* data, gmm_params* inout, int32_t to
   double* sxx = reinterpret_cast<double*>(w + L.off_sxx);
   TopkStepArgs T;
   T.x = data->x;
-  T.bf16 = data->dtype == GMM_DT_BF16 ? 1 : 0;
+  T.xtype = data->dtype;
   T.B = p.B;
   T.N = p.N;
   T.ld_x = p.ld_x;

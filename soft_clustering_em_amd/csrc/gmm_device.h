@@ -13,6 +13,15 @@ namespace gmm {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
+// Element idx of rows stored as xtype (a gmm_dtype: 0 float32, 1 bfloat16,
+// 2 IEEE half), decoded exactly to float32.
+__device__ __forceinline__ float x_value(const void* x, int xtype, int64_t idx) {
+  if (xtype == 0) return reinterpret_cast<const float*>(x)[idx];
+  const unsigned short h = reinterpret_cast<const unsigned short*>(x)[idx];
+  if (xtype == 1) return __uint_as_float((unsigned)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // 16-lane all-reduce with DPP (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
 // row_mirror); every lane of a 16-lane row ends with the same value.
 template <int CTRL>

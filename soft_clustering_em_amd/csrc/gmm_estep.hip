@@ -150,12 +150,14 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
             (__attribute__((address_space(3))) void*)(rawbuf + c0 * 4), 16, 0, 0);
     }
   };
+  // element-wise staging (any row stride, any row type: 16-bit rows decoded
+  // exactly to float32 here)
   auto load_tile_sync = [&](int64_t tile, float* rawbuf) {
     const int64_t row0 = tile * T;
     for (int j = threadIdx.x; j < T * DP; j += nthr) {
       const int r = j / DP, d = j % DP;
       const int64_t row = row0 + r;
-      rawbuf[j] = (row < N && d < D) ? xb[row * A.ld_x + d] : 0.f;
+      rawbuf[j] = (row < N && d < D) ? x_value(A.x, A.xtype, (int64_t)b * A.stride_b + row * A.ld_x + d) : 0.f;
     }
   };
 

@@ -63,6 +63,7 @@ struct Plan {
 
 struct EStepArgs {
   const void* x;
+  int xtype;           // gmm_dtype of the rows (16-bit rows are staged element-wise, decoded to float32)
   int64_t N, D, ld_x, stride_b;
   int K, KP, NW, Gb;
   int64_t ntiles;
@@ -140,6 +141,7 @@ constexpr int kTopmMaxK = 256;
 
 struct TopmArgs {
   const void* x;
+  int xtype;           // gmm_dtype of the rows
   int64_t N, D, ld_x, stride_b;
   int K, KP, NW, Gb;
   int64_t ntiles;
@@ -183,8 +185,8 @@ hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* 
 // approximate top-k EM statistics (gmm_topk.hip)
 // approximate top-k EM statistics (gmm_topk.hip)
 struct TopkStepArgs {
-  const void* x;              // rows, float32 or bf16 bits
-  int bf16;
+  const void* x;              // rows, float32, bf16 or half bits
+  int xtype;                  // gmm_dtype of the rows
   int64_t B, N, ld_x, stride_b;
   int K, D, m, cov, S;        // S: contiguous parts each component's list is split into
   const float* resp;          // (B, N, m) kept responsibilities (normalised over the kept set), best first
@@ -239,7 +241,7 @@ hipError_t launch_fisher_replicate(int64_t B, int K, int D, const float* w, cons
 hipError_t launch_fisher(int64_t B, int K, int D, int64_t N, uint32_t flags, const float* w, const float* mu,
                          const float* var, const double* nk, const double* sx, const double* sxx, float* fv,
                          hipStream_t s);
-hipError_t launch_kmeans_update(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
+hipError_t launch_kmeans_update(const void* x, int xtype, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
                                 int D, const int64_t* offsets, const int32_t* rows, float* C, int64_t* counts,
                                 double* ip, double* inertia, hipStream_t s);
 

@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) kmeans_params_kernel(int K, int D, const 
 
 struct UpdateArgs {
   const void* x;
-  int bf16;
+  int xtype;                 // gmm_dtype of the rows
   int64_t N, ld_x, stride_b;
   int K, D, L;               // L: lanes per row (a power of two >= D, <= 256)
   const int64_t* offsets;    // (B, K+1)
@@ -78,9 +78,9 @@ struct UpdateArgs {
 };
 
 __device__ __forceinline__ double load_x(const UpdateArgs& A, const char* xb, int64_t r, int d) {
-  if (A.bf16) {
+  if (A.xtype != 0) {
     const unsigned short h = reinterpret_cast<const unsigned short*>(xb)[r * A.ld_x + d];
-    return (double)__uint_as_float((unsigned)h << 16);
+    return A.xtype == 1 ? (double)__uint_as_float((unsigned)h << 16) : (double)__builtin_bit_cast(_Float16, h);
   }
   return (double)reinterpret_cast<const float*>(xb)[r * A.ld_x + d];
 }
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(256) kmeans_update_kernel(UpdateArgs A) {
   const bool on = d < A.D;
   const int64_t o0 = A.offsets[(size_t)b * (A.K + 1) + k], o1 = A.offsets[(size_t)b * (A.K + 1) + k + 1];
   const int32_t* rb = A.rows + (size_t)b * A.N;
-  const char* xb = static_cast<const char*>(A.x) + (size_t)b * A.stride_b * (A.bf16 ? 2 : 4);
+  const char* xb = static_cast<const char*>(A.x) + (size_t)b * A.stride_b * (A.xtype != 0 ? 2 : 4);
   float* cb = A.C + ((size_t)b * A.K + k) * A.D;
   const double c = on ? (double)cb[d] : 0.0;
   double s = 0.0, q = 0.0;
@@ -157,12 +157,12 @@ hipError_t launch_kmeans_params(int64_t B, int K, int D, const float* C, float* 
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_update(const void* x, int bf16, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
+hipError_t launch_kmeans_update(const void* x, int xtype, int64_t B, int64_t N, int64_t ld_x, int64_t stride_b, int K,
                                 int D, const int64_t* offsets, const int32_t* rows, float* C, int64_t* counts,
                                 double* ip, double* inertia, hipStream_t s) {
   UpdateArgs A;
   A.x = x;
-  A.bf16 = bf16;
+  A.xtype = xtype;
   A.N = N;
   A.ld_x = ld_x;
   A.stride_b = stride_b;

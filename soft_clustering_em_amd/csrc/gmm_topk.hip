@@ -61,9 +61,9 @@ __global__ void __launch_bounds__(kRowsPerBlock) topk_rows_kernel(TopkStepArgs A
 }
 
 __device__ __forceinline__ double topk_load_x(const TopkStepArgs& A, const char* xb, int64_t r, int d) {
-  if (A.bf16) {
+  if (A.xtype != 0) {
     const unsigned short h = reinterpret_cast<const unsigned short*>(xb)[r * A.ld_x + d];
-    return (double)__uint_as_float((unsigned)h << 16);
+    return A.xtype == 1 ? (double)__uint_as_float((unsigned)h << 16) : (double)__builtin_bit_cast(_Float16, h);
   }
   return (double)reinterpret_cast<const float*>(xb)[r * A.ld_x + d];
 }
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) topk_stats_kernel(TopkStepArgs A, int L) 
   const int32_t* rb = A.rows + b * nm;
   const float* lr = A.lresp + b * nm;
   const double* ri = A.rinv + b * A.N;
-  const char* xb = static_cast<const char*>(A.x) + b * A.stride_b * (A.bf16 ? 2 : 4);
+  const char* xb = static_cast<const char*>(A.x) + b * A.stride_b * (A.xtype != 0 ? 2 : 4);
   const double c = on ? (double)A.mu[(b * A.K + k) * A.D + d] : 0.0;
   double a1 = 0.0, a2 = 0.0, aw = 0.0;
   for (int64_t e = p0 + g; e < p1; e += (int64_t)U * G) {

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
     ex[nt] = e.x;
     ey[nt] = e.y;
   }
-  const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)b * A.stride_b;
+  const int64_t xoff = (int64_t)b * A.stride_b;  // first element of problem b (elements of the row type)
 
   // rows of the next tile are fetched into registers while this tile computes,
   // when a tile is at most PF elements per thread (uniform across the block)
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       float v = 0.f;
       if (j < T * DP) {
         const int r = j / DP, d = j % DP;
-        if (r0 + r < N && d < D) v = xb[(r0 + r) * A.ld_x + d];
+        if (r0 + r < N && d < D) v = x_value(A.x, A.xtype, xoff + (r0 + r) * A.ld_x + d);
       }
       pv[i] = v;
     }
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(512) topm_kernel(TopmArgs A) {
       for (int j = threadIdx.x; j < T * DP; j += nthr) {
         const int r = j / DP, d = j % DP;
         const int64_t row = row0 + r;
-        raw[j] = (row < N && d < D) ? xb[row * A.ld_x + d] : 0.f;
+        raw[j] = (row < N && d < D) ? x_value(A.x, A.xtype, xoff + row * A.ld_x + d) : 0.f;
       }
     }
     for (int p = threadIdx.x; p < T; p += nthr) cnt[p] = 0;

@@ -164,22 +164,29 @@ def _bf16(N, D=128, B=1):
     return _data(N, D=D, B=B, dtype=_abi.DT_BF16)
 
 
-@pytest.mark.parametrize("cov,B,D,K,ok", [
-    (_abi.COV_SPHERICAL, 1, 128, 4096, True),
-    (_abi.COV_SPHERICAL, 1, 100, 300, True),
-    (_abi.COV_SPHERICAL, 1, 128, 16384, True),
-    (_abi.COV_SPHERICAL, 1, 128, 16385, False),   # above the large-K window
-    (_abi.COV_SPHERICAL, 1, 129, 64, False),      # D > 128
-    (_abi.COV_SPHERICAL, 2, 64, 64, False),       # one problem per call
-    (_abi.COV_DIAG, 1, 64, 64, False),            # bf16 rows: spherical only
-    (_abi.COV_FULL, 1, 8, 8, False),
+@pytest.mark.parametrize("cov,B,D,K,ok,ok16", [
+    (_abi.COV_SPHERICAL, 1, 128, 4096, True, False),   # bf16: large-K path; half rows: the fused window (K <= 256)
+    (_abi.COV_SPHERICAL, 1, 100, 300, True, False),
+    (_abi.COV_SPHERICAL, 1, 128, 16384, True, False),
+    (_abi.COV_SPHERICAL, 1, 128, 16385, False, False),  # above the large-K window
+    (_abi.COV_SPHERICAL, 1, 129, 64, False, False),     # D > 128
+    (_abi.COV_SPHERICAL, 2, 64, 64, True, True),        # several problems: the fused path
+    (_abi.COV_SPHERICAL, 2, 64, 300, False, False),     # ... and its K <= 256
+    (_abi.COV_DIAG, 1, 64, 64, True, True),
+    (_abi.COV_DIAG, 3, 128, 40, True, True),
+    (_abi.COV_FULL, 1, 8, 8, True, True),
+    (_abi.COV_TIED, 2, 16, 12, True, True),
+    (_abi.COV_FULL, 1, 17, 8, False, False),            # full/tied: D <= 16
 ])
-def test_bf16_support_window(cov, B, D, K, ok):
+def test_16bit_support_window(cov, B, D, K, ok, ok16):
+    """bf16 rows of one problem with spherical components take the large-K
+    path (any K); every other bf16 case and all half rows take the fused path
+    (its K and D window), the rows decoded exactly to float32."""
     L = _abi.lib()
     n = L.gmm_workspace_bytes(ctypes.byref(_bf16(10_000, D=D, B=B)), K, cov, _abi.OP_FIT, 0)
     assert (n > 0) == ok
-    f16 = _data(10_000, D=D, dtype=_abi.DT_F16)
-    assert L.gmm_workspace_bytes(ctypes.byref(f16), K, cov, _abi.OP_FIT, 0) == 0
+    f16 = _data(10_000, D=D, B=B, dtype=_abi.DT_F16)
+    assert (L.gmm_workspace_bytes(ctypes.byref(f16), K, cov, _abi.OP_FIT, 0) > 0) == ok16
 
 
 def test_bf16_workspace_stops_growing_after_one_chunk():
@@ -269,9 +276,10 @@ def test_gaussian_mixture_host_checks():
 
 
 def test_kmeans_workspace_and_window():
-    """The k-means step takes the top-m window (float32 rows: K <= 256; bf16
-    rows: one problem, any K) and a workspace that grows with N (posting
-    lists and one responsibility per row); sizes are 256-byte multiples."""
+    """The k-means step takes the top-m window (float32 and half rows, and bf16
+    rows of several problems: K <= 256; bf16 rows of one problem: any K) and a
+    workspace that grows with N (posting lists and one responsibility per
+    row); sizes are 256-byte multiples."""
     L = _abi.lib()
     for N, D, K in [(10_000, 8, 16), (1_000_000, 64, 256), (5003, 7, 1)]:
         n = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(N, D)), K)
@@ -281,7 +289,9 @@ def test_kmeans_workspace_and_window():
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 0) == 0
     bf = _data(100_000, 128, dtype=_abi.DT_BF16)
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(bf), 4096) > 0
-    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 64) == 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 64) > 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 300) == 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64, dtype=_abi.DT_F16)), 200) > 0
     a = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(100_000, 32)), 64)
     b = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(200_000, 32)), 64)
     assert b > a
