@@ -90,6 +90,7 @@ static void largek_layout(Plan& q, int64_t chunk) {
     q.off_prem = o; o = align_up(o + sizeof(float) * (size_t)chunk * q.S);
     q.off_lmx = o;  o = align_up(o + sizeof(float) * 4 * (size_t)chunk * q.S);
     q.off_kthr = o; o = align_up(o + sizeof(float) * (size_t)chunk);
+    q.off_hv = o;   o = align_up(o + (size_t)chunk / 4 + 1);
   }
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
   q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.llG);
@@ -259,7 +260,7 @@ static gmm_status fit_ws(Plan& p, size_t ws_bytes) {
     largek_layout(q, 32);
     if (ws_bytes >= q.ws_bytes) {
       size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
-      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (2 + 5 * (size_t)p.S) + sizeof(uint32_t) * (p.KP / 32);
+      if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (2 + 5 * (size_t)p.S) + sizeof(uint32_t) * (p.KP / 32) + 1;
       int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
       chunk = std::min<int64_t>(chunk, p.chunk_rows);
       for (largek_layout(q, chunk); q.ws_bytes > ws_bytes && chunk > 32; largek_layout(q, chunk)) chunk -= 32;
@@ -342,6 +343,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
     A.prem = reinterpret_cast<float*>(w + p.off_prem);
     A.lmx = reinterpret_cast<float4*>(w + p.off_lmx);
     A.kthr = reinterpret_cast<float*>(w + p.off_kthr);
+    A.hv = reinterpret_cast<unsigned char*>(w + p.off_hv);
   }
   return A;
 }

@@ -49,6 +49,7 @@ struct Plan {
   size_t lds_a = 0, lds_t = 0, lds_c = 0;
   size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
   size_t off_lmx = 0, off_kthr = 0;  // large-K top-k: per-(row, slice) lower-bound maxima, per-row threshold
+  size_t off_hv = 0;                 // large-K top-m: rows handed to the heavy rescoring kernel
   size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
@@ -114,6 +115,7 @@ struct LargeKArgs {
   int topk;
   float4* lmx;          // (chunk, S) per (row, slice): 4 lane-group maxima of (score - error bound), or null
   float* kthr;          // (chunk) per row: a lower bound of its topk-th best score (candidate threshold)
+  unsigned char* hv;    // (chunk / 4) rescoring: rows with many candidates, a 4-bit mask per four rows
   int m;
   float thr;
   int32_t* idx;         // outputs of the chunk's rows

@@ -1234,19 +1234,13 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
   return x - v;
 }
 
-__global__ void __launch_bounds__(64 * kFinalRows, 4) largek_topm_final_kernel(LargeKArgs A) {
+// One row by the whole wave (any number of candidates): L, KK (kSlots each)
+// and LST (kBatch) are the wave's LDS areas.
+__device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, double* L, int* KK,
+                                           unsigned short* LST) {
   constexpr double LN2 = 0.69314718055994530942;
-  __shared__ double sl[kFinalRows][kSlots];
-  __shared__ int skk[kFinalRows][kSlots];
-  __shared__ unsigned short slist[kFinalRows][kBatch];
   const int lane = threadIdx.x & 63;
-  const int wq = threadIdx.x >> 6;
   const int grp = lane >> 4, li = lane & 15;
-  const int64_t row = (int64_t)blockIdx.x * kFinalRows + wq;
-  if (row >= A.N) return;  // uniform across the wave; the block has no barrier
-  double* L = sl[wq];
-  int* KK = skk[wq];
-  unsigned short* LST = slist[wq];
   const int m = A.m;
   const int D = (int)A.D;
   const int nwords = A.KP / 32;
@@ -1436,6 +1430,200 @@ __global__ void __launch_bounds__(64 * kFinalRows, 4) largek_topm_final_kernel(L
   }
 }
 
+// The rescoring kernel: one wave per four rows, 16 lanes (a DPP row) per row.
+// A group counts its row's candidates (16-lane scan of the mask words'
+// popcounts); a row with at most kLight of them is scored by the group alone
+// (each candidate's 128-term float64 dot product split over the 16 lanes,
+// four candidates' loads in flight), its best m picked by m rounds of a
+// 16-lane best, LSE and outputs as in topm_row_wave.  Four independent rows per wave keep four chains of
+// dependent loads in flight where one row per wave kept one.
+constexpr int kLight = 32;
+
+__global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
+  constexpr double LN2 = 0.69314718055994530942;
+  __shared__ unsigned short light[4][kLight];
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 4 + g;
+  const bool live = row < A.N;
+  const int m = A.m;
+  const int D = (int)A.D;
+  const int K = A.K;
+  const int nwords = A.KP / 32;
+  const int64_t rc = live ? row : A.N - 1;
+  // ---- candidates of the group's row: words li, li + 16, ... (coalesced per group)
+  auto word_at = [&](int wi) -> uint32_t {
+    uint32_t wd = A.cmask[(size_t)rc * nwords + wi];
+    if (wi * 32 + 32 > K) wd &= wi * 32 >= K ? 0u : (1u << (K - wi * 32)) - 1u;  // padding is never a candidate
+    return wd;
+  };
+  int mycount = 0;
+  for (int wi = li; wi < nwords; wi += 16) mycount += __popc(word_at(wi));
+  int x = mycount;  // 16-lane inclusive scan
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const int y = __shfl_up(x, off, 16);
+    if (li >= off) x += y;
+  }
+  const int total = live ? __shfl(x, 15, 16) : 0;
+  const int mybase = x - mycount;
+  const bool is_light = total <= kLight;
+  if (is_light && live) {
+    int r = mybase;
+    for (int wi = li; wi < nwords; wi += 16) {
+      uint32_t wd = word_at(wi);
+      while (wd) {
+        const int bit = __builtin_ctz(wd);
+        wd &= wd - 1;
+        light[g][r++] = (unsigned short)(wi * 32 + bit);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (is_light && live) {
+    // this lane's 8 dims of the row
+    const unsigned short* xr = reinterpret_cast<const unsigned short*>(A.x) + row * A.ld_x;
+    double xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * li + e;
+      xv[e] = d < D ? (double)__uint_as_float((unsigned)xr[d] << 16) : 0.0;
+    }
+    const bool vec = (D & 7) == 0 && ((uintptr_t)A.mu & 15) == 0;
+    const int doff = vec ? min(8 * li, D - 8) : 0;
+    const double xsq = A.xsq[row];
+    // candidate c's score ends in lane c % 16, slot c / 16
+    constexpr int NS = kLight / 16;
+    double sc[NS];
+    int kc[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      sc[t] = -INFINITY;
+      kc[t] = 0x7fffffff;
+    }
+    constexpr int U = 4;
+    for (int c0 = 0; c0 < total; c0 += U) {
+      int ku[U];
+      double2 cu[U];
+      float4 m0[U], m1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ku[u] = light[g][min(c0 + u, total - 1)];
+        cu[u] = A.kconst[ku[u]];
+        const float* mu = A.mu + (size_t)ku[u] * D;
+        if (vec) {
+          m0[u] = *reinterpret_cast<const float4*>(mu + doff);
+          m1[u] = *reinterpret_cast<const float4*>(mu + doff + 4);
+        } else {
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = (8 * li + e < D) ? mu[8 * li + e] : 0.f;
+          m0[u] = float4{t[0], t[1], t[2], t[3]};
+          m1[u] = float4{t[4], t[5], t[6], t[7]};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double dot = xv[0] * (double)m0[u].x + xv[1] * (double)m0[u].y + xv[2] * (double)m0[u].z +
+                     xv[3] * (double)m0[u].w + xv[4] * (double)m1[u].x + xv[5] * (double)m1[u].y +
+                     xv[6] * (double)m1[u].z + xv[7] * (double)m1[u].w;
+        dot = row16_sum_f64(dot);
+        const int c = c0 + u;
+        const double v = cu[u].x + cu[u].y * (dot - 0.5 * xsq);
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+          if (c < total && li == (c & 15) && t == (c >> 4)) {
+            // score = (c0 - lambda log2(e) |mu|^2 / 2) + lambda log2(e) (x . mu - |x|^2 / 2)
+            sc[t] = v;
+            kc[t] = ku[u];
+          }
+      }
+    }
+    // top-m: the LSE over every candidate plus the slices' below-band mass
+    double Mx = sc[0];
+#pragma unroll
+    for (int t = 1; t < NS; ++t) Mx = fmax(Mx, sc[t]);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) Mx = fmax(Mx, __shfl_xor(Mx, off, 16));
+    double lse = 0.0;
+    if (!A.topk) {
+      double ssum = 0.0;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        if (sc[t] > -INFINITY) ssum += exp2_acc(sc[t] - Mx);
+      double rem = 0.0;
+      for (int s = li; s < A.S; s += 16) rem += (double)A.prem[(size_t)row * A.S + s];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        ssum += __shfl_xor(ssum, off, 16);
+        rem += __shfl_xor(rem, off, 16);
+      }
+      lse = Mx + log2(ssum + rem * exp2((double)A.mrow[row] - Mx));
+    }
+    // the best m, one per round; lane j of the group keeps round j's
+    double rl = -INFINITY;
+    int rk = 0x7fffffff;
+    for (int j = 0; j < m; ++j) {
+      double bl = sc[0];
+      int bk = kc[0];
+#pragma unroll
+      for (int t = 1; t < NS; ++t)
+        if (before(sc[t], kc[t], bl, bk)) { bl = sc[t]; bk = kc[t]; }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        const double l2 = __shfl_xor(bl, off, 16);
+        const int k2 = __shfl_xor(bk, off, 16);
+        if (before(l2, k2, bl, bk)) { bl = l2; bk = k2; }
+      }
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (kc[u] == bk && bk != 0x7fffffff) { sc[u] = -INFINITY; kc[u] = 0x7fffffff; }  // taken
+      if (li == j) {
+        rl = bl;
+        rk = bk;
+      }
+    }
+    if (A.topk) {
+      // top-k: the log-sum-exp of the kept m (round 0 holds the best)
+      double s = (li < m && rk < K) ? exp2(rl - Mx) : 0.0;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      lse = Mx + log2(s);
+    }
+    const double r = rk < K ? exp2(rl - lse) : 0.0;
+    const bool ok = li < m && rk < K && (A.topk || li == 0 || r >= (double)A.thr);
+    const unsigned okb = (unsigned)((__builtin_amdgcn_ballot_w64(ok) >> (16 * g)) & 0xFFFFu);
+    const int c = __builtin_ctz(~okb);  // the kept ranks are a prefix
+    if (li < m) {
+      A.idx[row * m + li] = li < c ? rk : -1;
+      A.resp[row * m + li] = li < c ? (float)r : 0.f;
+    }
+    if (li == 0) {
+      if (A.count) A.count[row] = c;
+      if (A.logp) A.logp[row] = (float)(lse * LN2);
+    }
+  }
+  // ---- rows past kLight candidates: flagged for the heavy kernel
+  const uint64_t heavy = __builtin_amdgcn_ballot_w64(live && !is_light && li == 0);  // bits 0, 16, 32, 48
+  if (lane == 0)
+    A.hv[blockIdx.x] = (unsigned char)((heavy & 1u) | ((heavy >> 15) & 2u) | ((heavy >> 30) & 4u) | ((heavy >> 45) & 8u));
+}
+
+// Rows flagged by largek_topm_final4_kernel, a whole wave each: waves stride
+// over the flag bytes (one per four rows).
+__global__ void __launch_bounds__(64) largek_topm_heavy_kernel(LargeKArgs A, int64_t nflags) {
+  __shared__ double sl[kSlots];
+  __shared__ int skk[kSlots];
+  __shared__ unsigned short slist[kBatch];
+  for (int64_t b = blockIdx.x; b < nflags; b += gridDim.x) {
+    const unsigned f = A.hv[b];  // uniform across the wave
+    for (int q = 0; q < 4; ++q)
+      if ((f >> q) & 1u) topm_row_wave(A, b * 4 + q, sl, skk, slist);
+  }
+}
+
 hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* w, const float* mu, const float* cv,
                               hipStream_t s) {
   LargeKArgs a = a0;
@@ -1498,8 +1686,11 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     else
       hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(largek_topm_final_kernel, dim3((unsigned)((ac.N + kFinalRows - 1) / kFinalRows)),
-                       dim3(64 * kFinalRows), 0, s, ac);
+    const int64_t nflags = (ac.N + 3) / 4;
+    hipLaunchKernelGGL(largek_topm_final4_kernel, dim3((unsigned)nflags), dim3(64), 0, s, ac);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(largek_topm_heavy_kernel, dim3((unsigned)std::min<int64_t>(nflags, 4096)), dim3(64), 0, s, ac,
+                       nflags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
