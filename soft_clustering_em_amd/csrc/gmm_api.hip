@@ -350,7 +350,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
 
 static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk,
                                    double* sx, double* sxx, double* ll, double* mean_ll, int accumulate,
-                                   const gmm_options* opts, hipStream_t s) {
+                                   const gmm_options* opts, hipStream_t s, const MstepFuse* fuse) {
   char* w = static_cast<char*>(ws);
   LargeKArgs A = largek_args(p, d, prm, ws);
   hipError_t e;
@@ -361,15 +361,17 @@ static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_p
   if (opts && opts->event_end && (e = hipEventRecord((hipEvent_t)opts->event_end, s)) != hipSuccess)
     return hip_fail(e, "event record");
   e = launch_reduce_raw(p, A.part, A.llpart, prm->means, reinterpret_cast<double*>(w + p.off_aux), nk, sx, sxx, ll,
-                        mean_ll, accumulate, s);
+                        mean_ll, accumulate, s, fuse);
   if (e != hipSuccess) return hip_fail(e, "reduction launch");
   return GMM_OK;
 }
 
+// fuse (nullable): the M-step of gmm_fit_step, run by the reduction's
+// component blocks (spherical, diag, full)
 static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk, double* sx,
                             double* sxx, double* ll, double* mean_ll, int accumulate, const gmm_options* opts,
-                            hipStream_t s) {
-  if (p.largek) return run_estep_largek(p, d, prm, ws, nk, sx, sxx, ll, mean_ll, accumulate, opts, s);
+                            hipStream_t s, const MstepFuse* fuse = nullptr) {
+  if (p.largek) return run_estep_largek(p, d, prm, ws, nk, sx, sxx, ll, mean_ll, accumulate, opts, s, fuse);
   char* w = static_cast<char*>(ws);
   float* W = reinterpret_cast<float*>(w + p.off_W);
   double* prec = reinterpret_cast<double*>(w + p.off_prec);
@@ -416,7 +418,7 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
     e = hipEventRecord((hipEvent_t)opts->event_end, s);
     if (e != hipSuccess) return hip_fail(e, "event record");
   }
-  e = launch_reduce_raw(p, part, llp, prm->means, raw, nk, sx, sxx, ll, mean_ll, accumulate, s);
+  e = launch_reduce_raw(p, part, llp, prm->means, raw, nk, sx, sxx, ll, mean_ll, accumulate, s, fuse);
   if (e != hipSuccess) return hip_fail(e, "reduction launch");
   return GMM_OK;
 }
@@ -560,9 +562,12 @@ static gmm_status fit_step_run(const Plan& p, const gmm_data* data, gmm_params* 
   double* sxx = reinterpret_cast<double*>(w + p.off_sxx);
   double* ll = reinterpret_cast<double*>(w + p.off_ll);
   hipStream_t s = (hipStream_t)stream;
-  st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s);
-  if (st != GMM_OK) return st;
   const int32_t* flag = p.largek ? nullptr : reinterpret_cast<const int32_t*>(w + p.off_flag);
+  // spherical, diag, full: the M-step runs in the reduction's component blocks
+  const bool fused = p.cov != TIED;
+  const MstepFuse fuse{inout->weights, inout->means, inout->covars, p.N, reg, flag, p.KP, comp_status};
+  st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s, fused ? &fuse : nullptr);
+  if (st != GMM_OK || fused) return st;
   hipError_t e = launch_mstep_strided(p.cov, p.B, p.D, p.K, nk, sx, sxx, p.N, inout->weights, inout->means,
                                       inout->covars, reg, flag, p.KP, comp_status, s);
   if (e != hipSuccess) return hip_fail(e, "M-step launch");

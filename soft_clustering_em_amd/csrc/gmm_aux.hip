@@ -291,6 +291,12 @@ hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* 
   return hipGetLastError();
 }
 
+__device__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
+                                const double* __restrict__ sx, const double* __restrict__ sxx, int64_t n_total,
+                                float* w, float* mu, float* cv, double reg, const int32_t* in_flag,
+                                int in_flag_stride, int32_t* comp_status, double* sm_delta, double* sm_S,
+                                double* sm_L, int* sm_pd);
+
 // ------------------------------------------------------------------ reduce
 // grid: B*K + B blocks.  Block (b, k) sums the Gb partials of component k in
 // workgroup order (float64) into raw[b][k][:], and (non-tied) writes the
@@ -301,9 +307,11 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
                                                      const double* __restrict__ llpart,
                                                      const float* __restrict__ mu, double* __restrict__ raw,
                                                      double* nk, double* sx, double* sxx, double* ll,
-                                                     double* mean_ll, int accumulate, int B) {
+                                                     double* mean_ll, int accumulate, int B, MstepFuse M) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   extern __shared__ double sm[];
+  __shared__ double sm_S[16 * 16], sm_L[16 * 16];
+  __shared__ int sm_pd;
   // fixed-order sum of n values v(g), g = 0..n-1, split into nseg contiguous
   // segments (segment q: thread-local sum, eight loads in flight), the
   // segment sums then added in segment order
@@ -387,6 +395,14 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
       sxx[bk * D * D + i] = accumulate ? sxx[bk * D * D + i] + v : v;
     }
   }
+  if (M.w) {
+    // the M-step of this component, from the statistics this block just wrote
+    // (the block's own global writes are visible to it after the barrier); it
+    // reads and then replaces this component's mean only
+    __syncthreads();
+    mstep_component(cov, D, b, K, k, nk, sx, sxx, M.n_total, M.w, M.mu, M.cv, M.reg, M.in_flag, M.in_flag_stride,
+                    M.comp_status, m, sm_S, sm_L, &sm_pd);
+  }
 }
 
 // Tied: sxx = sum_k sum_i r_ik (x_i - mu_k)(x_i - mu_k)^T from the raw sums.
@@ -422,12 +438,14 @@ __global__ void __launch_bounds__(256) centre_tied_kernel(int D, int K, int KP, 
 
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
-                             int accumulate, hipStream_t s) {
+                             int accumulate, hipStream_t s, const MstepFuse* fuse) {
   const unsigned threads = 256;
   const size_t lds = sizeof(double) * (size_t)(p.PR + p.D + threads);
+  MstepFuse M{};
+  if (fuse && p.cov != TIED && !accumulate) M = *fuse;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(p.B * p.K + p.B)), dim3(threads), lds, s, p.cov, (int)p.D,
                      (int)p.K, p.KP, p.DP, p.PR, p.Gb, p.llG, p.N, part, llpart, mu, raw, nk, sx, sxx, ll, mean_ll,
-                     accumulate, (int)p.B);
+                     accumulate, (int)p.B, M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.cov != TIED) return e;
   hipLaunchKernelGGL(centre_tied_kernel, dim3((unsigned)p.B), dim3(256), 0, s, (int)p.D, (int)p.K, p.KP, p.DP,
@@ -438,18 +456,16 @@ hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* ll
 // ------------------------------------------------------------------ M-step
 // Flash-GMM Section 2, eqs. 1-3 (pi_k = N_k / n; mu'_k = sx_k / N_k; variance
 // about the new mean, written through the centred statistics), diag / full
-// forms as in "ML0094 GMM vs K-Means", Mathematical Formulation.
-// grid: B*K blocks of 64 threads (spherical, diag, full).
-__global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const double* __restrict__ nk,
-                                                   const double* __restrict__ sx, const double* __restrict__ sxx,
-                                                   int64_t n_total, float* w, float* mu, float* cv, double reg,
-                                                   const int32_t* in_flag, int in_flag_stride,
-                                                   int32_t* comp_status) {
-  const int b = blockIdx.x / K, k = blockIdx.x % K, tid = threadIdx.x;
+// forms as in "ML0094 GMM vs K-Means", Mathematical Formulation.  One
+// component (b, k) by the threads of a block; sm_delta holds D doubles, sm_S
+// and sm_L 16 x 16.
+__device__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
+                                const double* __restrict__ sx, const double* __restrict__ sxx, int64_t n_total,
+                                float* w, float* mu, float* cv, double reg, const int32_t* in_flag,
+                                int in_flag_stride, int32_t* comp_status, double* sm_delta, double* sm_S,
+                                double* sm_L, int* sm_pd) {
+  const int tid = threadIdx.x;
   const size_t bk = (size_t)b * K + k;
-  __shared__ double sm_delta[128];
-  __shared__ double sm_S[16 * 16], sm_L[16 * 16];
-  __shared__ int sm_pd;
   const double n = nk[bk];
   const bool empty = !(n > 0.0);
   int32_t st = empty ? 1 : 0;
@@ -457,7 +473,7 @@ __global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const 
   if (tid == 0) w[bk] = (float)(n / (double)n_total);
   if (empty) {
     if (tid == 0 && comp_status) comp_status[bk] = st;
-    return;  // mu_k and Sigma_k kept
+    return;  // mu_k and Sigma_k kept (uniform across the block)
   }
   for (int d = tid; d < D; d += blockDim.x) {
     const double m1 = sx[bk * D + d] / n;
@@ -479,17 +495,30 @@ __global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const 
       sm_S[i] = sxx[bk * D * D + i] / n - sm_delta[d] * sm_delta[e] + (d == e ? reg : 0.0);
     }
     __syncthreads();
-    if (tid == 0) sm_pd = chol_serial(D, sm_S, sm_L);
+    if (tid == 0) *sm_pd = chol_serial(D, sm_S, sm_L);
     __syncthreads();
-    if (!sm_pd) {
+    if (!*sm_pd) {
       if (tid == 0 && comp_status) comp_status[bk] = st | 2;
-      return;  // previous mu_k and Sigma_k kept
+      return;  // previous mu_k and Sigma_k kept (uniform across the block)
     }
     for (int i = tid; i < D * D; i += blockDim.x) cv[bk * D * D + i] = (float)sm_S[i];
   }
   __syncthreads();
   for (int d = tid; d < D; d += blockDim.x) mu[bk * D + d] = (float)(sx[bk * D + d] / n);
   if (tid == 0 && comp_status) comp_status[bk] = st;
+}
+
+// grid: B*K blocks of 64 threads (spherical, diag, full).
+__global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const double* __restrict__ nk,
+                                                   const double* __restrict__ sx, const double* __restrict__ sxx,
+                                                   int64_t n_total, float* w, float* mu, float* cv, double reg,
+                                                   const int32_t* in_flag, int in_flag_stride,
+                                                   int32_t* comp_status) {
+  __shared__ double sm_delta[128];
+  __shared__ double sm_S[16 * 16], sm_L[16 * 16];
+  __shared__ int sm_pd;
+  mstep_component(cov, D, blockIdx.x / K, K, blockIdx.x % K, nk, sx, sxx, n_total, w, mu, cv, reg, in_flag,
+                  in_flag_stride, comp_status, sm_delta, sm_S, sm_L, &sm_pd);
 }
 
 // Tied: one block per problem.

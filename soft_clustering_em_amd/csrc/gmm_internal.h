@@ -256,9 +256,21 @@ hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const
                            double* prec, double* c0, double* c, double* a, int32_t* flag, int32_t* sharp,
                            hipStream_t s);
 hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* mean_ll, hipStream_t s);
+// The M-step fused into the statistics reduction (spherical, diag, full;
+// not when accumulating): w == nullptr means no M-step.
+struct MstepFuse {
+  float* w;
+  float* mu;
+  float* cv;
+  int64_t n_total;
+  double reg;
+  const int32_t* in_flag;
+  int in_flag_stride;
+  int32_t* comp_status;
+};
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
-                             int accumulate, hipStream_t s);
+                             int accumulate, hipStream_t s, const MstepFuse* fuse = nullptr);
 hipError_t launch_mstep_strided(int cov, int64_t B, int64_t D, int64_t K, const double* nk, const double* sx,
                                 const double* sxx, int64_t n_total, float* w, float* mu, float* cv, double reg,
                                 const int32_t* in_flag, int in_flag_stride, int32_t* comp_status, hipStream_t s);
