@@ -155,7 +155,7 @@ def _find(root, suffix):
 def _window(rows):
     """(first, last) dispatch ids strictly between the first two spin-kernel
     markers, or None when the trace has fewer than two."""
-    marks = sorted(int(r["Dispatch_Id"]) for r in rows if "spin" in r["Kernel_Name"].lower())
+    marks = sorted({int(r["Dispatch_Id"]) for r in rows if "spin" in r["Kernel_Name"].lower()})
     if len(marks) < 2:
         return None
     # the two markers of the timed loop are consecutive spin dispatches
@@ -317,6 +317,8 @@ def main():
     ap.add_argument("--workload", default="ivf_bf16",
                     choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-topm", action="store_true",
+                    help="skip the top-m / posting-list / k-means measurements after the fit (counter runs)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (traffic counter calibration)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -440,7 +442,7 @@ def main():
         },
         "mean_loglik_last": float(mll.mean().item()),
     }
-    if wl.topm is not None:
+    if wl.topm is not None and not args.no_topm:
         # soft multi-assignment under the fitted model: one pass, timed apart
         m, thr = wl.topm
         idx = torch.empty((wl.B, wl.N, m), dtype=torch.int32, device=dev)
