@@ -44,23 +44,46 @@ __device__ __forceinline__ size_t wfrag_index(int k, int f, int KW, int F) {
 // row-major upper-triangle index of (d, e), d <= e, in a DP x DP matrix
 __device__ __forceinline__ int quad_index(int d, int e, int DP) { return d * DP - d * (d - 1) / 2 + (e - d); }
 
-// Cholesky of the D x D matrix in S (row-major, float64) into L (lower);
-// returns false if S is not positive definite.  Serial, D <= 16.
-__device__ bool chol_serial(int D, const double* S, double* L) {
-  for (int i = 0; i < D * D; ++i) L[i] = 0.0;
+// Cholesky A = L L^T in place by the threads of a block.  A (row-major, row
+// stride ld, float64, in LDS) holds a D x D (D <= 16) symmetric matrix on entry and L
+// in its lower triangle on return (the upper triangle keeps its entries).
+// Right-looking: for column j the pivot l_jj = sqrt(a_jj), the column below
+// it divided by l_jj, then the trailing lower triangle updated by
+// a_ik -= l_ij l_kj (j < k <= i), so every entry subtracts its products in the
+// order p = 0, 1, ...  Returns whether A is positive definite (the same on
+// every thread).  Every thread of the block calls it (it holds barriers).
+__device__ bool chol_block(int D, double* A, int ld) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
   for (int j = 0; j < D; ++j) {
-    double s = S[j * D + j];
-    for (int p = 0; p < j; ++p) s -= L[j * D + p] * L[j * D + p];
-    if (!(s > 0.0)) return false;
-    const double l = sqrt(s);
-    L[j * D + j] = l;
-    for (int i = j + 1; i < D; ++i) {
-      double t = S[i * D + j];
-      for (int p = 0; p < j; ++p) t -= L[i * D + p] * L[j * D + p];
-      L[i * D + j] = t / l;
+    __syncthreads();
+    // a_jj is not written again once column j has been formed
+    const double piv = A[j * ld + j];
+    if (!(piv > 0.0)) return false;  // every thread read the same value
+    const double l = sqrt(piv);
+    for (int i = j + 1 + tid; i < D; i += nthr) A[i * ld + j] /= l;
+    __syncthreads();
+    // trailing entries (i, k), j < k <= i < D, on a 16-wide grid of threads
+    for (int t = tid; t < (D - 1 - j) * 16; t += nthr) {
+      const int i = j + 1 + (t >> 4), k = j + 1 + (t & 15);
+      if (k <= i) A[i * ld + k] -= A[i * ld + j] * A[k * ld + j];
     }
   }
+  __syncthreads();
+  for (int d = tid; d < D; d += nthr) A[d * ld + d] = sqrt(A[d * ld + d]);
+  __syncthreads();
   return true;
+}
+
+// fixed-order (butterfly) sum over the 64 lanes of a wave
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ double wave_max64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
 }
 
 // ------------------------------------------------------------------ prologue
@@ -80,8 +103,6 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
   __shared__ double sm_v[128];                // diag precisions / P mu
   __shared__ double sm_S[16 * 16], sm_L[16 * 16], sm_Li[16 * 16], sm_P[16 * 16];
   __shared__ double sm_c;
-  __shared__ double sm_red[64];               // one partial per thread (blockDim.x == 64)
-  __shared__ double sm_l1[64];                // per thread: squared norm of its linear weights
   __shared__ int sm_ok;
 
   if (k >= K) {  // padding component: never responsible
@@ -106,38 +127,25 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       sm_v[d] = (cov == SPH) ? 1.0 / (double)cv[(size_t)b * K + k] : 1.0 / (double)cv[((size_t)b * K + k) * D + d];
     __syncthreads();
     // per-dimension terms on the block's threads (one log per variance;
-    // spherical: one log in all), then summed in thread order by thread 0
-    {
-      double ld = 0.0, qd = 0.0, sd = 0.0, lm = 0.0, l1 = 0.0;
-      int bad = 0;
-      for (int d = tid; d < D; d += blockDim.x) {
-        const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
-        if (!(v > 0.0) || isinf(v)) bad = 1;
-        if (cov == DIAG) ld += log(v);
-        qd += sm_v[d] * sm_mu[d] * sm_mu[d];
-        lm = fmax(lm, sm_v[d]);
-        sd += sm_mu[d] * sm_mu[d] + v;
-        l1 += (sm_v[d] * sm_mu[d]) * (sm_v[d] * sm_mu[d]);
-      }
-      sm_l1[tid] = l1;
-      sm_S[tid] = ld;
-      sm_L[tid] = qd;
-      sm_Li[tid] = sd;
-      sm_P[tid] = lm;
-      sm_red[tid] = bad;
+    // spherical: one log in all), then fixed-order wave sums
+    double logdet = 0.0, quad = 0.0, scale = 0.0, lmax = 0.0, l1 = 0.0, bad = 0.0;
+    for (int d = tid; d < D; d += blockDim.x) {
+      const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
+      if (!(v > 0.0) || isinf(v)) bad = 1.0;
+      if (cov == DIAG) logdet += log(v);
+      quad += sm_v[d] * sm_mu[d] * sm_mu[d];
+      lmax = fmax(lmax, sm_v[d]);
+      scale += sm_mu[d] * sm_mu[d] + v;
+      l1 += (sm_v[d] * sm_mu[d]) * (sm_v[d] * sm_mu[d]);
     }
-    __syncthreads();
+    logdet = wave_sum64(logdet);
+    quad = wave_sum64(quad);
+    scale = wave_sum64(scale);
+    lmax = wave_max64(lmax);
+    l1 = wave_sum64(l1);
+    bad = wave_max64(bad);
     if (tid == 0) {
-      bool ok = true;
-      double logdet = 0.0, quad = 0.0, lmax = 0.0, scale = 0.0, l1 = 0.0;
-      for (int t = 0; t < (int)blockDim.x; ++t) {
-        logdet += sm_S[t];
-        quad += sm_L[t];
-        scale += sm_Li[t];
-        lmax = fmax(lmax, sm_P[t]);
-        l1 += sm_l1[t];
-        if (sm_red[t] != 0.0) ok = false;
-      }
+      const bool ok = bad == 0.0;
       // spherical: the lambda |x|^2 term is added in float64, only x . (lambda mu)
       // runs in float32; diagonal: sum_d lambda_d x_d^2 / 2 <= lambda_max |x|^2 / 2
       if (err)
@@ -176,63 +184,73 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     return;
   }
 
-  // full / tied: P = Sigma^{-1} through the Cholesky factor Sigma = L L^T
+  // full / tied: P = Sigma^{-1} through the Cholesky factor Sigma = L L^T;
+  // sm_L, sm_Li and sm_P are 16 x 16 with row stride 16
   const float* S = (cov == FULL) ? cv + ((size_t)b * K + k) * D * D : cv + (size_t)b * D * D;
-  for (int i = tid; i < D * D; i += blockDim.x) sm_S[i] = (double)S[i];
-  __syncthreads();
-  if (tid == 0) sm_ok = chol_serial(D, sm_S, sm_L);
-  __syncthreads();
-  const bool ok = sm_ok;
+  for (int i = tid; i < D * D; i += blockDim.x) {
+    sm_S[i] = (double)S[i];
+    sm_L[(i / D) * 16 + i % D] = (double)S[i];
+  }
+  const bool ok = chol_block(D, sm_L, 16);  // starts and ends with a barrier
   if (ok) {
-    // column j of L^{-1}: forward substitution on e_j
-    if (tid < D) {
+    // column j of L^{-1} on lane j: forward substitution on e_j (its entries
+    // above row j are zero, so the products over p < j add nothing); only the
+    // lower triangle of sm_L is read
+    if (tid < 16) {
       const int j = tid;
-      for (int i = 0; i < D; ++i) {
+      double col[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         double t = (i == j) ? 1.0 : 0.0;
-        for (int p = j; p < i; ++p) t -= sm_L[i * D + p] * sm_Li[p * D + j];
-        sm_Li[i * D + j] = (i < j) ? 0.0 : t / sm_L[i * D + i];
+#pragma unroll
+        for (int p = 0; p < i; ++p) t -= sm_L[i * 16 + p] * col[p];
+        col[i] = (i < j) ? 0.0 : t / sm_L[i * 16 + i];
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm_Li[i * 16 + j] = col[i];
     }
     __syncthreads();
-    for (int i = tid; i < D * D; i += blockDim.x) {
-      const int d = i / D, e = i % D;
+    // P = L^{-T} L^{-1}, four entries per thread
+    for (int i = tid; i < 256; i += blockDim.x) {
+      const int d = i / 16, e = i % 16;
       double s = 0.0;
-      for (int p = 0; p < D; ++p) s += sm_Li[p * D + d] * sm_Li[p * D + e];
+      if (d < D && e < D)
+        for (int p = 0; p < D; ++p) s += sm_Li[p * 16 + d] * sm_Li[p * 16 + e];
       sm_P[i] = s;
     }
     __syncthreads();
-    for (int d = tid; d < D; d += blockDim.x) {
+    // per-thread terms, then fixed-order wave sums: lambda_max(P) <=
+    // ||P^2||_F^(1/2) = (sum_i lambda_i^4)^(1/4) (P symmetric positive
+    // definite), an upper bound far tighter than tr P when the eigenvalues are
+    // spread; sum over d <= e of |x_d x_e W_de| = |x|^T |P| |x| / 2 <=
+    // ||P||_F |x|^2 / 2 bounds the quadratic terms
+    double s4 = 0.0, pf = 0.0;
+    for (int i = tid; i < 256; i += blockDim.x) {
+      const int d = i / 16, e = i % 16;
       double s = 0.0;
-      for (int e = 0; e < D; ++e) s += sm_P[d * D + e] * sm_mu[e];
-      sm_v[d] = s;
+      for (int p = 0; p < D; ++p) s += sm_P[d * 16 + p] * sm_P[p * 16 + e];
+      s4 += s * s;
+      pf += sm_P[i] * sm_P[i];
     }
-    // lambda_max(P) <= ||P^2||_F^(1/2) = (sum_i lambda_i^4)^(1/4) (P symmetric
-    // positive definite): an upper bound far tighter than tr P when the
-    // eigenvalues are spread
-    {
-      double s4 = 0.0;
-      for (int i = tid; i < D * D; i += blockDim.x) {
-        const int d = i / D, e = i % D;
-        double s = 0.0;
-        for (int p = 0; p < D; ++p) s += sm_P[d * D + p] * sm_P[p * D + e];
-        s4 += s * s;
-      }
-      sm_red[tid] = s4;
+    double logdet = 0.0, quad = 0.0, scale = 0.0, l1 = 0.0;
+    if (tid < D) {
+      const int d = tid;
+      double v = 0.0;
+      for (int e = 0; e < D; ++e) v += sm_P[d * 16 + e] * sm_mu[e];
+      sm_v[d] = v;
+      logdet = 2.0 * log(sm_L[d * 16 + d]);
+      quad = sm_mu[d] * v;
+      scale = sm_mu[d] * sm_mu[d] + sm_S[d * D + d];
+      l1 = v * v;
     }
-    __syncthreads();
+    s4 = wave_sum64(s4);
+    pf = wave_sum64(pf);
+    logdet = wave_sum64(logdet);
+    quad = wave_sum64(quad);
+    scale = wave_sum64(scale);
+    l1 = wave_sum64(l1);
     if (tid == 0) {
-      double logdet = 0.0, quad = 0.0, scale = 0.0, f4 = 0.0;
-      for (int d = 0; d < D; ++d) {
-        logdet += 2.0 * log(sm_L[d * D + d]);
-        quad += sm_mu[d] * sm_v[d];
-        scale += sm_mu[d] * sm_mu[d] + sm_S[d * D + d];
-      }
-      for (int q = 0; q < (int)blockDim.x; ++q) f4 += sm_red[q];
-      const double lmax = sqrt(sqrt(f4));
-      // sum over d <= e of |x_d x_e W_de| = |x|^T |P| |x| / 2 <= |P|_F |x|^2 / 2
-      double l1 = 0.0, pf = 0.0;
-      for (int d = 0; d < D; ++d) l1 += sm_v[d] * sm_v[d];
-      for (int i = 0; i < D * D; ++i) pf += sm_P[i] * sm_P[i];
+      const double lmax = sqrt(sqrt(s4));
       if (err)
         err[(size_t)b * KP + k] = float2{(float)(kScoreErr * kLog2e * sqrt(l1)), (float)(kScoreErr * kLog2e * 0.5 * sqrt(pf))};
       sm_c = (logpi - 0.5 * (D * kLog2Pi + logdet + quad)) * kLog2e;
@@ -241,7 +259,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     }
     for (int i = tid; i < DP * DP; i += blockDim.x) {
       const int d = i / DP, e = i % DP;
-      precb[i] = (d < D && e < D) ? sm_Li[d * D + e] : 0.0;
+      precb[i] = (d < D && e < D) ? sm_Li[d * 16 + e] : 0.0;
     }
   }
   __syncthreads();
@@ -255,7 +273,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
         int q = f - DP, d = 0, base = 0;
         while (q >= base + (DP - d)) { base += DP - d; ++d; }
         const int e = d + (q - base);
-        if (d < D && e < D) val = (d == e ? -0.5 : -1.0) * sm_P[d * D + e] * kLog2e;
+        if (d < D && e < D) val = (d == e ? -0.5 : -1.0) * sm_P[d * 16 + e] * kLog2e;
       }
     }
     Wb[wfrag_index(k, f, KW, F)] = (float)val;
@@ -291,18 +309,18 @@ hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* 
   return hipGetLastError();
 }
 
-__device__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
+__device__ __forceinline__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
                                 const double* __restrict__ sx, const double* __restrict__ sxx, int64_t n_total,
                                 float* w, float* mu, float* cv, double reg, const int32_t* in_flag,
                                 int in_flag_stride, int32_t* comp_status, double* sm_delta, double* sm_S,
-                                double* sm_L, int* sm_pd);
+                                double* sm_L);
 
 // ------------------------------------------------------------------ reduce
 // grid: B*K + B blocks.  Block (b, k) sums the Gb partials of component k in
 // workgroup order (float64) into raw[b][k][:], and (non-tied) writes the
 // statistics centred at the input means.  Blocks B*K + b sum the
 // log-likelihood partials.  Tied covariance is centred by centre_tied_kernel.
-__global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int KP, int DP, int PR, int Gb, int llG,
+__global__ void __launch_bounds__(1024) reduce_kernel(int cov, int D, int K, int KP, int DP, int PR, int Gb, int llG,
                                                      int64_t N, const double* __restrict__ part,
                                                      const double* __restrict__ llpart,
                                                      const float* __restrict__ mu, double* __restrict__ raw,
@@ -311,31 +329,33 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
   const int tid = threadIdx.x, nthr = blockDim.x;
   extern __shared__ double sm[];
   __shared__ double sm_S[16 * 16], sm_L[16 * 16];
-  __shared__ int sm_pd;
   // fixed-order sum of n values v(g), g = 0..n-1, split into nseg contiguous
-  // segments (segment q: thread-local sum, eight loads in flight), the
+  // segments (segment q: thread-local sum, sixteen loads in flight), the
   // segment sums then added in segment order
   auto seg_sum = [&](const double* src, size_t stride, int n, int nseg, int q) {
     const int g0 = (int)((int64_t)n * q / nseg), g1 = (int)((int64_t)n * (q + 1) / nseg);
     double s = 0.0;
     int g = g0;
-    for (; g + 8 <= g1; g += 8) {
-      double v[8];
+    for (; g + 16 <= g1; g += 16) {
+      double v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(g + u) * stride];
+      for (int u = 0; u < 16; ++u) v[u] = src[(size_t)(g + u) * stride];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 16; ++u) s += v[u];
     }
     for (; g < g1; ++g) s += src[(size_t)g * stride];
     return s;
   };
   if ((int64_t)blockIdx.x >= (int64_t)B * K) {
     const int b = blockIdx.x - B * K;
-    sm[tid] = seg_sum(llpart + (size_t)b * llG, 1, llG, nthr, tid);
+    // thread segments, summed per wave by a fixed butterfly, then the wave
+    // sums in wave order
+    const double v = wave_sum64(seg_sum(llpart + (size_t)b * llG, 1, llG, nthr, tid));
+    if ((tid & 63) == 0) sm[tid >> 6] = v;
     __syncthreads();
     if (tid == 0) {
       double s = 0.0;
-      for (int q = 0; q < nthr; ++q) s += sm[q];
+      for (int q = 0; q < nthr / 64; ++q) s += sm[q];
       ll[b] = accumulate ? ll[b] + s : s;
       if (mean_ll) mean_ll[b] = s / (double)N;
     }
@@ -353,7 +373,9 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
   if (nseg == 1) {
     for (int j = tid; j < PR; j += nthr) r[j] = seg_sum(src0 + j, stride, Gb, 1, 0);
   } else {
-    if (tid < PR * nseg) segs[tid] = seg_sum(src0 + tid / nseg, stride, Gb, nseg, tid % nseg);
+    // neighbouring threads take neighbouring statistics of one segment, so
+    // their loads coalesce
+    if (tid < PR * nseg) segs[(tid % PR) * nseg + tid / PR] = seg_sum(src0 + tid % PR, stride, Gb, nseg, tid / PR);
     __syncthreads();
     for (int j = tid; j < PR; j += nthr) {
       double s = 0.0;
@@ -401,7 +423,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(int cov, int D, int K, int 
     // reads and then replaces this component's mean only
     __syncthreads();
     mstep_component(cov, D, b, K, k, nk, sx, sxx, M.n_total, M.w, M.mu, M.cv, M.reg, M.in_flag, M.in_flag_stride,
-                    M.comp_status, m, sm_S, sm_L, &sm_pd);
+                    M.comp_status, m, sm_S, sm_L);
   }
 }
 
@@ -439,7 +461,11 @@ __global__ void __launch_bounds__(256) centre_tied_kernel(int D, int K, int KP, 
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s, const MstepFuse* fuse) {
-  const unsigned threads = 256;
+  // enough threads that each statistic is summed in segments of about 32
+  // workgroup partials (the loads in flight hide the memory latency), a
+  // multiple of the wave, 256 to 1024
+  const int64_t want = (int64_t)p.PR * ((p.Gb + 31) / 32);
+  const unsigned threads = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(256, (want + 63) / 64 * 64));
   const size_t lds = sizeof(double) * (size_t)(p.PR + p.D + threads);
   MstepFuse M{};
   if (fuse && p.cov != TIED && !accumulate) M = *fuse;
@@ -459,11 +485,11 @@ hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* ll
 // forms as in "ML0094 GMM vs K-Means", Mathematical Formulation.  One
 // component (b, k) by the threads of a block; sm_delta holds D doubles, sm_S
 // and sm_L 16 x 16.
-__device__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
+__device__ __forceinline__ void mstep_component(int cov, int D, int b, int K, int k, const double* __restrict__ nk,
                                 const double* __restrict__ sx, const double* __restrict__ sxx, int64_t n_total,
                                 float* w, float* mu, float* cv, double reg, const int32_t* in_flag,
                                 int in_flag_stride, int32_t* comp_status, double* sm_delta, double* sm_S,
-                                double* sm_L, int* sm_pd) {
+                                double* sm_L) {
   const int tid = threadIdx.x;
   const size_t bk = (size_t)b * K + k;
   const double n = nk[bk];
@@ -493,11 +519,9 @@ __device__ void mstep_component(int cov, int D, int b, int K, int k, const doubl
     for (int i = tid; i < D * D; i += blockDim.x) {
       const int d = i / D, e = i % D;
       sm_S[i] = sxx[bk * D * D + i] / n - sm_delta[d] * sm_delta[e] + (d == e ? reg : 0.0);
+      sm_L[d * 16 + e] = sm_S[i];
     }
-    __syncthreads();
-    if (tid == 0) *sm_pd = chol_serial(D, sm_S, sm_L);
-    __syncthreads();
-    if (!*sm_pd) {
+    if (!chol_block(D, sm_L, 16)) {
       if (tid == 0 && comp_status) comp_status[bk] = st | 2;
       return;  // previous mu_k and Sigma_k kept (uniform across the block)
     }
@@ -516,9 +540,8 @@ __global__ void __launch_bounds__(64) mstep_kernel(int cov, int D, int K, const 
                                                    int32_t* comp_status) {
   __shared__ double sm_delta[128];
   __shared__ double sm_S[16 * 16], sm_L[16 * 16];
-  __shared__ int sm_pd;
   mstep_component(cov, D, blockIdx.x / K, K, blockIdx.x % K, nk, sx, sxx, n_total, w, mu, cv, reg, in_flag,
-                  in_flag_stride, comp_status, sm_delta, sm_S, sm_L, &sm_pd);
+                  in_flag_stride, comp_status, sm_delta, sm_S, sm_L);
 }
 
 // Tied: one block per problem.
@@ -529,7 +552,6 @@ __global__ void __launch_bounds__(256) mstep_tied_kernel(int D, int K, const dou
                                                          int in_flag_stride, int32_t* comp_status) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ double sm_S[16 * 16], sm_L[16 * 16];
-  __shared__ int sm_pd;
   extern __shared__ double sm_delta[];  // K*D
   for (int i = tid; i < K * D; i += blockDim.x) {
     const int k = i / D;
@@ -542,11 +564,9 @@ __global__ void __launch_bounds__(256) mstep_tied_kernel(int D, int K, const dou
     double s = sxx[(size_t)b * D * D + i];
     for (int k = 0; k < K; ++k) s -= nk[(size_t)b * K + k] * sm_delta[k * D + d] * sm_delta[k * D + e];
     sm_S[i] = s / (double)n_total + (d == e ? reg : 0.0);
+    sm_L[d * 16 + e] = sm_S[i];
   }
-  __syncthreads();
-  if (tid == 0) sm_pd = chol_serial(D, sm_S, sm_L);
-  __syncthreads();
-  const bool pd = sm_pd;
+  const bool pd = chol_block(D, sm_L, 16);
   if (pd)
     for (int i = tid; i < D * D; i += blockDim.x) cv[(size_t)b * D * D + i] = (float)sm_S[i];
   for (int k = tid; k < K; k += blockDim.x) {

@@ -112,8 +112,10 @@ def test_streamed_device_memory_does_not_grow_with_n(torch_cuda):
         n = g.gmm_fit_step_streamed_workspace_bytes(X, K, "diag", C)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated()
+        # the peak from here on stays at the allocation of this moment unless
+        # something allocates (a tensor freed meanwhile does not lower it)
         torch.cuda.reset_peak_memory_stats()
+        before = torch.cuda.max_memory_allocated()
         g.gmm_fit_step_streamed(X, w, mu, cv, "diag", C, ws=ws)
         torch.cuda.synchronize()
         assert torch.cuda.max_memory_allocated() == before
