@@ -84,6 +84,10 @@ static void largek_layout(Plan& q, int64_t chunk) {
   q.off_P = o;    o = align_up(o + sizeof(float) * 2 * (size_t)chunk * q.S);
   q.off_lse = o;  o = align_up(o + sizeof(float) * (size_t)chunk);
   q.off_xsq = o;  o = align_up(o + sizeof(double) * (size_t)chunk);
+  q.off_ext = 0;
+  if (q.op != GMM_OP_TOPM) {
+    q.off_ext = o; o = align_up(o + 16 * (size_t)chunk);
+  }
   if (q.op == GMM_OP_TOPM) {
     q.off_mrow = o; o = align_up(o + sizeof(float) * (size_t)chunk);
     q.off_cmask = o; o = align_up(o + sizeof(uint32_t) * (size_t)chunk * (q.KP / 32));
@@ -260,6 +264,7 @@ static gmm_status fit_ws(Plan& p, size_t ws_bytes) {
     largek_layout(q, 32);
     if (ws_bytes >= q.ws_bytes) {
       size_t per_row = sizeof(float) * (2 * (size_t)p.S + 1) + sizeof(double);
+      if (p.op != GMM_OP_TOPM) per_row += 16;
       if (p.op == GMM_OP_TOPM) per_row += sizeof(float) * (2 + 5 * (size_t)p.S) + sizeof(uint32_t) * (p.KP / 32) + 1;
       int64_t chunk = (int64_t)((ws_bytes - q.ws_bytes) / per_row) / 32 * 32 + 32;
       chunk = std::min<int64_t>(chunk, p.chunk_rows);
@@ -331,6 +336,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
   A.P = reinterpret_cast<float2*>(w + p.off_P);
   A.lse = reinterpret_cast<float*>(w + p.off_lse);
   A.xsq = reinterpret_cast<double*>(w + p.off_xsq);
+  A.ext = p.off_ext ? static_cast<void*>(w + p.off_ext) : nullptr;
   A.llpart = reinterpret_cast<double*>(w + p.off_llp);
   A.part = reinterpret_cast<double*>(w + p.off_part);
   A.accumulate = 0;

@@ -47,7 +47,7 @@ struct Plan {
   int64_t chunk_rows = 0;   // rows per chunk (large K)
   int lse_blocks = 0;       // blocks of the large-K LSE pass
   size_t lds_a = 0, lds_t = 0, lds_c = 0;
-  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
+  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_ext = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
   size_t off_lmx = 0, off_kthr = 0;  // large-K top-k: per-(row, slice) lower-bound maxima, per-row threshold
   size_t off_hv = 0;                 // large-K top-m: rows handed to the heavy rescoring kernel
   size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
@@ -99,7 +99,9 @@ struct LargeKArgs {
   const float* esh;     // (KP, 2) error bound of the expanded score (0: component not sharp)
   float2* P;            // (chunk, S) per-slice (max, sum)
   float* lse;           // (chunk) row log-sum-exp, log2 units
-  double* xsq;          // (chunk) |x|^2 of each row (pass A writes, pass C reads)
+  double* xsq;          // (chunk) |x|^2 of each row (pass A writes, passes B and C read)
+  void* ext;            // (chunk, 8) bf16 per row: 1 and |x|^2 as five bf16 terms, then 0, 0 (pass B
+                        // writes for the statistics MFMA of pass C; null when no pass C runs)
   double* llpart;       // (lse blocks)
   double* part;         // (G, KP, 2 + DP)
   int accumulate;       // add to part / llpart (every chunk after the first)

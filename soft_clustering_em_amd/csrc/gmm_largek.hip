@@ -97,6 +97,7 @@ __device__ __forceinline__ void piece_of(int j, int& r, int& c8) {
 
 struct Piece {
   u16x8 v;
+  u16x8 ext;  // pass C: the statistics features 128..135 of row j (threads j < LT), from pass B
   double xs;  // pass C: |x|^2 of row j (threads j < LT), computed by pass A
   float ls;   // threads j < LT, row j: its LSE (pass C) or its maximum score (pass T)
   int nv;     // dims of v that belong to the row (the rest is zeroed when staged)
@@ -128,9 +129,12 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
   pc.ls = 0.f;
   const int64_t xrow = tile * LT + (j & (LT - 1));  // every wave: the tile's 32 rows (threads j < LT keep theirs)
   if constexpr (STATS) {
-    // pass B padded the LSE with +inf to whole tiles (ntiles * LT rows)
+    // pass B padded the LSE (+inf) and the statistics features to whole
+    // tiles (ntiles * LT rows)
+    const int64_t xpad = xrow < ntiles * LT ? xrow : ntiles * LT - 1;
     pc.xs = A.xsq[xrow < A.N ? xrow : A.N - 1];
-    pc.ls = A.lse[xrow < ntiles * LT ? xrow : ntiles * LT - 1];
+    pc.ls = A.lse[xpad];
+    pc.ext = reinterpret_cast<const u16x8*>(A.ext)[xpad];
   } else if constexpr (PASS == 1) {
     // top-m: the row maximum; top-k: the row's candidate threshold
     pc.ls = (A.topk ? A.kthr : A.mrow)[xrow < A.N ? xrow : A.N - 1];
@@ -159,20 +163,9 @@ __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc
   if constexpr (STATS) {
     if (j < LT) {
       xsq[j] = live ? pc.xs : 0.0;
-      // columns 128.. of the row's slot, the statistics MFMA's features
-      // 128..133: 1 and |x|^2 as five bf16 terms (each remainder exact in
-      // float64; 40 bits, as many as |x|^2 of a bf16 row can need), so N_k and
-      // sum r |x|^2 come out of both magnitude classes like sum r x, and a
-      // component collapsed onto one row gets them exactly
-      u16x8 ext = u16x8{(unsigned short)0x3F80, 0, 0, 0, 0, 0, 0, 0};
-      double q = live ? pc.xs : 0.0;
-#pragma unroll
-      for (int e = 1; e <= 5; ++e) {
-        const __bf16 h = (__bf16)(float)q;
-        ext[e] = __builtin_bit_cast(unsigned short, h);
-        q -= (double)(float)h;
-      }
-      *reinterpret_cast<u16x8*>(rows + tile_slot(j) * LRS + 128) = ext;
+      // columns 128.. of the row's slot: the statistics MFMA's features
+      // 128..133 (1 and |x|^2 in five bf16 terms, formed by pass B)
+      *reinterpret_cast<u16x8*>(rows + tile_slot(j) * LRS + 128) = pc.ext;
     }
   } else if (slice == 0) {
     double sq = 0.0;
@@ -1038,7 +1031,25 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
        row += (int64_t)gridDim.x * blockDim.x) {
     if (row >= A.N) {
       A.lse[row] = INFINITY;
+      if (A.ext) reinterpret_cast<u16x8*>(A.ext)[row] = u16x8{(unsigned short)0x3F80, 0, 0, 0, 0, 0, 0, 0};
       continue;
+    }
+    if (A.ext) {
+      // the statistics features of pass C: 1 and |x|^2 as five bf16 terms,
+      // each the bf16 rounding of the float64 remainder so far (every
+      // remainder exact in float64; 40 bits, as many as |x|^2 of a bf16 row
+      // can need), so that N_k and sum r |x|^2 come out of both magnitude
+      // classes like sum r x, and a component collapsed onto one row gets
+      // them exactly
+      u16x8 ext = u16x8{(unsigned short)0x3F80, 0, 0, 0, 0, 0, 0, 0};
+      double q = A.xsq[row];
+#pragma unroll
+      for (int e = 1; e <= 5; ++e) {
+        const __bf16 h = (__bf16)(float)q;
+        ext[e] = __builtin_bit_cast(unsigned short, h);
+        q -= (double)(float)h;
+      }
+      reinterpret_cast<u16x8*>(A.ext)[row] = ext;
     }
     const float2* P = A.P + (size_t)row * A.S;
     float M = P[0].x;
