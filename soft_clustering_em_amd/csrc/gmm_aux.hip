@@ -461,11 +461,13 @@ __global__ void __launch_bounds__(256) centre_tied_kernel(int D, int K, int KP, 
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,
                              int accumulate, hipStream_t s, const MstepFuse* fuse) {
-  // enough threads that each statistic is summed in segments of about 32
-  // workgroup partials (the loads in flight hide the memory latency), a
-  // multiple of the wave, 256 to 1024
+  // few components (fewer blocks than two per CU): enough threads that each
+  // statistic is summed in segments of about 32 workgroup partials (the
+  // loads in flight hide the memory latency), a multiple of the wave, 256 to
+  // 1024; many components: 256, the blocks themselves fill the chip
   const int64_t want = (int64_t)p.PR * ((p.Gb + 31) / 32);
-  const unsigned threads = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(256, (want + 63) / 64 * 64));
+  const unsigned threads = p.B * p.K >= 512 ? 256u
+                           : (unsigned)std::min<int64_t>(1024, std::max<int64_t>(256, (want + 63) / 64 * 64));
   const size_t lds = sizeof(double) * (size_t)(p.PR + p.D + threads);
   MstepFuse M{};
   if (fuse && p.cov != TIED && !accumulate) M = *fuse;

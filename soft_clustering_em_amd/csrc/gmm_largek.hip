@@ -797,6 +797,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         rv[rb][ks] = *reinterpret_cast<const bf16x8*>(xb + row * A.ld_x + ks * 32 + 8 * (lane >> 4));
     }
   };
+  // slices with and without a sharp component run their own copy of the
+  // row loop, so the common one carries no exact-score code
+  auto rows_loop = [&](auto sharp_c) {
+  constexpr bool SHARP = decltype(sharp_c)::value;
   int64_t t = g + (int64_t)A.G * wv;
   bf16x8 nxt[RB][KSTEP];
   if (t < ntiles) load_rows(t, nxt);
@@ -886,7 +890,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             for (int rb = 0; rb < RB; ++rb)
               acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, rv[rb][ks], acc[rb][nt], 0, 0, 0);
           }
-      if (any_sharp) {
+      if constexpr (SHARP) {
         // sharp components: scores that may come within 60 (log2 units) of the
         // best other score of the row seen so far in the slice, again exactly
 #pragma unroll
@@ -1006,6 +1010,9 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       }
     }
   }
+  };
+  if (any_sharp) rows_loop(std::true_type{});
+  else rows_loop(std::false_type{});
 }
 
 // 16-row blocks per tile of the barrier-free pass A: every weight fragment
