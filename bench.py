@@ -317,6 +317,9 @@ def main():
     ap.add_argument("--workload", default="ivf_bf16",
                     choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--streamed", type=int, default=0, metavar="CHUNK",
+                    help="also time gmm_fit_step_streamed from pinned host rows in chunks of CHUNK rows "
+                         "(the PCIe-inclusive rate; reported under 'streamed', never as the value)")
     ap.add_argument("--no-topm", action="store_true",
                     help="skip the top-m / posting-list / k-means measurements after the fit (counter runs)")
     ap.add_argument("--calib-copy", type=int, default=0,
@@ -497,6 +500,28 @@ def main():
             t_km = e0.elapsed_time(e1) / reps
             res["topm"]["kmeans_step"] = {"ms": t_km, "points_components_per_s": wl.N * wl.K / (t_km * 1e-3),
                                           "inertia_last": float(kin[0].item())}
+    if args.streamed:
+        # the same EM iteration with the rows in pinned host memory, copied in
+        # chunks on a second stream while the previous chunk's E-step runs
+        Xh = torch.empty(X.shape, dtype=X.dtype, pin_memory=True)
+        Xh.copy_(X.cpu())
+        sws = torch.empty(g.gmm_fit_step_streamed_workspace_bytes(Xh, wl.K, wl.cov, args.streamed), dtype=torch.uint8,
+                          device=dev)
+        copy = torch.cuda.Stream()
+        for t_, a_ in ((w, wl.w0), (mu, wl.mu0), (cv, wl.cv0)):
+            t_.copy_(torch.from_numpy(a_))
+        g.gmm_fit_step_streamed(Xh, w, mu, cv, wl.cov, args.streamed, reg_covar=wl.eps, ws=sws, copy_stream=copy)
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.gmm_fit_step_streamed(Xh, w, mu, cv, wl.cov, args.streamed, reg_covar=wl.eps, ws=sws, copy_stream=copy)
+        torch.cuda.synchronize()
+        t_s = (time.perf_counter() - t0) / reps
+        hbytes = Xh.numel() * Xh.element_size()
+        res["streamed"] = {"chunk_rows": args.streamed, "ms_per_step": t_s * 1e3, "points_components_per_s": pairs / t_s,
+                           "host_GBs": hbytes / t_s / 1e9, "device_workspace_bytes": sws.numel(),
+                           "rows_bytes": hbytes}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
