@@ -1223,7 +1223,7 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
 // wave-wide best.  The LSE adds pass T's below-band mass.  Rank 1 is always
 // kept, ranks 2..m while r >= thr.  Every step runs in a fixed order.
 constexpr int kTopmMaxM = 16;
-constexpr int kBatch = 512;                       // scores per batch
+constexpr int kBatch = 256;                       // scores per batch
 constexpr int kSlots = kTopmMaxM + kBatch;        // running best m, then the batch
 constexpr int kPer = (kSlots + 63) / 64;          // slots per lane in the selection
 constexpr int kMaskSlots = kLargeKMaxK / 32 / 64;  // mask words per lane at the largest K
@@ -1312,10 +1312,10 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 16 candidates per step (four per 16-lane group), their loads issued
+    // 8 candidates per step (two per 16-lane group), their loads issued
     // together (indices past the batch repeat its last entry; lanes past D
     // read inside the row and hold x = 0)
-    constexpr int U = 4;
+    constexpr int U = 2;
     for (int i0 = 0; i0 < nb; i0 += 4 * U) {
       int ku[U];
 #pragma unroll
@@ -1452,7 +1452,7 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
 // A group counts its row's candidates (16-lane scan of the mask words'
 // popcounts); a row with at most kLight of them is scored by the group alone
 // (each candidate's 128-term float64 dot product split over the 16 lanes,
-// four candidates' loads in flight), its best m picked by m rounds of a
+// two candidates' loads in flight), its best m picked by m rounds of a
 // 16-lane best, LSE and outputs as in topm_row_wave.  Four independent rows per wave keep four chains of
 // dependent loads in flight where one row per wave kept one.
 constexpr int kLight = 32;
@@ -1521,7 +1521,7 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
       sc[t] = -INFINITY;
       kc[t] = 0x7fffffff;
     }
-    constexpr int U = 4;
+    constexpr int U = 2;
     for (int c0 = 0; c0 < total; c0 += U) {
       int ku[U];
       double2 cu[U];
@@ -1631,7 +1631,10 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
 
 // Rows flagged by largek_topm_final4_kernel, a whole wave each: waves stride
 // over the flag bytes (one per four rows).
-__global__ void __launch_bounds__(64) largek_topm_heavy_kernel(LargeKArgs A, int64_t nflags) {
+// Four waves per SIMD (registers capped at 128; a few spill): the rows are
+// chains of dependent loads, and more of them in flight beat the spills
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4)))
+largek_topm_heavy_kernel(LargeKArgs A, int64_t nflags) {
   __shared__ double sl[kSlots];
   __shared__ int skk[kSlots];
   __shared__ unsigned short slist[kBatch];
@@ -1707,7 +1710,7 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     const int64_t nflags = (ac.N + 3) / 4;
     hipLaunchKernelGGL(largek_topm_final4_kernel, dim3((unsigned)nflags), dim3(64), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(largek_topm_heavy_kernel, dim3((unsigned)std::min<int64_t>(nflags, 4096)), dim3(64), 0, s, ac,
+    hipLaunchKernelGGL(largek_topm_heavy_kernel, dim3((unsigned)std::min<int64_t>(nflags, 16384)), dim3(64), 0, s, ac,
                        nflags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
