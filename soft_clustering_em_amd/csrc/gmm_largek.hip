@@ -777,6 +777,31 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   // gives contains every component's own band, a superset that the exact
   // rescoring sorts out
   float eam = 0.f, ea0m = 0.f;
+  // pass T of the top-m: the largest error bound over every component; the
+  // row maximum may come from one-term logits (MODE 2), whose error is at most
+  // 17 times the two-term bound (bf16 rounding of the weight, 2^-9 relative,
+  // against 2^-14 for hi + lo and the float32 sums), and the band widens by it
+  float egm = 0.f, eg0m = 0.f;
+  if constexpr (MODE == 1) {
+    // the waves' maxima meet in the candidate-word area, before its first use
+    float* egred = reinterpret_cast<float*>(cst + NCST * KSA);
+    for (int i = threadIdx.x; i < A.K; i += blockDim.x) {
+      egm = fmaxf(egm, A.eall[2 * i]);
+      eg0m = fmaxf(eg0m, A.eall[2 * i + 1]);
+    }
+    egm = (float)wave_max((double)egm);
+    eg0m = (float)wave_max((double)eg0m);
+    if (lane == 0) {
+      egred[wv] = egm;
+      egred[LNW + wv] = eg0m;
+    }
+    __syncthreads();
+    for (int w2 = 0; w2 < LNW; ++w2) {
+      egm = fmaxf(egm, egred[w2]);
+      eg0m = fmaxf(eg0m, egred[LNW + w2]);
+    }
+    __syncthreads();
+  }
   if constexpr (MARK) {
     for (int i = lane; i < KSA; i += 64) {
       eam = fmaxf(eam, cst[4 * KSA + i]);
@@ -801,6 +826,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   // row loop, so the common one carries no exact-score code
   auto rows_loop = [&](auto sharp_c) {
   constexpr bool SHARP = decltype(sharp_c)::value;
+  // weight terms per logit: the top-m's row maxima (MODE 2) take the hi term
+  // alone where no sharp component needs its exact score (pass T widens its
+  // band by that error); everything else takes hi + lo
+  constexpr int NHT = (MODE == 2 && !SHARP) ? 1 : 2;
   int64_t t = g + (int64_t)A.G * wv;
   bf16x8 nxt[RB][KSTEP];
   if (t < ntiles) load_rows(t, nxt);
@@ -863,7 +892,8 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         if constexpr (MODE == 4)
           thr[rb] = live[rb] ? A.kthr[row] : INFINITY;  // a lower bound of the row's top-k-th score
         else
-          thr[rb] = live[rb] ? mr[rb] - kTopmBand - 2.f * fmaf(eam, xs[rb], ea0m) : INFINITY;
+          thr[rb] = live[rb] ? mr[rb] - kTopmBand - 2.f * fmaf(eam, xs[rb], ea0m) - 17.f * fmaf(egm, xs[rb], eg0m)
+                             : INFINITY;
       }
     }
 #pragma unroll 1
@@ -882,7 +912,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NHT; ++h)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             const bf16x8 bw = Wl[(((cc * 2 + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
