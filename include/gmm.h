@@ -167,6 +167,21 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
                         double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* n_iter EM iterations in one call (Flash-GMM Section 2, the EM iteration
+ * repeated), with the same results, bit for bit, as n_iter calls of
+ * gmm_fit_step on this workspace.  Spherical, diagonal and full components:
+ * after the first iteration the prologue (the log-score weights and
+ * constants) is not launched; each iteration's M-step, in the reduction's
+ * component blocks, forms it for the next one right after the parameters
+ * (one launch fewer per iteration).  Tied components and the large-K path
+ * run n_iter fit steps.  n_iter >= 1.  mean_loglik: (n_iter, B) float64
+ * device, nullable; row t is the mean log-likelihood of the parameters that
+ * entered iteration t.  comp_status (B,K) nullable: the last iteration's
+ * flags.  The workspace is gmm_fit_step's (GMM_OP_FIT).  opts->event_begin /
+ * event_end, when set, bracket the last iteration's E-step. */
+gmm_status gmm_fit(const gmm_data* data, gmm_params* inout, const gmm_options* opts, int32_t n_iter,
+                   double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes, void* stream);
+
 /* One EM iteration exactly as gmm_fit_step (same kernels, same results), for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  It takes no

@@ -8,6 +8,7 @@ torch stream; every step of the computation runs in the HIP kernels.
   gmm_estep_stats(X, w, mu, cv, stats, accumulate=False, ws=None)
   gmm_mstep(stats, n_total, w, mu, cv, reg_covar=1e-6, comp_status=None)
   gmm_fit_step(X, w, mu, cv, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
+  gmm_fit(X, w, mu, cv, cov, n_iter, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None)
   gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None)
   gmm_fit_step_streamed(X_host, w, mu, cv, cov, chunk_rows, reg_covar=1e-6, mean_loglik=None,
                         comp_status=None, ws=None, copy_stream=None)   (rows stay in host memory)
@@ -148,6 +149,28 @@ def gmm_fit_step(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_statu
     ws = _workspace(X, p.K, cov, OP_FIT, 0, ws)
     _abi.check(_abi.lib().gmm_fit_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o), _ptr(mean_loglik),
                                        _ptr(comp_status), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gmm_fit(X, w, mu, cv, cov, n_iter, reg_covar=1e-6, mean_loglik=None, comp_status=None, ws=None, stream=None,
+            events=None):
+    """n_iter EM iterations in place, the results of n_iter gmm_fit_step calls.
+    mean_loglik: optional (n_iter, B) float64 device tensor, row t the mean
+    log-likelihood entering iteration t.  events: optional (begin, end) pair
+    recorded around the last iteration's E-step."""
+    d = _data(X)
+    p = _params(w, mu, cv, cov)
+    if mean_loglik is not None:
+        import torch
+        if (mean_loglik.dtype != torch.float64 or not mean_loglik.is_cuda or not mean_loglik.is_contiguous()
+                or mean_loglik.numel() < int(n_iter) * int(d.B)):
+            raise ValueError("mean_loglik must be a contiguous float64 device tensor of n_iter * B elements")
+    eb = ee = None
+    if events is not None:
+        eb, ee = (ctypes.c_void_p(e.cuda_event) for e in events)
+    o = GmmOptions(float(reg_covar), 0, eb, ee)
+    ws = _workspace(X, p.K, cov, OP_FIT, 0, ws)
+    _abi.check(_abi.lib().gmm_fit(ctypes.byref(d), ctypes.byref(p), ctypes.byref(o), int(n_iter),
+                                  _ptr(mean_loglik), _ptr(comp_status), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gmm_fit_step_noalloc(X, w, mu, cv, cov, reg_covar=1e-6, mean_loglik=None, comp_status=None, stream=None):

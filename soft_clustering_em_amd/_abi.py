@@ -19,7 +19,7 @@ DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 OP_FIT, OP_ESTEP, OP_TOPM = 0, 1, 2
 GMM_OK, GMM_ERR_INVALID_ARG, GMM_ERR_UNSUPPORTED, GMM_ERR_WORKSPACE, GMM_ERR_HIP, GMM_ERR_NOT_PD = 0, 1, 2, 3, 4, 5
 
-EXPORTED = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step", "gmm_fit_step_noalloc",
+EXPORTED = ["gmm_workspace_bytes", "gmm_estep_stats", "gmm_mstep", "gmm_fit_step", "gmm_fit", "gmm_fit_step_noalloc",
             "gmm_fit_step_streamed_workspace_bytes", "gmm_fit_step_streamed",
             "gmm_predict_proba_topm", "gmm_ivf_workspace_bytes", "gmm_ivf_lists", "gmm_kmeans_workspace_bytes",
             "gmm_kmeans_step", "gmm_fisher_vector_workspace_bytes", "gmm_fisher_vector",
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(GmmParams), ctypes.POINTER(GmmOptions), P, P]
         L.gmm_fit_step.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams),
                                    ctypes.POINTER(GmmOptions), P, P, P, ctypes.c_size_t, P]
+        L.gmm_fit.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams), ctypes.POINTER(GmmOptions),
+                              ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.gmm_fit_step_noalloc.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams),
                                            ctypes.POINTER(GmmOptions), P, P, P]
         L.gmm_fit_step_streamed_workspace_bytes.argtypes = [ctypes.POINTER(GmmData), ctypes.c_int32,
@@ -107,7 +109,7 @@ def lib() -> ctypes.CDLL:
         L.gmm_topk_fit_workspace_bytes.restype = ctypes.c_size_t
         L.gmm_topk_fit_step.argtypes = [ctypes.POINTER(GmmData), ctypes.POINTER(GmmParams), ctypes.c_int32,
                                         ctypes.POINTER(GmmOptions), P, P, P, ctypes.c_size_t, P]
-        for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_fit_step_noalloc, L.gmm_fit_step_streamed,
+        for f in (L.gmm_estep_stats, L.gmm_mstep, L.gmm_fit_step, L.gmm_fit, L.gmm_fit_step_noalloc, L.gmm_fit_step_streamed,
                   L.gmm_predict_proba_topm,
                   L.gmm_ivf_lists,
                   L.gmm_kmeans_step, L.gmm_fisher_vector, L.gmm_topk_fit_step, L.gmm_kde_score):

@@ -373,10 +373,11 @@ static gmm_status run_estep_largek(const Plan& p, const gmm_data* d, const gmm_p
 }
 
 // fuse (nullable): the M-step of gmm_fit_step, run by the reduction's
-// component blocks (spherical, diag, full)
+// component blocks (spherical, diag, full).  skip_prologue: the workspace
+// already holds this step's prologue (formed by the previous step's M-step).
 static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* prm, void* ws, double* nk, double* sx,
                             double* sxx, double* ll, double* mean_ll, int accumulate, const gmm_options* opts,
-                            hipStream_t s, const MstepFuse* fuse = nullptr) {
+                            hipStream_t s, const MstepFuse* fuse = nullptr, bool skip_prologue = false) {
   if (p.largek) return run_estep_largek(p, d, prm, ws, nk, sx, sxx, ll, mean_ll, accumulate, opts, s, fuse);
   char* w = static_cast<char*>(ws);
   float* W = reinterpret_cast<float*>(w + p.off_W);
@@ -389,8 +390,11 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   double* part = reinterpret_cast<double*>(w + p.off_part);
   double* llp = reinterpret_cast<double*>(w + p.off_llp);
   double* raw = reinterpret_cast<double*>(w + p.off_aux);
-  hipError_t e = launch_prologue(p, prm->weights, prm->means, prm->covars, nullptr, W, prec, c0, c, a, flag, sharp, s);
-  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  hipError_t e = hipSuccess;
+  if (!skip_prologue) {
+    e = launch_prologue(p, prm->weights, prm->means, prm->covars, nullptr, W, prec, c0, c, a, flag, sharp, s);
+    if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  }
   EStepArgs A;
   A.x = d->x;
   A.xtype = p.dtype;
@@ -558,8 +562,12 @@ static gmm_status fit_step_check(const gmm_data* data, const gmm_params* inout, 
 }
 
 // The launches of one EM iteration on a checked plan and workspace.
+// skip_prologue / prepare_next (fused path, spherical, diag, full only): the
+// workspace holds this step's prologue already / the M-step forms the next
+// step's.
 static gmm_status fit_step_run(const Plan& p, const gmm_data* data, gmm_params* inout, const gmm_options* opts,
-                               double* mean_loglik, int32_t* comp_status, void* ws, void* stream) {
+                               double* mean_loglik, int32_t* comp_status, void* ws, void* stream,
+                               bool skip_prologue = false, bool prepare_next = false) {
   gmm_status st;
   const double reg = opts ? opts->reg_covar : 1e-6;
   char* w = static_cast<char*>(ws);
@@ -571,8 +579,15 @@ static gmm_status fit_step_run(const Plan& p, const gmm_data* data, gmm_params* 
   const int32_t* flag = p.largek ? nullptr : reinterpret_cast<const int32_t*>(w + p.off_flag);
   // spherical, diag, full: the M-step runs in the reduction's component blocks
   const bool fused = p.cov != TIED;
-  const MstepFuse fuse{inout->weights, inout->means, inout->covars, p.N, reg, flag, p.KP, comp_status};
-  st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s, fused ? &fuse : nullptr);
+  MstepFuse fuse{inout->weights, inout->means, inout->covars, p.N, reg, flag, p.KP, comp_status, PrologueOut{}};
+  if (prepare_next && fused && !p.largek)
+    fuse.next = PrologueOut{p.DP, p.F, p.KW, p.KP, p.prec_stride,
+                            reinterpret_cast<float*>(w + p.off_W), reinterpret_cast<double*>(w + p.off_prec),
+                            reinterpret_cast<double*>(w + p.off_c0), reinterpret_cast<double*>(w + p.off_c),
+                            reinterpret_cast<double*>(w + p.off_a), reinterpret_cast<int32_t*>(w + p.off_flag),
+                            reinterpret_cast<int32_t*>(w + p.off_sharp)};
+  st = run_estep(p, data, inout, ws, nk, sx, sxx, ll, mean_loglik, 0, opts, s, fused ? &fuse : nullptr,
+                 skip_prologue && fused && !p.largek);
   if (st != GMM_OK || fused) return st;
   hipError_t e = launch_mstep_strided(p.cov, p.B, p.D, p.K, nk, sx, sxx, p.N, inout->weights, inout->means,
                                       inout->covars, reg, flag, p.KP, comp_status, s);
@@ -589,6 +604,26 @@ gmm_status gmm_fit_step(const gmm_data* data, gmm_params* inout, const gmm_optio
   st = check_ws(p, ws, ws_bytes);
   if (st != GMM_OK) return st;
   return fit_step_run(p, data, inout, opts, mean_loglik, comp_status, ws, stream);
+}
+
+gmm_status gmm_fit(const gmm_data* data, gmm_params* inout, const gmm_options* opts, int32_t n_iter,
+                   double* mean_loglik, int32_t* comp_status, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (n_iter < 1) return fail(GMM_ERR_INVALID_ARG, "n_iter must be >= 1");
+  Plan p;
+  gmm_status st = fit_step_check(data, inout, opts, &p);
+  if (st != GMM_OK) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != GMM_OK) return st;
+  // the next step's prologue is formed in the M-step's blocks where the
+  // M-step runs there (spherical, diag, full on the fused path)
+  const bool fold = !p.largek && p.cov != TIED;
+  for (int32_t t = 0; t < n_iter; ++t) {
+    st = fit_step_run(p, data, inout, opts, mean_loglik ? mean_loglik + (size_t)t * p.B : nullptr, comp_status, ws,
+                      stream, fold && t > 0, fold && t + 1 < n_iter);
+    if (st != GMM_OK) return st;
+  }
+  return GMM_OK;
 }
 
 gmm_status gmm_fit_step_noalloc(const gmm_data* data, gmm_params* inout, const gmm_options* opts,

@@ -87,16 +87,19 @@ __device__ __forceinline__ double wave_max64(double v) {
 }
 
 // ------------------------------------------------------------------ prologue
-// grid: B*KP blocks of 64 threads; block (b, k).
-__global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int KP, int DP, int F, int KW,
-                                                      const float* __restrict__ w, const float* __restrict__ mu,
-                                                      const float* __restrict__ cv, float2* __restrict__ err,
-                                                      float* __restrict__ W,
-                                                      double* __restrict__ prec, int prec_stride,
-                                                      double* __restrict__ c0, double* __restrict__ c,
-                                                      double* __restrict__ a, int32_t* __restrict__ flag,
-                                                      int32_t* __restrict__ sharp) {
-  const int b = blockIdx.x / KP, k = blockIdx.x % KP, tid = threadIdx.x;
+// Component (b, k) by the threads of one block (any multiple of 64; every
+// thread calls it, it holds barriers).  Its sums run on the first wave in a
+// fixed lane order, so the values do not depend on the block size: the
+// prologue kernel (64 threads) and the reduction's M-step blocks (which form
+// the next iteration's prologue in gmm_fit) write the same bits.
+__device__ __forceinline__ void prologue_component(int cov, int D, int K, int KP, int DP, int F, int KW, int b, int k,
+                                   const float* __restrict__ w, const float* __restrict__ mu,
+                                   const float* __restrict__ cv, float2* __restrict__ err, float* __restrict__ W,
+                                   double* __restrict__ prec, int prec_stride, double* __restrict__ c0,
+                                   double* __restrict__ c, double* __restrict__ a, int32_t* __restrict__ flag,
+                                   int32_t* __restrict__ sharp) {
+  const int tid = threadIdx.x;
+  const bool w0 = tid < 64;  // the reductions run on the block's first wave
   float* Wb = W + (size_t)b * KP * F;
   double* precb = prec + ((size_t)b * KP + k) * prec_stride;
   __shared__ double sm_mu[128];
@@ -129,7 +132,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     // per-dimension terms on the block's threads (one log per variance;
     // spherical: one log in all), then fixed-order wave sums
     double logdet = 0.0, quad = 0.0, scale = 0.0, lmax = 0.0, l1 = 0.0, bad = 0.0;
-    for (int d = tid; d < D; d += blockDim.x) {
+    for (int d = tid; w0 && d < D; d += 64) {
       const double v = (cov == SPH) ? (double)cv[(size_t)b * K + k] : (double)cv[((size_t)b * K + k) * D + d];
       if (!(v > 0.0) || isinf(v)) bad = 1.0;
       if (cov == DIAG) logdet += log(v);
@@ -138,12 +141,14 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       scale += sm_mu[d] * sm_mu[d] + v;
       l1 += (sm_v[d] * sm_mu[d]) * (sm_v[d] * sm_mu[d]);
     }
-    logdet = wave_sum64(logdet);
-    quad = wave_sum64(quad);
-    scale = wave_sum64(scale);
-    lmax = wave_max64(lmax);
-    l1 = wave_sum64(l1);
-    bad = wave_max64(bad);
+    if (w0) {
+      logdet = wave_sum64(logdet);
+      quad = wave_sum64(quad);
+      scale = wave_sum64(scale);
+      lmax = wave_max64(lmax);
+      l1 = wave_sum64(l1);
+      bad = wave_max64(bad);
+    }
     if (tid == 0) {
       const bool ok = bad == 0.0;
       // spherical: the lambda |x|^2 term is added in float64, only x . (lambda mu)
@@ -225,7 +230,7 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
     // spread; sum over d <= e of |x_d x_e W_de| = |x|^T |P| |x| / 2 <=
     // ||P||_F |x|^2 / 2 bounds the quadratic terms
     double s4 = 0.0, pf = 0.0;
-    for (int i = tid; i < 256; i += blockDim.x) {
+    for (int i = tid; w0 && i < 256; i += 64) {
       const int d = i / 16, e = i % 16;
       double s = 0.0;
       for (int p = 0; p < D; ++p) s += sm_P[d * 16 + p] * sm_P[p * 16 + e];
@@ -243,12 +248,14 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       scale = sm_mu[d] * sm_mu[d] + sm_S[d * D + d];
       l1 = v * v;
     }
-    s4 = wave_sum64(s4);
-    pf = wave_sum64(pf);
-    logdet = wave_sum64(logdet);
-    quad = wave_sum64(quad);
-    scale = wave_sum64(scale);
-    l1 = wave_sum64(l1);
+    if (w0) {
+      s4 = wave_sum64(s4);
+      pf = wave_sum64(pf);
+      logdet = wave_sum64(logdet);
+      quad = wave_sum64(quad);
+      scale = wave_sum64(scale);
+      l1 = wave_sum64(l1);
+    }
     if (tid == 0) {
       const double lmax = sqrt(sqrt(s4));
       if (err)
@@ -287,6 +294,19 @@ __global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int
       if (err) err[(size_t)b * KP + k] = float2{0.f, 0.f};
     }
   }
+}
+
+// grid: B*KP blocks of 64 threads; block (b, k).
+__global__ void __launch_bounds__(64) prologue_kernel(int cov, int D, int K, int KP, int DP, int F, int KW,
+                                                      const float* __restrict__ w, const float* __restrict__ mu,
+                                                      const float* __restrict__ cv, float2* __restrict__ err,
+                                                      float* __restrict__ W,
+                                                      double* __restrict__ prec, int prec_stride,
+                                                      double* __restrict__ c0, double* __restrict__ c,
+                                                      double* __restrict__ a, int32_t* __restrict__ flag,
+                                                      int32_t* __restrict__ sharp) {
+  prologue_component(cov, D, K, KP, DP, F, KW, blockIdx.x / KP, blockIdx.x % KP, w, mu, cv, err, W, prec,
+                     prec_stride, c0, c, a, flag, sharp);
 }
 
 hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const float* cv, float2* err, float* W,
@@ -424,6 +444,14 @@ __global__ void __launch_bounds__(1024) reduce_kernel(int cov, int D, int K, int
     __syncthreads();
     mstep_component(cov, D, b, K, k, nk, sx, sxx, M.n_total, M.w, M.mu, M.cv, M.reg, M.in_flag, M.in_flag_stride,
                     M.comp_status, m, sm_S, sm_L);
+    if (M.next.W) {
+      // the next iteration's prologue of this component, from the parameters
+      // just written (visible to the block after the barrier)
+      __syncthreads();
+      const PrologueOut& P = M.next;
+      prologue_component(cov, D, K, P.KP, P.DP, P.F, P.KW, b, k, M.w, M.mu, M.cv, nullptr, P.W, P.prec,
+                         P.prec_stride, P.c0, P.c, P.a, P.flag, P.sharp);
+    }
   }
 }
 

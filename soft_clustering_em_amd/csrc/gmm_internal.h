@@ -260,6 +260,19 @@ hipError_t launch_prologue(const Plan& p, const float* w, const float* mu, const
 hipError_t launch_mean_ll(int64_t B, const double* ll, int64_t n_total, double* mean_ll, hipStream_t s);
 // The M-step fused into the statistics reduction (spherical, diag, full;
 // not when accumulating): w == nullptr means no M-step.
+// The prologue outputs of a fit step's workspace (log-score weights and
+// constants), for an M-step that forms the next iteration's prologue right
+// after the parameters (W null: it does not).
+struct PrologueOut {
+  int DP, F, KW, KP, prec_stride;
+  float* W;
+  double* prec;
+  double* c0;
+  double* c;
+  double* a;
+  int32_t* flag;
+  int32_t* sharp;
+};
 struct MstepFuse {
   float* w;
   float* mu;
@@ -269,6 +282,7 @@ struct MstepFuse {
   const int32_t* in_flag;
   int in_flag_stride;
   int32_t* comp_status;
+  PrologueOut next;
 };
 hipError_t launch_reduce_raw(const Plan& p, const double* part, const double* llpart, const float* mu,
                              double* raw, double* nk, double* sx, double* sxx, double* ll, double* mean_ll,

@@ -29,7 +29,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (gmm_estep_stats, gmm_fit_step, gmm_kde_score, gmm_kmeans_step, gmm_predict_proba_topm,
+from . import (gmm_estep_stats, gmm_fit, gmm_fit_step, gmm_kde_score, gmm_kmeans_step, gmm_predict_proba_topm,
                gmm_topk_fit_step, gmm_topk_fit_workspace_bytes, new_stats)
 
 
@@ -137,11 +137,16 @@ def random_init(X, K, cov, generator):
     return w, mu, cv
 
 
-def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=None, topk=None):
+def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=None, topk=None, check_every=1):
     """EM from n_init starts (random_init with a seeded generator, or the
     given init = (w, mu, cv) for the first start); each runs until the change
     of the problem-averaged mean log-likelihood falls below tol or n_iter
     iterations.  Keeps the start whose last mean log-likelihood is highest.
+    check_every: iterations per gmm_fit call between two reads of the
+    log-likelihoods on the host (1: the test after every iteration, as above;
+    c > 1: one synchronisation per c iterations, and up to c - 1 iterations
+    past the one where the test first holds, which EM only improves; the
+    history and n_iter still end at that iteration).
     topk: run approximate top-k EM steps instead (each row keeps its topk best
     components; spherical and diagonal covariance); the history then holds
     the top-k steps' log-likelihoods, the final score the full mixture's."""
@@ -159,19 +164,36 @@ def fit(X, K, cov, n_iter=100, tol=1e-3, n_init=1, reg_covar=1e-6, seed=0, init=
             w, mu, cv = (t.clone().contiguous() for t in init)
         else:
             w, mu, cv = random_init(X, K, cov, gen)
-        mll = torch.zeros(B, dtype=torch.float64, device=X.device)
         hist, prev, converged, it = [], None, False, 0
-        for it in range(1, n_iter + 1):
-            if topk is None:
-                gmm_fit_step(X, w, mu, cv, cov, reg_covar=reg_covar, mean_loglik=mll)
-            else:
-                gmm_topk_fit_step(X, w, mu, cv, cov, int(topk), reg_covar=reg_covar, mean_loglik=mll, ws=tws)
-            cur = float(mll.mean().item())  # the LL of the parameters that entered this step
-            hist.append(cur)
-            if prev is not None and abs(cur - prev) < tol:
-                converged = True
-                break
-            prev = cur
+        if topk is None and check_every > 1:
+            # blocks of check_every iterations in one call each, their
+            # log-likelihoods read once per block
+            mlls = torch.zeros((int(check_every), B), dtype=torch.float64, device=X.device)
+            done = 0
+            while done < n_iter and not converged:
+                c = min(int(check_every), n_iter - done)
+                gmm_fit(X, w, mu, cv, cov, c, reg_covar=reg_covar, mean_loglik=mlls)
+                for cur in mlls[:c].mean(dim=1).tolist():  # the LL entering each iteration
+                    it += 1
+                    hist.append(cur)
+                    if prev is not None and abs(cur - prev) < tol:
+                        converged = True
+                        break
+                    prev = cur
+                done += c
+        else:
+            mll = torch.zeros(B, dtype=torch.float64, device=X.device)
+            for it in range(1, n_iter + 1):
+                if topk is None:
+                    gmm_fit_step(X, w, mu, cv, cov, reg_covar=reg_covar, mean_loglik=mll)
+                else:
+                    gmm_topk_fit_step(X, w, mu, cv, cov, int(topk), reg_covar=reg_covar, mean_loglik=mll, ws=tws)
+                cur = float(mll.mean().item())  # the LL of the parameters that entered this step
+                hist.append(cur)
+                if prev is not None and abs(cur - prev) < tol:
+                    converged = True
+                    break
+                prev = cur
         history.append(hist)
         final = score(X, w, mu, cv, cov)
         if best is None or final.mean() > best.mean_ll.mean():
@@ -192,13 +214,14 @@ class GaussianMixture:
 
     def __init__(self, n_components, covariance_type="full", max_iter=100, tol=1e-3, reg_covar=1e-6, n_init=1,
                  random_state=0, weights_init=None, means_init=None, covariances_init=None, init_params="random",
-                 topk=None):
+                 topk=None, check_every=1):
         if covariance_type not in ("spherical", "diag", "tied", "full"):
             raise ValueError(f"unknown covariance_type {covariance_type!r}")
         if init_params not in ("random", "kmeans"):
             raise ValueError(f"unknown init_params {init_params!r}")
         self.init_params = init_params
         self.topk = None if topk is None else int(topk)
+        self.check_every = max(1, int(check_every))  # iterations per host read of the log-likelihood
         self.n_components = int(n_components)
         self.covariance_type = covariance_type
         self.max_iter = int(max_iter)
@@ -234,7 +257,7 @@ class GaussianMixture:
             raise ValueError("X is (N, D)")
         res = fit(X, self.n_components, self.covariance_type, n_iter=self.max_iter, tol=self.tol,
                   n_init=self.n_init, reg_covar=self.reg_covar, seed=self.random_state or 0, init=self._init(X),
-                  topk=self.topk)
+                  topk=self.topk, check_every=self.check_every)
         self.weights_, self.means_, self.covariances_ = res.weights, res.means, res.covars
         self.lower_bound_ = float(res.mean_ll[0])
         self.lower_bound_history_ = list(res.history[res.restart])

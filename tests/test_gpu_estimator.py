@@ -81,6 +81,29 @@ def test_fit_keeps_the_best_restart_and_ascends(torch_cuda):
     assert len(res.history) == 3 and res.n_iter == 15
 
 
+def test_fit_in_blocks_matches_fit_per_iteration(torch_cuda):
+    """check_every = 4 (gmm_fit blocks, one host read per block) gives the
+    same history up to the converged iteration, and parameters that are the
+    per-iteration fit's after the block's extra iterations (checked against
+    gmm_fit_step from the same init, bit for bit)."""
+    import soft_clustering_em_amd as g
+    from soft_clustering_em_amd import estimator as est
+    from soft_clustering_em_amd import synth
+    torch = torch_cuda
+    wl = synth.spherical_small()
+    X = torch.from_numpy(wl.X[0]).cuda()
+    init = tuple(torch.from_numpy(np.ascontiguousarray(a[0])).cuda() for a in (wl.w0, wl.mu0, wl.cv0))
+    one = est.fit(X, wl.K, "spherical", n_iter=30, tol=1e-4, n_init=1, init=init)
+    blk = est.fit(X, wl.K, "spherical", n_iter=30, tol=1e-4, n_init=1, init=init, check_every=4)
+    assert blk.history[0] == one.history[0] and blk.n_iter == one.n_iter and blk.converged == one.converged
+    ran = min(-(-blk.n_iter // 4) * 4, 30) if blk.converged else 30  # iterations the blocks ran
+    w, mu, cv = (t.clone() for t in init)
+    for _ in range(ran):
+        g.gmm_fit_step(X, w, mu, cv, "spherical", reg_covar=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(w, blk.weights) and torch.equal(mu, blk.means) and torch.equal(cv, blk.covars)
+
+
 def test_fit_from_given_init_follows_the_oracle(torch_cuda):
     """fit() from an explicit init runs the same steps as the oracle from
     that init (first three iterations, one-step parity at 1e-4)."""
