@@ -67,6 +67,28 @@ __device__ __forceinline__ uint32_t rows4_or(uint32_t v) {
   return b[0] | b[1];
 }
 
+// all-reduce across the two 32-lane halves of a wave (lanes l, l ^ 32): given
+// the same value twice, v_permlane32_swap returns the two halves
+__device__ __forceinline__ float halves_max(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint32_t halves_or(uint32_t v) {
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] | b[1];
+}
+__device__ __forceinline__ double halves_sum_f64(double v) {
+  const unsigned long long w = (unsigned long long)__double_as_longlong(v);
+  auto lo = __builtin_amdgcn_permlane32_swap((unsigned)w, (unsigned)w, false, false);
+  auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(w >> 32), (unsigned)(w >> 32), false, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0])) +
+         __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+}
+
 __device__ __forceinline__ double rows4_sum_f64(double v) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(v);
   auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);

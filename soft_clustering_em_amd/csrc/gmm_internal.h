@@ -47,7 +47,7 @@ struct Plan {
   int64_t chunk_rows = 0;   // rows per chunk (large K)
   int lse_blocks = 0;       // blocks of the large-K LSE pass
   size_t lds_a = 0, lds_t = 0, lds_c = 0;
-  size_t off_P = 0, off_lse = 0, off_xsq = 0, off_ext = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
+  size_t off_W32 = 0, off_P = 0, off_lse = 0, off_xsq = 0, off_ext = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
   size_t off_lmx = 0, off_kthr = 0;  // large-K top-k: per-(row, slice) lower-bound maxima, per-row threshold
   size_t off_hv = 0;                 // large-K top-m: rows handed to the heavy rescoring kernel
   size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
@@ -91,6 +91,7 @@ struct LargeKArgs {
   int vec16;            // rows can be read with 16-byte loads
   int K, KP, S, G;      // S slices of kLargeKSlice components; G row groups of the launch
   const void* W;        // (KP/16, 2, DP/32, 64, 8) bf16 weights, hi and lo parts, fragment order
+  const void* W32;      // (KP/32, 2, DP/16, 64, 8) the same weights in the operand order of the 32x32 MFMA
   const double* c;      // (KP)
   const double* a;      // (KP)
   const float* mu;      // (K, D) means, for the exact scores of sharp components

@@ -49,6 +49,7 @@ namespace gmm {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -719,28 +720,32 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // aligned): the slice's weights and constants go to LDS once; then each wave
 // streams its own row tiles (tile g + G (8 i + w) for wave w), reading a tile's
 // rows from memory straight into registers as the B operand of the transposed
-// logit MFMA (lane l: rows l % 16 (+16), dims 8 (l / 16) .. +7 of each 32-dim
-// step), the next tile's loads in flight while it works.  It covers all 256
-// components of the slice in 32-component chunks with a running per-row max
-// and a per-lane running sum rescaled to it, so a row's (max, sum) for the
-// slice needs no other wave and the waves never wait for each other.
-// MODE 0: per-row maximum and sum of 2^(l - max) over the slice (pass A of a
-// fit step); 1: candidate marks and below-band mass against the row maximum
-// (pass T of the top-m); 2: the maximum alone (pass A of the top-m, whose
-// last kernel needs only the row maxima and pass T's masses)
+// logit MFMA, v_mfma_f32_32x32x16_bf16 (lane l: row l % 32 of each 32-row
+// block, dims 16 s + 8 (l / 32) .. +7 of 16-dim step s), the next tile's loads
+// in flight while it works.  The 32x32 shape sustains about twice the rate of
+// the 16x16x32 one on gfx950, and its accumulator gives each lane 16 of a
+// 32-component chunk's scores of one row (components 8 (v / 4) + 4 (l / 32) +
+// v % 4), so a row's max and sum over the chunk are an in-lane fold and one
+// swap of the wave's halves.  It covers all 256 components of the slice in
+// 32-component chunks with a running per-row max and a per-lane running sum
+// rescaled to it, so a row's (max, sum) for the slice needs no other wave and
+// the waves never wait for each other.
 // MODE: 0 = pass A of the fit (slice max and sum), 1 = pass T of the top-m
-// (candidate masks), 2 = pass A of the top-m (slice max), 3 = pass A of the
-// top-k (slice max, and per lane group the maximum of score - error bound),
-// 4 = pass T of the top-k (candidates against the row's top-k threshold).
+// (candidate masks and below-band mass against the row maximum), 2 = pass A of
+// the top-m (slice max: its last kernel needs only the row maxima and pass T's
+// masses), 3 = pass A of the top-k (slice max, and per lane group the maximum
+// of score - error bound), 4 = pass T of the top-k (candidates against the
+// row's top-k threshold).
 template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   constexpr bool MARK = MODE == 1 || MODE == 4;
   constexpr bool KLB = MODE == 3;  // lane-group lower-bound maxima
-  constexpr int DP = 128, KSTEP = DP / 32, NCH = KSA / 32;
-  constexpr int PT = 16 * RB;  // rows per tile
+  constexpr int DP = 128, KSTEP = DP / 16, NCH = KSA / 32;
+  constexpr int PT = 32 * RB;  // rows per tile
   constexpr int NCST = (MARK || KLB) ? 6 : 4;  // per-component constants in LDS
-  constexpr int WFRAG = (KSA / 16) * 2 * KSTEP * 64;
+  constexpr int WFRAG = NCH * 2 * KSTEP * 64;
   const int lane = threadIdx.x & 63;
+  const int hl = lane >> 5;  // the wave half: components 4 hl + (v % 4) of each 8
   const int wv = threadIdx.x >> 6;
   const int slice = blockIdx.x / A.G;
   const int g = blockIdx.x % A.G;
@@ -753,7 +758,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   // pass T: each wave's candidate words of its tile's rows, (row, chunk)
   uint32_t* wbuf = reinterpret_cast<uint32_t*>(cst + NCST * KSA) + (threadIdx.x >> 6) * PT * NCH;
   {
-    const uint4* src = reinterpret_cast<const uint4*>(A.W) + (size_t)slice * WFRAG;
+    const uint4* src = reinterpret_cast<const uint4*>(A.W32) + (size_t)slice * WFRAG;
     uint4* dst = reinterpret_cast<uint4*>(Wl);
     for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
     for (int i = threadIdx.x; i < KSA; i += blockDim.x) {
@@ -815,15 +820,17 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   auto load_rows = [&](int64_t t, bf16x8 (&rv)[RB][KSTEP]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      int64_t row = t * PT + rb * 16 + (lane & 15);
+      int64_t row = t * PT + rb * 32 + (lane & 31);
       row = row < nrows ? row : nrows - 1;
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
-        rv[rb][ks] = *reinterpret_cast<const bf16x8*>(xb + row * A.ld_x + ks * 32 + 8 * (lane >> 4));
+        rv[rb][ks] = *reinterpret_cast<const bf16x8*>(xb + row * A.ld_x + ks * 16 + 8 * hl);
     }
   };
-  // slices with and without a sharp component run their own copy of the
-  // row loop, so the common one carries no exact-score code
+  // the slice component of accumulator entry v of chunk cc
+  auto comp = [&](int cc, int v) { return cc * 32 + 8 * (v >> 2) + 4 * hl + (v & 3); };
+  // slices with and without a sharp component run their own copy of the row
+  // loop, so the common one carries no exact-score code
   auto rows_loop = [&](auto sharp_c) {
   constexpr bool SHARP = decltype(sharp_c)::value;
   // weight terms per logit: the top-m's row maxima (MODE 2) take the hi term
@@ -840,8 +847,8 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks) rv[rb][ks] = nxt[rb][ks];
     if (t + (int64_t)A.G * LNW < ntiles) load_rows(t + (int64_t)A.G * LNW, nxt);
-    // |x|^2 of the lane's two rows: exact (float64) in slice 0, which stores
-    // it for pass C and the top-m rescoring; float32 elsewhere
+    // |x|^2 of the lane's rows: exact (float64) in slice 0, which stores it
+    // for pass C and the top-m rescoring; float32 elsewhere
     float xs[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -854,10 +861,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             const float f = (float)rv[rb][ks][e];
             q += (double)(f * f);
           }
-        q = rows4_sum_f64(q);
+        q = halves_sum_f64(q);
         xs[rb] = (float)q;
-        const int64_t row = t * PT + rb * 16 + lane;
-        if (!MARK && lane < 16 && row < nrows) A.xsq[row] = q;
+        const int64_t row = t * PT + rb * 32 + lane;
+        if (!MARK && lane < 32 && row < nrows) A.xsq[row] = q;
       } else {
         float q = 0.f;
 #pragma unroll
@@ -867,16 +874,16 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             const float f = (float)rv[rb][ks][e];
             q = fmaf(f, f, q);
           }
-        xs[rb] = rows4_sum(q);
+        xs[rb] = halves_sum(q);
       }
     }
-    float M[RB], Sl[RB], R[RB], Lb[RB];
+    float M[RB], Sl[RB], R[RB], Lb[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       M[rb] = kDead;
       Sl[rb] = 0.f;
       R[rb] = kDead;
-      Lb[rb] = kDead;
+      Lb[rb][0] = Lb[rb][1] = kDead;
     }
     // pass T: the row maximum (pass B) is the reference of the candidate band
     // and of the sharp rescoring; rows past N have no candidates and no mass
@@ -885,7 +892,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     if constexpr (MARK) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int64_t row = t * PT + rb * 16 + (lane & 15);
+        const int64_t row = t * PT + rb * 32 + (lane & 31);
         live[rb] = row < nrows;
         mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
         R[rb] = mr[rb];
@@ -898,28 +905,29 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     }
 #pragma unroll 1
     for (int cc = 0; cc < NCH; ++cc) {
-      // components cc 32 + nt 16 + 4 (lane / 16) + v of the slice
-      floatx4 acc[RB][2];
+      floatx16 acc[RB];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // entries 4 q4 .. +3: components cc 32 + 8 q4 + 4 hl .. +3
+        const float4 c4 = *reinterpret_cast<const float4*>(cst + cc * 32 + 8 * q4 + 4 * hl);
+        const float4 a4 = *reinterpret_cast<const float4*>(cst + KSA + cc * 32 + 8 * q4 + 4 * hl);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
-          const float c = cst[kl], a = cst[KSA + kl];
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb][nt][v] = fmaf(a, xs[rb], c);
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[rb][4 * q4 + 0] = fmaf(a4.x, xs[rb], c4.x);
+          acc[rb][4 * q4 + 1] = fmaf(a4.y, xs[rb], c4.y);
+          acc[rb][4 * q4 + 2] = fmaf(a4.z, xs[rb], c4.z);
+          acc[rb][4 * q4 + 3] = fmaf(a4.w, xs[rb], c4.w);
         }
+      }
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
 #pragma unroll
-        for (int h = 0; h < NHT; ++h)
+        for (int h = 0; h < NHT; ++h) {
+          const bf16x8 bw = Wl[((cc * 2 + h) * KSTEP + ks) * 64 + lane];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const bf16x8 bw = Wl[(((cc * 2 + nt) * 2 + h) * KSTEP + ks) * 64 + lane];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              acc[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, rv[rb][ks], acc[rb][nt], 0, 0, 0);
-          }
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, rv[rb][ks], acc[rb], 0, 0, 0);
+        }
       if constexpr (SHARP) {
         // sharp components: scores that may come within 60 (log2 units) of the
         // best other score of the row seen so far in the slice, again exactly
@@ -928,25 +936,20 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           if constexpr (!MARK) {
             float r = R[rb];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (!(cst[2 * KSA + cc * 32 + nt * 16 + 4 * (lane >> 4) + v] > 0.f)) r = fmaxf(r, acc[rb][nt][v]);
-            R[rb] = rows4_max(r);
+            for (int v = 0; v < 16; ++v)
+              if (!(cst[2 * KSA + comp(cc, v)] > 0.f)) r = fmaxf(r, acc[rb][v]);
+            R[rb] = halves_max(r);
           }
-          const int64_t row = t * PT + rb * 16 + (lane & 15);
+          const int64_t row = t * PT + rb * 32 + (lane & 31);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
-              const float eb = cst[2 * KSA + kl], e0 = cst[3 * KSA + kl];
-              if (eb > 0.f && row < nrows && acc[rb][nt][v] + eb * xs[rb] + e0 >= R[rb] - 60.f) {
-                const int k = slice * KSA + kl;
-                acc[rb][nt][v] =
-                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, xb + row * A.ld_x);
-              }
+          for (int v = 0; v < 16; ++v) {
+            const int kl = comp(cc, v);
+            const float eb = cst[2 * KSA + kl], e0 = cst[3 * KSA + kl];
+            if (eb > 0.f && row < nrows && acc[rb][v] + eb * xs[rb] + e0 >= R[rb] - 60.f) {
+              const int k = slice * KSA + kl;
+              acc[rb][v] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, xb + row * A.ld_x);
             }
+          }
         }
       }
       if constexpr (MARK) {
@@ -959,47 +962,40 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           uint32_t word = 0;
           float rem = 0.f;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              bool cand;  // never for rows past N (thr = +inf)
-              if constexpr (MODE == 4) {
-                // top-k: the score's upper end reaches the row's threshold
-                const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
-                cand = acc[rb][nt][v] + fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]) >= thr[rb];
-              } else {
-                cand = acc[rb][nt][v] >= thr[rb];
-                if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][nt][v] - mr[rb]);
-              }
-              word |= (cand ? 1u : 0u) << (nt * 16 + 4 * (lane >> 4) + v);
+          for (int v = 0; v < 16; ++v) {
+            bool cand;  // never for rows past N (thr = +inf)
+            if constexpr (MODE == 4) {
+              // top-k: the score's upper end reaches the row's threshold
+              const int kl = comp(cc, v);
+              cand = acc[rb][v] + fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]) >= thr[rb];
+            } else {
+              cand = acc[rb][v] >= thr[rb];
+              if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][v] - mr[rb]);
             }
-          word = rows4_or(word);
+            word |= (cand ? 1u : 0u) << (8 * (v >> 2) + 4 * hl + (v & 3));
+          }
+          word = halves_or(word);
           Sl[rb] += rem;
-          if (lane < 16) wbuf[(rb * 16 + lane) * NCH + cc] = word;
+          if (lane < 32) wbuf[(rb * 32 + lane) * NCH + cc] = word;
         }
         continue;
       }
       // running max per row, and the lane's sum rescaled to it
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float cm = acc[rb][0][0];
+        float cm = acc[rb][0];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) cm = fmaxf(cm, acc[rb][nt][v]);
+        for (int v = 1; v < 16; ++v) cm = fmaxf(cm, acc[rb][v]);
         if constexpr (KLB) {
-          // this lane group's largest lower end, score - its error bound
-          float lb = Lb[rb];
+          // the largest lower end, score - its error bound, of this lane's
+          // entries 0..7 and 8..15: four disjoint lane groups per row
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int kl = cc * 32 + nt * 16 + 4 * (lane >> 4) + v;
-              lb = fmaxf(lb, acc[rb][nt][v] - fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]));
-            }
-          Lb[rb] = lb;
+          for (int v = 0; v < 16; ++v) {
+            const int kl = comp(cc, v);
+            Lb[rb][v >> 3] = fmaxf(Lb[rb][v >> 3], acc[rb][v] - fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]));
+          }
         }
-        cm = rows4_max(cm);
+        cm = halves_max(cm);
         if constexpr (MODE == 2 || MODE == 3) {
           M[rb] = fmaxf(M[rb], cm);
           continue;
@@ -1007,30 +1003,30 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         const float Mn = fmaxf(M[rb], cm);
         float s = Sl[rb] * __builtin_amdgcn_exp2f(M[rb] - Mn);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) s += __builtin_amdgcn_exp2f(acc[rb][nt][v] - Mn);
+        for (int v = 0; v < 16; ++v) s += __builtin_amdgcn_exp2f(acc[rb][v] - Mn);
         Sl[rb] = s;
         M[rb] = Mn;
       }
     }
     if constexpr (KLB) {
-      // lane group lane / 16 of row rb 16 + lane % 16: entry lane / 16 of (row, slice)
+      // lane group 2 (lane / 32) + j of row rb 32 + lane % 32: entry 2 (lane / 32) + j of (row, slice)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int64_t row = t * PT + rb * 16 + (lane & 15);
-        if (row < nrows) reinterpret_cast<float*>(A.lmx)[((size_t)row * A.S + slice) * 4 + (lane >> 4)] = Lb[rb];
+        const int64_t row = t * PT + rb * 32 + (lane & 31);
+        if (row < nrows)
+          *reinterpret_cast<float2*>(reinterpret_cast<float*>(A.lmx) + ((size_t)row * A.S + slice) * 4 + 2 * hl) =
+              float2{Lb[rb][0], Lb[rb][1]};
       }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float S = rows4_sum(Sl[rb]);
-      const int64_t row = t * PT + rb * 16 + lane;
-      if (lane < 16 && row < nrows) {
+      const float S = halves_sum(Sl[rb]);
+      const int64_t row = t * PT + rb * 32 + lane;
+      if (lane < 32 && row < nrows) {
         if constexpr (MARK) {
           // this slice's below-band mass and its 8 candidate words of the row
           A.prem[(size_t)row * A.S + slice] = S;
-          const uint32_t* src = wbuf + (rb * 16 + lane) * NCH;
+          const uint32_t* src = wbuf + (rb * 32 + lane) * NCH;
           uint4* dst = reinterpret_cast<uint4*>(A.cmask + (size_t)row * (A.KP / 32) + slice * NCH);
           dst[0] = uint4{src[0], src[1], src[2], src[3]};
           dst[1] = uint4{src[4], src[5], src[6], src[7]};
@@ -1045,14 +1041,14 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   else rows_loop(std::false_type{});
 }
 
-// 16-row blocks per tile of the barrier-free pass A: every weight fragment
+// 32-row blocks per tile of the barrier-free pass A: every weight fragment
 // read from LDS feeds kPassARB MFMAs
-constexpr int kPassARB = 4;
+constexpr int kPassARB = 2;
 
 size_t largek_pass_a_lds_bytes(int mode) {
   const bool mark = mode == 1 || mode == 4;
-  return (size_t)(KSA / 16) * 2 * (128 / 32) * 64 * 16 + ((mark || mode == 3) ? 6 : 4) * KSA * sizeof(float) +
-         (mark ? (size_t)LNW * 16 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
+  return (size_t)(KSA / 32) * 2 * (128 / 16) * 64 * 16 + ((mark || mode == 3) ? 6 : 4) * KSA * sizeof(float) +
+         (mark ? (size_t)LNW * 32 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
 }
 
 // Pass B: per row, combine the slices' (max, sum) into the LSE (log2 units);
@@ -1134,13 +1130,14 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
 }
 
 // Prologue: weights w = lambda mu log2(e) split into bf16 hi + lo in the
-// B-fragment order of v_mfma_f32_16x16x32_bf16 (16-component tiles), the
+// B-fragment order of v_mfma_f32_16x16x32_bf16 (16-component tiles) and in
+// the A-operand order of v_mfma_f32_32x32x16_bf16 (32-component tiles), the
 // constants c, a, c0, lambda (float64) and the sharp-component error bounds.
 // grid: KP blocks of 64 threads.
 __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int DP, const float* __restrict__ w,
                                                              const float* __restrict__ mu,
                                                              const float* __restrict__ cv, __bf16* __restrict__ W,
-                                                             double* __restrict__ c, double* __restrict__ a,
+                                                             __bf16* __restrict__ W32, double* __restrict__ c, double* __restrict__ a,
                                                              double* __restrict__ c0, double* __restrict__ lamk,
                                                              float* __restrict__ esh, float* __restrict__ eall,
                                                              double* __restrict__ mmk, double2* __restrict__ kconst) {
@@ -1162,6 +1159,14 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
     for (int h = 0; h < 2; ++h) {
       const size_t idx = ((size_t)kt * 2 + h) * KSTEP + ks;
       W[(idx * 64 + lane) * 8 + e] = h == 0 ? hi : lo;
+    }
+    // the 32x32x16 operand order: lane 32 (j / 8) + k % 32 of 16-dim step
+    // f / 16 holds dims 16 (f / 16) + 8 (j / 8) .. +7, j = f % 16
+    const int ks2 = f / 16, j2 = f % 16;
+    const int lane2 = (j2 / 8) * 32 + k % 32;
+    for (int h = 0; h < 2; ++h) {
+      const size_t idx = ((size_t)(k / 32) * 2 + h) * (DP / 16) + ks2;
+      W32[(idx * 64 + lane2) * 8 + j2 % 8] = h == 0 ? hi : lo;
     }
   }
   if (tid == 0) {
@@ -1199,7 +1204,8 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
                          hipStream_t s) {
   LargeKArgs a = a0;
   hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
-                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)), const_cast<double*>(a.c),
+                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)), const_cast<double*>(a.c),
                      const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
                      const_cast<float*>(a.esh), const_cast<float*>(a.eall),
                      const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
@@ -1679,7 +1685,8 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
                               hipStream_t s) {
   LargeKArgs a = a0;
   hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
-                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)), const_cast<double*>(a.c),
+                     cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)), const_cast<double*>(a.c),
                      const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
                      const_cast<float*>(a.esh), const_cast<float*>(a.eall),
                      const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
