@@ -172,8 +172,9 @@ def summarize(root, counters, calib_mib):
     calls and durations of the dispatches between the timed-loop markers, then
     of those after them.  Counters: per kernel in the timed window, the
     counters' mean per dispatch; FETCH_SIZE / WRITE_SIZE also scaled by what
-    they read on the calibration copy of calib_mib MiB (the last copy kernel
-    before the window)."""
+    they read on the calibration copy of calib_mib MiB (the copy kernel before
+    the window with the largest counts: smaller copies of the model state may
+    follow it)."""
     if not counters:
         files = _find(root, "kernel_trace.csv")
         if not files:
@@ -218,7 +219,7 @@ def summarize(root, counters, calib_mib):
         copies = [(d, c) for (d, k), c in per.items() if "copy" in k.lower() and d < win[0]]
         if copies:
             kib = calib_mib * 1024.0
-            c = max(copies)[1]
+            c = max(copies, key=lambda dc: max(dc[1].values()))[1]
             for name in ("FETCH_SIZE", "WRITE_SIZE"):
                 if c.get(name):
                     scale[name] = kib / c[name]
