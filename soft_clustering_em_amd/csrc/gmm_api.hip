@@ -73,7 +73,7 @@ static void largek_layout(Plan& q, int64_t chunk) {
   q.chunk_rows = chunk;
   size_t o = 0;
   q.off_W = o;    o = align_up(o + (size_t)q.KP * q.DP * 2 * 2);
-  q.off_W32 = o;  o = align_up(o + (size_t)q.KP * q.DP * 2 * 2);
+  q.off_W32 = o;  o = align_up(o + (size_t)q.KP * q.DP * 2 * 2 + (size_t)q.KP * 32);
   q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.KP);
   q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.KP);
   q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.KP);
@@ -329,6 +329,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
   A.G = p.Gb;
   A.W = w + p.off_W;
   A.W32 = w + p.off_W32;
+  A.W32C = w + p.off_W32 + (size_t)p.KP * p.DP * 2 * 2;
   A.c = reinterpret_cast<double*>(w + p.off_c);
   A.a = reinterpret_cast<double*>(w + p.off_a);
   A.mu = prm->means;

@@ -92,6 +92,8 @@ struct LargeKArgs {
   int K, KP, S, G;      // S slices of kLargeKSlice components; G row groups of the launch
   const void* W;        // (KP/16, 2, DP/32, 64, 8) bf16 weights, hi and lo parts, fragment order
   const void* W32;      // (KP/32, 2, DP/16, 64, 8) the same weights in the operand order of the 32x32 MFMA
+  const void* W32C;     // (KP/32, 64, 8) bf16: c and a in three terms each, the 32x32 MFMA step that adds
+                        // c + a |x|^2 in the barrier-free pass A
   const double* c;      // (KP)
   const double* a;      // (KP)
   const float* mu;      // (K, D) means, for the exact scores of sharp components

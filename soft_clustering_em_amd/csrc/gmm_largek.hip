@@ -742,8 +742,9 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   constexpr bool KLB = MODE == 3;  // lane-group lower-bound maxima
   constexpr int DP = 128, KSTEP = DP / 16, NCH = KSA / 32;
   constexpr int PT = 32 * RB;  // rows per tile
-  constexpr int NCST = (MARK || KLB) ? 6 : 4;  // per-component constants in LDS
+  constexpr int NCST = (MARK || KLB) ? 4 : 2;  // per-component error bounds in LDS
   constexpr int WFRAG = NCH * 2 * KSTEP * 64;
+  constexpr int CFRAG = NCH * 64;  // the c + a |x|^2 step of each chunk
   const int lane = threadIdx.x & 63;
   const int hl = lane >> 5;  // the wave half: components 4 hl + (v % 4) of each 8
   const int wv = threadIdx.x >> 6;
@@ -754,28 +755,29 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
-  float* cst = reinterpret_cast<float*>(Wl + WFRAG);  // c, a, eb, e0 (and ea, ea0) of the slice's components
+  bf16x8* Wc = Wl + WFRAG;
+  float* cst = reinterpret_cast<float*>(Wc + CFRAG);  // eb, e0 (and ea, ea0) of the slice's components
   // pass T: each wave's candidate words of its tile's rows, (row, chunk)
   uint32_t* wbuf = reinterpret_cast<uint32_t*>(cst + NCST * KSA) + (threadIdx.x >> 6) * PT * NCH;
   {
     const uint4* src = reinterpret_cast<const uint4*>(A.W32) + (size_t)slice * WFRAG;
     uint4* dst = reinterpret_cast<uint4*>(Wl);
     for (int i = threadIdx.x; i < WFRAG; i += blockDim.x) dst[i] = src[i];
+    const uint4* srcc = reinterpret_cast<const uint4*>(A.W32C) + (size_t)slice * CFRAG;
+    for (int i = threadIdx.x; i < CFRAG; i += blockDim.x) reinterpret_cast<uint4*>(Wc)[i] = srcc[i];
     for (int i = threadIdx.x; i < KSA; i += blockDim.x) {
       const int k = slice * KSA + i;
-      cst[i] = (float)A.c[k];
-      cst[KSA + i] = (float)A.a[k];
-      cst[2 * KSA + i] = A.esh[2 * k];
-      cst[3 * KSA + i] = A.esh[2 * k + 1];
+      cst[i] = A.esh[2 * k];
+      cst[KSA + i] = A.esh[2 * k + 1];
       if constexpr (MARK || KLB) {
-        cst[4 * KSA + i] = A.eall[2 * k];
-        cst[5 * KSA + i] = A.eall[2 * k + 1];
+        cst[2 * KSA + i] = A.eall[2 * k];
+        cst[3 * KSA + i] = A.eall[2 * k + 1];
       }
     }
   }
   __syncthreads();
   bool any_sharp = false;
-  for (int i = lane; i < KSA; i += 64) any_sharp = any_sharp || cst[2 * KSA + i] > 0.f;
+  for (int i = lane; i < KSA; i += 64) any_sharp = any_sharp || cst[i] > 0.f;
   any_sharp = __builtin_amdgcn_ballot_w64(any_sharp) != 0;
   // pass T: the largest error bound of the slice's components (slope in |x|^2,
   // offset), so that a row's candidate threshold is one number: the band it
@@ -809,8 +811,8 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   }
   if constexpr (MARK) {
     for (int i = lane; i < KSA; i += 64) {
-      eam = fmaxf(eam, cst[4 * KSA + i]);
-      ea0m = fmaxf(ea0m, cst[5 * KSA + i]);
+      eam = fmaxf(eam, cst[2 * KSA + i]);
+      ea0m = fmaxf(ea0m, cst[3 * KSA + i]);
     }
     eam = (float)wave_max((double)eam);
     ea0m = (float)wave_max((double)ea0m);
@@ -877,6 +879,21 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         xs[rb] = halves_sum(q);
       }
     }
+    // the B operand of the chunk's c + a |x|^2 step: lane l carries row
+    // l % 32's features (1, 1, 1, x1, x2, x3, x1, x2 | x1, 0, ...), x1 + x2 + x3
+    // the bf16 terms of |x|^2 (successive remainders), against the prologue's
+    // (c1, c2, c3, a1, a1, a1, a2, a2 | a3, 0, ...)
+    bf16x8 cfr[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float q = xs[rb];
+      const __bf16 x1 = (__bf16)q;
+      const float q2 = q - (float)x1;
+      const __bf16 x2 = (__bf16)q2;
+      const __bf16 x3 = (__bf16)(q2 - (float)x2);
+      const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
+      cfr[rb] = hl == 0 ? bf16x8{one, one, one, x1, x2, x3, x1, x2} : bf16x8{x1, zero, zero, zero, zero, zero, zero, zero};
+    }
     float M[RB], Sl[RB], R[RB], Lb[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -906,18 +923,13 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll 1
     for (int cc = 0; cc < NCH; ++cc) {
       floatx16 acc[RB];
+      {
+        const bf16x8 wc = Wc[cc * 64 + lane];
+        floatx16 z;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // entries 4 q4 .. +3: components cc 32 + 8 q4 + 4 hl .. +3
-        const float4 c4 = *reinterpret_cast<const float4*>(cst + cc * 32 + 8 * q4 + 4 * hl);
-        const float4 a4 = *reinterpret_cast<const float4*>(cst + KSA + cc * 32 + 8 * q4 + 4 * hl);
+        for (int v = 0; v < 16; ++v) z[v] = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          acc[rb][4 * q4 + 0] = fmaf(a4.x, xs[rb], c4.x);
-          acc[rb][4 * q4 + 1] = fmaf(a4.y, xs[rb], c4.y);
-          acc[rb][4 * q4 + 2] = fmaf(a4.z, xs[rb], c4.z);
-          acc[rb][4 * q4 + 3] = fmaf(a4.w, xs[rb], c4.w);
-        }
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc, cfr[rb], z, 0, 0, 0);
       }
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks)
@@ -937,14 +949,14 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             float r = R[rb];
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (!(cst[2 * KSA + comp(cc, v)] > 0.f)) r = fmaxf(r, acc[rb][v]);
+              if (!(cst[comp(cc, v)] > 0.f)) r = fmaxf(r, acc[rb][v]);
             R[rb] = halves_max(r);
           }
           const int64_t row = t * PT + rb * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kl = comp(cc, v);
-            const float eb = cst[2 * KSA + kl], e0 = cst[3 * KSA + kl];
+            const float eb = cst[kl], e0 = cst[KSA + kl];
             if (eb > 0.f && row < nrows && acc[rb][v] + eb * xs[rb] + e0 >= R[rb] - 60.f) {
               const int k = slice * KSA + kl;
               acc[rb][v] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, xb + row * A.ld_x);
@@ -967,7 +979,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             if constexpr (MODE == 4) {
               // top-k: the score's upper end reaches the row's threshold
               const int kl = comp(cc, v);
-              cand = acc[rb][v] + fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]) >= thr[rb];
+              cand = acc[rb][v] + fmaf(cst[2 * KSA + kl], xs[rb], cst[3 * KSA + kl]) >= thr[rb];
             } else {
               cand = acc[rb][v] >= thr[rb];
               if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][v] - mr[rb]);
@@ -992,7 +1004,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kl = comp(cc, v);
-            Lb[rb][v >> 3] = fmaxf(Lb[rb][v >> 3], acc[rb][v] - fmaf(cst[4 * KSA + kl], xs[rb], cst[5 * KSA + kl]));
+            Lb[rb][v >> 3] = fmaxf(Lb[rb][v >> 3], acc[rb][v] - fmaf(cst[2 * KSA + kl], xs[rb], cst[3 * KSA + kl]));
           }
         }
         cm = halves_max(cm);
@@ -1047,7 +1059,7 @@ constexpr int kPassARB = 2;
 
 size_t largek_pass_a_lds_bytes(int mode) {
   const bool mark = mode == 1 || mode == 4;
-  return (size_t)(KSA / 32) * 2 * (128 / 16) * 64 * 16 + ((mark || mode == 3) ? 6 : 4) * KSA * sizeof(float) +
+  return (size_t)(KSA / 32) * (2 * (128 / 16) + 1) * 64 * 16 + ((mark || mode == 3) ? 4 : 2) * KSA * sizeof(float) +
          (mark ? (size_t)LNW * 32 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
 }
 
@@ -1137,7 +1149,8 @@ __global__ void __launch_bounds__(256) largek_lse_kernel(LargeKArgs A) {
 __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int DP, const float* __restrict__ w,
                                                              const float* __restrict__ mu,
                                                              const float* __restrict__ cv, __bf16* __restrict__ W,
-                                                             __bf16* __restrict__ W32, double* __restrict__ c, double* __restrict__ a,
+                                                             __bf16* __restrict__ W32, __bf16* __restrict__ W32C,
+                                                             double* __restrict__ c, double* __restrict__ a,
                                                              double* __restrict__ c0, double* __restrict__ lamk,
                                                              float* __restrict__ esh, float* __restrict__ eall,
                                                              double* __restrict__ mmk, double2* __restrict__ kconst) {
@@ -1169,16 +1182,17 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
       W32[(idx * 64 + lane2) * 8 + j2 % 8] = h == 0 ? hi : lo;
     }
   }
-  if (tid == 0) {
-    if (!ok) {
-      c[k] = c0[k] = kDead;
-      a[k] = lamk[k] = 0.0;
-      esh[2 * k] = esh[2 * k + 1] = 0.f;
-      eall[2 * k] = eall[2 * k + 1] = 0.f;
-      mmk[k] = 0.0;
-      kconst[k] = double2{(double)kDead, 0.0};
-      return;
-    }
+  __shared__ double ca[2];  // c and a of the component, for the constant step below
+  if (tid == 0 && !ok) {
+    c[k] = c0[k] = kDead;
+    a[k] = lamk[k] = 0.0;
+    esh[2 * k] = esh[2 * k + 1] = 0.f;
+    eall[2 * k] = eall[2 * k + 1] = 0.f;
+    mmk[k] = 0.0;
+    kconst[k] = double2{(double)kDead, 0.0};
+    ca[0] = kDead;
+    ca[1] = 0.0;
+  } else if (tid == 0) {
     double mm = 0.0;
     for (int d = 0; d < D; ++d) mm += (double)mu[(size_t)k * D + d] * (double)mu[(size_t)k * D + d];
     c0[k] = (log((double)w[k]) - 0.5 * (D * kLog2Pi + D * log(var))) * kLog2e;
@@ -1197,6 +1211,31 @@ __global__ void __launch_bounds__(64) largek_prologue_kernel(int D, int K, int D
     eall[2 * k + 1] = (float)(ea * mm);
     mmk[k] = mm;
     kconst[k] = double2{c0[k] - 0.5 * lam * mm * kLog2e, lam * kLog2e};
+    ca[0] = c[k];
+    ca[1] = a[k];
+  }
+  __syncthreads();
+  // pass A's c + a |x|^2 as one more 32x32x16 MFMA step (A operand, the
+  // 32-component tile's order): slots (c1, c2, c3, a1, a1, a1, a2, a2 | a3,
+  // 0, ...) against the row's (1, 1, 1, x1, x2, x3, x1, x2 | x1, 0, ...), c and a
+  // split into three bf16 terms each (successive remainders), every product
+  // exact in the float32 accumulation
+  if (tid < 16) {
+    __bf16 ct[3], at[3];
+    double cr = ca[0], ar = ca[1];
+    for (int i = 0; i < 3; ++i) {
+      ct[i] = (__bf16)cr;
+      cr -= (double)(float)ct[i];
+      at[i] = (__bf16)ar;
+      ar -= (double)(float)at[i];
+    }
+    const int j = tid;
+    __bf16 val = (__bf16)0.f;
+    if (j < 3) val = ct[j];
+    else if (j < 6) val = at[0];
+    else if (j < 8) val = at[1];
+    else if (j == 8) val = at[2];
+    W32C[(((size_t)(k / 32)) * 64 + (j / 8) * 32 + k % 32) * 8 + j % 8] = val;
   }
 }
 
@@ -1205,7 +1244,8 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   LargeKArgs a = a0;
   hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
                      cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)),
-                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)), const_cast<double*>(a.c),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32C)), const_cast<double*>(a.c),
                      const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
                      const_cast<float*>(a.esh), const_cast<float*>(a.eall),
                      const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
@@ -1686,7 +1726,8 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
   LargeKArgs a = a0;
   hipLaunchKernelGGL(largek_prologue_kernel, dim3((unsigned)p.KP), dim3(64), 0, s, (int)p.D, (int)p.K, p.DP, w, mu,
                      cv, reinterpret_cast<__bf16*>(const_cast<void*>(a.W)),
-                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)), const_cast<double*>(a.c),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32)),
+                     reinterpret_cast<__bf16*>(const_cast<void*>(a.W32C)), const_cast<double*>(a.c),
                      const_cast<double*>(a.a), const_cast<double*>(a.c0), const_cast<double*>(a.lam),
                      const_cast<float*>(a.esh), const_cast<float*>(a.eall),
                      const_cast<double*>(a.mmk), const_cast<double2*>(a.kconst));
