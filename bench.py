@@ -61,9 +61,10 @@ def largek_roofline(D):
     """(algorithmic flops, executed flops) per pair of the bf16 large-K E-step.
     Algorithmic: logits 2D and statistics 2D, plus N_k and sum r|x|^2.
     Executed: logits with the hi and lo weight terms in pass A and again in
-    pass C (4 x 2D), statistics in two magnitude classes over D features plus
-    the 16-feature block that carries 1 and |x|^2 (2 x 2 (D + 16))."""
-    return 4 * D + 4, 8 * D + 4 * (D + 16)
+    pass C (4 x 2D), pass A's 16-feature step for c + a |x|^2 (2 x 16),
+    statistics in two magnitude classes over D features plus the 16-feature
+    block that carries 1 and |x|^2 (2 x 2 (D + 16))."""
+    return 4 * D + 4, 8 * D + 2 * 16 + 4 * (D + 16)
 
 
 def contraction_split(cov, D):
@@ -396,7 +397,7 @@ def main():
                      f"|x|^2 terms)")
         extra = {"executed_flops_per_launch": pairs * executed,
                  "executed_frac": pairs * executed / (k_ms * 1e-3) / 1e12 / peak,
-                 "executed_note": (f"{executed} flop/pair executed: two-term weights, logits again in pass C, "
+                 "executed_note": (f"{executed} flop/pair executed: two-term weights, logits again in pass C, c + a|x|^2 step in pass A, "
                                    f"statistics in two magnitude classes")}
         dtype = "bf16"
     else:
