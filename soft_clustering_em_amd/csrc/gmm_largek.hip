@@ -55,6 +55,13 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+// LDS pointers: address arithmetic in 32 bits
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
+typedef __attribute__((address_space(3))) double lds_f64;
 
 namespace {
 
@@ -146,28 +153,35 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
 // Write a thread's piece into the LDS tile.  Pass A also forms |x|^2 of each
 // row: in the workgroups of slice 0 exactly (each bf16 square is exact in
 // float32, their sum exact in float64), stored for pass C and the top-m
-// rescoring; elsewhere in float32.
+// rescoring; elsewhere in float32.  Pass C keeps |x|^2 as float32 (the first
+// half of the area) and the LSE as loaded: pass B padded both to whole
+// tiles, rows past N carry LSE = +inf (r = 0), and their loads were clamped
+// to row N - 1, so with 128-dim rows nothing past N needs zeroing.
 template <bool STATS>
 __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc, int64_t row0, int slice,
-                                            unsigned short* rows, double* xsq, float* ls) {
+                                            lds_u16* rows, lds_f64* xsq, lds_f32* ls) {
   const int j = threadIdx.x;
   int r, c8;
   piece_of(j, r, c8);
   u16x8 v = pc.v;
-  if (pc.nv < 8) {
+  if (pc.nv < 8 && (!STATS || A.D != 128)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = e < pc.nv ? v[e] : (unsigned short)0;
   }
-  *reinterpret_cast<u16x8*>(rows + tile_slot(r) * LRS + c8) = v;
+  *(lds_u16x8*)(rows + tile_slot(r) * LRS + c8) = v;
   const bool live = row0 + j < A.N;  // threads j < LT: row j of the tile
-  if (j < LT) ls[j] = live ? pc.ls : (STATS ? INFINITY : 0.f);
   if constexpr (STATS) {
     if (j < LT) {
-      xsq[j] = live ? pc.xs : 0.0;
+      ls[j] = pc.ls;
+      ((lds_f32*)xsq)[j] = (float)pc.xs;
       // columns 128.. of the row's slot: the statistics MFMA's features
       // 128..133 (1 and |x|^2 in five bf16 terms, formed by pass B)
-      *reinterpret_cast<u16x8*>(rows + tile_slot(j) * LRS + 128) = pc.ext;
+      *(lds_u16x8*)(rows + tile_slot(j) * LRS + 128) = pc.ext;
     }
+  } else if (j < LT) {
+    ls[j] = live ? pc.ls : 0.f;
+  }
+  if constexpr (STATS) {
   } else if (slice == 0) {
     double sq = 0.0;
 #pragma unroll
@@ -255,9 +269,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   extern __shared__ float lds[];
   bf16x8* Wl = reinterpret_cast<bf16x8*>(lds);
   unsigned char* bufs = reinterpret_cast<unsigned char*>(Wl + WLDS);
-  auto rows_of = [&](int bi) { return reinterpret_cast<unsigned short*>(bufs + bi * BUFB); };
-  auto xsq_of = [&](int bi) { return reinterpret_cast<double*>(rows_of(bi) + LT * LRS); };
-  auto ls_of = [&](int bi) { return reinterpret_cast<float*>(xsq_of(bi) + LT); };
+  __attribute__((address_space(3))) unsigned char* bufs3 = (__attribute__((address_space(3))) unsigned char*)bufs;
+  auto rows_of = [&](int bi) { return (lds_u16*)(bufs3 + bi * BUFB); };
+  auto xsq_of = [&](int bi) { return (lds_f64*)(rows_of(bi) + LT * LRS); };
+  auto ls_of = [&](int bi) { return (lds_f32*)(xsq_of(bi) + LT); };
   float* red = reinterpret_cast<float*>(bufs + NB * BUFB);  // pass A: 2 buffers of LNW * LT * 2
   // pass T: 2 buffers of (LT rows, LNW waves) candidate masks, bit j of word
   // (row, w) = component w * 32 + j of the slice
@@ -358,23 +373,25 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   // x . w_hi + x . w_lo, the MFMA chain starting from the constant part.
   // Lane's rows: q = rb * 4 + v <-> tile row rb * 16 + 4 (lane / 16) + v.
   auto logits = [&](int bi, floatx4 (&acc)[2][NT]) {
-    const unsigned short* rows = rows_of(bi);
-    const double* xsq = xsq_of(bi);
+    const lds_u16* rows = rows_of(bi);
+    const lds_f64* xsq = xsq_of(bi);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      floatx4 xs4;  // pass C: four consecutive rows' float32 |x|^2
+      if constexpr (STATS) xs4 = *(const lds_floatx4*)((const lds_f32*)xsq + rb * 16 + 4 * (lane >> 4));
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float xs = (float)xsq[rb * 16 + (TR ? (lane & 15) : 4 * (lane >> 4) + v)];
+        const float xs = STATS ? xs4[v] : (float)xsq[rb * 16 + (TR ? (lane & 15) : 4 * (lane >> 4) + v)];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[rb][nt][v] = fmaf(areg[nt][TR ? v : 0], xs, creg[nt][TR ? v : 0]);
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
       bf16x8 av[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        av[rb] = *reinterpret_cast<const bf16x8*>(rows + tile_slot(rb * 16 + (lane & 15)) * LRS + ks * 32 +
-                                                  8 * (lane >> 4));
+        av[rb] = *(const lds_bf16x8*)(rows + tile_slot(rb * 16 + (lane & 15)) * LRS + ks * 32 + 8 * (lane >> 4));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -395,9 +412,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   // constant): this wave holds a sharp component
   auto finish = [&](int64_t row0, int it, auto sharp_c, const floatx4 (&acc)[2][NT], int bi) {
     constexpr bool SHARP = decltype(sharp_c)::value;
-    const unsigned short* rows = rows_of(bi);
-    const double* xsq = xsq_of(bi);
-    const float* lsb = ls_of(bi);
+    const lds_u16* rows = rows_of(bi);
+    const lds_f64* xsq = xsq_of(bi);
+    const lds_f32* lsb = ls_of(bi);
     if constexpr (PASS == 0) {
       // ---- per-row max and sum of 2^(l - max) over this wave's components
       float lg[2][NT][4];
@@ -427,8 +444,8 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
             for (int v = 0; v < 4; ++v) {
               if (eb[nt][v] > 0.f && row0 + p < nrows && lg[rb][nt][v] + eb[nt][v] * xs + e0[nt][v] >= ref - 60.f) {
                 const int k = comp_of(nt, v);
-                lg[rb][nt][v] =
-                    largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + tile_slot(p) * LRS);
+                lg[rb][nt][v] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D,
+                                                   (const unsigned short*)(rows + tile_slot(p) * LRS));
               }
             }
         }
@@ -466,7 +483,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
     if constexpr (STATS) {
       // four consecutive rows per load; rows past N hold +inf (r = 0)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) lse4[rb] = *reinterpret_cast<const floatx4*>(lsb + rb * 16 + 4 * (lane >> 4));
+      for (int rb = 0; rb < 2; ++rb) lse4[rb] = *(const lds_floatx4*)(lsb + rb * 16 + 4 * (lane >> 4));
     }
     float lg[8][NT];
 #pragma unroll
@@ -487,12 +504,13 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int p = (q >> 2) * 16 + 4 * (lane >> 4) + (q & 3);
-        const float xs = (float)xsq[p];
+        const float xs = STATS ? ((const lds_f32*)xsq)[p] : (float)xsq[p];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if (eb[nt][0] > 0.f && row0 + p < nrows && lg[q][nt] + eb[nt][0] * xs + e0[nt][0] >= ref[q] - 60.f) {
             const int k = comp_of(nt, 0);
-            lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D, rows + tile_slot(p) * LRS);
+            lg[q][nt] = largek_exact_score(A.mu + (size_t)k * A.D, A.c0[k], A.lam[k], (int)A.D,
+                                           (const unsigned short*)(rows + tile_slot(p) * LRS));
           }
         }
       }
@@ -573,7 +591,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         // lane 16 g + i: features 16 mt + i of rows 4 g + e (read 1) and
         // 16 + 4 g + e (read 2), e = 0..3 -- k = 8 g + e and 8 g + 4 + e
         // (slot(16 + r) = 16 + slot(r): read 2 is 16 slots further)
-        const unsigned short* src = rows + tile_slot(lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
+        const lds_u16* src = rows + tile_slot(lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * LRS));
         bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -643,25 +661,22 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xsq_of(1), ls_of(1));
       pf[1] = fetch_piece<PASS, VEC>(A, g + (int64_t)4 * A.G, ntiles);
       __syncthreads();
-      floatx4 acc[2][NT];
-      logits(0, acc);
-      for (int64_t i0 = 0; i0 < nmine; i0 += 3) {
+      // tile i's logits in acc[i % 2]: six tiles per round, so both the
+      // buffer (i % 3) and the accumulator index are compile-time constants
+      floatx4 acc[2][2][NT];
+      logits(0, acc[0]);
+      for (int64_t i0 = 0; i0 < nmine; i0 += 6) {
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < 6; ++u) {
           const int64_t i = i0 + u;
           if (i >= nmine) break;
-          const int bn = (u + 1) % 3, bs = (u + 2) % 3;
+          const int b = u % 3, bn = (u + 1) % 3, bs = (u + 2) % 3;
           stage_piece<STATS>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
                              ls_of(bs));
           pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 5) * A.G, ntiles);
-          floatx4 accn[2][NT];
-          logits(bn, accn);
-          finish((g + i * A.G) * LT, (int)i, sharp_c, acc, u);
+          logits(bn, acc[(u + 1) % 2]);
+          finish((g + i * A.G) * LT, (int)i, sharp_c, acc[u % 2], b);
           __syncthreads();
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = accn[rb][nt];
           ++it;
         }
       }
