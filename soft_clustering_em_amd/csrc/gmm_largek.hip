@@ -122,30 +122,33 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
   const int j = threadIdx.x;
   int r, c8;
   piece_of(j, r, c8);
-  const int64_t row = tile * LT + r;
-  const int64_t rc = row < A.N ? row : A.N - 1;
+  // row indices within the chunk (at most 2^20 rows, tiles a few past the
+  // end) in 32-bit arithmetic
+  const int n = (int)A.N, tl = (int)tile, npad = (int)ntiles * LT;
+  const int row = tl * LT + r;
+  const int rc = min(row, n - 1);
   const int D = (int)A.D;
   Piece pc;
-  pc.nv = (tile < ntiles && row < A.N) ? min(max(D - c8, 0), 8) : 0;
+  pc.nv = (tl < (int)ntiles && row < n) ? min(max(D - c8, 0), 8) : 0;
   if constexpr (VEC) {
-    pc.v = *reinterpret_cast<const u16x8*>(xb + rc * A.ld_x + min(c8, (int)A.ld_x - 8));
+    pc.v = *reinterpret_cast<const u16x8*>(xb + (int64_t)rc * A.ld_x + min(c8, (int)A.ld_x - 8));
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pc.v[e] = xb[rc * A.ld_x + min(c8 + e, D - 1)];
+    for (int e = 0; e < 8; ++e) pc.v[e] = xb[(int64_t)rc * A.ld_x + min(c8 + e, D - 1)];
   }
   pc.xs = 0.0;
   pc.ls = 0.f;
-  const int64_t xrow = tile * LT + (j & (LT - 1));  // every wave: the tile's 32 rows (threads j < LT keep theirs)
+  const int xrow = tl * LT + (j & (LT - 1));  // every wave: the tile's 32 rows (threads j < LT keep theirs)
   if constexpr (STATS) {
     // pass B padded the LSE (+inf) and the statistics features to whole
     // tiles (ntiles * LT rows)
-    const int64_t xpad = xrow < ntiles * LT ? xrow : ntiles * LT - 1;
-    pc.xs = A.xsq[xrow < A.N ? xrow : A.N - 1];
+    const int xpad = min(xrow, npad - 1);
+    pc.xs = A.xsq[min(xrow, n - 1)];
     pc.ls = A.lse[xpad];
     pc.ext = reinterpret_cast<const u16x8*>(A.ext)[xpad];
   } else if constexpr (PASS == 1) {
     // top-m: the row maximum; top-k: the row's candidate threshold
-    pc.ls = (A.topk ? A.kthr : A.mrow)[xrow < A.N ? xrow : A.N - 1];
+    pc.ls = (A.topk ? A.kthr : A.mrow)[min(xrow, n - 1)];
   }
   return pc;
 }
@@ -156,15 +159,15 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
 // rescoring; elsewhere in float32.  Pass C keeps |x|^2 as float32 (the first
 // half of the area) and the LSE as loaded: pass B padded both to whole
 // tiles, rows past N carry LSE = +inf (r = 0), and their loads were clamped
-// to row N - 1, so with 128-dim rows nothing past N needs zeroing.
-template <bool STATS>
+// to row N - 1, so with 128-dim rows (FULL) nothing past N needs zeroing.
+template <bool STATS, bool FULL = false>
 __device__ __forceinline__ void stage_piece(const LargeKArgs& A, const Piece& pc, int64_t row0, int slice,
                                             lds_u16* rows, lds_f64* xsq, lds_f32* ls) {
   const int j = threadIdx.x;
   int r, c8;
   piece_of(j, r, c8);
   u16x8 v = pc.v;
-  if (pc.nv < 8 && (!STATS || A.D != 128)) {
+  if (!(STATS && FULL) && pc.nv < 8) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = e < pc.nv ? v[e] : (unsigned short)0;
   }
@@ -235,8 +238,9 @@ size_t largek_lds_bytes(int DP, int pass) {
 }
 
 // PASS: 0 = A (slice max/sum), 1 = T (top-m candidates), 2 = C (statistics).
+// FULL: rows of exactly DP dims (no staged piece needs zeroing in pass C).
 // Weights in global memory: 16-component tiles, [tile][hi/lo][kstep][lane] x 16 bytes.
-template <int DP, int PASS>
+template <int DP, int PASS, bool FULL = false>
 __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
   constexpr bool STATS = (PASS == 2);
   constexpr int KSL = STATS ? KSC : KSA;  // components of this workgroup
@@ -627,7 +631,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // other half of the double buffer, last read by the combine of tile
       // i - 2 in iteration i - 1.
       static_assert(PF == NB, "prefetch slots follow the buffers");
-      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
+      stage_piece<STATS, FULL>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
       pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)2 * A.G, ntiles);
       __syncthreads();
       for (int64_t i0 = 0; i0 < nmine; i0 += 2) {
@@ -636,7 +640,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           const int64_t i = i0 + u;
           if (i >= nmine) break;
           const int bs = 1 - u;
-          stage_piece<STATS>(A, pf[bs], (g + (i + 1) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
+          stage_piece<STATS, FULL>(A, pf[bs], (g + (i + 1) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
                              ls_of(bs));
           pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 3) * A.G, ntiles);
           if (i > 0 && wv == (i & (LNW - 1))) combine((g + (i - 1) * A.G) * LT, red + ((i - 1) & 1) * (LNW * LT * 2));
@@ -656,9 +660,9 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
       // i - 1.  Staging and logits past the workgroup's last tile touch only
       // a free buffer and are never used.
       static_assert(PF == NB, "prefetch slots follow the buffers");
-      stage_piece<STATS>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
+      stage_piece<STATS, FULL>(A, pf[0], (int64_t)g * LT, slice, rows_of(0), xsq_of(0), ls_of(0));
       pf[0] = fetch_piece<PASS, VEC>(A, g + (int64_t)3 * A.G, ntiles);
-      stage_piece<STATS>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xsq_of(1), ls_of(1));
+      stage_piece<STATS, FULL>(A, pf[1], (g + (int64_t)A.G) * LT, slice, rows_of(1), xsq_of(1), ls_of(1));
       pf[1] = fetch_piece<PASS, VEC>(A, g + (int64_t)4 * A.G, ntiles);
       __syncthreads();
       // tile i's logits in acc[i % 2]: six tiles per round, so both the
@@ -671,7 +675,7 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
           const int64_t i = i0 + u;
           if (i >= nmine) break;
           const int b = u % 3, bn = (u + 1) % 3, bs = (u + 2) % 3;
-          stage_piece<STATS>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
+          stage_piece<STATS, FULL>(A, pf[bs], (g + (i + 2) * A.G) * LT, slice, rows_of(bs), xsq_of(bs),
                              ls_of(bs));
           pf[bs] = fetch_piece<PASS, VEC>(A, g + (i + 5) * A.G, ntiles);
           logits(bn, acc[(u + 1) % 2]);
@@ -1267,11 +1271,14 @@ hipError_t launch_largek(const Plan& p, const LargeKArgs& a0, const float* w, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kA = largek_kernel<128, 0>;
-  auto kC = largek_kernel<128, 2>;
+  auto kC = p.D == 128 ? largek_kernel<128, 2, true> : largek_kernel<128, 2, false>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kA, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)kC, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_kernel<128, 2, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_kernel<128, 2, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
     attr_set = true;
