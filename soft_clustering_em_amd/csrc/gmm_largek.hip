@@ -138,17 +138,22 @@ __device__ __forceinline__ Piece fetch_piece(const LargeKArgs& A, int64_t tile, 
   }
   pc.xs = 0.0;
   pc.ls = 0.f;
-  const int xrow = tl * LT + (j & (LT - 1));  // every wave: the tile's 32 rows (threads j < LT keep theirs)
-  if constexpr (STATS) {
-    // pass B padded the LSE (+inf) and the statistics features to whole
-    // tiles (ntiles * LT rows)
-    const int xpad = min(xrow, npad - 1);
-    pc.xs = A.xsq[min(xrow, n - 1)];
-    pc.ls = A.lse[xpad];
-    pc.ext = reinterpret_cast<const u16x8*>(A.ext)[xpad];
-  } else if constexpr (PASS == 1) {
-    // top-m: the row maximum; top-k: the row's candidate threshold
-    pc.ls = (A.topk ? A.kthr : A.mrow)[min(xrow, n - 1)];
+  pc.ext = u16x8{};
+  // the per-row values: threads j < LT stage them, so only the first wave
+  // loads (a wave-uniform branch: the others skip the address arithmetic)
+  const int xrow = tl * LT + (j & (LT - 1));
+  if (j < 64) {
+    if constexpr (STATS) {
+      // pass B padded the LSE (+inf) and the statistics features to whole
+      // tiles (ntiles * LT rows)
+      const int xpad = min(xrow, npad - 1);
+      pc.xs = A.xsq[min(xrow, n - 1)];
+      pc.ls = A.lse[xpad];
+      pc.ext = reinterpret_cast<const u16x8*>(A.ext)[xpad];
+    } else if constexpr (PASS == 1) {
+      // top-m: the row maximum; top-k: the row's candidate threshold
+      pc.ls = (A.topk ? A.kthr : A.mrow)[min(xrow, n - 1)];
+    }
   }
   return pc;
 }
@@ -598,9 +603,10 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
         const lds_u16* src = rows + tile_slot(lane >> 2) * LRS + 16 * mt + 4 * (lane & 3);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)src);
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 16 * LRS));
-        bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        // the last block's features 136..143 lie past the slot's 136 columns
-        if (mt == GM && (lane & 15) >= 8) av = bf16x8{};
+        // (the last block's features 136..143 lie past the slot's 136 columns:
+        // other bytes of the buffer, which reach only accumulator rows
+        // 136..143, never read)
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           sbig[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bbig[nt], sbig[mt][nt], 0, 0, 0);
