@@ -993,11 +993,17 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         // candidates: every component whose score may lie within kTopmBand of
         // the row's maximum (the slice's largest expanded-form error counted
         // twice); the mass 2^(l - max) of the others; bit j of word (row, cc)
-        // is component cc 32 + j of the slice
+        // is component cc 32 + j of the slice.  Every component adds
+        // 2^(min(l, thr) - max): the others their own mass, each candidate
+        // 2^(thr - max), taken off once per row at the end of the tile (all
+        // these terms lie below 2^-20 of the row's mass, so the difference
+        // loses nothing that matters).  Rows past N (thr = +inf) are never
+        // written.
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           uint32_t word = 0;
           float rem = 0.f;
+          const float tm = thr[rb] - mr[rb];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             bool cand;  // never for rows past N (thr = +inf)
@@ -1007,11 +1013,12 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
               cand = acc[rb][v] + fmaf(cst[2 * KSA + kl], xs[rb], cst[3 * KSA + kl]) >= thr[rb];
             } else {
               cand = acc[rb][v] >= thr[rb];
-              if (!cand && live[rb]) rem += __builtin_amdgcn_exp2f(acc[rb][v] - mr[rb]);
+              rem += __builtin_amdgcn_exp2f(fminf(acc[rb][v] - mr[rb], tm));
             }
-            word |= (cand ? 1u : 0u) << (8 * (v >> 2) + 4 * hl + (v & 3));
+            // this half's bits first, moved to 4 (l / 32) below
+            word |= cand ? (1u << (8 * (v >> 2) + (v & 3))) : 0u;
           }
-          word = halves_or(word);
+          word = halves_or(word << (4 * hl));
           Sl[rb] += rem;
           if (lane < 32) wbuf[(rb * 32 + lane) * NCH + cc] = word;
         }
@@ -1062,8 +1069,15 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       if (lane < 32 && row < nrows) {
         if constexpr (MARK) {
           // this slice's below-band mass and its 8 candidate words of the row
-          A.prem[(size_t)row * A.S + slice] = S;
           const uint32_t* src = wbuf + (rb * 32 + lane) * NCH;
+          float Sb = S;
+          if constexpr (MODE == 1) {
+            int nc = 0;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) nc += __popc(src[c]);
+            Sb = fmaxf(S - (float)nc * __builtin_amdgcn_exp2f(thr[rb] - mr[rb]), 0.f);
+          }
+          A.prem[(size_t)row * A.S + slice] = Sb;
           uint4* dst = reinterpret_cast<uint4*>(A.cmask + (size_t)row * (A.KP / 32) + slice * NCH);
           dst[0] = uint4{src[0], src[1], src[2], src[3]};
           dst[1] = uint4{src[4], src[5], src[6], src[7]};
