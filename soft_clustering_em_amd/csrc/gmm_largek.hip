@@ -16,10 +16,12 @@
 //      statistics
 // Scratch is O(chunk), not O(N).
 //
-// gfx950 specifics: the x . (lambda mu) contraction runs on
-// v_mfma_f32_16x16x32_bf16 with the weights split into bf16 hi + lo parts (x
-// itself is exact in bf16); the statistics contraction X^T R runs on the same
-// instruction with r rounded to bf16.  Every statistic (N_k, sum r x,
+// gfx950 specifics: the x . (lambda mu) contraction runs on bf16 MFMA with
+// the weights split into bf16 hi + lo parts (x itself is exact in bf16):
+// v_mfma_f32_32x32x16_bf16 in the barrier-free pass A (which also adds
+// c + a |x|^2 as one more MFMA step), v_mfma_f32_16x16x32_bf16 in pass C and
+// the barrier-based passes; the statistics contraction X^T R runs on the
+// 16x16x32 instruction with r rounded to bf16.  Every statistic (N_k, sum r x,
 // sum r |x|^2) uses that same rounded r, so the M-step sees the exact moments
 // of one set of weights; N_k and sum r |x|^2 ride on the same MFMAs as extra
 // features (1, and |x|^2 as five bf16 terms).  The responsibilities are summed in two magnitude
