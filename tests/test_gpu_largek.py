@@ -95,6 +95,18 @@ def test_padded_row_stride(torch_cuda):
     check(torch_cuda, wl, thetas[0], outs[0], Xw, label="bf16 ld_x=45")
 
 
+def test_full_width_rows_unaligned(torch_cuda):
+    """128-dim bf16 rows with a leading dimension of 130 (not 16-byte aligned):
+    the element-wise loads of the barrier-based pass A with the statistics pass
+    for full-width rows."""
+    wl = bf16_workload(3000, 128, 300, seed=13)
+    thetas, outs = oracle_trajectory(wl, 1)
+    wide = np.zeros((1, 3000, 130), np.uint16)
+    wide[..., :128] = wl.X
+    Xw = bf16_tensor(torch_cuda, wide)[..., :128]
+    check(torch_cuda, wl, thetas[0], outs[0], Xw, label="bf16 D=128 ld_x=130")
+
+
 def test_short_chunks_from_a_small_workspace(torch_cuda):
     """A workspace smaller than the preferred size streams the rows in shorter
     chunks: the result still matches the oracle and the one-chunk call."""
