@@ -877,11 +877,13 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       for (int ks = 0; ks < KSTEP; ++ks) rv[rb][ks] = nxt[rb][ks];
     if (t + (int64_t)A.G * LNW < ntiles) load_rows(t + (int64_t)A.G * LNW, nxt);
     // |x|^2 of the lane's rows: exact (float64) in slice 0, which stores it
-    // for pass C and the top-m rescoring; float32 elsewhere
+    // for pass B, pass C and the top-m rescoring; float32 elsewhere and in
+    // pass T, which stores nothing
+    const bool exact = !MARK && slice == 0;
     float xs[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (slice == 0) {
+      if (exact) {
         double q = 0.0;
 #pragma unroll
         for (int ks = 0; ks < KSTEP; ++ks)
@@ -893,7 +895,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         q = halves_sum_f64(q);
         xs[rb] = (float)q;
         const int64_t row = t * PT + rb * 32 + lane;
-        if (!MARK && lane < 32 && row < nrows) A.xsq[row] = q;
+        if (lane < 32 && row < nrows) A.xsq[row] = q;
       } else {
         float q = 0.f;
 #pragma unroll
