@@ -200,16 +200,21 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
       }
     }
     if constexpr (QUAD) {
+      // product features: a thread takes one feature (d, e) for all T rows,
+      // so the table lookup and its checks happen once per feature and the
+      // rows run with compile-time offsets
       constexpr int NQP = F - DP;
-      for (int j = threadIdx.x; j < T * NQP; j += nthr) {
-        const int r = j / NQP, qi = j % NQP;
+      const int nvalid = (int)((N - row0) < T ? (N - row0) : T);
+      for (int qi = threadIdx.x; qi < NQP; qi += nthr) {
         const int de = qtab[DP + qi];
-        float v = 0.f;
-        if (de >= 0 && row0 + r < N) {
-          const int d = de >> 16, e = de & 0xFFFF;
-          if (d < D && e < D) v = raw[r * rawstride + d] * raw[r * rawstride + e];
+        const int d = de >> 16, e = de & 0xFFFF;
+        const bool ok = de >= 0 && d < D && e < D;
+        const int dd = ok ? d : 0, ee = ok ? e : 0;
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+          const float v = raw[r * rawstride + dd] * raw[r * rawstride + ee];
+          phi[r * FS + DP + qi] = (ok && r < nvalid) ? v : 0.f;
         }
-        phi[r * FS + DP + qi] = v;
       }
     }
     // the next tile's rows into the other raw buffer, in flight during the compute below
