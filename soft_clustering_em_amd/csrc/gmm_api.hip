@@ -96,6 +96,7 @@ static void largek_layout(Plan& q, int64_t chunk) {
     q.off_lmx = o;  o = align_up(o + sizeof(float) * 4 * (size_t)chunk * q.S);
     q.off_kthr = o; o = align_up(o + sizeof(float) * (size_t)chunk);
     q.off_hv = o;   o = align_up(o + (size_t)chunk / 4 + 1);
+    q.off_egb = o;  o = align_up(o + 2 * sizeof(float));
   }
   q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.Gb * q.KP * q.PR);
   q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.llG);
@@ -353,6 +354,7 @@ static LargeKArgs largek_args(const Plan& p, const gmm_data* d, const gmm_params
     A.lmx = reinterpret_cast<float4*>(w + p.off_lmx);
     A.kthr = reinterpret_cast<float*>(w + p.off_kthr);
     A.hv = reinterpret_cast<unsigned char*>(w + p.off_hv);
+    A.egb = reinterpret_cast<float*>(w + p.off_egb);
   }
   return A;
 }
@@ -438,14 +440,20 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
 
 // The top-m launch sequence of a planned call (N >= 1, workspace checked).
 // topk != 0: the top-k mode (every row keeps its m best components, normalised
-// over them; threshold unused).
+// over them; threshold unused).  one_pass != 0 (large K): candidates are marked
+// against each slice's running maximum in one pass instead of against the row
+// maximum found by a pass of its own -- the k-means model, whose shared
+// variance puts one component of every row far above the rest, so that the
+// running maximum finds the band of the row maximum; with a softer model a
+// row's slices below its best mark many components the rescoring then scores.
 static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
                            int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, hipStream_t s,
-                           int topk = 0) {
+                           int topk = 0, int one_pass = 0) {
   if (p.largek) {
     LargeKArgs A = largek_args(p, data, params, ws);
     A.topm = 1;
     A.topk = topk;
+    A.fused_t = one_pass;
     A.m = m;
     A.thr = threshold;
     A.idx = idx;
@@ -916,7 +924,8 @@ gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, in
     prm.weights = wk;
     prm.means = centroids;
     prm.covars = cv;
-    st = run_topm(p, data, &prm, 1, 0.0f, labels, reinterpret_cast<float*>(w + L.off_resp), nullptr, nullptr, ws, s);
+    st = run_topm(p, data, &prm, 1, 0.0f, labels, reinterpret_cast<float*>(w + L.off_resp), nullptr, nullptr, ws, s,
+                  0, 1);
     if (st != GMM_OK) return st;
   }
   IvfArgs A;

@@ -50,6 +50,7 @@ struct Plan {
   size_t off_W32 = 0, off_P = 0, off_lse = 0, off_xsq = 0, off_ext = 0, off_eall = 0, off_mmk = 0, off_kconst = 0, off_prem = 0, off_mrow = 0, off_cmask = 0;
   size_t off_lmx = 0, off_kthr = 0;  // large-K top-k: per-(row, slice) lower-bound maxima, per-row threshold
   size_t off_hv = 0;                 // large-K top-m: rows handed to the heavy rescoring kernel
+  size_t off_egb = 0;                // large-K top-m: the largest error bound over the components
   size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
   int64_t ntiles = 0;       // row tiles per problem
   size_t lds = 0;           // dynamic LDS of the fused kernel
@@ -116,6 +117,13 @@ struct LargeKArgs {
   float* mrow;          // (chunk) row maximum of the log-scores (pass B)
   uint32_t* cmask;      // (chunk, KP/32) candidate components of each row, one bit per component
   int topm;             // pass B: write mrow
+  // one-pass marking (fused_t, set by the caller for the k-means model and
+  // taken on full-width rows): P holds per (row, slice) the slice maximum and
+  // whole mass, prem the non-candidates' mass, both relative to that maximum,
+  // and egb the largest error bound over every component (slope in |x|^2,
+  // offset); the rescoring forms the row maximum and drops far slices
+  int fused_t;
+  float* egb;           // (2)
   // top-k mode (topk > 0): each row keeps its topk best components, normalised over them
   int topk;
   float4* lmx;          // (chunk, S) per (row, slice): 4 lane-group maxima of (score - error bound), or null

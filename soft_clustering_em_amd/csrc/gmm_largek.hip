@@ -762,10 +762,25 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // the top-m (slice max: its last kernel needs only the row maxima and pass T's
 // masses), 3 = pass A of the top-k (slice max, and per lane group the maximum
 // of score - error bound), 4 = pass T of the top-k (candidates against the
-// row's top-k threshold).
+// row's top-k threshold), 5 = the one-pass top-m marking: candidates against
+// the slice's running maximum, and per (row, slice) the slice maximum, its
+// whole mass and the mass of its non-candidates (no row maximum needed first).
+//
+// Why mode 5 loses no candidate.  Write l~ for a two-term score and E_k(x) for
+// component k's error bound (|l~ - l| <= E_k), E_s and E_g for the largest
+// bound in slice s and over every component.  Slice s marks k when
+// l~_k >= m_run - band - E_s - E_g, m_run its running maximum at that chunk.
+// With M~ the largest slice maximum, the true row maximum is at least
+// M~ - E_g, and m_run <= M~; so every k whose true score reaches the row
+// maximum minus band has l~_k >= M~ - band - E_k - E_g and is marked.  A
+// slice whose maximum m_s lies below M~ - band - 2 E_g holds no such k at all
+// (l_k <= m_s + E_g < M~ - band - E_g); the rescoring drops its candidates and
+// counts its whole mass, the others' candidates are scored exactly and their
+// non-candidates' mass added.
 template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
-  constexpr bool MARK = MODE == 1 || MODE == 4;
+  constexpr bool FUSED = MODE == 5;
+  constexpr bool MARK = MODE == 1 || MODE == 4 || FUSED;
   constexpr bool KLB = MODE == 3;  // lane-group lower-bound maxima
   constexpr int DP = 128, KSTEP = DP / 16, NCH = KSA / 32;
   constexpr int PT = 32 * RB;  // rows per tile
@@ -816,7 +831,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   // 17 times the two-term bound (bf16 rounding of the weight, 2^-9 relative,
   // against 2^-14 for hi + lo and the float32 sums), and the band widens by it
   float egm = 0.f, eg0m = 0.f;
-  if constexpr (MODE == 1) {
+  if constexpr (MODE == 1 || FUSED) {
     // the waves' maxima meet in the candidate-word area, before its first use
     float* egred = reinterpret_cast<float*>(cst + NCST * KSA);
     for (int i = threadIdx.x; i < A.K; i += blockDim.x) {
@@ -835,6 +850,13 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       eg0m = fmaxf(eg0m, egred[LNW + w2]);
     }
     __syncthreads();
+    // the rescoring's slice test takes the same bound (every workgroup
+    // forms the same value; the first one stores it)
+    if constexpr (FUSED)
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        A.egb[0] = egm;
+        A.egb[1] = eg0m;
+      }
   }
   if constexpr (MARK) {
     for (int i = lane; i < KSA; i += 64) {
@@ -879,7 +901,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     // |x|^2 of the lane's rows: exact (float64) in slice 0, which stores it
     // for pass B, pass C and the top-m rescoring; float32 elsewhere and in
     // pass T, which stores nothing
-    const bool exact = !MARK && slice == 0;
+    const bool exact = (!MARK || FUSED) && slice == 0;
     float xs[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -923,11 +945,12 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
       cfr[rb] = hl == 0 ? bf16x8{one, one, one, x1, x2, x3, x1, x2} : bf16x8{x1, zero, zero, zero, zero, zero, zero, zero};
     }
-    float M[RB], Sl[RB], R[RB], Lb[RB][2];
+    float M[RB], Sl[RB], Sn[RB], R[RB], Lb[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       M[rb] = kDead;
       Sl[rb] = 0.f;
+      Sn[rb] = 0.f;
       R[rb] = kDead;
       Lb[rb][0] = Lb[rb][1] = kDead;
     }
@@ -940,6 +963,11 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       for (int rb = 0; rb < RB; ++rb) {
         const int64_t row = t * PT + rb * 32 + (lane & 31);
         live[rb] = row < nrows;
+        if constexpr (FUSED) {
+          // the band below the running maximum (rows past N: none)
+          thr[rb] = live[rb] ? kTopmBand + fmaf(eam, xs[rb], ea0m) + fmaf(egm, xs[rb], eg0m) : -INFINITY;
+          continue;
+        }
         mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
         R[rb] = mr[rb];
         if constexpr (MODE == 4)
@@ -974,7 +1002,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         // best other score of the row seen so far in the slice, again exactly
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          if constexpr (!MARK) {
+          if constexpr (!MARK || FUSED) {
             float r = R[rb];
 #pragma unroll
             for (int v = 0; v < 16; ++v)
@@ -992,6 +1020,39 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
             }
           }
         }
+      }
+      if constexpr (FUSED) {
+        // running maximum of the slice per row, sums rescaled to it; a
+        // component is a candidate when it comes within the row's band of
+        // that maximum (thr holds the band); Sl sums every component's mass,
+        // Sn the non-candidates' (each below 2^-20 of the maximum, so Sn keeps
+        // their sum to float32 precision)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float cm = acc[rb][0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) cm = fmaxf(cm, acc[rb][v]);
+          cm = halves_max(cm);
+          const float Mn = fmaxf(M[rb], cm);
+          const float sc = __builtin_amdgcn_exp2f(M[rb] - Mn);
+          M[rb] = Mn;
+          const float th = Mn - thr[rb];
+          uint32_t word = 0;
+          float sa = 0.f, sn = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const bool cand = acc[rb][v] >= th;  // never for rows past N (th = +inf)
+            const float e = __builtin_amdgcn_exp2f(acc[rb][v] - Mn);
+            sa += e;
+            sn += cand ? 0.f : e;
+            word |= cand ? (1u << (8 * (v >> 2) + (v & 3))) : 0u;
+          }
+          word = halves_or(word << (4 * hl));
+          Sl[rb] = fmaf(Sl[rb], sc, sa);
+          Sn[rb] = fmaf(Sn[rb], sc, sn);
+          if (lane < 32) wbuf[(rb * 32 + lane) * NCH + cc] = word;
+        }
+        continue;
       }
       if constexpr (MARK) {
         // candidates: every component whose score may lie within kTopmBand of
@@ -1069,12 +1130,17 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float S = halves_sum(Sl[rb]);
+      const float Sns = FUSED ? halves_sum(Sn[rb]) : 0.f;
       const int64_t row = t * PT + rb * 32 + lane;
       if (lane < 32 && row < nrows) {
         if constexpr (MARK) {
           // this slice's below-band mass and its 8 candidate words of the row
           const uint32_t* src = wbuf + (rb * 32 + lane) * NCH;
           float Sb = S;
+          if constexpr (FUSED) {
+            A.P[(size_t)row * A.S + slice] = float2{M[rb], S};
+            Sb = Sns;
+          }
           if constexpr (MODE == 1) {
             int nc = 0;
 #pragma unroll
@@ -1101,7 +1167,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
 constexpr int kPassARB = 2;
 
 size_t largek_pass_a_lds_bytes(int mode) {
-  const bool mark = mode == 1 || mode == 4;
+  const bool mark = mode == 1 || mode == 4 || mode == 5;
   return (size_t)(KSA / 32) * (2 * (128 / 16) + 1) * 64 * 16 + ((mark || mode == 3) ? 4 : 2) * KSA * sizeof(float) +
          (mark ? (size_t)LNW * 32 * kPassARB * (KSA / 32) * sizeof(uint32_t) : 0);
 }
@@ -1386,6 +1452,26 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
   const int nwords = A.KP / 32;
   // this lane's words of the row's candidate mask: lanes cover words lane*wpl .. +wpl-1
   const int wpl = (nwords + 63) / 64;
+  // one-pass marking: the row maximum over the slice maxima, the slices that
+  // can hold a component within the band of it, and the mass outside the
+  // candidates (as in largek_topm_final4_kernel)
+  uint64_t qm = ~0ull;
+  double mref = 0.0, remf = 0.0;
+  if (A.fused_t) {
+    float ms = kDead, sa = 0.f, sn = 0.f;
+    if (lane < A.S) {
+      const float2 pv = A.P[(size_t)row * A.S + lane];
+      ms = pv.x;
+      sa = pv.y;
+      sn = A.prem[(size_t)row * A.S + lane];
+    }
+    const float mx = (float)wave_max((double)ms);
+    const float bq = kTopmBand + 2.f * fmaf(A.egb[0], (float)A.xsq[row], A.egb[1]);
+    const bool q = lane < A.S && ms >= mx - bq;
+    qm = __builtin_amdgcn_ballot_w64(q);
+    remf = wave_sum(lane < A.S ? exp2((double)ms - (double)mx) * (double)(q ? sn : sa) : 0.0);
+    mref = mx;
+  }
   uint32_t mw[kMaskSlots];
   int mycount = 0;
 #pragma unroll
@@ -1393,6 +1479,7 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
     const int wi = lane * wpl + t;
     uint32_t wd = (t < wpl && wi < nwords) ? A.cmask[(size_t)row * nwords + wi] : 0u;
     if (wi * 32 + 32 > A.K) wd &= wi * 32 >= A.K ? 0u : (1u << (A.K - wi * 32)) - 1u;  // padding is never a candidate
+    if (!((qm >> ((wi * 32) / KSA)) & 1ull)) wd = 0u;  // a far slice
     mw[t] = wd;
     mycount += __popc(mw[t]);
   }
@@ -1550,8 +1637,8 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
     lse = L[0] + log2(S);
   } else {
     // below-band mass of every slice, relative to the expanded-form maximum
-    const double rem = wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
-    const double S = Srun + rem * exp2((double)A.mrow[row] - Mrun);
+    const double rem = A.fused_t ? remf : wave_sum(lane < A.S ? (double)A.prem[(size_t)row * A.S + lane] : 0.0);
+    const double S = Srun + rem * exp2((A.fused_t ? mref : (double)A.mrow[row]) - Mrun);
     lse = Mrun + log2(S);
   }
   if (lane == 0) {
@@ -1591,10 +1678,47 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
   const int K = A.K;
   const int nwords = A.KP / 32;
   const int64_t rc = live ? row : A.N - 1;
+  // ---- one-pass marking: the row maximum over the slice maxima, the slices
+  // that can hold a component within the band of it (slice bits qm; the
+  // others' candidates are dropped and their whole mass counted), and this
+  // lane's share of the mass outside the candidates, relative to that maximum
+  uint64_t qm = ~0ull;
+  float mref = 0.f;
+  double remf = 0.0;
+  if (A.fused_t) {
+    float ms[4], sa[4], sn[4];
+    float mx = kDead;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sl = li + 16 * j;
+      ms[j] = kDead;
+      sa[j] = sn[j] = 0.f;
+      if (sl < A.S) {
+        const float2 pv = A.P[(size_t)rc * A.S + sl];
+        ms[j] = pv.x;
+        sa[j] = pv.y;
+        sn[j] = A.prem[(size_t)rc * A.S + sl];
+      }
+      mx = fmaxf(mx, ms[j]);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+    const float bq = kTopmBand + 2.f * fmaf(A.egb[0], (float)A.xsq[rc], A.egb[1]);
+    qm = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool q = li + 16 * j < A.S && ms[j] >= mx - bq;
+      const uint64_t b = __builtin_amdgcn_ballot_w64(q);
+      qm |= ((b >> (16 * g)) & 0xFFFFull) << (16 * j);
+      remf += exp2((double)ms[j] - (double)mx) * (double)(q ? sn[j] : sa[j]);
+    }
+    mref = mx;
+  }
   // ---- candidates of the group's row: words li, li + 16, ... (coalesced per group)
   auto word_at = [&](int wi) -> uint32_t {
     uint32_t wd = A.cmask[(size_t)rc * nwords + wi];
     if (wi * 32 + 32 > K) wd &= wi * 32 >= K ? 0u : (1u << (K - wi * 32)) - 1u;  // padding is never a candidate
+    if (!((qm >> ((wi * 32) / KSA)) & 1ull)) wd = 0u;  // a far slice
     return wd;
   };
   int mycount = 0;
@@ -1693,14 +1817,16 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
         if (sc[t] > -INFINITY) ssum += exp2_acc(sc[t] - Mx);
-      double rem = 0.0;
-      for (int s = li; s < A.S; s += 16) rem += (double)A.prem[(size_t)row * A.S + s];
+      double rem = remf;
+      if (!A.fused_t)
+        for (int s = li; s < A.S; s += 16) rem += (double)A.prem[(size_t)row * A.S + s];
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) {
         ssum += __shfl_xor(ssum, off, 16);
         rem += __shfl_xor(rem, off, 16);
       }
-      lse = Mx + log2(ssum + rem * exp2((double)A.mrow[row] - Mx));
+      const double mb = A.fused_t ? (double)mref : (double)A.mrow[row];
+      lse = Mx + log2(ssum + rem * exp2(mb - Mx));
     }
     // the best m, one per round; lane j of the group keeps round j's
     double rl = -INFINITY;
@@ -1793,6 +1919,8 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
                               (int)kLdsBytes);
     (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsBytes);
+    (void)hipFuncSetAttribute((const void*)largek_pass_a_kernel<kPassARB, 5>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsBytes);
     attr_set = true;
   }
   const int64_t N = a.N;
@@ -1811,6 +1939,13 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     // component of a row is a top-k candidate
     const bool bf = p.D == 128 && ac.vec16;
     if (!bf) ac.lmx = nullptr;
+    ac.fused_t = a0.fused_t && bf && !ac.topk;
+    if (ac.fused_t) {
+      // top-m over full-width rows: one marking pass, then the rescoring
+      hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 5>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
+                         largek_pass_a_lds_bytes(5), s, ac);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
     if (bf && ac.topk)
       hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 3>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
                          largek_pass_a_lds_bytes(3), s, ac);
@@ -1831,6 +1966,7 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     else
       hipLaunchKernelGGL(kT, dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW), p.lds_t, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t nflags = (ac.N + 3) / 4;
     hipLaunchKernelGGL(largek_topm_final4_kernel, dim3((unsigned)nflags), dim3(64), 0, s, ac);
     if ((e = hipGetLastError()) != hipSuccess) return e;
