@@ -185,47 +185,66 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     kws[0] = 32;
     kws[1] = 16;
   }
-  q.T = 0;
+  // more spherical / diagonal components than one workgroup's tiling holds:
+  // blocks of kMaxWaves waves, the rows' normaliser over every block
+  // (launch_estep_blocked)
+  const bool can_block = op != GMM_OP_TOPM && (cov == SPH || cov == DIAG);
+  bool blocked = false;
   bool waves_ok = false;
-  for (int kw : kws) {
-    if ((K + kw - 1) / kw > kMaxWaves) continue;
-    waves_ok = true;
-    q.KW = kw;
-    q.NW = (K + q.KW - 1) / q.KW;
-    q.KP = q.KW * q.NW;
-    if (op == GMM_OP_TOPM) {
-      if (K > kTopmMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m supports K <= %d", kTopmMaxK);
-      const size_t T = kTopmRows, C = kTopmCap;
-      q.T = (int)T;
-      q.direct = false;
-      q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F + 3 * T) +
-              sizeof(double) * (T + (size_t)q.NW * T + T * C);
-      if (q.lds > kLdsBytes)
-        return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K, (long long)d->D);
-      break;
-    }
-    // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
-    for (int nraw : {2, 1}) {
-      if (nraw == 2 && !direct_ok) continue;
-      for (int T : {64, 32, 16}) {
-        if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
-          q.T = T;
-          q.direct = nraw == 2;
-          break;
+  for (int attempt = 0; attempt < 2 && !q.T; ++attempt) {
+    blocked = attempt == 1;
+    if (blocked && !can_block) break;
+    for (int kw : kws) {
+      const int Kc = blocked ? kw * kMaxWaves : K;  // components of one workgroup
+      if ((Kc + kw - 1) / kw > kMaxWaves) continue;
+      waves_ok = true;
+      q.KW = kw;
+      q.NW = (Kc + q.KW - 1) / q.KW;
+      q.KP = q.KW * q.NW;
+      if (op == GMM_OP_TOPM) {
+        if (K > kTopmMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m supports K <= %d", kTopmMaxK);
+        const size_t T = kTopmRows, C = kTopmCap;
+        q.T = (int)T;
+        q.direct = false;
+        q.lds = sizeof(float) * ((size_t)q.KP * q.F + T * q.FS + T * q.DP + T * C + (size_t)q.NW * T + T + q.F + 3 * T) +
+                sizeof(double) * (T + (size_t)q.NW * T + T * C);
+        if (q.lds > kLdsBytes)
+          return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld top-m tile does not fit in LDS", K, (long long)d->D);
+        break;
+      }
+      // largest tile that fits: double-buffered asynchronous row loads first, then one synchronous buffer
+      for (int nraw : {2, 1}) {
+        if (nraw == 2 && !direct_ok) continue;
+        for (int T : {64, 32, 16}) {
+          if (lds_for(T, nraw) <= kLdsBytes && estep_variant_exists(cov, q.DP, q.KW, T)) {
+            q.T = T;
+            q.direct = nraw == 2;
+            break;
+          }
         }
+        if (q.T) break;
       }
       if (q.T) break;
     }
-    if (q.T) break;
   }
   if (!waves_ok) return fail(GMM_ERR_UNSUPPORTED, "K=%d is above the single-pass window (<= %d)", K, 32 * kMaxWaves);
   if (!q.T) return fail(GMM_ERR_UNSUPPORTED, "K=%d x D=%lld does not fit in LDS", K, (long long)d->D);
   if (op != GMM_OP_TOPM) q.lds = lds_for(q.T, q.direct ? 2 : 1);
-  q.ntiles = (q.N + q.T - 1) / q.T;
+  q.KPB = q.KP;
+  q.chunk_rows = q.N;
+  if (blocked) {
+    if (K > kBlockedMaxK) return fail(GMM_ERR_UNSUPPORTED, "K=%d: spherical / diagonal components <= %d", K, kBlockedMaxK);
+    q.nblk = (K + q.KPB - 1) / q.KPB;
+    q.KP = q.nblk * q.KPB;
+    // rows in chunks (the per-row block maxima and sums are O(chunk)); a
+    // multiple of 4 keeps the chunks' float32 rows 16-byte aligned
+    q.chunk_rows = std::min<int64_t>((q.N + 3) / 4 * 4, kBlockedChunk);
+  }
+  q.ntiles = (q.chunk_rows + q.T - 1) / q.T;
   const int wg_lds = (int)std::max<size_t>(1, kLdsBytes / q.lds);
   const int wg_per_cu = std::max(1, std::min(wg_lds, 8 / q.NW));
   const int64_t total = (int64_t)kNumCU * wg_per_cu;
-  int64_t gb = std::max<int64_t>(1, total / q.B);
+  int64_t gb = std::max<int64_t>(1, total / (q.B * q.nblk));
   gb = std::min<int64_t>(gb, std::max<int64_t>(1, q.ntiles));
   q.Gb = (int)gb;
   q.llG = q.Gb;
@@ -245,6 +264,10 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     q.off_part = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb * q.KP * q.PR);
     q.off_llp = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.Gb);
     q.off_aux = o;  o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.PR);
+  }
+  if (q.nblk > 1) {
+    q.off_pb = o;   o = align_up(o + sizeof(float2) * (size_t)q.B * q.chunk_rows * q.nblk);
+    q.off_lrow = o; o = align_up(o + sizeof(float2) * (size_t)q.B * q.chunk_rows);
   }
   if (op == GMM_OP_FIT) {
     q.off_nk = o;  o = align_up(o + sizeof(double) * (size_t)q.B * K);
@@ -423,12 +446,41 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
   A.a = a;
   A.part = part;
   A.llpart = llp;
+  A.KPT = p.KP;
+  A.nblk = 1;
+  A.accumulate = 0;
+  A.ldl = 0;
+  A.pb = nullptr;
+  A.lrow = nullptr;
   if (opts && opts->event_begin) {
     e = hipEventRecord((hipEvent_t)opts->event_begin, s);
     if (e != hipSuccess) return hip_fail(e, "event record");
   }
-  e = launch_estep(p, A, s);
-  if (e != hipSuccess) return hip_fail(e, "fused E-step launch");
+  if (p.nblk > 1) {
+    // components in blocks: per chunk of rows the (max, sum) pass, the row
+    // combine and the statistics pass, the chunks' partials added up
+    A.KP = p.KPB;
+    A.nblk = p.nblk;
+    A.ldl = p.chunk_rows;
+    A.pb = reinterpret_cast<float2*>(w + p.off_pb);
+    float2* lrow = reinterpret_cast<float2*>(w + p.off_lrow);
+    A.lrow = lrow;
+    const size_t esz = p.dtype == GMM_DT_F32 ? 4 : 2;
+    for (int64_t r0 = 0; r0 < p.N; r0 += p.chunk_rows) {
+      const int64_t rows = std::min<int64_t>(p.chunk_rows, p.N - r0);
+      A.x = static_cast<const char*>(d->x) + (size_t)r0 * p.ld_x * esz;
+      A.N = rows;
+      A.ntiles = (rows + p.T - 1) / p.T;
+      A.accumulate = r0 > 0;
+      if ((e = launch_estep_blocked(p, A, 1, s)) != hipSuccess) return hip_fail(e, "blocked E-step (max, sum) launch");
+      if ((e = launch_block_combine(p.B, rows, p.nblk, p.chunk_rows, p.Gb, A.pb, lrow, llp, r0 > 0, s)) != hipSuccess)
+        return hip_fail(e, "blocked E-step row combine launch");
+      if ((e = launch_estep_blocked(p, A, 2, s)) != hipSuccess) return hip_fail(e, "blocked E-step statistics launch");
+    }
+  } else {
+    e = launch_estep(p, A, s);
+    if (e != hipSuccess) return hip_fail(e, "fused E-step launch");
+  }
   if (opts && opts->event_end) {
     e = hipEventRecord((hipEvent_t)opts->event_end, s);
     if (e != hipSuccess) return hip_fail(e, "event record");

@@ -137,12 +137,14 @@ __device__ __forceinline__ int quad_pair(int q) {
 // lower-triangular L^{-1} of Sigma = L L^T as DP x DP, zero past D.  UNROLL:
 // that product runs fully unrolled over DP (the padding contributes 0), so
 // its loads are issued together rather than one per loop trip -- for callers
-// with the registers to spare.
+// with the registers to spare.  kpt: components per problem in prec and c0
+// when that differs from A.KP (components in blocks); 0 takes A.KP.
 template <int COV, int DP, bool UNROLL = true, class Args>
-__device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D, const float* x) {
+__device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D, const float* x, int kpt = 0) {
   constexpr double kLog2e = 1.4426950408889634074;
+  const size_t KPx = kpt ? (size_t)kpt : (size_t)A.KP;  // components per problem in prec and c0
   const float* mu = A.mu + ((size_t)b * A.K + k) * D;
-  const double* P = A.prec + ((size_t)b * A.KP + k) * (size_t)A.prec_stride;
+  const double* P = A.prec + ((size_t)b * KPx + k) * (size_t)A.prec_stride;
   double q = 0.0;
   // spherical and diagonal: eight trips per unrolled body so their loads are
   // in flight together; the sum keeps its order
@@ -177,7 +179,7 @@ __device__ __forceinline__ double exact_score(const Args& A, int b, int k, int D
       q = fma(z, z, q);
     }
   }
-  return A.c0[(size_t)b * A.KP + k] - 0.5 * kLog2e * q;
+  return A.c0[(size_t)b * KPx + k] - 0.5 * kLog2e * q;
 }
 
 // ranking order of (log-score, component): higher score first, lower index on ties

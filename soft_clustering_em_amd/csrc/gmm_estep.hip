@@ -47,7 +47,12 @@
 
 namespace gmm {
 
-template <int COV, int DP, int KW, int T>
+// BM (components in blocks, see launch_estep_blocked): 0 = the whole step in
+// one launch; 1 = per (row, block) the maximum and the sum of 2^(l - max) over
+// the block's components, nothing else; 2 = responsibilities against the row's
+// maximum and log2 sum over every block (lrow), statistics added to the
+// problem's partials at the block's components.
+template <int COV, int DP, int KW, int T, int BM = 0>
 __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   constexpr int F = feat_F(COV, DP);
   constexpr int G = feat_G(COV, DP);
@@ -64,8 +69,12 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   const int wv = threadIdx.x >> 6;
   const int nthr = blockDim.x;
   const int NW = A.NW, KP = A.KP;
-  const int b = blockIdx.x / A.Gb;
+  const int b = blockIdx.x / A.Gb;  // (problem, block) when blocked
   const int g = blockIdx.x % A.Gb;
+  const int bp = BM ? b / A.nblk : b;  // the problem
+  const int jb = BM ? b % A.nblk : 0;  // its component block
+  // this launch's first component in the (B, KPT) arrays
+  const size_t kbase = BM ? (size_t)bp * A.KPT + (size_t)jb * KP : (size_t)b * KP;
   const int64_t N = A.N;
   const int D = (int)A.D;
 
@@ -79,7 +88,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 
   // ---- stage this problem's logit weights in LDS (linear copy, 16 B per lane)
   {
-    const floatx4* src = reinterpret_cast<const floatx4*>(A.W + (size_t)b * KP * F);
+    const floatx4* src = reinterpret_cast<const floatx4*>(A.W + kbase * F);
     floatx4* dst = reinterpret_cast<floatx4*>(Wl);
     const int n4 = KP * F / 4;
     for (int i = threadIdx.x; i < n4; i += nthr) dst[i] = src[i];
@@ -94,9 +103,9 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int k = wv * KW + nt * 16 + (lane & 15);
-    creg[nt] = A.c[(size_t)b * KP + k];
-    areg[nt] = (COV == SPH) ? A.a[(size_t)b * KP + k] : 0.0;
-    sharp[nt] = A.sharp[(size_t)b * KP + k] != 0;
+    creg[nt] = A.c[kbase + k];
+    areg[nt] = (COV == SPH) ? A.a[kbase + k] : 0.0;
+    sharp[nt] = A.sharp[kbase + k] != 0;
     // one decision per wave: does any of its components need the exact path
     any_sharp = any_sharp || (__builtin_amdgcn_ballot_w64(sharp[nt]) != 0);
   }
@@ -136,7 +145,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
   // ---- rows: a tile of T rows x D floats.  Direct path: the rows of a tile
   // are contiguous and 16-byte aligned, so they are copied into LDS with
   // global_load_lds_dwordx4 (one 16-byte chunk per lane, lanes in order).
-  const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)b * A.stride_b;
+  const float* xb = reinterpret_cast<const float*>(A.x) + (size_t)bp * A.stride_b;
   const int rawstride = A.direct ? D : DP;  // floats per row in the raw LDS tile
   auto issue_tile = [&](int64_t tile, float* rawbuf) {
     const int64_t row0 = tile * T;
@@ -157,7 +166,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     for (int j = threadIdx.x; j < T * DP; j += nthr) {
       const int r = j / DP, d = j % DP;
       const int64_t row = row0 + r;
-      rawbuf[j] = (row < N && d < D) ? x_value(A.x, A.xtype, (int64_t)b * A.stride_b + row * A.ld_x + d) : 0.f;
+      rawbuf[j] = (row < N && d < D) ? x_value(A.x, A.xtype, (int64_t)bp * A.stride_b + row * A.ld_x + d) : 0.f;
     }
   };
 
@@ -304,7 +313,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
           const int v = bit & 3, nt = (bit >> 2) % NT, rb = (bit >> 2) / NT;
           const int p = rb * 16 + 4 * (lane >> 4) + v;
           const int k = wv * KW + nt * 16 + (lane & 15);
-          const double e = exact_score<COV, DP>(A, b, k, D, phi + p * FS);
+          const double e = exact_score<COV, DP>(A, bp, jb * KP + k, D, phi + p * FS, BM ? A.KPT : 0);
 #pragma unroll
           for (int rb2 = 0; rb2 < RB; ++rb2)
 #pragma unroll
@@ -332,7 +341,7 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
           for (int nt = 0; nt < NT; ++nt) {
             if (sharp[nt] && (float)lg[rb][nt][v] >= m - 60.f && row0 + p < N) {
               const int k = wv * KW + nt * 16 + (lane & 15);
-              lg[rb][nt][v] = exact_score<COV, DP>(A, b, k, D, phi + p * FS);
+              lg[rb][nt][v] = exact_score<COV, DP>(A, bp, jb * KP + k, D, phi + p * FS, BM ? A.KPT : 0);
             }
           }
           m = (float)lg[rb][0][v];
@@ -357,7 +366,21 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     // (lanes 4v..4v+3) reduces with DPP and its first lane's result is
     // broadcast to the group with ds_swizzle.  Waves enter in a fixed order.
     float scale[RB][4];
-    if (NW > 1) {
+    if constexpr (BM == 2) {
+      // r = 2^(l - m_own) 2^(m_own - M - log2 S), M and log2 S of the row over every block
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int p = rb * 16 + 4 * (lane >> 4) + v;
+          const bool valid = row0 + p < N;
+          const float2 lr = A.lrow[(size_t)bp * A.ldl + (valid ? row0 + p : 0)];
+          // the exponent is <= 0 (the wave's maximum is at most the row's, log2 S >= 0)
+          // except for a wave with no live component, whose maximum was set to
+          // 0 and whose terms are all 0: the clamp keeps its scale finite
+          scale[rb][v] = valid ? __builtin_amdgcn_exp2f(fminf((mrow[rb][v] - lr.x) - lr.y, 0.f)) : 0.f;
+        }
+    } else if (NW > 1) {
       float* redm = red;            // [NW][T]
       float* reds = red + NW * T;   // [NW][T]
       if ((lane & 15) == 0)
@@ -385,8 +408,15 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
         // this wave's share of row v: 2^(m_own - M) / S
         const float mown = vq == 0 ? mrow[rb][0] : vq == 1 ? mrow[rb][1] : vq == 2 ? mrow[rb][2] : mrow[rb][3];
         const bool valid = row0 + p < N && S > 0.f;
-        const float sc = valid ? __builtin_amdgcn_exp2f(mown - M) / S : 0.f;
-        if (wv == 0 && q == 0 && valid) ll += ((double)M + (double)__builtin_amdgcn_logf(S)) * LN2;
+        // mown <= M except for a wave with no live component (mown set to 0,
+        // every term 0), where 2^(0 - M) would overflow to +inf for a row
+        // whose best score lies below -128 and 0 * inf give NaN: clamped
+        const float sc = valid ? __builtin_amdgcn_exp2f(fminf(mown - M, 0.f)) / S : 0.f;
+        if constexpr (BM == 1) {
+          if (wv == 0 && q == 0 && row0 + p < N) A.pb[((size_t)bp * A.ldl + row0 + p) * A.nblk + jb] = float2{M, S};
+        } else {
+          if (wv == 0 && q == 0 && valid) ll += ((double)M + (double)__builtin_amdgcn_logf(S)) * LN2;
+        }
         // broadcast lane 4v of the 16-lane group: and_mask 0x10, or_mask 4v
         scale[rb][0] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (0 << 5)));
         scale[rb][1] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x10 | (4 << 5)));
@@ -401,10 +431,16 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
           const int p = rb * 16 + 4 * (lane >> 4) + v;
           const bool valid = row0 + p < N;
           scale[rb][v] = valid ? 1.0f / srow[rb][v] : 0.f;
-          if ((lane & 15) == 0 && valid)
-            ll += ((double)mrow[rb][v] + (double)__builtin_amdgcn_logf(srow[rb][v])) * LN2;
+          if constexpr (BM == 1) {
+            if ((lane & 15) == 0 && valid)
+              A.pb[((size_t)bp * A.ldl + row0 + p) * A.nblk + jb] = float2{mrow[rb][v], srow[rb][v]};
+          } else {
+            if ((lane & 15) == 0 && valid)
+              ll += ((double)mrow[rb][v] + (double)__builtin_amdgcn_logf(srow[rb][v])) * LN2;
+          }
         }
     }
+    if constexpr (BM == 1) continue;  // the (max, sum) pass ends here
     // ---- responsibilities (rows past N get weight 0)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -457,10 +493,13 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
     }
   }
 
-  // ---- epilogue: this workgroup's float64 partial
-  const size_t bg = (size_t)b * A.Gb + g;
+  if constexpr (BM == 1) return;
+  // ---- epilogue: this workgroup's float64 partial (blocked: the block's
+  // components of the problem's partial, added to it after the first chunk)
+  const size_t bg = (size_t)bp * A.Gb + g;
   constexpr int PR = 2 + G;
-  double* part = A.part + bg * (size_t)KP * PR;
+  double* part = BM ? A.part + (bg * (size_t)A.KPT + (size_t)jb * KP) * PR : A.part + bg * (size_t)KP * PR;
+  const bool addp = BM == 2 && A.accumulate;
 #pragma unroll
   for (int mt = 0; mt < GM; ++mt)
 #pragma unroll
@@ -470,7 +509,8 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
       for (int v = 0; v < 4; ++v) {
         // float64 MFMA output layout: lane l holds rows l/16 + 4 v of column l%16
         const int row = mt * 16 + (lane >> 4) + 4 * v;
-        part[(size_t)k * PR + 2 + row] = sacc[mt][nt][v];
+        double* dst = &part[(size_t)k * PR + 2 + row];
+        *dst = addp ? *dst + sacc[mt][nt][v] : sacc[mt][nt][v];
       }
     }
   // N_k and sum r|x|^2: the four lanes l, l+16, l+32, l+48 hold the same component
@@ -490,28 +530,58 @@ __global__ void __launch_bounds__(512) estep_kernel(EStepArgs A) {
       s0 += red64[(k * 4 + q) * 2 + 0];
       s1 += red64[(k * 4 + q) * 2 + 1];
     }
-    part[(size_t)k * PR + 0] = s0;
-    part[(size_t)k * PR + 1] = s1;
+    part[(size_t)k * PR + 0] = addp ? part[(size_t)k * PR + 0] + s0 : s0;
+    part[(size_t)k * PR + 1] = addp ? part[(size_t)k * PR + 1] + s1 : s1;
   }
-  if (threadIdx.x == 0) {
+  if (BM == 0 && threadIdx.x == 0) {
     double s = 0.0;
     for (int q = 0; q < 64; ++q) s += red64[(size_t)KP * 8 + q];
     A.llpart[bg] = s;
   }
 }
 
-// ------------------------------------------------------------------ dispatch
-template <int COV, int DP, int KW, int T>
-static hipError_t launch_one(const Plan& p, const EStepArgs& a, hipStream_t s) {
-  auto kern = estep_kernel<COV, DP, KW, T>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    attr_set = true;
+// Variants the planner may choose: the instantiated ones whose register
+// allocation fits without spilling (checked with -Rpass-analysis=kernel-resource-usage).
+static constexpr bool variant_ok(int cov, int dp, int kw, int t) {
+  if (kw != 16 && kw != 32) return false;
+  if (t != 16 && t != 32 && t != 64) return false;
+  if (cov == SPH) {
+    if (dp == 16 || dp == 32) return !(kw == 32 && t == 64);
+    if (dp == 64) return kw == 16 || t <= 32;
+    if (dp == 128) return kw == 16 ? t <= 32 : t == 16;
+    return false;
   }
-  dim3 grid((unsigned)(p.B * p.Gb)), block((unsigned)(64 * p.NW));
-  hipLaunchKernelGGL(kern, grid, block, p.lds, s, a);
-  return hipGetLastError();
+  if (cov == DIAG) {
+    if (dp == 16 || dp == 32) return kw == 16 || t <= 32;
+    if (dp == 64) return kw == 16 ? t <= 32 : t == 16;
+    if (dp == 128) return kw == 16 && t == 16;
+    return false;
+  }
+  if (cov == FULL || cov == TIED) {
+    if (dp == 8) return t <= 32;
+    if (dp == 16) return kw == 16 && t == 16;
+    return false;
+  }
+  return false;
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int COV, int DP, int KW, int T, int BM = 0>
+static hipError_t launch_one(const Plan& p, const EStepArgs& a, hipStream_t s) {
+  if constexpr (!variant_ok(COV, DP, KW, T) || (BM != 0 && COV != SPH && COV != DIAG)) {
+    return hipErrorInvalidValue;  // never planned: not instantiated
+  } else {
+    auto kern = estep_kernel<COV, DP, KW, T, BM>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+      attr_set = true;
+    }
+    // blocked: one workgroup row group per (problem, block)
+    dim3 grid((unsigned)(p.B * (BM ? p.nblk : 1) * p.Gb)), block((unsigned)(64 * p.NW));
+    hipLaunchKernelGGL(kern, grid, block, p.lds, s, a);
+    return hipGetLastError();
+  }
 }
 
 #define GMM_T_SWITCH(COV, DP, KW)                               \
@@ -557,29 +627,88 @@ hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s) {
   }
 }
 
-// Variants the planner may choose: the instantiated ones whose register
-// allocation fits without spilling (checked with -Rpass-analysis=kernel-resource-usage).
-bool estep_variant_exists(int cov, int dp, int kw, int t) {
-  if (kw != 16 && kw != 32) return false;
-  if (t != 16 && t != 32 && t != 64) return false;
-  if (cov == SPH) {
-    if (dp == 16 || dp == 32) return !(kw == 32 && t == 64);
-    if (dp == 64) return kw == 16 || t <= 32;
-    if (dp == 128) return kw == 16 ? t <= 32 : t == 16;
-    return false;
+bool estep_variant_exists(int cov, int dp, int kw, int t) { return variant_ok(cov, dp, kw, t); }
+
+// ------------------------------------------------------------ blocked components
+// When a problem has more components than one workgroup holds, they go in
+// nblk blocks of p.NW * p.KW, each (problem, block) a problem index of the
+// launch with the rows shared (Flash-GMM Section 3's tiling, the row's
+// normaliser taken over every block): the (max, sum) pass, the row combine,
+// then the statistics pass, whose partials land at the block's components.
+#define GMM_T_SWITCH_B(COV, DP, KW, BM)                         \
+  switch (p.T) {                                                \
+    case 16: return launch_one<COV, DP, KW, 16, BM>(p, a, s);   \
+    case 32: return launch_one<COV, DP, KW, 32, BM>(p, a, s);   \
+    case 64: return launch_one<COV, DP, KW, 64, BM>(p, a, s);   \
+    default: return hipErrorInvalidValue;                       \
   }
-  if (cov == DIAG) {
-    if (dp == 16 || dp == 32) return kw == 16 || t <= 32;
-    if (dp == 64) return kw == 16 ? t <= 32 : t == 16;
-    if (dp == 128) return kw == 16 && t == 16;
-    return false;
+#define GMM_KW_SWITCH_B(COV, DP, BM)                            \
+  switch (p.KW) {                                               \
+    case 16: GMM_T_SWITCH_B(COV, DP, 16, BM)                    \
+    case 32: GMM_T_SWITCH_B(COV, DP, 32, BM)                    \
+    default: return hipErrorInvalidValue;                       \
   }
-  if (cov == FULL || cov == TIED) {
-    if (dp == 8) return t <= 32;
-    if (dp == 16) return kw == 16 && t == 16;
-    return false;
+
+template <int COV, int BM>
+static hipError_t launch_blocked_cov(const Plan& p, const EStepArgs& a, hipStream_t s) {
+  switch (p.DP) {
+    case 16: GMM_KW_SWITCH_B(COV, 16, BM)
+    case 32: GMM_KW_SWITCH_B(COV, 32, BM)
+    case 64: GMM_KW_SWITCH_B(COV, 64, BM)
+    case 128: GMM_KW_SWITCH_B(COV, 128, BM)
+    default: return hipErrorInvalidValue;
   }
-  return false;
+}
+
+hipError_t launch_estep_blocked(const Plan& p, const EStepArgs& a, int mode, hipStream_t s) {
+  if (p.cov == SPH) return mode == 1 ? launch_blocked_cov<SPH, 1>(p, a, s) : launch_blocked_cov<SPH, 2>(p, a, s);
+  if (p.cov == DIAG) return mode == 1 ? launch_blocked_cov<DIAG, 1>(p, a, s) : launch_blocked_cov<DIAG, 2>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
+// The row combine: per row the maximum M over its blocks and
+// S = sum_j S_j 2^(M_j - M) in float64, kept as (M, log2 S); the row's
+// log-likelihood (M + log2 S) ln 2 summed per workgroup in thread order into
+// its partial (added to it after the first chunk).  A row whose blocks all
+// have S_j = 0 (no live component) gets (0, +inf): responsibilities 0, and no
+// log-likelihood, as in the one-launch step.  grid: B * Gb blocks of 256.
+__global__ void __launch_bounds__(256) block_combine_kernel(int64_t N, int nblk, int64_t ldl, int Gb,
+                                                            const float2* __restrict__ pb, float2* __restrict__ lrow,
+                                                            double* __restrict__ llpart, int accumulate) {
+  constexpr double LN2 = 0.69314718055994530942;
+  __shared__ double red[256];
+  const int b = blockIdx.x / Gb, g = blockIdx.x % Gb;
+  double ll = 0.0;
+  for (int64_t row = (int64_t)g * 256 + threadIdx.x; row < N; row += (int64_t)Gb * 256) {
+    const float2* P = pb + ((size_t)b * ldl + row) * nblk;
+    float M = -INFINITY;
+    for (int j = 0; j < nblk; ++j)
+      if (P[j].y > 0.f) M = fmaxf(M, P[j].x);
+    double S = 0.0;
+    for (int j = 0; j < nblk; ++j)
+      if (P[j].y > 0.f) S += (double)P[j].y * exp2((double)P[j].x - (double)M);
+    float2 out = float2{0.f, INFINITY};
+    if (S > 0.0) {
+      const double l2 = log2(S);
+      out = float2{M, (float)l2};
+      ll += ((double)M + l2) * LN2;
+    }
+    lrow[(size_t)b * ldl + row] = out;
+  }
+  red[threadIdx.x] = ll;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+    for (int i = 0; i < 256; ++i) sum += red[i];
+    llpart[blockIdx.x] = (accumulate ? llpart[blockIdx.x] : 0.0) + sum;
+  }
+}
+
+hipError_t launch_block_combine(int64_t B, int64_t N, int nblk, int64_t ldl, int Gb, const float2* pb, float2* lrow,
+                                double* llpart, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(block_combine_kernel, dim3((unsigned)(B * Gb)), dim3(256), 0, s, N, nblk, ldl, Gb, pb, lrow,
+                     llpart, accumulate);
+  return hipGetLastError();
 }
 
 }  // namespace gmm

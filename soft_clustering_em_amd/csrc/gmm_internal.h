@@ -13,6 +13,8 @@ enum Cov { SPH = 0, DIAG = 1, TIED = 2, FULL = 3 };
 constexpr int kNumCU = 256;          // MI355X compute units (8 XCDs x 32)
 constexpr size_t kLdsBytes = 163840; // LDS per workgroup on gfx950
 constexpr int kMaxWaves = 8;         // waves per workgroup (512 threads)
+constexpr int kBlockedMaxK = 8192;   // float32-path spherical / diagonal components in blocks, at most
+constexpr int64_t kBlockedChunk = 1 << 20;  // rows per chunk of the blocked E-step
 constexpr size_t kAlign = 256;
 
 // Number of logit features F and statistic rows G for a covariance type and a
@@ -52,7 +54,13 @@ struct Plan {
   size_t off_hv = 0;                 // large-K top-m: rows handed to the heavy rescoring kernel
   size_t off_egb = 0;                // large-K top-m: the largest error bound over the components
   size_t off_err = 0;                // small-K top-m: per-component error coefficients (float2)
-  int64_t ntiles = 0;       // row tiles per problem
+  int64_t ntiles = 0;       // row tiles per problem (of a row chunk when blocked)
+  // fused path with components in blocks (float32-path rows, K above one
+  // workgroup): KP, NW and the workspace arrays cover a problem's nblk blocks
+  // of KPB components; the rows go in chunks of chunk_rows, each through the
+  // (max, sum) pass, the row combine and the statistics pass
+  int nblk = 1, KPB = 0;
+  size_t off_pb = 0, off_lrow = 0;
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
   // workspace layout (byte offsets)
@@ -78,8 +86,17 @@ struct EStepArgs {
   const double* prec;  // (B, KP, prec_stride) precisions / inverse Cholesky factors, float64
   const double* c0;    // (B, KP) log2 pi_k - 1/2 log2 det(2 pi Sigma_k)
   int prec_stride;
-  double* part;        // (B*Gb, KP, PR)
+  double* part;        // (B*Gb, KPT, PR)
   double* llpart;      // (B*Gb)
+  // Components in blocks (more than one workgroup's components): the launch's
+  // problem index runs over (problem, block), KP is one block's components and
+  // KPT a problem's (the stride of W, c, a, sharp, prec, c0 and the partials);
+  // without blocks nblk = 1 and KPT = KP.
+  int KPT, nblk;
+  int accumulate;      // blocked statistics pass: add to the partials (row chunks after the first)
+  int64_t ldl;         // row stride of pb and lrow per problem
+  float2* pb;          // blocked (max, sum) pass: (B, ldl, nblk) per row and block, max and sum of 2^(l - max)
+  const float2* lrow;  // blocked statistics pass: (B, ldl) per row, its maximum and log2 of its sum over all blocks
 };
 
 // spherical E-step for large K and bfloat16 rows (gmm_largek.hip)
@@ -262,6 +279,12 @@ hipError_t launch_kmeans_update(const void* x, int xtype, int64_t B, int64_t N, 
 
 // fused E-step + statistics (gmm_estep.hip)
 hipError_t launch_estep(const Plan& p, const EStepArgs& a, hipStream_t s);
+// blocked components: mode 1 the per-(row, block) (max, sum) pass, 2 the
+// statistics pass against the rows' combined maxima and sums (grid over
+// B * nblk * Gb workgroups); the row combine between them
+hipError_t launch_estep_blocked(const Plan& p, const EStepArgs& a, int mode, hipStream_t s);
+hipError_t launch_block_combine(int64_t B, int64_t N, int nblk, int64_t ldl, int Gb, const float2* pb, float2* lrow,
+                                double* llpart, int accumulate, hipStream_t s);
 bool estep_variant_exists(int cov, int dp, int kw, int t);
 
 // prologue / reduction / M-step (gmm_aux.hip)

@@ -165,13 +165,14 @@ def _bf16(N, D=128, B=1):
 
 
 @pytest.mark.parametrize("cov,B,D,K,ok,ok16", [
-    (_abi.COV_SPHERICAL, 1, 128, 4096, True, False),   # bf16: large-K path; half rows: the fused window (K <= 256)
-    (_abi.COV_SPHERICAL, 1, 100, 300, True, False),
-    (_abi.COV_SPHERICAL, 1, 128, 16384, True, False),
+    (_abi.COV_SPHERICAL, 1, 128, 4096, True, True),    # bf16: large-K path; half rows: the fused path in blocks
+    (_abi.COV_SPHERICAL, 1, 100, 300, True, True),
+    (_abi.COV_SPHERICAL, 1, 128, 16384, True, False),   # half rows: above the blocked window (K <= 8192)
     (_abi.COV_SPHERICAL, 1, 128, 16385, False, False),  # above the large-K window
     (_abi.COV_SPHERICAL, 1, 129, 64, False, False),     # D > 128
     (_abi.COV_SPHERICAL, 2, 64, 64, True, True),        # several problems: the fused path
-    (_abi.COV_SPHERICAL, 2, 64, 300, False, False),     # ... and its K <= 256
+    (_abi.COV_SPHERICAL, 2, 64, 300, True, True),       # ... in blocks above 256 components
+    (_abi.COV_SPHERICAL, 2, 64, 8193, False, False),    # ... up to 8192
     (_abi.COV_DIAG, 1, 64, 64, True, True),
     (_abi.COV_DIAG, 3, 128, 40, True, True),
     (_abi.COV_FULL, 1, 8, 8, True, True),
@@ -180,8 +181,10 @@ def _bf16(N, D=128, B=1):
 ])
 def test_16bit_support_window(cov, B, D, K, ok, ok16):
     """bf16 rows of one problem with spherical components take the large-K
-    path (any K); every other bf16 case and all half rows take the fused path
-    (its K and D window), the rows decoded exactly to float32."""
+    path (K <= 16384); every other bf16 case and all half rows take the fused
+    path (its K and D window: spherical and diagonal components in blocks up to
+    K = 8192, full and tied within one workgroup), the rows decoded exactly to
+    float32."""
     L = _abi.lib()
     n = L.gmm_workspace_bytes(ctypes.byref(_bf16(10_000, D=D, B=B)), K, cov, _abi.OP_FIT, 0)
     assert (n > 0) == ok

@@ -244,7 +244,8 @@ def test_component_status_flags(torch_cuda):
     np.testing.assert_allclose(mg[0, 0], out["mu"][0, 0], rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("case", ["D=129", "K=257", "full D=17", "bf16 diag K=300", "half K=300", "small ws"])
+@pytest.mark.parametrize("case", ["D=129", "K=8193", "full D=17", "full K=257", "bf16 diag K=8193", "half K=8193",
+                                  "small ws"])
 def test_errors_are_reported(torch_cuda, case):
     import soft_clustering_em_amd as g
     from soft_clustering_em_amd import _abi
@@ -252,22 +253,24 @@ def test_errors_are_reported(torch_cuda, case):
     D, K, cov, dt = 8, 4, "diag", torch.float32
     if case == "D=129":
         D = 129
-    elif case == "K=257":
-        K = 257
+    elif case == "K=8193":  # spherical and diagonal components in blocks: K <= 8192
+        K = 8193
     elif case == "full D=17":
         D, cov = 17, "full"
-    elif case == "bf16 diag K=300":  # 16-bit rows beyond spherical take the fused window (K <= 256)
-        dt, K = torch.bfloat16, 300
-    elif case == "half K=300":
-        dt, K, cov = torch.float16, 300, "spherical"
+    elif case == "full K=257":  # full and tied components: one workgroup's (K <= 256)
+        K, cov = 257, "full"
+    elif case == "bf16 diag K=8193":  # 16-bit rows beyond spherical take the fused window
+        dt, K = torch.bfloat16, 8193
+    elif case == "half K=8193":
+        dt, K, cov = torch.float16, 8193, "spherical"
     X = torch.zeros(100, D, device="cuda", dtype=dt)
     w = torch.full((1, K), 1.0 / K, device="cuda")
     mu = torch.zeros(1, K, D, device="cuda")
     cv = torch.ones(*g.cov_shape(cov, 1, K, D), device="cuda")
     ws = torch.empty(256, dtype=torch.uint8, device="cuda") if case == "small ws" else None
-    expect = {"D=129": _abi.GMM_ERR_UNSUPPORTED, "K=257": _abi.GMM_ERR_UNSUPPORTED,
-              "full D=17": _abi.GMM_ERR_UNSUPPORTED, "bf16 diag K=300": _abi.GMM_ERR_UNSUPPORTED,
-              "half K=300": _abi.GMM_ERR_UNSUPPORTED,
+    expect = {"D=129": _abi.GMM_ERR_UNSUPPORTED, "K=8193": _abi.GMM_ERR_UNSUPPORTED,
+              "full D=17": _abi.GMM_ERR_UNSUPPORTED, "full K=257": _abi.GMM_ERR_UNSUPPORTED,
+              "bf16 diag K=8193": _abi.GMM_ERR_UNSUPPORTED, "half K=8193": _abi.GMM_ERR_UNSUPPORTED,
               "small ws": _abi.GMM_ERR_WORKSPACE}[case]
     with pytest.raises(g.GmmError) as ei:
         g.gmm_fit_step(X, w, mu, cv, cov, ws=ws)
