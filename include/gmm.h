@@ -136,7 +136,16 @@ typedef struct {
 /* Bytes of workspace needed by an operation on `data` with K components of
  * type `cov` (op: GMM_OP_FIT / GMM_OP_ESTEP / GMM_OP_TOPM; m: the top-m width,
  * ignored otherwise).  Returns 0 when the arguments are invalid or the shape is
- * unsupported (the compute call then reports why).  Host-only; no HIP call. */
+ * unsupported (the compute call then reports why).  Host-only; no HIP call.
+ *
+ * Shape window of the fit / statistics calls on float32 rows (and 16-bit rows
+ * outside the bf16 large-K path): spherical and diagonal components with
+ * D <= 128 and K <= 8192, full and tied components with D <= 16 and K <= 256.
+ * Spherical and diagonal problems with more components than one workgroup
+ * holds (256; 128 for diagonal at D = 128) run their E-step in blocks of
+ * components over chunks of 2^20 rows (the rows' log-sum-exp taken over
+ * every block, Flash-GMM Section 3); their workspace then also holds two
+ * float2 per (problem, row of a chunk) and one per (problem, row, block). */
 size_t gmm_workspace_bytes(const gmm_data* data, int32_t K, int32_t cov, int32_t op, int32_t m);
 
 /* E-step with statistics (Flash-GMM Section 2; the fused, R-free form of
