@@ -185,6 +185,35 @@ static gmm_status make_plan(const gmm_data* d, int K, int cov, int op, Plan* p) 
     kws[0] = 32;
     kws[1] = 16;
   }
+  if (op == GMM_OP_TOPM && K > kTopmMaxK && (cov == SPH || cov == DIAG)) {
+    // top-m of more components than the tiled kernel holds: the exact kernel
+    // (every score in float64); the prologue's layout with 32 per wave
+    if (K > kBlockedMaxK) return fail(GMM_ERR_UNSUPPORTED, "top-m: K=%d above %d", K, kBlockedMaxK);
+    q.topm_exact = true;
+    q.op = op;
+    q.KW = 32;
+    q.NW = (K + 31) / 32;
+    q.KP = q.KW * q.NW;
+    q.T = 256;
+    q.Gb = 1;
+    q.llG = 1;
+    q.ntiles = (q.N + 255) / 256;
+    q.KPB = q.KP;
+    q.chunk_rows = q.N;
+    size_t o = 0;
+    q.off_W = o;    o = align_up(o + sizeof(float) * (size_t)q.B * q.KP * q.F);
+    q.prec_stride = (cov == SPH) ? 1 : (int)q.D;
+    q.off_prec = o; o = align_up(o + sizeof(double) * (size_t)q.B * q.KP * q.prec_stride);
+    q.off_c0 = o;   o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
+    q.off_c = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
+    q.off_a = o;    o = align_up(o + sizeof(double) * (size_t)q.B * q.KP);
+    q.off_flag = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
+    q.off_sharp = o; o = align_up(o + sizeof(int32_t) * (size_t)q.B * q.KP);
+    q.off_err = o;  o = align_up(o + sizeof(float2) * (size_t)q.B * q.KP);
+    q.ws_bytes = o;
+    *p = q;
+    return GMM_OK;
+  }
   // more spherical / diagonal components than one workgroup's tiling holds:
   // blocks of kMaxWaves waves, the rows' normaliser over every block
   // (launch_estep_blocked)
@@ -554,7 +583,7 @@ static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params
   A.resp = resp;
   A.count = count;
   A.logp = logp;
-  e = launch_topm(p, A, s);
+  e = p.topm_exact ? launch_topm_exact(p, A, s) : launch_topm(p, A, s);
   if (e != hipSuccess) return hip_fail(e, "top-m launch");
   return GMM_OK;
 }

@@ -60,6 +60,7 @@ struct Plan {
   // of KPB components; the rows go in chunks of chunk_rows, each through the
   // (max, sum) pass, the row combine and the statistics pass
   int nblk = 1, KPB = 0;
+  bool topm_exact = false;  // top-m of more spherical / diagonal components than the tiled kernel holds
   size_t off_pb = 0, off_lrow = 0;
   size_t lds = 0;           // dynamic LDS of the fused kernel
   bool direct = false;      // tiles of rows can be copied to LDS with 16-byte DMA loads
@@ -194,6 +195,9 @@ struct TopmArgs {
   float* logp;
 };
 hipError_t launch_topm(const Plan& p, const TopmArgs& a, hipStream_t s);
+// spherical / diagonal problems above kTopmMaxK components: every score
+// exactly in float64 (Plan::topm_exact)
+hipError_t launch_topm_exact(const Plan& p, const TopmArgs& a, hipStream_t s);
 
 // IVF posting lists from a soft multi-assignment (gmm_ivf.hip)
 constexpr int kIvfBlock = 4096;     // rows per walking wave

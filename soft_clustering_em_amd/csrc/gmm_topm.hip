@@ -507,6 +507,170 @@ static hipError_t launch_topm_cov(const Plan& p, const TopmArgs& a, hipStream_t 
   }
 }
 
+// ---------------------------------------------------------------- exact top-m
+// Spherical and diagonal problems with more components than the tiled kernel
+// holds (K > kTopmMaxK, float32-path rows): every score of a row exactly, in
+// float64 by direct differences, c0_k - 1/2 log2(e) sum_d P_kd (x_d - mu_kd)^2
+// (the oracle's own form), with a running log-sum-exp and the best m kept in
+// registers (score descending, index ascending: the components arrive in
+// increasing index, and an equal score never passes an earlier one).  One row
+// per thread, its values in registers; the components stream through LDS in
+// tiles of kExactTile (means as float32, precisions and constants as float64).
+// The kept ranks follow the rule of topm_kernel.  At DP = 128 a row takes two
+// lanes, each holding half its values (one row's 128 in registers spill): their
+// partial sums meet by one exchange, and both lanes, with the same score, keep
+// the same list.  grid: B * ceil(N / rows per block).
+constexpr int kExactTile = 32;
+constexpr int kExactMaxM = 16;  // the widest m the API accepts
+
+template <int DP>
+constexpr int exact_split() { return DP >= 128 ? 2 : 1; }
+
+template <int COV, int DP>
+__global__ void __launch_bounds__(256) topm_exact_kernel(TopmArgs A) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  constexpr double LN2 = 0.69314718055994530942;
+  constexpr int PS = (COV == DIAG) ? DP : 1;  // precision values per component
+  constexpr int SPLIT = exact_split<DP>();    // lanes per row
+  constexpr int DH = DP / SPLIT;              // values per lane
+  constexpr int RPB = 256 / SPLIT;            // rows per block
+  __shared__ float smu[kExactTile * DP];
+  __shared__ double sp[kExactTile * PS];
+  __shared__ double sc0[kExactTile];
+  const int nrb = (int)((A.N + RPB - 1) / RPB);
+  const int b = blockIdx.x / nrb;
+  const int half = SPLIT == 2 ? (threadIdx.x & 1) : 0;
+  const int64_t row = (int64_t)(blockIdx.x % nrb) * RPB + threadIdx.x / SPLIT;
+  const bool live = row < A.N;
+  const int D = (int)A.D, K = A.K, m = A.m;
+  const int64_t rc = live ? row : A.N - 1;
+  const int d0 = half * DH;
+  float x[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d)
+    x[d] = d0 + d < D ? x_value(A.x, A.xtype, (int64_t)b * A.stride_b + rc * A.ld_x + d0 + d) : 0.f;
+  double L[kExactMaxM];
+  int Kx[kExactMaxM];
+#pragma unroll
+  for (int j = 0; j < kExactMaxM; ++j) {
+    L[j] = -INFINITY;
+    Kx[j] = 0x7fffffff;
+  }
+  double worst = -INFINITY;  // the m-th best so far
+  int worstk = 0x7fffffff;
+  double M = -INFINITY, S = 0.0;  // running maximum and sum of 2^(score - M)
+  for (int k0 = 0; k0 < K; k0 += kExactTile) {
+    const int nk = min(kExactTile, K - k0);
+    __syncthreads();  // the previous tile is consumed
+    for (int i = threadIdx.x; i < nk * DP; i += 256) {
+      const int kk = i / DP, d = i % DP;
+      smu[i] = d < D ? A.mu[((size_t)b * K + k0 + kk) * D + d] : 0.f;
+    }
+    for (int i = threadIdx.x; i < nk * PS; i += 256) {
+      const int kk = i / PS, d = i % PS;
+      sp[i] = (COV == SPH || d < D) ? A.prec[((size_t)b * A.KP + k0 + kk) * (size_t)A.prec_stride + d] : 0.0;
+    }
+    for (int i = threadIdx.x; i < nk; i += 256) sc0[i] = A.c0[(size_t)b * A.KP + k0 + i];
+    __syncthreads();
+    for (int kk = 0; kk < nk; ++kk) {
+      double q = 0.0;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        const double t = (double)x[d] - (double)smu[kk * DP + d0 + d];
+        q = COV == DIAG ? fma(sp[kk * PS + d0 + d] * t, t, q) : fma(t, t, q);
+      }
+      if constexpr (SPLIT == 2) q += __shfl_xor(q, 1);  // the row's other half (a + b == b + a)
+      if constexpr (COV == SPH) q *= sp[kk];
+      const double sc = sc0[kk] - 0.5 * kLog2e * q;
+      const int k = k0 + kk;
+      if (!(sc > -INFINITY)) continue;  // a component without weight: no mass, never ranked
+      if (sc > M) {
+        S = S * exp2(M - sc) + 1.0;
+        M = sc;
+      } else {
+        S += exp2(sc - M);
+      }
+      if (before(sc, k, worst, worstk)) {
+        // insert into the kept list (fixed slots, so no register is indexed
+        // at run time): the new entry sinks past every better one
+        double cl = sc;
+        int ck = k;
+#pragma unroll
+        for (int j = 0; j < kExactMaxM; ++j) {
+          if (j < m && before(cl, ck, L[j], Kx[j])) {
+            const double tl = L[j];
+            const int tk = Kx[j];
+            L[j] = cl;
+            Kx[j] = ck;
+            cl = tl;
+            ck = tk;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kExactMaxM; ++j)
+          if (j == m - 1) {
+            worst = L[j];
+            worstk = Kx[j];
+          }
+      }
+    }
+  }
+  if (!live || half != 0) return;
+  const size_t o = ((size_t)b * A.N + row) * m;
+  double lse;
+  int c = 0;
+  if (A.topk) {
+    // the m best, normalised over themselves
+    double St = 0.0;
+#pragma unroll
+    for (int j = 0; j < kExactMaxM; ++j)
+      if (j < m && Kx[j] < K) St += exp2(L[j] - L[0]);
+    lse = L[0] + log2(St);
+  } else {
+    lse = M + log2(S);
+  }
+#pragma unroll
+  for (int j = 0; j < kExactMaxM; ++j) {
+    if (j >= m) break;
+    int kk = -1;
+    float rr = 0.f;
+    if (Kx[j] < K) {
+      const double r = exp2(L[j] - lse);
+      if ((A.topk || j == 0 || r >= (double)A.thr) && c == j) {
+        kk = Kx[j];
+        rr = (float)r;
+        ++c;
+      }
+    }
+    A.idx[o + j] = kk;
+    A.resp[o + j] = rr;
+  }
+  if (A.count) A.count[(size_t)b * A.N + row] = c;
+  if (A.logp) A.logp[(size_t)b * A.N + row] = (float)(lse * LN2);
+}
+
+template <int COV>
+static hipError_t launch_topm_exact_cov(const Plan& p, const TopmArgs& a, hipStream_t s) {
+  constexpr int RPB16 = 256 / exact_split<16>(), RPB128 = 256 / exact_split<128>();
+  static_assert(RPB16 == 256 && RPB128 == 128, "rows per block");
+  const int rpb = p.DP >= 128 ? RPB128 : RPB16;
+  const unsigned grid = (unsigned)(p.B * ((p.N + rpb - 1) / rpb));
+  switch (p.DP) {
+    case 16: hipLaunchKernelGGL((topm_exact_kernel<COV, 16>), dim3(grid), dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((topm_exact_kernel<COV, 32>), dim3(grid), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((topm_exact_kernel<COV, 64>), dim3(grid), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((topm_exact_kernel<COV, 128>), dim3(grid), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topm_exact(const Plan& p, const TopmArgs& a, hipStream_t s) {
+  if (p.cov == SPH) return launch_topm_exact_cov<SPH>(p, a, s);
+  if (p.cov == DIAG) return launch_topm_exact_cov<DIAG>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_topm(const Plan& p, const TopmArgs& a, hipStream_t s) {
   switch (p.cov) {
     case SPH: return launch_topm_cov<SPH>(p, a, s);

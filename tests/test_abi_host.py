@@ -288,12 +288,14 @@ def test_kmeans_workspace_and_window():
         n = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(N, D)), K)
         assert n > 0 and n % 256 == 0
         assert n >= N * 8
-    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 257) == 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 257) > 0  # the exact top-m kernel
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 8193) == 0
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64)), 0) == 0
     bf = _data(100_000, 128, dtype=_abi.DT_BF16)
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(bf), 4096) > 0
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 64) > 0
-    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 300) == 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 300) > 0
+    assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 128, B=2, dtype=_abi.DT_BF16)), 8193) == 0
     assert L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(1000, 64, dtype=_abi.DT_F16)), 200) > 0
     a = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(100_000, 32)), 64)
     b = L.gmm_kmeans_workspace_bytes(ctypes.byref(_data(200_000, 32)), 64)
@@ -310,7 +312,7 @@ def test_kmeans_rejects_bad_arguments_before_the_device():
         "centroids": ((ctypes.byref(d), 8, None, p, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
         "labels": ((ctypes.byref(d), 8, p, None, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
         "K": ((ctypes.byref(d), 0, p, p, None, None, ws, n, None), _abi.GMM_ERR_INVALID_ARG),
-        "K window": ((ctypes.byref(d), 300, p, p, None, None, ws, n, None), _abi.GMM_ERR_UNSUPPORTED),
+        "K window": ((ctypes.byref(d), 8193, p, p, None, None, ws, n, None), _abi.GMM_ERR_UNSUPPORTED),
         "ws align": ((ctypes.byref(d), 8, p, p, None, None, ctypes.c_void_p(4100), n, None), _abi.GMM_ERR_WORKSPACE),
         "ws size": ((ctypes.byref(d), 8, p, p, None, None, ws, n - 256, None), _abi.GMM_ERR_WORKSPACE),
     }

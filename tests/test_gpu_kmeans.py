@@ -62,7 +62,8 @@ def compare(label, X64, C, o, g, rtol_c=1e-6):
 
 
 @pytest.mark.parametrize("N,D,K", [(10_000, 8, 16), (5003, 7, 13), (4096, 64, 256), (2500, 128, 40),
-                                   (777, 3, 1), (1, 16, 4), (65, 33, 64)])
+                                   (777, 3, 1), (1, 16, 4), (65, 33, 64),
+                                   (6_000, 24, 700)])  # K > 256: labels from the exact top-m kernel
 def test_kmeans_step_float32_rows(torch_cuda, N, D, K):
     torch = torch_cuda
     rng = np.random.default_rng(N + 7 * D + K)

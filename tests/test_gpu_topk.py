@@ -57,7 +57,8 @@ def check(label, cov, X64, th, got, mll, topk):
 
 
 @pytest.mark.parametrize("cov", ["spherical", "diag"])
-@pytest.mark.parametrize("B,N,D,K,topk", [(1, 3001, 12, 20, 3), (3, 2000, 7, 33, 1), (2, 1500, 16, 40, 16)])
+@pytest.mark.parametrize("B,N,D,K,topk", [(1, 3001, 12, 20, 3), (3, 2000, 7, 33, 1), (2, 1500, 16, 40, 16),
+                                          (1, 4000, 10, 300, 4)])  # K > 256: the exact top-m kernel
 def test_topk_step_float32(torch_cuda, cov, B, N, D, K, topk):
     torch = torch_cuda
     rng = np.random.default_rng(N + K + topk)

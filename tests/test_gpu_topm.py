@@ -169,3 +169,27 @@ def test_topm_collapsed_component(torch_cuda, cov):
         cv = rng.uniform(1.0, 3.0, (1, K, D)).astype(np.float32)
         cv[0, 0] = 1e-6
     check_topm(torch_cuda, X, cov, w, mu, cv, m=3, thr=0.05, label=f"collapsed {cov}")
+
+
+@pytest.mark.parametrize("cov,B,N,D,K,m,thr", [("spherical", 1, 6_000, 16, 300, 4, 0.1),
+                                                ("diag", 1, 4_001, 32, 520, 4, 0.05),
+                                                ("diag", 2, 3_000, 8, 400, 16, 0.001),
+                                                ("spherical", 1, 3_000, 128, 1100, 1, 0.1)])
+def test_topm_above_the_tiled_window(torch_cuda, cov, B, N, D, K, m, thr):
+    """More spherical / diagonal components than the tiled kernel holds
+    (K > 256): every score of a row in float64 by direct differences, a running
+    log-sum-exp and the best m kept in order.  The model is one oracle EM step
+    from K random rows, so rows see a mix of near ties and clear winners."""
+    rng = np.random.default_rng(K + D + m)
+    centers = 3.0 * rng.standard_normal((B, K // 2, D))
+    lab = rng.integers(0, K // 2, (B, N))
+    X = (np.take_along_axis(centers, lab[..., None], 1) + rng.standard_normal((B, N, D))).astype(np.float32)
+    w = np.full((B, K), 1.0 / K, np.float32)
+    mu = np.stack([X[b][rng.choice(N, K, replace=False)] for b in range(B)]).astype(np.float32)
+    cv = np.ones((B, K), np.float32) if cov == "spherical" else rng.uniform(0.5, 2.0, (B, K, D)).astype(np.float32)
+    wn, mun, cvn = [], [], []
+    for b in range(B):
+        o = oracle.fit_step(cov, X[b], w[b].astype(np.float64), mu[b].astype(np.float64), cv[b].astype(np.float64))
+        wn.append(o["w"].reshape(K)), mun.append(o["mu"].reshape(K, D)), cvn.append(o["cv"].reshape(cv[b].shape))
+    w, mu, cv = (np.stack(a).astype(np.float32) for a in (wn, mun, cvn))
+    check_topm(torch_cuda, X, cov, w, mu, cv, m=m, thr=thr, label=f"{cov} B={B} K={K} m={m}", max_excluded=0.01)
