@@ -235,7 +235,11 @@ gmm_status gmm_fit_step_streamed(const gmm_data* host_data, gmm_params* inout, c
  *   count (B,N) int32, nullable          logp (B,N) float32 = log p(x_i), nullable
  * The ranking and the kept responsibilities are decided in float64 for every
  * component whose single-precision score lies within a safety band of the
- * best one.  1 <= m <= 16. */
+ * best one.  1 <= m <= 16.  Window: bf16 rows of one problem with spherical
+ * components, K <= 16384 (the large-K path); other rows, full and tied
+ * components with K <= 256 (D <= 16), spherical and diagonal components with
+ * K <= 8192 (D <= 128) -- above 256 every score of a row is computed exactly
+ * in float64 instead of through the band. */
 gmm_status gmm_predict_proba_topm(const gmm_data* data, const gmm_params* params, int32_t m,
                                   float threshold, int32_t* idx, float* resp, int32_t* count,
                                   float* logp, void* ws, size_t ws_bytes, void* stream);
@@ -275,8 +279,8 @@ gmm_status gmm_ivf_lists(int64_t B, int64_t N, int32_t m, int32_t K, const int32
  *   inertia (B) float64 out, nullable: sum_i min_k |x_i - c_k|^2 under the
  *     entering centroids.
  * Same row types and shape window as gmm_predict_proba_topm with spherical
- * components (float32 rows: K <= 256, any B; bf16 rows: B = 1, any K), and
- * N < 2^31.  Workspace: gmm_kmeans_workspace_bytes (it grows with N: the
+ * components (float32 and half rows: K <= 8192, any B; bf16 rows: B = 1,
+ * K <= 16384, or as float32 rows for several problems), and N < 2^31.  Workspace: gmm_kmeans_workspace_bytes (it grows with N: the
  * labels' posting lists and a responsibility per row).  The assignment is the
  * library's exact top-1 under equal weights and one shared variance, so its
  * labels agree with a float64 nearest-centroid search wherever the two
@@ -296,8 +300,8 @@ gmm_status gmm_kmeans_step(const gmm_data* data, int32_t K, float* centroids, in
  * mean_loglik (B) float64, nullable: the mean over rows of log sum over each
  * row's kept components of pi_k N(x | theta_k), under the entering theta.
  * Spherical and diagonal components; the top-m window (float32 rows: K <=
- * 256, any B; bf16 rows: spherical, B = 1, any K); 1 <= topk <= 16; N * topk
- * < 2^31.  The candidates of a row are the components whose score can reach
+ * 8192, any B; bf16 rows: spherical, B = 1, K <= 16384); 1 <= topk <= 16;
+ * N * topk < 2^31.  The candidates of a row are the components whose score can reach
  * a lower bound of its topk-th best score; with bf16 rows of D != 128 (or not
  * 16-byte aligned) that bound is not formed and every component of the row
  * is rescored (correct, slower).  Workspace: gmm_topk_fit_workspace_bytes (it
