@@ -36,7 +36,9 @@ def _theta(rng, cov, N, D, K):
 
 
 @pytest.mark.parametrize("cov,N,D,K", [("spherical", 5000, 8, 16), ("diag", 3001, 24, 40),
-                                       ("tied", 2000, 6, 9), ("full", 2048, 16, 32)])
+                                       ("tied", 2000, 6, 9), ("full", 2048, 16, 32),
+                                       ("diag", 4000, 20, 600),        # E-step in blocks, exact top-m
+                                       ("spherical", 3000, 128, 300)])
 def test_score_samples_predict_score(torch_cuda, cov, N, D, K):
     from soft_clustering_em_amd import estimator as est
     torch = torch_cuda

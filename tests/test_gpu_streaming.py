@@ -54,7 +54,8 @@ def pinned(torch, a):
                                                ("spherical", 3, 20_001, 16, 24, 5000),
                                                ("full", 1, 50_000, 16, 8, 7777),
                                                ("tied", 2, 30_000, 8, 6, 4096),
-                                               ("diag", 2, 9_000, 32, 40, 20_000)])
+                                               ("diag", 2, 9_000, 32, 40, 20_000),
+                                               ("spherical", 1, 60_000, 16, 300, 25_000)])  # blocks of components
 def test_streamed_step_equals_single_call_and_oracle(torch_cuda, cov, B, N, D, K, chunk):
     torch = torch_cuda
     rng = np.random.default_rng(N + K)
