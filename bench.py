@@ -317,7 +317,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ivf_bf16",
-                    choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde"])
+                    choices=["diag_large", "spherical_small", "diag_batched", "full_large", "ivf_bf16", "kde",
+                             "diag_blocked"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--streamed", type=int, default=0, metavar="CHUNK",
                     help="also time gmm_fit_step_streamed from pinned host rows in chunks of CHUNK rows "
@@ -405,7 +406,8 @@ def main():
         flops = pairs * (f32f + f64f)
         peak = PEAK_FP32_MFMA
         blend = (f32f + f64f) / (f32f / PEAK_FP32_MFMA + f64f / PEAK_FP64_MFMA)
-        kernel = "fused E-step + statistics"
+        kernel = ("fused E-step + statistics" if wl.K <= 256 else
+                  "fused E-step in blocks of components (max/sum pass, row combine, statistics pass per row chunk)")
         peak_note = (f"float32 MFMA dense peak; {f32f + f64f} algorithmic flop/pair (logits and statistics "
                      f"contractions)")
         extra = {"frac_vs_fp32_fp64_blend": flops / (k_ms * 1e-3) / 1e12 / blend,

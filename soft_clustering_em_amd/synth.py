@@ -10,6 +10,7 @@ Workloads (sizes, value distributions and initialisations):
   ivf_bf16         N=10,000,000 D=128 K=4096 bf16, 10 iterations, top-4 / 0.1
   diag_batched     B=64 x N=65,536 D=32 K=64 fp32, 15 iterations
   full_large       N=2,000,000 D=16 K=32 fp32, 20 iterations
+  diag_blocked     the diag_large recipe at K=1024 (components in blocks)
 Every size can be overridden (smaller copies are parity cases).
 
 The IVF workload stands in for the approximate-nearest-neighbour training sets
@@ -140,6 +141,13 @@ def diag_large(N=1_000_000, D=64, K=256, seed=0, iters=20, sub=10_000) -> Worklo
     cv0 = np.broadcast_to(var.astype(np.float32), (K, D)).copy()
     return Workload("diag_large", "diag", X[None], "f32", np.full((1, K), 1.0 / K, np.float32),
                     mu0[None], cv0[None], iters)
+
+
+def diag_blocked(N=1_000_000, D=64, K=1024, seed=0, iters=20, sub=10_000) -> Workload:
+    """The diag_large recipe with K = 1024 components: more than one
+    workgroup holds, so the E-step runs in blocks of components."""
+    wl = diag_large(N=N, D=D, K=K, seed=seed, iters=iters, sub=sub)
+    return Workload("diag_blocked", wl.cov, wl.X, wl.xdtype, wl.w0, wl.mu0, wl.cv0, wl.iters)
 
 
 def diag_batched(B=64, N=65_536, D=32, K=64, seed=0, iters=15) -> Workload:
@@ -287,4 +295,5 @@ WORKLOADS = {
     "ivf_bf16": ivf_bf16,
     "diag_batched": diag_batched,
     "full_large": full_large,
+    "diag_blocked": diag_blocked,
 }
