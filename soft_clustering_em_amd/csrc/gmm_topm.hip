@@ -514,13 +514,13 @@ static hipError_t launch_topm_cov(const Plan& p, const TopmArgs& a, hipStream_t 
 // (the oracle's own form), with a running log-sum-exp and the best m kept in
 // registers (score descending, index ascending: the components arrive in
 // increasing index, and an equal score never passes an earlier one).  One row
-// per thread, its values in registers; the components stream through LDS in
-// tiles of kExactTile (means as float32, precisions and constants as float64).
+// per thread, its values in registers (float64); the components stream through
+// LDS in tiles (means, precisions and constants as float64).
 // The kept ranks follow the rule of topm_kernel.  At DP = 128 a row takes two
 // lanes, each holding half its values (one row's 128 in registers spill): their
 // partial sums meet by one exchange, and both lanes, with the same score, keep
 // the same list.  grid: B * ceil(N / rows per block).
-constexpr int kExactTile = 32;
+constexpr int kExactTile = 32;  // components per LDS tile (16 at DP = 128: static LDS stays under 64 KiB)
 constexpr int kExactMaxM = 16;  // the widest m the API accepts
 
 template <int DP>
@@ -534,9 +534,10 @@ __global__ void __launch_bounds__(256) topm_exact_kernel(TopmArgs A) {
   constexpr int SPLIT = exact_split<DP>();    // lanes per row
   constexpr int DH = DP / SPLIT;              // values per lane
   constexpr int RPB = 256 / SPLIT;            // rows per block
-  __shared__ float smu[kExactTile * DP];
-  __shared__ double sp[kExactTile * PS];
-  __shared__ double sc0[kExactTile];
+  constexpr int TILE = DP >= 128 ? kExactTile / 2 : kExactTile;
+  __shared__ double smu[TILE * DP];
+  __shared__ double sp[TILE * PS];
+  __shared__ double sc0[TILE];
   const int nrb = (int)((A.N + RPB - 1) / RPB);
   const int b = blockIdx.x / nrb;
   const int half = SPLIT == 2 ? (threadIdx.x & 1) : 0;
@@ -545,10 +546,10 @@ __global__ void __launch_bounds__(256) topm_exact_kernel(TopmArgs A) {
   const int D = (int)A.D, K = A.K, m = A.m;
   const int64_t rc = live ? row : A.N - 1;
   const int d0 = half * DH;
-  float x[DH];
+  double x[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d)
-    x[d] = d0 + d < D ? x_value(A.x, A.xtype, (int64_t)b * A.stride_b + rc * A.ld_x + d0 + d) : 0.f;
+    x[d] = d0 + d < D ? (double)x_value(A.x, A.xtype, (int64_t)b * A.stride_b + rc * A.ld_x + d0 + d) : 0.0;
   double L[kExactMaxM];
   int Kx[kExactMaxM];
 #pragma unroll
@@ -559,12 +560,12 @@ __global__ void __launch_bounds__(256) topm_exact_kernel(TopmArgs A) {
   double worst = -INFINITY;  // the m-th best so far
   int worstk = 0x7fffffff;
   double M = -INFINITY, S = 0.0;  // running maximum and sum of 2^(score - M)
-  for (int k0 = 0; k0 < K; k0 += kExactTile) {
-    const int nk = min(kExactTile, K - k0);
+  for (int k0 = 0; k0 < K; k0 += TILE) {
+    const int nk = min(TILE, K - k0);
     __syncthreads();  // the previous tile is consumed
     for (int i = threadIdx.x; i < nk * DP; i += 256) {
       const int kk = i / DP, d = i % DP;
-      smu[i] = d < D ? A.mu[((size_t)b * K + k0 + kk) * D + d] : 0.f;
+      smu[i] = d < D ? (double)A.mu[((size_t)b * K + k0 + kk) * D + d] : 0.0;
     }
     for (int i = threadIdx.x; i < nk * PS; i += 256) {
       const int kk = i / PS, d = i % PS;
@@ -576,7 +577,7 @@ __global__ void __launch_bounds__(256) topm_exact_kernel(TopmArgs A) {
       double q = 0.0;
 #pragma unroll
       for (int d = 0; d < DH; ++d) {
-        const double t = (double)x[d] - (double)smu[kk * DP + d0 + d];
+        const double t = x[d] - smu[kk * DP + d0 + d];
         q = COV == DIAG ? fma(sp[kk * PS + d0 + d] * t, t, q) : fma(t, t, q);
       }
       if constexpr (SPLIT == 2) q += __shfl_xor(q, 1);  // the row's other half (a + b == b + a)
