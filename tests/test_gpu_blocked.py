@@ -203,3 +203,36 @@ def test_blocked_window_limit(torch_cuda):
         with pytest.raises(g.GmmError) as ei:
             g.gmm_fit_step(X, w, mu, cv, cov)
         assert ei.value.status == _abi.GMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("K", [64, 300])
+def test_wave_without_live_components_and_low_scores(torch_cuda, K):
+    """Components 32..255 carry weight 0, so whole waves hold no live
+    component (K = 300 adds the padding waves of its last block), and every
+    row's best log2 score lies below -128 (D = 64, unit variances, rows 1.5
+    sigma from their mean: about -190).  A wave with no live component once
+    took 2^(0 - M) = +inf as its share of such a row (NaN statistics); the step
+    must stay finite and match the oracle, the empty components flagged and
+    kept at weight 0."""
+    rng = np.random.default_rng(K)
+    N, D = 6_000, 64
+    live = np.r_[np.arange(32), np.arange(256, K)]
+    mu = (3.0 * rng.standard_normal((1, K, D))).astype(np.float32)
+    lab = rng.choice(live, N)
+    X = (mu[0][lab] + 1.5 * rng.standard_normal((N, D)))[None].astype(np.float32)
+    w = np.zeros((1, K), np.float32)
+    w[0, live] = 1.0 / len(live)
+    cv = np.ones((1, K, D), np.float32)
+    o = oracle.fit_step("diag", X[0], w[0].astype(np.float64), mu[0].astype(np.float64), cv[0].astype(np.float64))
+    _, _, lse = oracle.responsibilities("diag", X[0], w[0].astype(np.float64), mu[0].astype(np.float64),
+                                        cv[0].astype(np.float64))
+    assert np.max(lse) < -128 * np.log(2), "every row's best score below -128 in log2 units"
+    (wg, mg, cg), mll, cs = fit_step(torch_cuda, torch_cuda.from_numpy(X).cuda(), (w, mu, cv), "diag", 1, K)
+    assert np.isfinite(wg).all() and np.isfinite(mg).all() and np.isfinite(cg).all() and np.isfinite(mll).all()
+    e = param_errors("diag", 1, K, D, (wg, mg, cg), (o["w"], o["mu"], o["cv"]), o["stats"]["nk"])
+    e_ll = abs(float(mll[0]) - o["mean_ll"][0]) / abs(o["mean_ll"][0])
+    print(f"waves without live components, K={K}: mu={e['mu']:.1e} cv={e['cv']:.1e} w={e['w']:.1e} "
+          f"ll={e_ll:.1e}", flush=True)
+    assert max(e["mu"], e["cv"], e["w"], e_ll) <= TOL_F32, (e, e_ll)
+    dead = w[0] == 0
+    assert (wg.reshape(K)[dead] == 0).all() and (cs.reshape(K)[dead] == 1).all()
