@@ -521,12 +521,12 @@ static gmm_status run_estep(const Plan& p, const gmm_data* d, const gmm_params* 
 
 // The top-m launch sequence of a planned call (N >= 1, workspace checked).
 // topk != 0: the top-k mode (every row keeps its m best components, normalised
-// over them; threshold unused).  one_pass != 0 (large K): candidates are marked
-// against each slice's running maximum in one pass instead of against the row
-// maximum found by a pass of its own -- the k-means model, whose shared
-// variance puts one component of every row far above the rest, so that the
-// running maximum finds the band of the row maximum; with a softer model a
-// row's slices below its best mark many components the rescoring then scores.
+// over them; threshold unused).  one_pass != 0 (large K, m = 1, no counts or
+// log-likelihoods): k-means labels -- each row's best component alone, its
+// candidates marked against each slice's running maximum within the error
+// band in one pass instead of against the row maximum found by a pass of its
+// own, and no mass summed (the responsibility written is relative to the
+// candidates only).
 static gmm_status run_topm(const Plan& p, const gmm_data* data, const gmm_params* params, int32_t m, float threshold,
                            int32_t* idx, float* resp, int32_t* count, float* logp, void* ws, hipStream_t s,
                            int topk = 0, int one_pass = 0) {

@@ -135,10 +135,10 @@ struct LargeKArgs {
   float* mrow;          // (chunk) row maximum of the log-scores (pass B)
   uint32_t* cmask;      // (chunk, KP/32) candidate components of each row, one bit per component
   int topm;             // pass B: write mrow
-  // one-pass marking (fused_t, set by the caller for the k-means model and
-  // taken on full-width rows): P holds per (row, slice) the slice maximum and
-  // whole mass, prem the non-candidates' mass, both relative to that maximum,
-  // and egb the largest error bound over every component (slope in |x|^2,
+  // one-pass marking of each row's best component alone (fused_t, set by the
+  // caller for k-means labels and taken on full-width rows with m = 1 and no
+  // counts or log-likelihoods): P.x holds per (row, slice) the slice maximum,
+  // egb the largest error bound over every component (slope in |x|^2,
   // offset); the rescoring forms the row maximum and drops far slices
   int fused_t;
   float* egb;           // (2)

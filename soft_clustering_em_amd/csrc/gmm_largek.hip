@@ -762,21 +762,19 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // the top-m (slice max: its last kernel needs only the row maxima and pass T's
 // masses), 3 = pass A of the top-k (slice max, and per lane group the maximum
 // of score - error bound), 4 = pass T of the top-k (candidates against the
-// row's top-k threshold), 5 = the one-pass top-m marking: candidates against
-// the slice's running maximum, and per (row, slice) the slice maximum, its
-// whole mass and the mass of its non-candidates (no row maximum needed first).
+// row's top-k threshold), 5 = the one-pass marking of a row's best component
+// alone (k-means labels): candidates against the slice's running maximum, and
+// per (row, slice) the slice maximum; no mass (no row maximum needed first).
 //
-// Why mode 5 loses no candidate.  Write l~ for a two-term score and E_k(x) for
-// component k's error bound (|l~ - l| <= E_k), E_s and E_g for the largest
-// bound in slice s and over every component.  Slice s marks k when
-// l~_k >= m_run - band - E_s - E_g, m_run its running maximum at that chunk.
-// With M~ the largest slice maximum, the true row maximum is at least
-// M~ - E_g, and m_run <= M~; so every k whose true score reaches the row
-// maximum minus band has l~_k >= M~ - band - E_k - E_g and is marked.  A
-// slice whose maximum m_s lies below M~ - band - 2 E_g holds no such k at all
-// (l_k <= m_s + E_g < M~ - band - E_g); the rescoring drops its candidates and
-// counts its whole mass, the others' candidates are scored exactly and their
-// non-candidates' mass added.
+// Why mode 5 loses the best component of no row.  Write l~ for a two-term
+// score and E_k(x) for component k's error bound (|l~ - l| <= E_k), E_s and E_g
+// for the largest bound in slice s and over every component.  Slice s marks k
+// when l~_k >= m_run - E_s - E_g, m_run its running maximum at that chunk.
+// With M~ the largest slice maximum (from component j), the best component k*
+// has l~_k* >= l_k* - E_k* >= l_j - E_k* >= M~ - E_j - E_k*, and m_run <= M~;
+// so k* is marked.  A slice whose maximum m_s lies below M~ - 2 E_g cannot hold
+// k* (l_k <= m_s + E_g < M~ - E_g <= l_j); the rescoring drops its candidates
+// and scores the others' exactly.
 template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   constexpr bool FUSED = MODE == 5;
@@ -945,12 +943,11 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
       const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
       cfr[rb] = hl == 0 ? bf16x8{one, one, one, x1, x2, x3, x1, x2} : bf16x8{x1, zero, zero, zero, zero, zero, zero, zero};
     }
-    float M[RB], Sl[RB], Sn[RB], R[RB], Lb[RB][2];
+    float M[RB], Sl[RB], R[RB], Lb[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       M[rb] = kDead;
       Sl[rb] = 0.f;
-      Sn[rb] = 0.f;
       R[rb] = kDead;
       Lb[rb][0] = Lb[rb][1] = kDead;
     }
@@ -965,7 +962,7 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         live[rb] = row < nrows;
         if constexpr (FUSED) {
           // the band below the running maximum (rows past N: none)
-          thr[rb] = live[rb] ? kTopmBand + fmaf(eam, xs[rb], ea0m) + fmaf(egm, xs[rb], eg0m) : -INFINITY;
+          thr[rb] = live[rb] ? fmaf(eam, xs[rb], ea0m) + fmaf(egm, xs[rb], eg0m) : -INFINITY;
           continue;
         }
         mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
@@ -1022,11 +1019,8 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         }
       }
       if constexpr (FUSED) {
-        // running maximum of the slice per row, sums rescaled to it; a
-        // component is a candidate when it comes within the row's band of
-        // that maximum (thr holds the band); Sl sums every component's mass,
-        // Sn the non-candidates' (each below 2^-20 of the maximum, so Sn keeps
-        // their sum to float32 precision)
+        // running maximum of the slice per row; a component is a candidate
+        // when it comes within the row's error band of that maximum (thr)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           float cm = acc[rb][0];
@@ -1034,22 +1028,15 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
           for (int v = 1; v < 16; ++v) cm = fmaxf(cm, acc[rb][v]);
           cm = halves_max(cm);
           const float Mn = fmaxf(M[rb], cm);
-          const float sc = __builtin_amdgcn_exp2f(M[rb] - Mn);
           M[rb] = Mn;
           const float th = Mn - thr[rb];
           uint32_t word = 0;
-          float sa = 0.f, sn = 0.f;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const bool cand = acc[rb][v] >= th;  // never for rows past N (th = +inf)
-            const float e = __builtin_amdgcn_exp2f(acc[rb][v] - Mn);
-            sa += e;
-            sn += cand ? 0.f : e;
             word |= cand ? (1u << (8 * (v >> 2) + (v & 3))) : 0u;
           }
           word = halves_or(word << (4 * hl));
-          Sl[rb] = fmaf(Sl[rb], sc, sa);
-          Sn[rb] = fmaf(Sn[rb], sc, sn);
           if (lane < 32) wbuf[(rb * 32 + lane) * NCH + cc] = word;
         }
         continue;
@@ -1129,25 +1116,25 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float S = halves_sum(Sl[rb]);
-      const float Sns = FUSED ? halves_sum(Sn[rb]) : 0.f;
+      const float S = FUSED ? 0.f : halves_sum(Sl[rb]);
       const int64_t row = t * PT + rb * 32 + lane;
       if (lane < 32 && row < nrows) {
         if constexpr (MARK) {
-          // this slice's below-band mass and its 8 candidate words of the row
+          // this slice's below-band mass (mode 5: its maximum) and its 8
+          // candidate words of the row
           const uint32_t* src = wbuf + (rb * 32 + lane) * NCH;
-          float Sb = S;
           if constexpr (FUSED) {
-            A.P[(size_t)row * A.S + slice] = float2{M[rb], S};
-            Sb = Sns;
-          }
-          if constexpr (MODE == 1) {
-            int nc = 0;
+            A.P[(size_t)row * A.S + slice] = float2{M[rb], 0.f};
+          } else {
+            float Sb = S;
+            if constexpr (MODE == 1) {
+              int nc = 0;
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) nc += __popc(src[c]);
-            Sb = fmaxf(S - (float)nc * __builtin_amdgcn_exp2f(thr[rb] - mr[rb]), 0.f);
+              for (int c = 0; c < NCH; ++c) nc += __popc(src[c]);
+              Sb = fmaxf(S - (float)nc * __builtin_amdgcn_exp2f(thr[rb] - mr[rb]), 0.f);
+            }
+            A.prem[(size_t)row * A.S + slice] = Sb;
           }
-          A.prem[(size_t)row * A.S + slice] = Sb;
           uint4* dst = reinterpret_cast<uint4*>(A.cmask + (size_t)row * (A.KP / 32) + slice * NCH);
           dst[0] = uint4{src[0], src[1], src[2], src[3]};
           dst[1] = uint4{src[4], src[5], src[6], src[7]};
@@ -1452,24 +1439,16 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
   const int nwords = A.KP / 32;
   // this lane's words of the row's candidate mask: lanes cover words lane*wpl .. +wpl-1
   const int wpl = (nwords + 63) / 64;
-  // one-pass marking: the row maximum over the slice maxima, the slices that
-  // can hold a component within the band of it, and the mass outside the
-  // candidates (as in largek_topm_final4_kernel)
+  // one-pass marking (best component alone): the row maximum over the slice
+  // maxima and the slices that can hold the best component (as in
+  // largek_topm_final4_kernel); no mass outside the candidates
   uint64_t qm = ~0ull;
   double mref = 0.0, remf = 0.0;
   if (A.fused_t) {
-    float ms = kDead, sa = 0.f, sn = 0.f;
-    if (lane < A.S) {
-      const float2 pv = A.P[(size_t)row * A.S + lane];
-      ms = pv.x;
-      sa = pv.y;
-      sn = A.prem[(size_t)row * A.S + lane];
-    }
+    const float ms = lane < A.S ? A.P[(size_t)row * A.S + lane].x : kDead;
     const float mx = (float)wave_max((double)ms);
-    const float bq = kTopmBand + 2.f * fmaf(A.egb[0], (float)A.xsq[row], A.egb[1]);
-    const bool q = lane < A.S && ms >= mx - bq;
-    qm = __builtin_amdgcn_ballot_w64(q);
-    remf = wave_sum(lane < A.S ? exp2((double)ms - (double)mx) * (double)(q ? sn : sa) : 0.0);
+    const float bq = 2.f * fmaf(A.egb[0], (float)A.xsq[row], A.egb[1]);
+    qm = __builtin_amdgcn_ballot_w64(lane < A.S && ms >= mx - bq);
     mref = mx;
   }
   uint32_t mw[kMaskSlots];
@@ -1678,39 +1657,30 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
   const int K = A.K;
   const int nwords = A.KP / 32;
   const int64_t rc = live ? row : A.N - 1;
-  // ---- one-pass marking: the row maximum over the slice maxima, the slices
-  // that can hold a component within the band of it (slice bits qm; the
-  // others' candidates are dropped and their whole mass counted), and this
-  // lane's share of the mass outside the candidates, relative to that maximum
+  // ---- one-pass marking (best component alone): the row maximum over the
+  // slice maxima and the slices that can hold the best component (slice bits
+  // qm; the others' candidates are dropped); no mass outside the candidates
   uint64_t qm = ~0ull;
   float mref = 0.f;
-  double remf = 0.0;
+  const double remf = 0.0;
   if (A.fused_t) {
-    float ms[4], sa[4], sn[4];
+    float ms[4];
     float mx = kDead;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = li + 16 * j;
-      ms[j] = kDead;
-      sa[j] = sn[j] = 0.f;
-      if (sl < A.S) {
-        const float2 pv = A.P[(size_t)rc * A.S + sl];
-        ms[j] = pv.x;
-        sa[j] = pv.y;
-        sn[j] = A.prem[(size_t)rc * A.S + sl];
-      }
+      ms[j] = sl < A.S ? A.P[(size_t)rc * A.S + sl].x : kDead;
       mx = fmaxf(mx, ms[j]);
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-    const float bq = kTopmBand + 2.f * fmaf(A.egb[0], (float)A.xsq[rc], A.egb[1]);
+    const float bq = 2.f * fmaf(A.egb[0], (float)A.xsq[rc], A.egb[1]);
     qm = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool q = li + 16 * j < A.S && ms[j] >= mx - bq;
       const uint64_t b = __builtin_amdgcn_ballot_w64(q);
       qm |= ((b >> (16 * g)) & 0xFFFFull) << (16 * j);
-      remf += exp2((double)ms[j] - (double)mx) * (double)(q ? sn[j] : sa[j]);
     }
     mref = mx;
   }
@@ -1939,7 +1909,9 @@ hipError_t launch_largek_topm(const Plan& p, const LargeKArgs& a0, const float* 
     // component of a row is a top-k candidate
     const bool bf = p.D == 128 && ac.vec16;
     if (!bf) ac.lmx = nullptr;
-    ac.fused_t = a0.fused_t && bf && !ac.topk;
+    // the one-pass marking keeps the best component alone: a row's label, no
+    // responsibilities, counts or log-likelihoods
+    ac.fused_t = a0.fused_t && bf && !ac.topk && ac.m == 1 && !ac.count && !ac.logp;
     if (ac.fused_t) {
       // top-m over full-width rows: one marking pass, then the rescoring
       hipLaunchKernelGGL((largek_pass_a_kernel<kPassARB, 5>), dim3((unsigned)(p.S * p.GbA)), dim3(64 * LNW),
