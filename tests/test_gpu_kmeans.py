@@ -130,6 +130,31 @@ def test_kmeans_ivf_rows_sampled(torch_cuda):
         np.testing.assert_allclose(g_newC[k], want.astype(np.float32), rtol=1e-6, atol=1e-7)
 
 
+def test_kmeans_bf16_near_ties_across_slices(torch_cuda):
+    """Rows near the midpoint of two centroids whose indices lie in different
+    256-centroid slices (K = 4096, bf16 rows of 128): the best and second best
+    distances nearly tie, so each row's label rests on the candidate band of
+    the one-pass marking (the error bounds alone) and on the slice test of the
+    rescoring.  Labels equal the oracle's on every row the float64 gap
+    decides, and most rows are decided."""
+    torch = torch_cuda
+    rng = np.random.default_rng(41)
+    K, D, N = 4096, 128, 3000
+    C = rng.standard_normal((K, D)).astype(np.float32).astype(np.float64)
+    a = rng.integers(0, K, N)
+    b = (a + 256 * rng.integers(1, 16, N) + rng.integers(0, 256, N)) % K
+    X = 0.5 * (C[a] + C[b]) + 1e-3 * rng.standard_normal((N, D))
+    bits = synth.f32_to_bf16_bits(X.astype(np.float32))
+    X64 = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    o = oracle.kmeans_step((bits, "bf16"), C)
+    Xd = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    g = gpu_kmeans(torch, Xd, C)
+    ok = decided(X64, C, o[1])
+    assert ok.mean() > 0.9, ok.mean()
+    assert set(np.unique(o[0][ok] // 256).tolist()) != {0}  # labels spread over the slices
+    compare("bf16 near ties across slices", X64, C, o, (g[0][0], g[1], g[2][0], g[3][0]))
+
+
 def test_kmeans_empty_cluster_and_no_rows(torch_cuda):
     """A centroid no row is nearest to keeps its bits and counts 0; with
     N = 0 every centroid is kept, counts are 0 and the inertia is 0."""
