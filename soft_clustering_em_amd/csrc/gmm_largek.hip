@@ -766,15 +766,18 @@ __global__ void __launch_bounds__(512) largek_kernel(LargeKArgs A) {
 // alone (k-means labels): candidates against the slice's running maximum, and
 // per (row, slice) the slice maximum; no mass (no row maximum needed first).
 //
-// Why mode 5 loses the best component of no row.  Write l~ for a two-term
-// score and E_k(x) for component k's error bound (|l~ - l| <= E_k), E_s and E_g
-// for the largest bound in slice s and over every component.  Slice s marks k
-// when l~_k >= m_run - E_s - E_g, m_run its running maximum at that chunk.
-// With M~ the largest slice maximum (from component j), the best component k*
-// has l~_k* >= l_k* - E_k* >= l_j - E_k* >= M~ - E_j - E_k*, and m_run <= M~;
-// so k* is marked.  A slice whose maximum m_s lies below M~ - 2 E_g cannot hold
-// k* (l_k <= m_s + E_g < M~ - E_g <= l_j); the rescoring drops its candidates
-// and scores the others' exactly.
+// Why mode 5 loses the best component of no row.  Write E_k(x) for component
+// k's two-term error bound, E_s and E_g for the largest bound in slice s and
+// over every component.  A slice with no sharp component scores with the hi
+// weight term alone, within F = 17 times that bound (bf16 rounding of the
+// weight, 2^-9 relative, against 2^-14), a slice with one with both terms
+// (F = 1); write l~ for either score, |l~_k - l_k| <= F_s E_k.  Slice s marks k
+// when l~_k >= m_run - F_s E_s - 17 E_g, m_run its running maximum at that
+// chunk.  With M~ the largest slice maximum (from component j), the best
+// component k* has l~_k* >= l_k* - F E_k* >= l_j - F E_k* >= M~ - 17 E_j -
+// F E_k*, and m_run <= M~; so k* is marked.  A slice whose maximum m_s lies
+// below M~ - 34 E_g cannot hold k* (l_k <= m_s + 17 E_g < M~ - 17 E_g <= l_j);
+// the rescoring drops its candidates and scores the others' exactly.
 template <int RB, int MODE>
 __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   constexpr bool FUSED = MODE == 5;
@@ -882,10 +885,10 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
   // loop, so the common one carries no exact-score code
   auto rows_loop = [&](auto sharp_c) {
   constexpr bool SHARP = decltype(sharp_c)::value;
-  // weight terms per logit: the top-m's row maxima (MODE 2) take the hi term
-  // alone where no sharp component needs its exact score (pass T widens its
-  // band by that error); everything else takes hi + lo
-  constexpr int NHT = (MODE == 2 && !SHARP) ? 1 : 2;
+  // weight terms per logit: the top-m's row maxima (MODE 2) and the one-pass
+  // marking (MODE 5) take the hi term alone where no sharp component needs its
+  // exact score (the bands widen by that error); everything else takes hi + lo
+  constexpr int NHT = ((MODE == 2 || MODE == 5) && !SHARP) ? 1 : 2;
   int64_t t = g + (int64_t)A.G * wv;
   bf16x8 nxt[RB][KSTEP];
   if (t < ntiles) load_rows(t, nxt);
@@ -962,7 +965,8 @@ __global__ void __launch_bounds__(512) largek_pass_a_kernel(LargeKArgs A) {
         live[rb] = row < nrows;
         if constexpr (FUSED) {
           // the band below the running maximum (rows past N: none)
-          thr[rb] = live[rb] ? fmaf(eam, xs[rb], ea0m) + fmaf(egm, xs[rb], eg0m) : -INFINITY;
+          thr[rb] = live[rb] ? (NHT == 1 ? 17.f : 1.f) * fmaf(eam, xs[rb], ea0m) + 17.f * fmaf(egm, xs[rb], eg0m)
+                             : -INFINITY;
           continue;
         }
         mr[rb] = A.mrow[live[rb] ? row : nrows - 1];
@@ -1447,7 +1451,7 @@ __device__ __forceinline__ void topm_row_wave(const LargeKArgs& A, int64_t row, 
   if (A.fused_t) {
     const float ms = lane < A.S ? A.P[(size_t)row * A.S + lane].x : kDead;
     const float mx = (float)wave_max((double)ms);
-    const float bq = 2.f * fmaf(A.egb[0], (float)A.xsq[row], A.egb[1]);
+    const float bq = 34.f * fmaf(A.egb[0], (float)A.xsq[row], A.egb[1]);
     qm = __builtin_amdgcn_ballot_w64(lane < A.S && ms >= mx - bq);
     mref = mx;
   }
@@ -1674,7 +1678,7 @@ __global__ void __launch_bounds__(64) largek_topm_final4_kernel(LargeKArgs A) {
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-    const float bq = 2.f * fmaf(A.egb[0], (float)A.xsq[rc], A.egb[1]);
+    const float bq = 34.f * fmaf(A.egb[0], (float)A.xsq[rc], A.egb[1]);
     qm = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
